@@ -1,0 +1,290 @@
+"""Benchmark of the Gated DeltaNet layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|verify|copy]
+
+Headline (`value`): prefill tokens/s of one layer on one sequence of 4096 tokens, 16 key / 16 value
+heads, d_k = d_v = 128, bf16 activations, fp32 state, continued from a saved state (one step = one
+gdn_prefill_chunk call: conv, gates, L2 norms, chunked delta rule, gated RMSNorm, state and tail
+write-back). Input sets rotate so that the 256 MB last-level cache does not hold the step's inputs.
+
+The same run also measures, each as a sub-object of the one JSON line:
+  decode  - 36 GDN layers x 256 sequences x 1 token (one step = 36 gdn_decode_step calls), state GB/s
+  verify  - 64 sequences x (1+4) tokens with checkpoints, then accept and the commit copy
+  copy    - the O(1) state bridge: 256 records {fp32 state, conv tail} of one layer
+  cpu_baseline - the fp64 oracle on the host cores on the prefill workload
+
+Roofline: HBM-bound by algorithmic intensity (141 FLOP/B against a ridge of ~312 FLOP/B), so the
+prefill call is priced against 8 TB/s with algorithmic bytes; the counted MFMA fraction (bf16/f16
+dense peak 2.5 PFLOP/s) is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0
+
+
+def prefill_work(dims, T: int, C: int = 64):
+    """Algorithmic FLOP and HBM bytes of one prefill call over T tokens of one sequence."""
+    nk, nv, dk, dv = dims.n_k, dims.n_v, dims.d_k, dims.d_v
+    flop_tok = nv * (2 * C * (dk + 2 * dv) + 6 * dk * dv) + nk * 4 * C * dk
+    bytes_tok = 2 * (dims.conv_dim + 2 * nv * dv + 2 * nv)
+    bytes_seq = 2 * nv * dk * dv * 4 + 2 * 3 * dims.conv_dim * 2
+    return flop_tok * T, bytes_tok * T + bytes_seq
+
+
+def decode_bytes(dims):
+    """HBM bytes of one decode token of one sequence in one layer."""
+    return 2 * dims.n_v * dims.d_k * dims.d_v * 4 + 2 * 3 * dims.conv_dim * 2 + 2 * (
+        dims.conv_dim + 2 * dims.n_v * dims.d_v + 2 * dims.n_v)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_44_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per call from the committed PMC summary, if it was taken on the current kernels."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_call")
+
+
+class Timer:
+    """HIP events on the current stream (the stream the library launches on)."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            s, e = self.ev[i]
+            s.record()
+            fn(warmup + i)
+            e.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [s.elapsed_time(e) for s, e in self.ev[:steps]]
+        return float(np.mean(per)), wall * 1e3 / steps
+
+
+def bench_prefill(torch, gdn, args):
+    from gdn_inputs import SMALL, make_layer, random_state
+    from tests.gpu_helpers import act, desc_of, f32, i32, weights
+    dims = SMALL
+    T = 4096
+    nsets = 4
+    d = desc_of(dims)
+    sets = []
+    for k in range(nsets):
+        w, x, rng = make_layer(100 + k, dims, 1, T)
+        S0, tail0 = random_state(rng, dims, 1)
+        sets.append(dict(w=weights(w, dims), mixed=act(x.mixed, dims), z=act(x.z, dims), a=act(x.a, dims),
+                         b=act(x.b, dims), lens=i32(x.lens), tail=act(tail0, dims), state=f32(S0),
+                         out=torch.empty(1, T, dims.value_dim, dtype=torch.bfloat16, device="cuda"),
+                         ws=gdn.prefill_workspace(d, 1, T)))
+
+    def step(i):
+        s = sets[i % nsets]
+        gdn.prefill_chunk(d, s["w"], s["mixed"], s["z"], s["a"], s["b"], s["lens"], s["tail"], s["state"],
+                          s["out"], s["ws"])
+
+    ms_event, ms_wall = Timer(torch, args.steps).run(step, args.steps, args.warmup)
+    flop, nbytes = prefill_work(dims, T)
+    sec = ms_event / 1e3
+    achieved = nbytes / sec / 1e9
+    traffic = measured_traffic("prefill_4k")
+    res = {
+        "tokens_per_s": T / sec, "ms_per_call": ms_event, "ms_wall_per_step": ms_wall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gdn_prefill_chunk (chunk_prep + state_pass launches)",
+                     "algorithmic_bytes_per_call": nbytes, "algorithmic_flop_per_call": flop},
+        "mfma": {"achieved_tflops": flop / sec / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
+                 "frac": flop / sec / 1e12 / MFMA_PEAK_TFLOPS},
+    }
+    return res, dims, T
+
+
+def bench_decode(torch, gdn, args):
+    from gdn_inputs import NEXT, make_layer
+    from tests.gpu_helpers import act, desc_of, weights
+    dims = NEXT
+    L, B = 36, 256
+    d = desc_of(dims)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    layers = []
+    for l in range(L):
+        w, x, rng = make_layer(200 + l, dims, B, 1)
+        st = torch.empty(B, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda").normal_(0, 0.05, generator=g)
+        tl = torch.empty(B, 3, dims.conv_dim, dtype=torch.float32, device="cuda").normal_(0, 1, generator=g).bfloat16()
+        layers.append(dict(w=weights(w, dims), mixed=act(x.mixed[:, 0], dims), z=act(x.z[:, 0], dims),
+                           a=act(x.a[:, 0], dims), b=act(x.b[:, 0], dims), tail=tl, state=st,
+                           out=torch.empty(B, dims.value_dim, dtype=torch.bfloat16, device="cuda")))
+
+    def step(i):
+        for s in layers:
+            gdn.decode_step(d, s["w"], s["mixed"], s["z"], s["a"], s["b"], None, s["tail"], s["state"], s["out"])
+
+    steps = max(3, args.steps // 5)
+    ms, _ = Timer(torch, steps).run(step, steps, max(1, args.warmup // 2))
+    nbytes = L * B * decode_bytes(dims)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    traffic = measured_traffic("decode_layer_b256")
+    return {"workload": "36 GDN layers x 256 sequences x 1 token, 16/32 heads, d=128, fp32 state",
+            "tokens_per_s": B / (ms / 1e3), "ms_per_step": ms, "ms_per_layer": ms / L,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "kernel": "step_kernel (decode, T=1)",
+                         "algorithmic_bytes_per_call": nbytes / L}}
+
+
+def bench_verify(torch, gdn, args):
+    from gdn_inputs import NEXT, make_layer, random_state, verify_draws
+    from tests.gpu_helpers import act, desc_of, f32, i32, weights
+    dims = NEXT
+    B, K = 64, 4
+    T = K + 1
+    d = desc_of(dims)
+    w, x, rng = make_layer(300, dims, B, T)
+    S0, tail0 = random_state(rng, dims, B)
+    drafts, preds, _ = verify_draws(rng, B, K)
+    W = weights(w, dims)
+    pools = [(f32(S0), act(tail0, dims)) for _ in range(3)]  # 3 x 128 MiB rotate past the LLC
+    mx, zz, aa, bb = act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims)
+    ck_s = torch.empty(B, T, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda")
+    ck_t = torch.empty(B, T, 3, dims.conv_dim, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(B, T, dims.value_dim, dtype=torch.bfloat16, device="cuda")
+    dr, pr = i32(drafts), i32(preds)
+    slots = i32(np.arange(B))
+
+    def step(i):
+        sp, tp = pools[i % len(pools)]
+        gdn.verify_with_checkpoints(d, W, mx, zz, aa, bb, None, tp, sp, ck_s, ck_t, out)
+        _, _, _, ci = gdn.accept(dr, pr)
+        gdn.state_copy(d, sp, tp, slots, ck_s, ck_t, ci, B)
+
+    ms, _ = Timer(torch, args.steps).run(step, args.steps, args.warmup)
+    rec = dims.n_v * dims.d_k * dims.d_v * 4
+    tail_b = 3 * dims.conv_dim * 2
+    nbytes = B * (rec * (1 + T) + T * tail_b + 2 * (rec + tail_b))
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "64 sequences x (1+4) tokens, 16/32 heads, d=128: verify + accept + commit",
+            "ms_per_step": ms, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}
+
+
+def bench_copy(torch, gdn, args):
+    from gdn_inputs import NEXT
+    from tests.gpu_helpers import desc_of
+    dims = NEXT
+    n = 256
+    d = desc_of(dims)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    src = [(torch.empty(n, dims.n_v, dims.d_k, dims.d_v, device="cuda").normal_(generator=g),
+            torch.empty(n, 3, dims.conv_dim, device="cuda").normal_(generator=g).bfloat16()) for _ in range(2)]
+    dst = [(torch.empty_like(s), torch.empty_like(t)) for s, t in src]
+
+    def step(i):
+        (ss, st), (ds, dt) = src[i % 2], dst[i % 2]
+        gdn.state_copy(d, ds, dt, None, ss, st, None, n)
+
+    ms, _ = Timer(torch, args.steps).run(step, args.steps, args.warmup)
+    nbytes = 2 * n * gdn.state_record_bytes(d)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "256 state records (fp32 state + bf16 conv tail) of one 16/32-head layer",
+            "ms_per_call": ms, "mib": nbytes / 2 / 2 ** 20, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+
+
+def cpu_baseline():
+    """The oracle (fp64, OpenMP over value heads) on the prefill workload, on the host cores."""
+    import oracle
+    from gdn_inputs import SMALL, make_layer
+    dims = SMALL
+    T = 4096
+    w, x, rng = make_layer(100, dims, 1, T)
+    threads = oracle.default_threads()
+    best = None
+    for _ in range(2):
+        t0 = time.perf_counter()
+        oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, threads=threads)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    return {"value": T / best, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole prefill workload (1 x 4096 tokens, 16/16 heads, d=128), best of 2 runs",
+            "seconds": best}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="all")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_44_amd as gdn
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    gdn.load_library()
+    only = args.only
+
+    line = {"metric": "GDN layer prefill tokens/s (% MFMA peak); decode state GB/s (% HBM peak)",
+            "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic"}
+    if only in ("all", "prefill"):
+        pre, dims, T = bench_prefill(torch, gdn, args)
+        line.update(value=pre["tokens_per_s"], ms_per_step=pre["ms_per_call"])
+        line["config"] = {"workload": "prefill_4k: 1 sequence x 4096 tokens, 16 key / 16 value heads, d=128",
+                          "global_batch": 1, "seq_len": T, "chunk": 64, "parallelism": "single GPU"}
+        line["roofline"] = pre["roofline"]
+        line["mfma"] = pre["mfma"]
+        line["ms_wall_per_step"] = pre["ms_wall_per_step"]
+    if only in ("all", "decode"):
+        line["decode"] = bench_decode(torch, gdn, args)
+        torch.cuda.empty_cache()
+    if only in ("all", "verify"):
+        line["verify"] = bench_verify(torch, gdn, args)
+    if only in ("all", "copy"):
+        line["copy"] = bench_copy(torch, gdn, args)
+    if not args.no_cpu and only in ("all", "prefill"):
+        line["cpu_baseline"] = cpu_baseline()
+    line["kernel_hash"] = kernel_hash()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+// The C ABI of libgdn.so (declared in include/gdn.h): argument checks, then kernel launches on the
+// caller's stream. Nothing here allocates device memory or synchronises with the host.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "gdn_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err[0] = 0;
+    return GDN_OK;
+  }
+  return fail(GDN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+long conv_channels(const gdn_desc* d) { return 2L * d->n_k * d->d_k + (long)d->n_v * d->d_v; }
+
+// shape checks shared by the layer entry points
+int check_desc(const gdn_desc* d) {
+  if (!d) return fail(GDN_EINVAL, "desc is NULL");
+  if (d->n_k <= 0 || d->n_v <= 0) return fail(GDN_EINVAL, "n_k=%d n_v=%d must be positive", d->n_k, d->n_v);
+  if (d->act_dtype != GDN_BF16 && d->act_dtype != GDN_F32) return fail(GDN_EINVAL, "act_dtype=%d", d->act_dtype);
+  if (d->conv_k != 4) return fail(GDN_EUNSUPPORTED, "conv_k=%d (only 4 is built)", d->conv_k);
+  if (d->n_v % d->n_k) return fail(GDN_EUNSUPPORTED, "n_v=%d is not a multiple of n_k=%d", d->n_v, d->n_k);
+  const int R = d->n_v / d->n_k;
+  if (R != 1 && R != 2 && R != 4) return fail(GDN_EUNSUPPORTED, "GQA ratio n_v/n_k=%d (built: 1, 2, 4)", R);
+  if (d->d_k != d->d_v) return fail(GDN_EUNSUPPORTED, "d_k=%d != d_v=%d", d->d_k, d->d_v);
+  if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128)
+    return fail(GDN_EUNSUPPORTED, "d_k=%d (built: 32, 64, 128)", d->d_k);
+  if (!(d->l2_eps >= 0.f) || !(d->rms_eps >= 0.f)) return fail(GDN_EINVAL, "negative or NaN epsilon");
+  return GDN_OK;
+}
+
+float q_scale(const gdn_desc* d) { return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->d_k); }
+
+int check_weights(const gdn_weights* w) {
+  if (!w) return fail(GDN_EINVAL, "weights is NULL");
+  if (!w->conv_w || !w->A_log || !w->dt_bias || !w->norm_w) return fail(GDN_EINVAL, "a weight pointer is NULL");
+  if (!aligned16(w->conv_w)) return fail(GDN_EINVAL, "conv_w must be 16-byte aligned");
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_err; }
+
+const char* gdn_version(void) { return "gdn-mi355x 0.1 (gfx950)"; }
+
+size_t gdn_state_record_bytes(const gdn_desc* d) {
+  if (check_desc(d)) return 0;
+  const size_t act = d->act_dtype == GDN_BF16 ? 2 : 4;
+  return (size_t)d->n_v * d->d_k * d->d_v * 4 + (size_t)(d->conv_k - 1) * conv_channels(d) * act;
+}
+
+int gdn_conv_chunk(const gdn_desc* d, const void* conv_w, const void* mixed, const int32_t* len, void* conv_tail,
+                   void* y, int B, int Lb, gdn_stream_t stream) {
+  if (int rc = check_desc(d)) return rc;
+  if (!conv_w || !mixed || !len || !conv_tail || !y) return fail(GDN_EINVAL, "gdn_conv_chunk: NULL pointer");
+  if (B <= 0 || Lb <= 0) return fail(GDN_EINVAL, "gdn_conv_chunk: B=%d Lb=%d must be positive", B, Lb);
+  if (!aligned16(conv_w) || !aligned16(mixed) || !aligned16(conv_tail) || !aligned16(y))
+    return fail(GDN_EINVAL, "gdn_conv_chunk: buffers must be 16-byte aligned");
+  if (y == mixed || y == conv_tail) return fail(GDN_EINVAL, "gdn_conv_chunk: y aliases an input");
+  gdn::ConvArgs p{conv_w, mixed, len, conv_tail, y, B, Lb, (int)conv_channels(d)};
+  return hip_status(gdn::launch_conv(p, d->act_dtype, (hipStream_t)stream), "gdn_conv_chunk");
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_desc* d, int B, int Lb) {
+  if (check_desc(d) || B <= 0 || Lb <= 0) return 0;
+  const int n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
+  return gdn::prefill_ws_bytes(B, d->n_v, d->d_k, n_chunks);
+}
+
+int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
+                      const void* b, const int32_t* len, void* conv_tail, float* state, void* out, int B, int Lb,
+                      void* ws, size_t ws_bytes, gdn_stream_t stream) {
+  if (int rc = check_desc(d)) return rc;
+  if (int rc = check_weights(w)) return rc;
+  if (!mixed || !z || !a || !b || !len || !conv_tail || !state || !out || !ws)
+    return fail(GDN_EINVAL, "gdn_prefill_chunk: NULL pointer");
+  if (B <= 0 || Lb <= 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d Lb=%d must be positive", B, Lb);
+  const size_t need = gdn_prefill_workspace_bytes(d, B, Lb);
+  if (ws_bytes < need) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (((uintptr_t)ws & 255u) != 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace must be 256-byte aligned");
+  if (!aligned16(state)) return fail(GDN_EINVAL, "gdn_prefill_chunk: state must be 16-byte aligned");
+  if (out == mixed || out == z || (void*)state == out || conv_tail == out)
+    return fail(GDN_EINVAL, "gdn_prefill_chunk: out aliases another buffer");
+  gdn::PrefillArgs p{};
+  p.conv_w = w->conv_w; p.A_log = w->A_log; p.dt_bias = w->dt_bias; p.norm_w = w->norm_w;
+  p.mixed = mixed; p.z = z; p.a = a; p.b = b; p.len = len; p.tail = conv_tail; p.state = state; p.out = out;
+  p.ws = ws; p.B = B; p.Lb = Lb; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d);
+  p.n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
+  p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
+  return hip_status(gdn::launch_prefill(p, d->act_dtype, d->d_k, d->n_v / d->n_k, (hipStream_t)stream),
+                    "gdn_prefill_chunk");
+}
+
+static int step_common(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
+                       const void* b, int T, const int32_t* slot, const void* tail_in, const float* state_in,
+                       void* tail_out, float* state_out, void* out, int B, int verify, gdn_stream_t stream,
+                       const char* name) {
+  if (int rc = check_desc(d)) return rc;
+  if (int rc = check_weights(w)) return rc;
+  if (!mixed || !z || !a || !b || !tail_in || !state_in || !tail_out || !state_out || !out)
+    return fail(GDN_EINVAL, "%s: NULL pointer", name);
+  if (B <= 0 || T <= 0) return fail(GDN_EINVAL, "%s: B=%d T=%d must be positive", name, B, T);
+  if (B > 65535) return fail(GDN_EINVAL, "%s: B=%d exceeds 65535", name, B);
+  if (!aligned16(state_in) || !aligned16(state_out)) return fail(GDN_EINVAL, "%s: states must be 16-byte aligned", name);
+  gdn::StepArgs p{};
+  p.conv_w = w->conv_w; p.A_log = w->A_log; p.dt_bias = w->dt_bias; p.norm_w = w->norm_w;
+  p.mixed = mixed; p.z = z; p.a = a; p.b = b; p.slot = slot; p.tail_in = tail_in; p.state_in = state_in;
+  p.tail_out = tail_out; p.state_out = state_out; p.out = out;
+  p.B = B; p.T = T; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d); p.verify = verify;
+  p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
+  return hip_status(gdn::launch_step(p, d->act_dtype, d->d_k, d->n_v / d->n_k, (hipStream_t)stream), name);
+}
+
+int gdn_decode_step(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
+                    const void* b, const int32_t* slot, void* conv_tail_pool, float* state_pool, void* out, int B,
+                    gdn_stream_t stream) {
+  return step_common(d, w, mixed, z, a, b, 1, slot, conv_tail_pool, state_pool, conv_tail_pool, state_pool, out, B,
+                     0, stream, "gdn_decode_step");
+}
+
+int gdn_verify_with_checkpoints(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z,
+                                const void* a, const void* b, int T, const int32_t* slot, const void* conv_tail_pool,
+                                const float* state_pool, float* ckpt_state, void* ckpt_tail, void* out, int B,
+                                gdn_stream_t stream) {
+  if (ckpt_state == state_pool || ckpt_tail == conv_tail_pool)
+    return fail(GDN_EINVAL, "gdn_verify_with_checkpoints: checkpoints alias the pools");
+  return step_common(d, w, mixed, z, a, b, T, slot, conv_tail_pool, state_pool, ckpt_tail, ckpt_state, out, B, 1,
+                     stream, "gdn_verify_with_checkpoints");
+}
+
+int gdn_accept(const int32_t* drafts, const int32_t* preds, int B, int K, int32_t* m, int32_t* emitted,
+               int32_t* n_emitted, int32_t* ckpt_index, gdn_stream_t stream) {
+  if (!drafts || !preds || !m || !emitted || !n_emitted) return fail(GDN_EINVAL, "gdn_accept: NULL pointer");
+  if (B <= 0 || K < 0) return fail(GDN_EINVAL, "gdn_accept: B=%d K=%d", B, K);
+  gdn::AcceptArgs p{drafts, preds, m, emitted, n_emitted, ckpt_index, B, K};
+  return hip_status(gdn::launch_accept(p, (hipStream_t)stream), "gdn_accept");
+}
+
+int gdn_state_copy(const gdn_desc* d, float* dst_state, void* dst_tail, const int32_t* dst_idx,
+                   const float* src_state, const void* src_tail, const int32_t* src_idx, int n, gdn_stream_t stream) {
+  if (int rc = check_desc(d)) return rc;
+  if (n <= 0) return fail(GDN_EINVAL, "gdn_state_copy: n=%d must be positive", n);
+  if (n > 65535) return fail(GDN_EINVAL, "gdn_state_copy: n=%d exceeds 65535", n);
+  if ((!dst_state) != (!src_state)) return fail(GDN_EINVAL, "gdn_state_copy: state pointers must both be set or both NULL");
+  if ((!dst_tail) != (!src_tail)) return fail(GDN_EINVAL, "gdn_state_copy: tail pointers must both be set or both NULL");
+  if (!dst_state && !dst_tail) return fail(GDN_EINVAL, "gdn_state_copy: nothing to copy");
+  if ((dst_state && (dst_state == src_state)) || (dst_tail && (dst_tail == src_tail)))
+    return fail(GDN_EINVAL, "gdn_state_copy: dst aliases src");
+  if (!aligned16(dst_state) || !aligned16(src_state) || !aligned16(dst_tail) || !aligned16(src_tail))
+    return fail(GDN_EINVAL, "gdn_state_copy: buffers must be 16-byte aligned");
+  const long act = d->act_dtype == GDN_BF16 ? 2 : 4;
+  gdn::CopyArgs p{};
+  p.dst_state = dst_state; p.dst_tail = dst_tail; p.dst_idx = dst_idx;
+  p.src_state = src_state; p.src_tail = src_tail; p.src_idx = src_idx;
+  p.state_floats = (long)d->n_v * d->d_k * d->d_v;
+  p.tail_bytes = (long)(d->conv_k - 1) * conv_channels(d) * act;
+  p.n = n;
+  if (p.tail_bytes % 16) return fail(GDN_EUNSUPPORTED, "gdn_state_copy: tail record of %ld bytes", p.tail_bytes);
+  return hip_status(gdn::launch_copy(p, (hipStream_t)stream), "gdn_state_copy");
+}
+
+}  // extern "C"

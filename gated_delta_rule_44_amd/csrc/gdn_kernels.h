@@ -1,0 +1,93 @@
+// Internal launch interface between the C ABI (gdn_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kActBf16 = 0;
+constexpr int kActF32 = 1;
+
+// ---- decode / verify ------------------------------------------------------------------------------
+struct StepArgs {
+  const void* conv_w;
+  const float* A_log;
+  const float* dt_bias;
+  const float* norm_w;
+  const void* mixed;    // [B][T][C]
+  const void* z;        // [B][T][n_v*D]
+  const void* a;        // [B][T][n_v]
+  const void* b;        // [B][T][n_v]
+  const int32_t* slot;  // [B] or null
+  const void* tail_in;  // pool [*][3][C]
+  const float* state_in;  // pool [*][n_v][D][D]
+  void* tail_out;       // decode: the pool; verify: [B*T][3][C]
+  float* state_out;     // decode: the pool; verify: [B*T][n_v][D][D]
+  void* out;            // [B][T][n_v*D]
+  int B, T, n_k, n_v, C;
+  int verify;
+  float scale, l2_eps, rms_eps;
+};
+hipError_t launch_step(const StepArgs& p, int act_dtype, int D, int R, hipStream_t st);
+
+// ---- standalone conv ------------------------------------------------------------------------------
+struct ConvArgs {
+  const void* conv_w;   // [C][4]
+  const void* mixed;    // [B][Lb][C]
+  const int32_t* len;   // [B]
+  void* tail;           // [B][3][C] in/out
+  void* y;              // [B][Lb][C]
+  int B, Lb, C;
+};
+hipError_t launch_conv(const ConvArgs& p, int act_dtype, hipStream_t st);
+
+// ---- chunked prefill ------------------------------------------------------------------------------
+constexpr int kChunk = 64;
+
+struct PrefillArgs {
+  const void* conv_w;
+  const float* A_log;
+  const float* dt_bias;
+  const float* norm_w;
+  const void* mixed;    // [B][Lb][C]
+  const void* z;        // [B][Lb][n_v*D]
+  const void* a;        // [B][Lb][n_v]
+  const void* b;        // [B][Lb][n_v]
+  const int32_t* len;   // [B]
+  void* tail;           // [B][3][C] in/out
+  float* state;         // [B][n_v][D][D] in/out
+  void* out;            // [B][Lb][n_v*D]
+  void* ws;             // workspace
+  int B, Lb, n_k, n_v, C, n_chunks;
+  float scale, l2_eps, rms_eps;
+};
+size_t prefill_ws_bytes(int B, int n_v, int D, int n_chunks);
+hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hipStream_t st);
+
+// ---- state records and accept ---------------------------------------------------------------------
+struct CopyArgs {
+  float* dst_state;
+  void* dst_tail;
+  const int32_t* dst_idx;
+  const float* src_state;
+  const void* src_tail;
+  const int32_t* src_idx;
+  long state_floats;   // per record
+  long tail_bytes;     // per record
+  int n;
+};
+hipError_t launch_copy(const CopyArgs& p, hipStream_t st);
+
+struct AcceptArgs {
+  const int32_t* drafts;
+  const int32_t* preds;
+  int32_t* m;
+  int32_t* emitted;
+  int32_t* n_emitted;
+  int32_t* ckpt_index;
+  int B, K;
+};
+hipError_t launch_accept(const AcceptArgs& p, hipStream_t st);
+
+}  // namespace gdn

@@ -1,0 +1,94 @@
+// State-record copy (gather/scatter) and the accepted-prefix rule (gfx950).
+//
+// A record is {fp32 state [n_v][d_k][d_v], conv tail [3][C_ch]}: fixed size, O(1) in context length
+// (the "uni_engine.py" page: copy_cache_ copies the conv and recurrent tables in place, its bridge
+// moves only that fixed payload). The copy streams 16-byte vectors, 4 per thread in flight; grid.y
+// is the record, grid.x tiles the record's bytes.
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs p) {
+  const int i = blockIdx.y;
+  const long si = p.src_idx ? (long)p.src_idx[i] : (long)i;
+  const long di = p.dst_idx ? (long)p.dst_idx[i] : (long)i;
+  const long nstate = p.src_state ? p.state_floats / 4 : 0;   // 16-byte vectors
+  const long ntail = p.src_tail ? p.tail_bytes / 16 : 0;
+  const long base = ((long)blockIdx.x * kThreads * kUnroll) + threadIdx.x;
+  uint4 v[kUnroll];
+  // state part
+  if (base < nstate) {
+    const uint4* s = (const uint4*)(p.src_state + si * p.state_floats);
+    uint4* d = (uint4*)(p.dst_state + di * p.state_floats);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const long k = base + (long)u * kThreads;
+      if (k < nstate) v[u] = s[k];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const long k = base + (long)u * kThreads;
+      if (k < nstate) d[k] = v[u];
+    }
+  }
+  // tail part (its own block range after the state's)
+  const long nsb = (nstate + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  const long tb = (long)blockIdx.x - nsb;
+  if (tb >= 0 && ntail > 0) {
+    const long tbase = tb * kThreads * kUnroll + threadIdx.x;
+    const uint4* s = (const uint4*)((const char*)p.src_tail + si * p.tail_bytes);
+    uint4* d = (uint4*)((char*)p.dst_tail + di * p.tail_bytes);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const long k = tbase + (long)u * kThreads;
+      if (k < ntail) v[u] = s[k];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const long k = tbase + (long)u * kThreads;
+      if (k < ntail) d[k] = v[u];
+    }
+  }
+}
+
+// the "mtp/generate.py" page's accept_prefix, one sequence per thread
+__global__ void accept_kernel(AcceptArgs p) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= p.B) return;
+  const int K = p.K;
+  const int32_t* dr = p.drafts + (long)b * K;
+  const int32_t* pr = p.preds + (long)b * (K + 1);
+  int m = 0;
+  while (m < K && pr[m] == dr[m]) ++m;
+  int32_t* em = p.emitted + (long)b * (K + 1);
+  for (int i = 0; i <= K; ++i) em[i] = i < m ? dr[i] : (i == m ? pr[m] : 0);
+  p.m[b] = m;
+  p.n_emitted[b] = m + 1;
+  if (p.ckpt_index) p.ckpt_index[b] = b * (K + 1) + m;
+}
+
+}  // namespace
+
+hipError_t launch_copy(const CopyArgs& p, hipStream_t st) {
+  const long per_block = (long)kThreads * kUnroll;
+  const long nstate = p.src_state ? p.state_floats / 4 : 0;
+  const long ntail = p.src_tail ? p.tail_bytes / 16 : 0;
+  const long blocks = (nstate + per_block - 1) / per_block + (ntail + per_block - 1) / per_block;
+  if (blocks <= 0 || p.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks, p.n), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const AcceptArgs& p, hipStream_t st) {
+  if (p.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(accept_kernel, dim3((p.B + 127) / 128), dim3(128), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,168 @@
+/*
+ * gdn.h — C ABI of libgdn.so: the Gated DeltaNet (gated delta-rule) layer hot path on MI355X (gfx950).
+ *
+ * The layer (as the "qev_fast/statecache.py" page's CacheQwen35._gdn runs it on one chunk continued
+ * from a saved state): a causal depthwise conv1d + SiLU over [saved Kc inputs | chunk], the q|k|v
+ * channel split, the gates g = -exp(A_log) * softplus(a + dt_bias) and beta = sigmoid(b) with padding
+ * masked to g = 0 and beta = 0, q/k L2-normalised per key head, value head h reading key head
+ * h / (n_v / n_k), the delta rule
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = scale * S_t q_t,
+ * the fp32 final state written back in place, and the gated RMSNorm w * o / rms(o) * silu(z).
+ *
+ * Conventions shared by every entry point
+ *  - All pointers are caller-owned DEVICE buffers, contiguous, row-major (last index fastest), of
+ *    exactly the shape stated, unless marked "host". The library never allocates or frees device
+ *    memory; prefill takes a caller workspace. Buffers updated in place keep their addresses (the
+ *    "uni_engine.py" page's copy_cache_: destination storage already materialised, addresses kept).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream); nothing
+ *    synchronises with the host. A non-zero return means nothing was launched, except GDN_EHIP
+ *    which reports a launch failure; gdn_last_error() then holds a message (thread-local).
+ *  - Activation buffers (mixed, z, a, b, out, conv tails, conv_w, y) have dtype desc->act_dtype:
+ *    GDN_BF16 (bfloat16) or GDN_F32. Recurrent states and checkpoints are fp32. A_log, dt_bias and
+ *    norm_w are fp32. Lengths, slots and indices are int32.
+ *  - Index arrays living on the device (len, slot, *_idx) are not range-checked on the device: an
+ *    out-of-range value is undefined behaviour. The Python binding checks host copies first.
+ *  - State layout per sequence: [n_v][d_k][d_v] (H = S^T, the layout the statecache.py page's
+ *    StateCache allocates). Conv tail per sequence: [Kc][C_ch], Kc = conv_k - 1, oldest row first,
+ *    C_ch = 2*n_k*d_k + n_v*d_v with channels ordered [q heads | k heads | v heads], head-major.
+ *
+ * Status codes: GDN_OK = 0; GDN_EINVAL = -1 (null pointer, non-positive size, inconsistent sizes,
+ * workspace too small); GDN_EUNSUPPORTED = -2 (a shape this build has no kernel for: d_k or d_v not
+ * in {32, 64, 128}, conv_k != 4, n_v not a multiple of n_k; the caller falls back, as the
+ * statecache.py page's StateCache falls back to the plain path on _NotCached); GDN_EHIP = -3.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* gdn_stream_t; /* the same handle as hipStream_t */
+
+enum { GDN_OK = 0, GDN_EINVAL = -1, GDN_EUNSUPPORTED = -2, GDN_EHIP = -3 };
+enum { GDN_BF16 = 0, GDN_F32 = 1 };
+
+/* Layer shape and constants (host struct, read during the call only). */
+typedef struct {
+  int32_t n_k, n_v;   /* key heads, value heads; n_v % n_k == 0 */
+  int32_t d_k, d_v;   /* head dims, each in {32, 64, 128} */
+  int32_t conv_k;     /* conv kernel width; must be 4 */
+  int32_t act_dtype;  /* GDN_BF16 or GDN_F32 */
+  float scale;        /* q scale; <= 0 selects d_k^-1/2 */
+  float l2_eps;       /* q/k L2 norm: x / sqrt(sum x^2 + l2_eps) */
+  float rms_eps;      /* gated RMSNorm epsilon */
+} gdn_desc;
+
+/* Layer weights (host struct holding device pointers). */
+typedef struct {
+  const void* conv_w;   /* [C_ch][conv_k], act dtype; tap conv_k-1 meets the current token */
+  const float* A_log;   /* [n_v] */
+  const float* dt_bias; /* [n_v] */
+  const float* norm_w;  /* [d_v], shared by all value heads */
+} gdn_weights;
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* Library version string. */
+const char* gdn_version(void);
+
+/*
+ * Causal conv1d + SiLU over [conv_tail | mixed] (statecache.py page, CacheQwen35._gdn: the conv on
+ * [saved conv inputs | chunk], no bias, SiLU, the first Kc outputs dropped; then the tail copy).
+ *   mixed     [B][Lb][C_ch]   pre-conv inputs of one padded chunk per sequence
+ *   len       [B]             real lengths, 0 <= len[b] <= Lb (device)
+ *   conv_tail [B][Kc][C_ch]   in/out: replaced by rows len[b] .. len[b]+Kc-1 of [tail | mixed],
+ *                             i.e. the last Kc real inputs, old rows kept when len[b] < Kc
+ *   y         [B][Lb][C_ch]   y[t][c] = silu(sum_j conv_w[c][j] * xin[t+j][c]); rows >= len[b] are
+ *                             computed like the others and carry no meaning
+ * Must not alias: y with mixed or conv_tail.
+ */
+int gdn_conv_chunk(const gdn_desc* desc, const void* conv_w, const void* mixed, const int32_t* len,
+                   void* conv_tail, void* y, int B, int Lb, gdn_stream_t stream);
+
+/* Bytes of device workspace gdn_prefill_chunk needs for B sequences of Lb padded tokens. */
+size_t gdn_prefill_workspace_bytes(const gdn_desc* desc, int B, int Lb);
+
+/*
+ * One padded chunk per sequence through the whole layer, continued from the saved state
+ * (statecache.py page, CacheQwen35._gdn; padding gets g = 0 and beta = 0 so the state stops at the
+ * real end, as that page's module text says).
+ *   mixed [B][Lb][C_ch], z [B][Lb][n_v*d_v], a and b [B][Lb][n_v]: projected inputs
+ *   len   [B] real lengths (device), 0 <= len[b] <= Lb
+ *   conv_tail [B][Kc][C_ch] in/out (as gdn_conv_chunk); state [B][n_v][d_k][d_v] fp32 in/out
+ *   out   [B][Lb][n_v*d_v] gated-RMSNorm output; rows >= len[b] carry no meaning
+ *   ws    device workspace of at least gdn_prefill_workspace_bytes(desc, B, Lb) bytes, 256-aligned;
+ *         its contents on entry do not matter and are garbage on return
+ * Must not alias: out with any input; state or conv_tail with anything else.
+ */
+int gdn_prefill_chunk(const gdn_desc* desc, const gdn_weights* w, const void* mixed, const void* z,
+                      const void* a, const void* b, const int32_t* len, void* conv_tail, float* state,
+                      void* out, int B, int Lb, void* ws, size_t ws_bytes, gdn_stream_t stream);
+
+/*
+ * One decode token for each of B sequences (the recurrence with Lb = len = 1).
+ *   mixed [B][C_ch], z [B][n_v*d_v], a and b [B][n_v]
+ *   slot  [B] rows of the pools that sequence b owns (device), or NULL for slot[b] = b; slots must
+ *         be distinct
+ *   conv_tail_pool [*][Kc][C_ch], state_pool [*][n_v][d_k][d_v]: row slot[b] updated in place
+ *   out   [B][n_v*d_v]
+ */
+int gdn_decode_step(const gdn_desc* desc, const gdn_weights* w, const void* mixed, const void* z,
+                    const void* a, const void* b, const int32_t* slot, void* conv_tail_pool,
+                    float* state_pool, void* out, int B, gdn_stream_t stream);
+
+/*
+ * Verify with per-token checkpoints (the "mtp/generate.py" page: forward_with_hidden_stepwise runs
+ * the verify tokens one at a time and snapshots the cache after each; its batched multistate
+ * kernel captures the same per-token states in one pass). T tokens per sequence run one at a time,
+ * with exactly the decode-step arithmetic, from the pool row slot[b], which is NOT modified.
+ *   mixed [B][T][C_ch], z [B][T][n_v*d_v], a and b [B][T][n_v], slot as in gdn_decode_step
+ *   ckpt_state [B][T][n_v][d_k][d_v]: state after tokens 0..i (checkpoint i)
+ *   ckpt_tail  [B][T][Kc][C_ch]:      conv tail after tokens 0..i
+ *   out        [B][T][n_v*d_v]
+ * Checkpoint i is bitwise equal to i+1 gdn_decode_step calls on the same inputs.
+ */
+int gdn_verify_with_checkpoints(const gdn_desc* desc, const gdn_weights* w, const void* mixed,
+                                const void* z, const void* a, const void* b, int T, const int32_t* slot,
+                                const void* conv_tail_pool, const float* state_pool, float* ckpt_state,
+                                void* ckpt_tail, void* out, int B, gdn_stream_t stream);
+
+/*
+ * Accepted prefix of a speculative verify (mtp/generate.py page: accept_prefix, and its caller's
+ * emitted tokens drafts[:m] + [preds[m]]). Integer work, bit-exact.
+ *   drafts [B][K], preds [B][K+1] (device)
+ *   m [B]          longest prefix length with preds[j] == drafts[j], j < K
+ *   emitted [B][K+1]  drafts[:m], then preds[m], then zeros
+ *   n_emitted [B]  m + 1
+ *   ckpt_index [B] b*(K+1) + m: the verify checkpoint row (of [B*(K+1)] records when the verify
+ *                  ran T = K+1 tokens) to restore; may be NULL
+ */
+int gdn_accept(const int32_t* drafts, const int32_t* preds, int B, int K, int32_t* m, int32_t* emitted,
+               int32_t* n_emitted, int32_t* ckpt_index, gdn_stream_t stream);
+
+/*
+ * Copy n fixed-size state records {fp32 state [n_v][d_k][d_v], conv tail [Kc][C_ch]} — O(1) in
+ * context length (uni_engine.py page: copy_cache_, cache_payload_bytes, the bridge). Record i goes
+ * from src row src_idx[i] (or i when src_idx is NULL) to dst row dst_idx[i] (or i). Either tail
+ * pointer pair may be NULL to copy states only; both state pointers may be NULL to copy tails only.
+ * Destination rows must be distinct and must not overlap source rows read by the same call.
+ * Commit after verify = gdn_state_copy from the checkpoint records (src_idx = ckpt_index) into the
+ * pools (dst_idx = slot).
+ */
+int gdn_state_copy(const gdn_desc* desc, float* dst_state, void* dst_tail, const int32_t* dst_idx,
+                   const float* src_state, const void* src_tail, const int32_t* src_idx, int n,
+                   gdn_stream_t stream);
+
+/* Bytes of one state record: n_v*d_k*d_v*4 + Kc*C_ch*sizeof(act) (uni_engine.py page,
+ * cache_payload_bytes per sequence per layer). */
+size_t gdn_state_record_bytes(const gdn_desc* desc);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

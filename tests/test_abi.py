@@ -1,0 +1,81 @@
+"""Host-side checks of libgdn.so: it loads, exports every entry point include/gdn.h declares, and its
+argument checks reject bad calls before any device work (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_44_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gdn.load_library()
+    names = _declared()
+    assert "gdn_prefill_chunk" in names and "gdn_decode_step" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/gdn.h but not exported"
+    assert set(names) == set(gdn.EXPORTS)
+
+
+def test_version_string():
+    assert "gfx950" in gdn.version()
+
+
+def _desc(**kw):
+    base = dict(n_k=2, n_v=4, d_k=32, d_v=32)
+    base.update(kw)
+    return gdn.GdnDesc(**base).c()
+
+
+def test_unsupported_shapes_are_reported():
+    lib = gdn.load_library()
+    for kw in (dict(d_k=48, d_v=48), dict(conv_k=3), dict(n_v=6, n_k=4), dict(n_k=1, n_v=8), dict(d_k=64, d_v=32)):
+        d = _desc(**kw)
+        rc = lib.gdn_conv_chunk(ctypes.byref(d), None, None, None, None, None, 1, 1, None)
+        assert rc == -2, (kw, rc)
+        assert lib.gdn_last_error()
+
+
+def test_null_and_size_errors():
+    lib = gdn.load_library()
+    d = _desc()
+    assert lib.gdn_conv_chunk(ctypes.byref(d), None, None, None, None, None, 1, 1, None) == -1
+    assert b"NULL" in lib.gdn_last_error()
+    p = ctypes.c_void_p(256)
+    assert lib.gdn_conv_chunk(ctypes.byref(d), p, p, p, ctypes.c_void_p(512), ctypes.c_void_p(768), 0, 4, None) == -1
+    assert lib.gdn_accept(None, None, 4, 4, None, None, None, None, None) == -1
+    assert lib.gdn_state_copy(ctypes.byref(d), None, None, None, None, None, None, 1, None) == -1
+    assert lib.gdn_state_copy(ctypes.byref(d), p, None, None, p, None, None, 1, None) == -1  # aliasing
+    w = gdn._Weights(256, 512, 768, 1024)
+    # workspace too small is caught before any launch
+    rc = lib.gdn_prefill_chunk(ctypes.byref(d), ctypes.byref(w), p, p, p, p, p, p, ctypes.c_void_p(4096),
+                               ctypes.c_void_p(8192), 1, 64, ctypes.c_void_p(1 << 20), 16, None)
+    assert rc == -1 and b"workspace" in lib.gdn_last_error()
+
+
+def test_sizes():
+    lib = gdn.load_library()
+    d = gdn.GdnDesc(n_k=16, n_v=32, d_k=128, d_v=128)
+    assert gdn.state_record_bytes(d) == 32 * 128 * 128 * 4 + 3 * 8192 * 2
+    n = gdn.prefill_workspace_bytes(d, 2, 100)
+    assert n > 0 and n % 256 == 0
+    assert gdn.prefill_workspace_bytes(d, 2, 128) == n  # 100 and 128 tokens both take two chunks
+
+
+def test_python_layer_rejects_cpu_tensors():
+    import torch
+    d = gdn.GdnDesc(n_k=2, n_v=4, d_k=32, d_v=32)
+    x = torch.zeros(1, 4, d.conv_dim, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError):
+        gdn.conv_chunk(d, torch.zeros(d.conv_dim, 4, dtype=torch.bfloat16), x, torch.ones(1, dtype=torch.int32),
+                       torch.zeros(1, 3, d.conv_dim, dtype=torch.bfloat16))

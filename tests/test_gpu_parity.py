@@ -1,0 +1,282 @@
+"""GPU parity: every libgdn entry point against the fp64 oracle on the same seeded inputs.
+
+Run on an MI355X: python -u -m pytest tests -m gpu -x -v --timeout 300 --timeout-method thread
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_44_amd as gdn
+from gdn_inputs import (ACT_BF16, ACT_F32, NEXT, SMALL, TINY, LayerDims, chunk_lengths, make_layer, random_state,
+                        verify_draws)
+from tests.gpu_helpers import (act, assert_out_close, assert_state_close, desc_of, f32, host, i32, out_excess,
+                               state_rel_err, weights)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    gdn.load_library()
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------------------------------------------
+# prefill
+
+def _prefill_case(dims: LayerDims, seed, B, L, lens, state_std=0.0, tail_rand=False, sample=None):
+    _say(f"prefill seed={seed} B={B} L={L} lens={list(lens)[:4]} dims={dims}")
+    w, x, rng = make_layer(seed, dims, B, L, lens)
+    H0 = (rng.standard_normal(dims.state_shape(B)) * state_std).astype(np.float32)
+    t0 = random_state(rng, dims, B)[1] if tail_rand else np.zeros(dims.tail_shape(B), np.float32)
+    d = desc_of(dims)
+    tail = act(t0, dims)
+    st = f32(H0)
+    out = gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims),
+                            act(x.b, dims), i32(x.lens), tail, st)
+    torch.cuda.synchronize()
+    idx = range(B) if sample is None else sample
+    od = oracle.Dims.of(dims)
+    for s in idx:
+        n = int(x.lens[s])
+        ref = oracle.layer_forward(od, w, x.mixed[s:s + 1], x.z[s:s + 1], x.a[s:s + 1], x.b[s:s + 1],
+                                   x.lens[s:s + 1], t0[s:s + 1], H0[s:s + 1])
+        assert_out_close(host(out[s, :n]), ref["out"][0, :n], dims, f"out[seq {s}]")
+        assert_state_close(host(st[s]), ref["H"][0], f"state[seq {s}]")
+        np.testing.assert_array_equal(host(tail[s]), ref["tail"][0].astype(np.float32))
+    return out, st, tail
+
+
+def test_prefill_tiny_fp32():
+    """The tiny CPU-checkable layer: T=64, 2 key / 4 value heads, d=32, fp32 I/O."""
+    _prefill_case(TINY, 0, 1, 64, [64])
+
+
+@pytest.mark.parametrize("D,R", [(32, 2), (64, 1), (128, 2), (128, 4)])
+def test_prefill_ragged_multichunk(D, R):
+    """Several chunks with a ragged tail and a padded sequence, from a non-zero state and tail."""
+    dims = LayerDims(n_k=2, n_v=2 * R, d_k=D, d_v=D)
+    _prefill_case(dims, 3, 3, 300, [300, 171, 1], state_std=0.05, tail_rand=True)
+
+
+def test_prefill_fp32_multichunk():
+    dims = LayerDims(n_k=2, n_v=4, d_k=64, d_v=64, act=ACT_F32)
+    _prefill_case(dims, 4, 2, 200, [200, 129], state_std=0.05, tail_rand=True)
+
+
+def test_prefill_zero_length_leaves_state():
+    dims = LayerDims(n_k=2, n_v=4, d_k=128, d_v=128)
+    _prefill_case(dims, 5, 2, 64, [0, 2], state_std=0.05, tail_rand=True)
+
+
+def test_prefill_4k_single_layer():
+    """One sequence of 4096 tokens, 16 key / 16 value heads, d=128, bf16 activations, fp32 state."""
+    _prefill_case(SMALL, 0, 1, 4096, [4096])
+
+
+def test_prefill_stack_layer_sampled():
+    """Stack-layer shape (8 x 8192 tokens, 16/32 heads) on the GPU; sequences 0 and 7 against the oracle."""
+    _prefill_case(NEXT, 1, 8, 8192, [8192] * 8, sample=[0, 7])
+
+
+def test_prefill_scale_one():
+    dims = LayerDims(n_k=2, n_v=4, d_k=64, d_v=64, scale=1.0)
+    _prefill_case(dims, 6, 1, 130, [130], state_std=0.05)
+
+
+def test_continuation_equals_single_pass():
+    """A 32768-token prompt in bucketed chunks (real lengths drawn inside each bucket, padded with
+    g = beta = 0), each continuing from the saved fp32 state and conv tail, against the oracle's single
+    pass and against the GPU's own single pass."""
+    dims = NEXT
+    total = 32768
+    w, x, rng = make_layer(2, dims, 1, total)
+    parts = chunk_lengths(rng, total)
+    _say(f"continuation {len(parts)} chunks")
+    d = desc_of(dims)
+    W = weights(w, dims)
+    tail = act(np.zeros(dims.tail_shape(1)), dims)
+    st = f32(np.zeros(dims.state_shape(1)))
+    outs = []
+    t0 = 0
+    for n, bucket in parts:
+        def pad(a):
+            seg = a[:, t0:t0 + n]
+            fill = rng.standard_normal((1, bucket - n, a.shape[2])).astype(np.float32)
+            return act(np.concatenate([seg, fill], 1), dims)
+        o = gdn.prefill_chunk(d, W, pad(x.mixed), pad(x.z), pad(x.a), pad(x.b), i32([n]), tail, st)
+        outs.append(host(o[0, :n]))
+        t0 += n
+    torch.cuda.synchronize()
+    cont = np.concatenate(outs, 0)
+    ref = oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b)
+    assert_out_close(cont, ref["out"][0], dims, "continued out vs oracle")
+    assert_state_close(host(st[0]), ref["H"][0], "continued state vs oracle")
+    np.testing.assert_array_equal(host(tail[0]), ref["tail"][0].astype(np.float32))
+    # the GPU's own single pass
+    tail1 = act(np.zeros(dims.tail_shape(1)), dims)
+    st1 = f32(np.zeros(dims.state_shape(1)))
+    o1 = gdn.prefill_chunk(d, W, act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims), i32([total]),
+                           tail1, st1)
+    torch.cuda.synchronize()
+    assert_out_close(host(o1[0]), ref["out"][0], dims, "single-pass out vs oracle")
+    assert out_excess(cont, host(o1[0]), dims) <= 2e-3
+    assert state_rel_err(host(st1[0]), host(st[0])) <= 1e-3
+
+
+# ---------------------------------------------------------------------------------------------------
+# conv
+
+@pytest.mark.parametrize("dims,B,L,lens", [(TINY, 1, 64, [64]), (NEXT, 3, 70, [70, 2, 0]), (SMALL, 2, 33, [33, 17])])
+def test_conv_chunk(dims, B, L, lens):
+    _say(f"conv B={B} L={L}")
+    w, x, rng = make_layer(7, dims, B, L, lens)
+    t0 = random_state(rng, dims, B)[1]
+    d = desc_of(dims)
+    tail = act(t0, dims)
+    y = gdn.conv_chunk(d, act(w.conv_w, dims), act(x.mixed, dims), i32(lens), tail)
+    torch.cuda.synchronize()
+    for s in range(B):
+        yr, tr = oracle.conv(w.conv_w, t0[s], x.mixed[s], lens[s])
+        assert_out_close(host(y[s]), yr, dims, f"y[{s}]")
+        np.testing.assert_array_equal(host(tail[s]), tr.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------------------------------
+# decode, verify, accept, commit, copy
+
+def _saved_states(dims, w, rng, B, prefix=64):
+    """Saved states as a seeded random prefix leaves them (oracle run, cast to fp32), and the tails."""
+    from gdn_inputs import make_inputs
+    x = make_inputs(rng, dims, B, prefix)
+    r = oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b)
+    tails = r["tail"].astype(np.float32)
+    return r["H"].astype(np.float32), tails
+
+
+def _decode_inputs(dims, rng, B, T):
+    from gdn_inputs import make_inputs
+    return make_inputs(rng, dims, B, T)
+
+
+@pytest.mark.parametrize("dims,B", [(NEXT, 8), (SMALL, 4), (LayerDims(n_k=2, n_v=8, d_k=64, d_v=64), 3),
+                                    (LayerDims(n_k=2, n_v=4, d_k=32, d_v=32, act=ACT_F32), 2)])
+def test_decode_step_vs_oracle(dims, B):
+    _say(f"decode B={B} dims={dims}")
+    w, _, rng = make_layer(8, dims, 1, 1)
+    H0, T0 = _saved_states(dims, w, rng, B)
+    x = _decode_inputs(dims, rng, B, 1)
+    d = desc_of(dims)
+    # pool with extra rows and a permuted slot map
+    npool = B + 3
+    slots = rng.permutation(npool)[:B].astype(np.int32)
+    poolH = np.zeros(dims.state_shape(npool), np.float32)
+    poolT = np.zeros(dims.tail_shape(npool), np.float32)
+    poolH[slots], poolT[slots] = H0, T0
+    sp, tp = f32(poolH), act(poolT, dims)
+    out = gdn.decode_step(d, weights(w, dims), act(x.mixed[:, 0], dims), act(x.z[:, 0], dims), act(x.a[:, 0], dims),
+                          act(x.b[:, 0], dims), i32(slots), tp, sp, check_slots=True)
+    torch.cuda.synchronize()
+    ref = oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, None, T0, H0)
+    assert_out_close(host(out), ref["out"][:, 0], dims)
+    hp = host(sp)
+    assert_state_close(hp[slots], ref["H"])
+    np.testing.assert_array_equal(host(tp)[slots], ref["tail"].astype(np.float32))
+    others = np.setdiff1d(np.arange(npool), slots)
+    assert np.all(hp[others] == 0)
+
+
+def test_verify_checkpoints_and_commit():
+    """Verify batch: 64 sequences x (1+4) tokens with per-token checkpoints; accept with m ~ U{0..4};
+    restore the checkpoint; compare with the oracle and, bitwise, with repeated GPU decode."""
+    dims, B, K = NEXT, 64, 4
+    T = K + 1
+    _say("verify B=64 K=4")
+    w, _, rng = make_layer(9, dims, 1, 1)
+    H0, T0 = _saved_states(dims, w, rng, B)
+    x = _decode_inputs(dims, rng, B, T)
+    drafts, preds, m_true = verify_draws(rng, B, K)
+    d = desc_of(dims)
+    W = weights(w, dims)
+    sp, tp = f32(H0), act(T0, dims)
+    mx, zz, aa, bb = act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims)
+    ck_s, ck_t, out = gdn.verify_with_checkpoints(d, W, mx, zz, aa, bb, None, tp, sp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sp), H0), "verify modified the pool"
+    ref = oracle.verify(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, T0, H0)
+    assert_out_close(host(out), ref["out"], dims, "verify out")
+    cks = host(ck_s)
+    for i in range(T):
+        assert_state_close(cks[:, i], ref["ckpt_H"][:, i], f"checkpoint {i}")
+    np.testing.assert_array_equal(host(ck_t), ref["ckpt_tail"].astype(np.float32))
+    # bitwise against repeated decode on a copy of the pool
+    sp2, tp2 = sp.clone(), tp.clone()
+    for i in range(T):
+        o = gdn.decode_step(d, W, mx[:, i].contiguous(), zz[:, i].contiguous(), aa[:, i].contiguous(),
+                            bb[:, i].contiguous(), None, tp2, sp2)
+        torch.cuda.synchronize()
+        assert torch.equal(sp2, ck_s[:, i]), f"checkpoint {i} differs bitwise from {i + 1} decode calls"
+        assert torch.equal(tp2, ck_t[:, i])
+        assert torch.equal(o, out[:, i])
+    # accept (bit-exact) and commit through the state copy
+    m, em, ne, ci = gdn.accept(i32(drafts), i32(preds))
+    torch.cuda.synchronize()
+    m_ref, em_ref, ne_ref = oracle.accept(drafts, preds)
+    np.testing.assert_array_equal(m.cpu().numpy(), m_ref)
+    np.testing.assert_array_equal(m_ref, m_true)
+    np.testing.assert_array_equal(em.cpu().numpy(), em_ref)
+    np.testing.assert_array_equal(ne.cpu().numpy(), ne_ref)
+    np.testing.assert_array_equal(ci.cpu().numpy(), np.arange(B) * T + m_ref)
+    slots = i32(np.arange(B))
+    gdn.state_copy(d, sp, tp, slots, ck_s, ck_t, ci, B)
+    torch.cuda.synchronize()
+    for s in range(B):
+        assert torch.equal(sp[s], ck_s[s, m_ref[s]])
+        assert torch.equal(tp[s], ck_t[s, m_ref[s]])
+    assert_state_close(host(sp), ref["ckpt_H"][np.arange(B), m_ref])
+
+
+def test_accept_exhaustive():
+    import itertools
+    K = 4
+    dr = np.array(list(itertools.product(range(3), repeat=K)), np.int32)
+    pr = np.array(list(itertools.product(range(3), repeat=K + 1)), np.int32)
+    D = np.repeat(dr, len(pr), 0)
+    P = np.tile(pr, (len(dr), 1))
+    m, em, ne, ci = gdn.accept(i32(D), i32(P))
+    torch.cuda.synchronize()
+    m_ref, em_ref, ne_ref = oracle.accept(D, P)
+    np.testing.assert_array_equal(m.cpu().numpy(), m_ref)
+    np.testing.assert_array_equal(em.cpu().numpy(), em_ref)
+    np.testing.assert_array_equal(ne.cpu().numpy(), ne_ref)
+
+
+def test_state_copy_gather_scatter():
+    dims = NEXT
+    d = desc_of(dims)
+    rng = np.random.default_rng(10)
+    n_src, n_dst, n = 7, 9, 5
+    Sx, Tx = random_state(rng, dims, n_src)
+    src_s, src_t = f32(Sx), act(Tx, dims)
+    dst_s = f32(np.zeros(dims.state_shape(n_dst)))
+    dst_t = act(np.zeros(dims.tail_shape(n_dst)), dims)
+    si = rng.permutation(n_src)[:n].astype(np.int32)
+    di = rng.permutation(n_dst)[:n].astype(np.int32)
+    gdn.state_copy(d, dst_s, dst_t, i32(di), src_s, src_t, i32(si), n)
+    torch.cuda.synchronize()
+    for k in range(n):
+        assert torch.equal(dst_s[di[k]], src_s[si[k]])
+        assert torch.equal(dst_t[di[k]], src_t[si[k]])
+    untouched = np.setdiff1d(np.arange(n_dst), di)
+    assert float(dst_s[untouched].abs().max()) == 0.0
+    # states only, identity indices
+    dst2 = f32(np.zeros(dims.state_shape(n_src)))
+    gdn.state_copy(d, dst2, None, None, src_s, None, None, n_src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst2, src_s)
