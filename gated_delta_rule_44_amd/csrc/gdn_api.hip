@@ -84,8 +84,9 @@ int gdn_conv_chunk(const gdn_desc* d, const void* conv_w, const void* mixed, con
 
 size_t gdn_prefill_workspace_bytes(const gdn_desc* d, int B, int Lb) {
   if (check_desc(d) || B <= 0 || Lb <= 0) return 0;
+  if (d->act_dtype == GDN_F32 && d->d_k > 64) return 0;
   const int n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
-  return gdn::prefill_ws_bytes(B, d->n_v, d->d_k, n_chunks);
+  return gdn::prefill_ws_bytes(B, d->n_v, d->d_k, Lb, n_chunks, d->act_dtype == GDN_F32);
 }
 
 int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
@@ -96,10 +97,14 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
   if (!mixed || !z || !a || !b || !len || !conv_tail || !state || !out || !ws)
     return fail(GDN_EINVAL, "gdn_prefill_chunk: NULL pointer");
   if (B <= 0 || Lb <= 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d Lb=%d must be positive", B, Lb);
+  if (B > 65535) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d exceeds 65535", B);
+  if (d->act_dtype == GDN_F32 && d->d_k > 64)
+    return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunk: fp32 activations are built for d <= 64 (got %d)", d->d_k);
   const size_t need = gdn_prefill_workspace_bytes(d, B, Lb);
   if (ws_bytes < need) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace %zu bytes < %zu needed", ws_bytes, need);
   if (((uintptr_t)ws & 255u) != 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace must be 256-byte aligned");
-  if (!aligned16(state)) return fail(GDN_EINVAL, "gdn_prefill_chunk: state must be 16-byte aligned");
+  if (!aligned16(state) || !aligned16(mixed) || !aligned16(z) || !aligned16(out) || !aligned16(conv_tail))
+    return fail(GDN_EINVAL, "gdn_prefill_chunk: buffers must be 16-byte aligned");
   if (out == mixed || out == z || (void*)state == out || conv_tail == out)
     return fail(GDN_EINVAL, "gdn_prefill_chunk: out aliases another buffer");
   gdn::PrefillArgs p{};
@@ -108,6 +113,7 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
   p.ws = ws; p.B = B; p.Lb = Lb; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d);
   p.n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
   p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
+  gdn::prefill_ws_layout(p, d->d_k, d->act_dtype == GDN_F32);
   return hip_status(gdn::launch_prefill(p, d->act_dtype, d->d_k, d->n_v / d->n_k, (hipStream_t)stream),
                     "gdn_prefill_chunk");
 }

@@ -60,11 +60,11 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(ConvArgs p) {
   }
   float4 x[kTok + 3];
 #pragma unroll
-  for (int i = 0; i < kTok + 3; ++i) {
+  for (int i = 0; i < kTok + 3; ++i) {  // unconditional loads from clamped rows, masked after
     const int t = t0 - 3 + i;
-    if (t < 0) x[i] = Vec4<ActT>::load(tail + (long)(t + 3) * C + c0);
-    else if (t < Lb) x[i] = Vec4<ActT>::load(mixed + (long)t * C + c0);
-    else x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
+    const float4 v = Vec4<ActT>::load(src + c0);
+    x[i] = t < Lb ? v : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int tt = 0; tt < kTok; ++tt) {
@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(ConvArgs p) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int src = len + i;
-      nt[i] = src < 3 ? x[src] : Vec4<ActT>::load(mixed + (long)(src - 3) * C + c0);
+      const float4 v = Vec4<ActT>::load(mixed + (long)(src >= 3 ? src - 3 : 0) * C + c0);
+      nt[i] = src < 3 ? (src == 0 ? x[0] : src == 1 ? x[1] : x[2]) : v;
     }
 #pragma unroll
     for (int i = 0; i < 3; ++i) Vec4<ActT>::store(tail + (long)i * C + c0, nt[i]);

@@ -23,11 +23,18 @@ namespace gdn {
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kMaxChanPerThread = 6;  // (2*128 + 4*128) / 256 = 3 with R <= 4; room to spare
 
+// 256 threads per workgroup; for R <= 2 the register budget is capped so that two workgroups share
+// a CU and one workgroup's state loads overlap the other's arithmetic and stores
+template <int D>
+struct StepThreads {
+  static constexpr int value = 256;
+};
+
 template <typename ActT, int D, int R>
-__global__ __launch_bounds__(kThreads) void step_kernel(StepArgs p) {
+__global__ __launch_bounds__(StepThreads<D>::value) __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void step_kernel(StepArgs p) {
+  constexpr int kThreads = StepThreads<D>::value;
   constexpr int QD = D / 4;              // column quads per row
   constexpr int RG = kThreads / QD;      // row groups
   constexpr int RPT = D / RG;            // rows per thread (>= 1 since D*D >= 4*256 for D >= 32)
@@ -66,15 +73,14 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs p) {
     else if (lc < 2 * D) gc = n_k * D + kh * D + (lc - D);
     else if (lc < NCH) gc = 2 * n_k * D + kh * R * D + (lc - 2 * D);
     gch[j] = gc;
-    if (gc >= 0) {
-      w0[j] = to_f32(conv_w[gc * 4 + 0]);
-      w1[j] = to_f32(conv_w[gc * 4 + 1]);
-      w2[j] = to_f32(conv_w[gc * 4 + 2]);
-      w3[j] = to_f32(conv_w[gc * 4 + 3]);
-      t0[j] = to_f32(tail_in[0L * C + gc]);
-      t1[j] = to_f32(tail_in[1L * C + gc]);
-      t2[j] = to_f32(tail_in[2L * C + gc]);
-    }
+    const int gl = gc >= 0 ? gc : 0;  // unconditional loads (a clamped channel for unowned slots)
+    w0[j] = to_f32(conv_w[gl * 4 + 0]);
+    w1[j] = to_f32(conv_w[gl * 4 + 1]);
+    w2[j] = to_f32(conv_w[gl * 4 + 2]);
+    w3[j] = to_f32(conv_w[gl * 4 + 3]);
+    t0[j] = to_f32(tail_in[0L * C + gl]);
+    t1[j] = to_f32(tail_in[1L * C + gl]);
+    t2[j] = to_f32(tail_in[2L * C + gl]);
   }
 
   // the R value heads' states in registers
@@ -92,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs p) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int gc = gch[j];
+      const float x = to_f32(mixed[row * C + (gc >= 0 ? gc : 0)]);
       if (gc >= 0) {
-        const float x = to_f32(mixed[row * C + gc]);
         float pre = w0[j] * t0[j];
         pre = pre + w1[j] * t1[j];
         pre = pre + w2[j] * t2[j];
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs p) {
 
 template <typename ActT, int D>
 hipError_t launch_step_d(const StepArgs& p, int R, hipStream_t st) {
-  dim3 grid(p.n_k, p.B), block(kThreads);
+  dim3 grid(p.n_k, p.B), block(StepThreads<D>::value);
   switch (R) {
     case 1: hipLaunchKernelGGL((step_kernel<ActT, D, 1>), grid, block, 0, st, p); break;
     case 2: hipLaunchKernelGGL((step_kernel<ActT, D, 2>), grid, block, 0, st, p); break;

@@ -27,9 +27,10 @@
  *    C_ch = 2*n_k*d_k + n_v*d_v with channels ordered [q heads | k heads | v heads], head-major.
  *
  * Status codes: GDN_OK = 0; GDN_EINVAL = -1 (null pointer, non-positive size, inconsistent sizes,
- * workspace too small); GDN_EUNSUPPORTED = -2 (a shape this build has no kernel for: d_k or d_v not
- * in {32, 64, 128}, conv_k != 4, n_v not a multiple of n_k; the caller falls back, as the
- * statecache.py page's StateCache falls back to the plain path on _NotCached); GDN_EHIP = -3.
+ * workspace too small); GDN_EUNSUPPORTED = -2 (a shape this build has no kernel for: d_k != d_v, d_k
+ * not in {32, 64, 128}, conv_k != 4, n_v / n_k not in {1, 2, 4}, or fp32 activations with d_k > 64 in
+ * gdn_prefill_chunk; the caller falls back, as the statecache.py page's StateCache falls back to the
+ * plain path on _NotCached); GDN_EHIP = -3.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -49,7 +50,7 @@ enum { GDN_BF16 = 0, GDN_F32 = 1 };
 /* Layer shape and constants (host struct, read during the call only). */
 typedef struct {
   int32_t n_k, n_v;   /* key heads, value heads; n_v % n_k == 0 */
-  int32_t d_k, d_v;   /* head dims, each in {32, 64, 128} */
+  int32_t d_k, d_v;   /* head dims: d_k == d_v, in {32, 64, 128} */
   int32_t conv_k;     /* conv kernel width; must be 4 */
   int32_t act_dtype;  /* GDN_BF16 or GDN_F32 */
   float scale;        /* q scale; <= 0 selects d_k^-1/2 */

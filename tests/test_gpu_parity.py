@@ -65,6 +65,11 @@ def test_prefill_ragged_multichunk(D, R):
     _prefill_case(dims, 3, 3, 300, [300, 171, 1], state_std=0.05, tail_rand=True)
 
 
+def test_prefill_fused_norm_d128():
+    """Enough (sequence, value head) pairs that one workgroup owns each head's columns (fused norm)."""
+    _prefill_case(NEXT, 11, 4, 150, [150, 64, 1, 100], state_std=0.05, tail_rand=True)
+
+
 def test_prefill_fp32_multichunk():
     dims = LayerDims(n_k=2, n_v=4, d_k=64, d_v=64, act=ACT_F32)
     _prefill_case(dims, 4, 2, 200, [200, 129], state_std=0.05, tail_rand=True)
@@ -126,8 +131,10 @@ def test_continuation_equals_single_pass():
                            tail1, st1)
     torch.cuda.synchronize()
     assert_out_close(host(o1[0]), ref["out"][0], dims, "single-pass out vs oracle")
-    assert out_excess(cont, host(o1[0]), dims) <= 2e-3
-    assert state_rel_err(host(st1[0]), host(st[0])) <= 1e-3
+    # continued vs single pass: each is within the bound of the oracle, so they differ by at most twice it
+    diff = np.abs(cont - host(o1[0]))
+    assert np.all(diff <= 2 * (2e-3 + 2.0 ** -8 * np.abs(ref["out"][0]))), float(diff.max())
+    assert state_rel_err(host(st1[0]), host(st[0])) <= 2e-3
 
 
 # ---------------------------------------------------------------------------------------------------
