@@ -33,17 +33,45 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
 }
 
 // ---- scalar maths (fp32) --------------------------------------------------------------------------
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// reciprocals and reciprocal square roots on the hardware rcp / rsq (about 1 ulp) instead of IEEE division
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float silu(float x) { return x * fast_rcp(1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + __expf(-x)); }
 // softplus(x) = log(1 + e^x), written as max(x, 0) + log1p(e^-|x|) so it never overflows
 __device__ __forceinline__ float softplus(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
 
 // ---- wave reductions -----------------------------------------------------------------------------
+// DPP moves inside 16-lane rows (no LDS round trip): quad_perm [1,0,3,2] and [2,3,0,1], then
+// row_half_mirror (lane i <-> 7-i) and row_mirror (lane i <-> 15-i) pair each partial sum with a
+// disjoint one, so after four steps every lane holds its row's total.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum8(float v) {  // aligned groups of 8 lanes
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) { return row_sum8(v) + dpp<0x140>(row_sum8(v)); }
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// sum over all 64 lanes, the same value in every lane
+__device__ __forceinline__ float wave_sum64(float v) {
+  v = row_sum16(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+// sum over aligned groups of kWidth lanes (8, 16, 32 or 64); every lane gets its group's sum
 template <int kWidth>
 __device__ __forceinline__ float wave_sum(float v) {
-  // sum over aligned groups of kWidth lanes (kWidth a power of two <= 64); every lane gets the sum
-#pragma unroll
-  for (int off = kWidth / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  static_assert(kWidth == 8 || kWidth == 16 || kWidth == 32 || kWidth == 64, "group width");
+  if (kWidth == 64) return wave_sum64(v);
+  if (kWidth == 8) return row_sum8(v);
+  v = row_sum16(v);
+  if (kWidth == 32) v += __shfl_xor(v, 16, kWave);
   return v;
 }
 

@@ -91,6 +91,11 @@ __device__ __forceinline__ char* rec_ptr(const PrefillArgs& p, int b, int h, int
   return (char*)p.ws + (((long)b * p.n_v + h) * p.n_chunks + c) * Rec<D, SPLIT>::kBytes;
 }
 
+// Barrier for LDS reads and writes only. __syncthreads() also fences the direct global->LDS copies
+// still in flight (vmcnt), which would serialise the next chunk's prefetch with this chunk's work;
+// the buffers those copies fill are not read until the wait at the top of the next chunk.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -115,6 +120,23 @@ __device__ __forceinline__ f16x8 pack_hi(f32x4 a, f32x4 b) {
   }
   return r;
 }
+
+// four activations as stored (8 bytes of bf16 or 16 of fp32), widened when used
+template <typename ActT>
+struct Raw4 {
+  typedef uint2 type;
+  static __device__ __forceinline__ type load(const ActT* p) { return *(const uint2*)p; }
+  static __device__ __forceinline__ float4 widen(type u) {
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+};
+template <>
+struct Raw4<float> {
+  typedef float4 type;
+  static __device__ __forceinline__ type load(const float* p) { return *(const float4*)p; }
+  static __device__ __forceinline__ float4 widen(type u) { return u; }
+};
 
 template <typename ActT>
 struct Act4;
@@ -241,7 +263,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) ss += y[tt][j] * y[tt][j];
       ss = wave_sum<kWave>(ss);
-      const float rn = 1.0f / sqrtf(ss + p.l2_eps);
+      const float rn = rsqrt_fast(ss + p.l2_eps);
 #pragma unroll
       for (int j = 0; j < CPL; ++j) y[tt][j] *= rn;
     }
@@ -498,15 +520,36 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
   const int cb = split * CW + w * 16 * NT;  // first d_v column of this wave
 
   // direct global->LDS copies, 1 KB per wave instruction (lane i's 16 bytes land at 16 i)
-  auto dma = [&](const char* src, char* dst, int nblk) {
-    for (int blk = w; blk < nblk; blk += NW)
-      __builtin_amdgcn_global_load_lds((const void*)(src + blk * 1024 + lane * 16), (lds_void*)(dst + blk * 1024), 16, 0, 0);
-  };
+  // (a fixed count per wave, so the compiler can count them when it waits for later loads)
+  static_assert((I::A_BYTES / 1024) % NW == 0 && (I::B_BYTES / 1024) % NW == 0, "copies split evenly over waves");
   char* const ldsA = smem;
   auto ldsB = [&](int buf) { return smem + I::A_BYTES + buf * I::B_BYTES; };
-  auto prefetch_A = [&](int c) { dma(rec_ptr<D, SPLIT>(p, b, h, c), ldsA, I::A_BYTES / 1024); };
-  auto prefetch_B = [&](int c, int buf) { dma(rec_ptr<D, SPLIT>(p, b, h, c) + I::A_BYTES, ldsB(buf), I::B_BYTES / 1024); };
-  auto load_up = [&](int c, f32x4 (*u)[NT], float& gc) {
+  auto prefetch_A = [&](int c) {
+    const char* src = rec_ptr<D, SPLIT>(p, b, h, c) + lane * 16;
+#pragma unroll
+    for (int k = 0; k < I::A_BYTES / 1024 / NW; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (w + k * NW) * 1024), (lds_void*)(ldsA + (w + k * NW) * 1024), 16, 0, 0);
+  };
+  auto prefetch_B = [&](int c, int buf) {
+    const char* src = rec_ptr<D, SPLIT>(p, b, h, c) + I::A_BYTES + lane * 16;
+    char* dst = ldsB(buf);
+#pragma unroll
+    for (int k = 0; k < I::B_BYTES / 1024 / NW; ++k)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (w + k * NW) * 1024), (lds_void*)(dst + (w + k * NW) * 1024), 16, 0, 0);
+  };
+  // U', e^{gamma_C} and (fused norm) z of chunk c, loaded one chunk ahead so that the wait at the top
+  // of the loop covers them
+  typedef typename Raw4<ActT>::type RawZ;
+  auto load_up = [&](int c, f32x4 (*u)[NT], float& gc, RawZ (*zr)[NT]) {
+    if (FUSED) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int t = c * C64 + 16 * mt + r16;  // rows past Lb read row Lb-1; their results are never stored
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          zr[mt][nt] = Raw4<ActT>::load((const ActT*)p.z + (((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h) * D + cb + 16 * nt + 4 * g16);
+      }
+    }
     const char* rec = rec_ptr<D, SPLIT>(p, b, h, c);
     const float* gUp = (const float*)(rec + Rec<D, SPLIT>::kUp);
 #pragma unroll
@@ -531,13 +574,13 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) nw[nt][i] = p.norm_w[cb + 16 * nt + 4 * g16 + i];
 
-  const ActT* zin = (const ActT*)p.z;
   ActT* out = (ActT*)p.out;
   float* oraw = (float*)((char*)p.ws + p.oraw_off);
   float* sspart = (float*)((char*)p.ws + p.ss_off);
 
   f32x4 Upn[4][NT];
   float gCn = 0.f;
+  RawZ zn[4][NT];
   f32x4 res[4][NT];      // finished rows of the previous chunk, stored at the top of the next iteration
   int res_c = -1;
   auto store_res = [&](int c) {
@@ -560,7 +603,7 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
   if (n_real > 0) {
     prefetch_A(0);
     prefetch_B(0, 0);
-    load_up(0, Upn, gCn);
+    load_up(0, Upn, gCn, zn);
   }
   for (int c = 0; c < n_real; ++c) {
     const int buf = c & 1;
@@ -575,20 +618,14 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) U[mt][nt] = Upn[mt][nt];
     const float gC = gCn;
+    RawZ zr[4][NT];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) zr[mt][nt] = zn[mt][nt];
     if (c + 1 < n_real) {
       prefetch_B(c + 1, buf ^ 1);
-      load_up(c + 1, Upn, gCn);
-    }
-    // z of this chunk (used by the fused norm)
-    float4 zv[4][NT];
-    if (FUSED) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int t = c * C64 + 16 * mt + r16;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)  // rows past Lb read row Lb-1; their results are never stored
-          zv[mt][nt] = Act4<ActT>::load(zin + (((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h) * D + cb + 16 * nt + 4 * g16);
-      }
+      load_up(c + 1, Upn, gCn, zn);
     }
 
     // H as an operand (rows d_k in the permuted 32-groups), hi/lo
@@ -627,7 +664,7 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
         }
     }
     // every wave is done with part A: the next chunk's copy can stream in now
-    __syncthreads();
+    lds_barrier();
     if (c + 1 < n_real) prefetch_A(c + 1);
     // U as an operand (tokens in the permuted 32-groups), hi/lo
     f16x8 Uh[2][NT], Ul[2][NT];
@@ -709,22 +746,23 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
     }
     if (FUSED) {
       // cross-wave sums through the image this chunk has finished with
-      __syncthreads();
+      lds_barrier();
       float* sSS = (float*)ldsB(buf);
       if (g16 == 0) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) sSS[w * C64 + 16 * mt + r16] = ssw[mt];
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         float ss = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) ss += sSS[ww * C64 + 16 * mt + r16];
-        const float inv = 1.0f / sqrtf(ss / (float)D + p.rms_eps);
+        const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const float zz[4] = {zv[mt][nt].x, zv[mt][nt].y, zv[mt][nt].z, zv[mt][nt].w};
+          const float4 zf = Raw4<ActT>::widen(zr[mt][nt]);
+          const float zz[4] = {zf.x, zf.y, zf.z, zf.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) res[mt][nt][i] = nw[nt][i] * (OT[mt][nt][i] * inv) * silu(zz[i]);
         }
@@ -790,7 +828,7 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < NPART; ++k) ss += sspart[row * NPART + k];
-    const float inv = 1.0f / sqrtf(ss / (float)D + p.rms_eps);
+    const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
     const float4 o = *(const float4*)(oraw + row * D + 4 * cq);
     const float4 z = Act4<ActT>::load((const ActT*)p.z + row * D + 4 * cq);
     const float* nw = p.norm_w + 4 * cq;

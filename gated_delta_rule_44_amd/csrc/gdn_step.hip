@@ -136,8 +136,8 @@ __global__ __launch_bounds__(StepThreads<D>::value) __attribute__((amdgpu_waves_
     sq = wave_sum<kWave>(sq);
     sk = wave_sum<kWave>(sk);
     skq = wave_sum<kWave>(skq);
-    const float rq = 1.0f / sqrtf(sq + p.l2_eps);
-    const float rk = 1.0f / sqrtf(sk + p.l2_eps);
+    const float rq = rsqrt_fast(sq + p.l2_eps);
+    const float rk = rsqrt_fast(sk + p.l2_eps);
     const float kq = (skq * rk) * rq;  // k^ . q^
 
     float kn[RPT], qn[RPT];
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(StepThreads<D>::value) __attribute__((amdgpu_waves_
       // gated RMSNorm over the D columns held by the QD lanes of this row group
       ss = wave_sum<QD>(ss);
       if (tid < QD) {
-        const float inv = 1.0f / sqrtf(ss / (float)D + p.rms_eps);
+        const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
         const long ob = row * (long)n_v * D + (long)h * D;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
