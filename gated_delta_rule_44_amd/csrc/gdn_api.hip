@@ -98,6 +98,8 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
     return fail(GDN_EINVAL, "gdn_prefill_chunk: NULL pointer");
   if (B <= 0 || Lb <= 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d Lb=%d must be positive", B, Lb);
   if (B > 65535) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d exceeds 65535", B);
+  if ((long)Lb * d->n_v * d->d_v >= (1L << 31))
+    return fail(GDN_EINVAL, "gdn_prefill_chunk: Lb * n_v * d_v = %ld must stay below 2^31", (long)Lb * d->n_v * d->d_v);
   if (d->act_dtype == GDN_F32 && d->d_k > 64)
     return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunk: fp32 activations are built for d <= 64 (got %d)", d->d_k);
   const size_t need = gdn_prefill_workspace_bytes(d, B, Lb);

@@ -11,24 +11,31 @@
 //
 // Launch 1, chunk_prep_kernel (every chunk in parallel; one workgroup per chunk x key head x sequence):
 //   conv + SiLU over [saved tail | chunk], q/k L2 norm, gates with the padding mask, the Gram products
-//   K K^T and Q K^T (f16 MFMA, hi/lo-split operands), then for each value head of the GQA group the UT
+//   K K^T and K Q^T (f16 MFMA, hi/lo-split operands), then for each value head of the GQA group the UT
 //   inverse T (fp32: diagonal 16x16 blocks by substitution, off-diagonal blocks on fp32 MFMA), W and U'
-//   (f16 MFMA), P~ = scale * P, Q~ = scale diag(e^gamma) Q, K~ = diag(e^{gamma_C - gamma}) K.
-//   Each chunk's operands are written as a byte image of exactly what the state pass keeps in LDS
-//   (rows padded against bank conflicts, k-index permuted inside 32-blocks), plus U' in MFMA fragment
-//   order.
-// Launch 2, state_pass_kernel (one workgroup per column slice x value head x sequence, chunks in order):
-//   H stays in MFMA accumulators for the whole call; the next chunk's image streams into the other LDS
-//   buffer by direct global->LDS loads while this chunk computes U = U' - W H, O^T = H^T Q~^T +
-//   U^T P~^T and H = e^{gamma_C} H + K~^T U; the gated RMSNorm is fused when one workgroup owns all
+//   (f16 MFMA), P~ = scale P, Q~ = scale diag(e^gamma) Q and K~ = diag(e^{gamma_C - gamma}) K. Every
+//   operand the state pass needs is written as a ready MFMA fragment: 1 KB blocks in which lane l's
+//   16 bytes are exactly what lane l of the consuming wave loads, so each store and each load is one
+//   fully coalesced 1 KB wave access.
+// Launch 2, state_pass_kernel (one workgroup per column slice x value head x sequence, chunks in order;
+//   wave w owns token tile w of U and O and the H row tiles w, w+4, ...):
+//   U = U' - W H  (wave w: tokens 16w..16w+15, H read as fragments from LDS)
+//   O^T = H^T Q~^T + U^T P~^T, H = e^{gamma_C} H + K~^T U  (U read back as fragments from LDS)
+//   Only H and U cross waves, through LDS; each wave loads its own fragments of the next chunk into
+//   registers while the current chunk computes. The gated RMSNorm is fused when one workgroup owns all
 //   d_v columns of the head, otherwise norm_kernel finishes it from the saved partial sums.
 //
+// Fragment convention (f16 16x16x32 MFMA, lane l = 16 g + c): a 32-wide k-block is split so that lane
+// group g holds k = {4g..4g+3, 16+4g..16+4g+3}. With that grouping the two 16x16 accumulator tiles of a
+// 32-row block give, lane by lane, exactly the operand fragment of that block, so results turn into
+// operands without moving between lanes.
+//
 // Precision: f16 operands with fp32 accumulation, and hi/lo f16 pairs (about 22 mantissa bits) where
-// rounding would otherwise show in the output: the Gram products, beta*V, H, U, K~ and P~. With fp32
-// activations every operand is split. MFMA flushes f16 subnormals, so the lo half of a split value
-// must stay >= 2^-14: operands of unit scale are carried multiplied by 2^8 (exact), and the scales
-// are chosen so that every product lands in a consistent domain: the state pass keeps H as 2^16 H,
-// U as 2^8 U and O^T as 2^16 O^T, with 2^8 Q~, 2^8 P~, 2^8 K~ and unscaled -W in the image.
+// rounding would otherwise show in the output: the Gram products, beta*V, H, U, K~, Q~ and P~. With
+// fp32 activations every operand is split. MFMA flushes f16 subnormals, so the lo half of a split value
+// must stay >= 2^-14: operands of unit scale are carried multiplied by 2^8 (exact), and the scales are
+// chosen so that every product lands in a consistent domain: the state pass keeps H as 2^16 H, U as
+// 2^8 U and O^T as 2^16 O^T, with 2^8 Q~, 2^8 P~, 2^8 K~, 2^8 U' and unscaled -W in the record.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -41,84 +48,75 @@ constexpr float kS8 = 256.f;              // 2^8 operand scale
 constexpr float kInvS8 = 1.f / 256.f;
 constexpr float kInvS16 = 1.f / 65536.f;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// position of k-index j (0..31) inside its 32-block: the group of lane-group g holds
-// {4g..4g+3, 16+4g..16+4g+3}, so that two stacked 16x16 accumulator tiles form one operand
-__device__ __forceinline__ int kperm(int j) { return ((j & 15) >> 2) * 8 + ((j >> 4) << 2) + (j & 3); }
-__device__ __forceinline__ int pcol(int c) { return (c & ~31) + kperm(c & 31); }
-
-// ---- the per-chunk operand image (identical in the workspace and in the state pass's LDS) --------
-// Tiles are f16, row-major and unpadded; the 16-byte groups of each row are XOR-swizzled with the row
-// index so that the 16 rows an MFMA operand load touches fall in different LDS banks.
-template <int D, bool SPLIT>
-struct Img {
-  // part A, read first in a chunk (U and the H^T Q~^T term)
-  static constexpr int W_HI = 0;                               // [64][D]: -W, row = token
-  static constexpr int W_LO = W_HI + C64 * D;
-  static constexpr int Q_HI = W_LO + (SPLIT ? C64 * D : 0);    // [64][D]: Q~, always split
-  static constexpr int Q_LO = Q_HI + C64 * D;
-  static constexpr int A_HALFS = Q_LO + C64 * D;
-  // part B, read second (the U^T P~^T term and the state update); offsets relative to part B
-  static constexpr int K_HI = 0;                               // [D][64]: K~^T, always split
-  static constexpr int K_LO = K_HI + D * C64;
-  static constexpr int P_HI = K_LO + D * C64;                  // [64][64]: P~, always split
-  static constexpr int P_LO = P_HI + C64 * C64;
-  static constexpr int B_HALFS = P_LO + C64 * C64;
-  static constexpr int A_BYTES = A_HALFS * 2, B_BYTES = B_HALFS * 2;
-  static constexpr int BYTES = A_BYTES + B_BYTES;
-  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "image parts stream in 1 KB wave loads");
-};
-
-// half index of (row, col) in a swizzled tile of NCOLS halfs per row
-template <int NCOLS>
-__device__ __forceinline__ int swz(int row, int col) {
-  constexpr int NG = NCOLS / 8;
-  constexpr int M = (NG < 8 ? NG : 8) - 1;
-  return row * NCOLS + ((((col >> 3) ^ (row & M))) << 3) + (col & 7);
-}
-
-template <int D, bool SPLIT>
-struct Rec {
-  static constexpr long kImg = 0;
-  static constexpr long kUp = Img<D, SPLIT>::BYTES;                // U' fp32, MFMA fragment order
-  static constexpr long kGc = kUp + 4L * C64 * D;                  // e^{gamma_C}
-  static constexpr long kBytes = ((kGc + 16 + 255) / 256) * 256;
-};
-
-template <int D, bool SPLIT>
-__device__ __forceinline__ char* rec_ptr(const PrefillArgs& p, int b, int h, int c) {
-  return (char*)p.ws + (((long)b * p.n_v + h) * p.n_chunks + c) * Rec<D, SPLIT>::kBytes;
-}
-
-// Barrier for LDS reads and writes only. __syncthreads() also fences the direct global->LDS copies
-// still in flight (vmcnt), which would serialise the next chunk's prefetch with this chunk's work;
-// the buffers those copies fill are not read until the wait at the top of the next chunk.
+// Barrier for LDS reads and writes only. __syncthreads() also waits for this wave's outstanding global
+// loads and stores (vmcnt), which would stall on the record stores of chunk_prep and serialise the
+// register prefetch of the next chunk in the state pass with the current chunk's work.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// k-index (inside a 32-block) of fragment slot e (0..7) of lane group g
+__device__ __forceinline__ int kslot(int g, int e) { return e < 4 ? 4 * g + e : 12 + 4 * g + e; }
+
 __device__ __forceinline__ f16x8 ld16(const _Float16* p) { return *(const f16x8*)p; }
 
-__device__ __forceinline__ void pack_split(f32x4 a, f32x4 b, f16x8& hi, f16x8& lo) {
+// the fragment slots of lane group g from a row of 32 halfs or floats: {4g..4g+3} then {16+4g..16+4g+3}
+__device__ __forceinline__ f16x8 frag_row_h(const _Float16* row32, int g) {
+  const f16x4 a = *(const f16x4*)(row32 + 4 * g), b = *(const f16x4*)(row32 + 16 + 4 * g);
+  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void frag_row_f(const float* row32, int g, float (&x)[8]) {
+  const float4 a = *(const float4*)(row32 + 4 * g), b = *(const float4*)(row32 + 16 + 4 * g);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void split8(const float (&x)[8], f16x8& hi, f16x8& lo) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = (_Float16)a[i];
-    lo[i] = (_Float16)(a[i] - (float)hi[i]);
-    hi[4 + i] = (_Float16)b[i];
-    lo[4 + i] = (_Float16)(b[i] - (float)hi[4 + i]);
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (_Float16)x[e];
+    lo[e] = (_Float16)(x[e] - (float)hi[e]);
   }
 }
-__device__ __forceinline__ f16x8 pack_hi(f32x4 a, f32x4 b) {
-  f16x8 r;
+__device__ __forceinline__ void split4(f32x4 x, f16x4& hi, f16x4& lo) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (_Float16)a[i];
-    r[4 + i] = (_Float16)b[i];
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = (_Float16)x[e];
+    lo[e] = (_Float16)(x[e] - (float)hi[e]);
   }
-  return r;
+}
+
+// ---- the per-chunk record (one per sequence x value head x chunk) -------------------------------
+// Fragment blocks of 1 KB: lane l's 16 bytes at 16 l. Token tile mt = 16 tokens, H row tile hm = 16
+// rows of d_k, kk = 32-block of the contraction index, hi/lo halves in separate blocks.
+template <int D, bool SPLIT>
+struct Rec {
+  static constexpr int KD = D / 32, HM = D / 16;
+  static constexpr int W_HI = 0;                               // [mt][kk]: -W[token][d_k]
+  static constexpr int W_LO = W_HI + 4 * KD;                   // (fp32 activations only)
+  static constexpr int Q_HI = W_LO + (SPLIT ? 4 * KD : 0);     // [mt][kk]: 2^8 Q~[token][d_k]
+  static constexpr int Q_LO = Q_HI + 4 * KD;
+  static constexpr int P_HI = Q_LO + 4 * KD;                   // [mt][kk]: 2^8 P~[token t][token s]
+  static constexpr int P_LO = P_HI + 8;
+  static constexpr int K_HI = P_LO + 8;                        // [hm][kk]: 2^8 K~^T[d_k][token]
+  static constexpr int K_LO = K_HI + 2 * HM;
+  static constexpr int UP = K_LO + 2 * HM;                     // [mt][nt]: 2^8 U' in accumulator order
+  static constexpr int NBLK = UP + 4 * HM;
+  static constexpr long kGc = NBLK * 1024L;                    // e^{gamma_C}
+  static constexpr long kBytes = kGc + 256;
+};
+
+template <int D, bool SPLIT>
+__device__ __forceinline__ char* rec_ptr(const PrefillArgs& p, int b, int h, int c) {
+  return (char*)p.ws + (((long)b * p.n_v + h) * p.n_chunks + c) * Rec<D, SPLIT>::kBytes;
+}
+__device__ __forceinline__ void put_frag(char* rec, int blk, int lane, f16x8 v) {
+  *(f16x8*)(rec + blk * 1024 + lane * 16) = v;
+}
+__device__ __forceinline__ f16x8 get_frag(const char* rec, int blk, int lane) {
+  return *(const f16x8*)(rec + blk * 1024 + lane * 16);
 }
 
 // four activations as stored (8 bytes of bf16 or 16 of fp32), widened when used
@@ -160,41 +158,45 @@ struct Act4<bf16_t> {
   }
 };
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 // -------------------------------------------------------------------------------------------------
 template <typename ActT, int D, int R, bool SPLIT>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
-  using I = Img<D, SPLIT>;
+  using RC = Rec<D, SPLIT>;
+  constexpr int KD = D / 32, HM = D / 16;
   constexpr int CPL = D >= 64 ? D / 64 : 1;   // channels per lane in the conv stage
-  constexpr int LDW = D + 8, LDT = C64 + 8, LF = C64 + 1;
-  constexpr int SZ_TOK = C64 * LDW * 2;       // f16 [64][LDW] (this kernel's own padded tiles)
-  constexpr int SZ_CH = D * LDT * 2;          // f16 [D][LDT]
-  constexpr int NKB = SPLIT ? 2 : 1;
-  constexpr int R1 = (4 * SZ_TOK > (NKB + 2) * SZ_CH) ? 4 * SZ_TOK : (NKB + 2) * SZ_CH;
-  constexpr int OFF_QH = 0, OFF_QL = SZ_TOK, OFF_KH = 2 * SZ_TOK, OFF_KL = 3 * SZ_TOK;  // Gram operands
-  constexpr int OFF_KB = 0, OFF_VBH = NKB * SZ_CH, OFF_VBL = OFF_VBH + SZ_CH;            // after the Gram
-  constexpr int OFF_KK = R1;
-  constexpr int OFF_QK = OFF_KK + C64 * LF * 4;
-  constexpr int OFF_A = OFF_QK + C64 * LF * 4;
-  constexpr int OFF_TF = OFF_A + C64 * LF * 4;
-  constexpr int OFF_T = OFF_TF + C64 * LF * 4;
+  constexpr int LQ = D + 8;                   // halfs per row, token-major f16 tiles
+  constexpr int LT = C64 + 4;                 // floats per row, channel-major fp32 tiles and Gram results
+  constexpr int LF = C64 + 1;                 // floats per row, A and T
+  constexpr int LDT = C64 + 8;                // halfs per row, T as f16
+  constexpr int SZ_TOK = C64 * LQ * 2;
+  constexpr int SZ_CHF = D * LT * 4;
+  constexpr int SZ_AT = 2 * C64 * LF * 4;
+  constexpr int SZ_R1 = cmax(2 * SZ_TOK, SZ_CHF);   // q hi|lo for the Gram, then v^T (fp32) per head
+  constexpr int SZ_R2 = cmax(2 * SZ_TOK, SZ_AT);    // k hi|lo for the Gram, then A | T (fp32) per head
+  constexpr int OFF_R1 = 0, OFF_R2 = SZ_R1;
+  constexpr int OFF_KT = OFF_R2 + SZ_R2;            // k^T fp32 [D][LT]
+  constexpr int OFF_KK = OFF_KT + SZ_CHF;           // 2^16 K K^T [r][s]
+  constexpr int OFF_QK = OFF_KK + C64 * LT * 4;     // 2^16 Q K^T [t][s]
+  constexpr int OFF_T = OFF_QK + C64 * LT * 4;      // 2^8 T as f16 hi (then lo)
   constexpr int OFF_X = OFF_T + (SPLIT ? 2 : 1) * C64 * LDT * 2;
   constexpr int OFF_G = OFF_X + 4 * 16 * 17 * 4;
   constexpr int OFF_B = OFF_G + R * C64 * 4;
   constexpr int LDS = OFF_B + R * C64 * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) char smem[LDS];
-  _Float16* sQh = (_Float16*)(smem + OFF_QH);
-  _Float16* sQl = (_Float16*)(smem + OFF_QL);
-  _Float16* sKh = (_Float16*)(smem + OFF_KH);
-  _Float16* sKl = (_Float16*)(smem + OFF_KL);
-  _Float16* sKb = (_Float16*)(smem + OFF_KB);   // (beta e^gamma k)^T, [D][LDT], hi (then lo if SPLIT)
-  _Float16* sVbh = (_Float16*)(smem + OFF_VBH); // (beta v)^T hi
-  _Float16* sVbl = (_Float16*)(smem + OFF_VBL); // (beta v)^T lo
+  _Float16* sQh = (_Float16*)(smem + OFF_R1);
+  _Float16* sQl = sQh + C64 * LQ;
+  float* sVt = (float*)(smem + OFF_R1);
+  _Float16* sKh = (_Float16*)(smem + OFF_R2);
+  _Float16* sKl = sKh + C64 * LQ;
+  float* sA = (float*)(smem + OFF_R2);
+  float* sTf = sA + C64 * LF;
+  float* sKt = (float*)(smem + OFF_KT);
   float* sKK = (float*)(smem + OFF_KK);
   float* sQK = (float*)(smem + OFF_QK);
-  float* sA = (float*)(smem + OFF_A);
-  float* sTf = (float*)(smem + OFF_TF);
-  _Float16* sT = (_Float16*)(smem + OFF_T);     // T hi [64][LDT] (then lo if SPLIT)
+  _Float16* sT = (_Float16*)(smem + OFF_T);
   float* sX = (float*)(smem + OFF_X);
   float* sGam = (float*)(smem + OFF_G);
   float* sBet = (float*)(smem + OFF_B);
@@ -275,48 +277,70 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
   for (int r = 0; r < R; ++r) conv16(2 * n_k * D + (kh * R + r) * D, vv[r]);
   l2norm16(qn);
   l2norm16(kn);
+  // token-major 2^8 q, 2^8 k (hi/lo) for the Gram products; channel-major k in fp32
 #pragma unroll
-  for (int tt = 0; tt < 16; ++tt)
+  for (int j = 0; j < CPL; ++j) {
+    const int ch = lane * CPL + j;
+    if (ch < D) {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int ch = lane * CPL + j;
-      if (ch < D) {
-        const int o = (16 * w + tt) * LDW + ch;
-        split_f16(kS8 * qn[tt][j], sQh[o], sQl[o]);   // Gram operands carried as 2^8 q, 2^8 k
+      for (int tt = 0; tt < 16; ++tt) {
+        const int o = (16 * w + tt) * LQ + ch;
+        split_f16(kS8 * qn[tt][j], sQh[o], sQl[o]);
         split_f16(kS8 * kn[tt][j], sKh[o], sKl[o]);
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4*)&sKt[ch * LT + 16 * w + 4 * q] = make_float4(kn[4 * q][j], kn[4 * q + 1][j], kn[4 * q + 2][j], kn[4 * q + 3][j]);
     }
-  __syncthreads();
+  }
+  lds_barrier();
 
-  // ---- 3. Gram products K K^T and Q K^T on the lower 16x16 tiles (split operands) ---------------
+  // ---- 3. Gram products on the lower 16x16 tiles (split operands) --------------------------------
+  // K K^T as [r][s] (for A); K Q^T computed as D[s][t] so that each lane ends up with four
+  // consecutive s of one row t of Q K^T (for P~)
   for (int job = w; job < 20; job += 4) {
     const int prod = job / 10, tile = job % 10;       // tiles (mt, nt), nt <= mt, in row order
     const int mt = tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0;
     const int nt = tile - mt * (mt + 1) / 2;
-    const _Float16* ah = prod ? sQh : sKh;
-    const _Float16* al = prod ? sQl : sKl;
+    // KK: A = K rows 16mt, B = K rows 16nt.  KQ: A = K rows 16nt (s), B = Q rows 16mt (t)
+    const _Float16* ah = sKh;
+    const _Float16* al = sKl;
+    const _Float16* bh = prod ? sQh : sKh;
+    const _Float16* bl = prod ? sQl : sKl;
+    const int ra0 = prod ? 16 * nt : 16 * mt, rb0 = prod ? 16 * mt : 16 * nt;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    f16x8 fah[D / 32], fal[D / 32], fbh[D / 32], fbl[D / 32];
+    f16x8 fah[KD], fal[KD], fbh[KD], fbl[KD];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const int ra = (16 * mt + r16) * LDW + 32 * ks + 8 * g16, rb = (16 * nt + r16) * LDW + 32 * ks + 8 * g16;
+    for (int ks = 0; ks < KD; ++ks) {
+      const int ra = (ra0 + r16) * LQ + 32 * ks + 8 * g16, rb = (rb0 + r16) * LQ + 32 * ks + 8 * g16;
       fah[ks] = ld16(ah + ra);
       fal[ks] = ld16(al + ra);
-      fbh[ks] = ld16(sKh + rb);
-      fbl[ks] = ld16(sKl + rb);
+      fbh[ks] = ld16(bh + rb);
+      fbl[ks] = ld16(bl + rb);
     }
     __builtin_amdgcn_sched_barrier(0);  // the reads go out together, then the MFMAs
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
+    for (int ks = 0; ks < KD; ++ks) {
       acc = mfma16(fal[ks], fbh[ks], acc);
       acc = mfma16(fah[ks], fbl[ks], acc);
       acc = mfma16(fah[ks], fbh[ks], acc);
     }
-    float* dst = prod ? sQK : sKK;
+    if (prod) {
+      *(f32x4*)&sQK[(16 * mt + r16) * LT + 16 * nt + 4 * g16] = acc;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(16 * mt + 4 * g16 + i) * LF + 16 * nt + r16] = acc[i];
+      for (int i = 0; i < 4; ++i) sKK[(16 * mt + 4 * g16 + i) * LT + 16 * nt + r16] = acc[i];
+    }
   }
-  __syncthreads();
+  // this wave's rows of 2^8 q (token tile w) as fragments, kept in registers for every value head
+  f16x8 qfh[KD], qfl[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) {
+    const int row = (16 * w + r16) * LQ + 32 * kk;
+    qfh[kk] = frag_row_h(sQh + row, g16);
+    qfl[kk] = frag_row_h(sQl + row, g16);
+  }
+  lds_barrier();
 
   // ---- 4. per value head of the group ------------------------------------------------------------
   for (int r = 0; r < R; ++r) {
@@ -324,60 +348,32 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
     const float* gam = sGam + r * C64;
     const float* bet = sBet + r * C64;
     char* rec = rec_ptr<D, SPLIT>(p, b, h, c);
-    _Float16* img = (_Float16*)(rec + Rec<D, SPLIT>::kImg);
-    _Float16* imgB = img + I::A_HALFS;
     const float gC = gam[C64 - 1];
 
-    // A (strictly lower, fp32), T's upper blocks cleared
+    // A (strictly lower, fp32), T's upper blocks cleared, this head's v channel-major
     for (int idx = tid; idx < C64 * C64; idx += 256) {
       const int i = idx >> 6, j = idx & 63;
-      sA[i * LF + j] = j < i ? bet[i] * __expf(gam[i] - gam[j]) * (kInvS16 * sKK[i * LF + j]) : 0.f;
+      sA[i * LF + j] = j < i ? bet[i] * __expf(gam[i] - gam[j]) * (kInvS16 * sKK[i * LT + j]) : 0.f;
       if ((j >> 4) > (i >> 4)) sTf[i * LF + j] = 0.f;
     }
-    // B operands of W and U' (channel-major) in LDS; Q~ and K~^T straight into the image
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-      const int tl = 16 * w + tt;
-      const float eg = __expf(gam[tl]);
-      const float bk = bet[tl] * eg, bv = bet[tl], ek = __expf(gC - gam[tl]), sq = p.scale * eg;
+    for (int rr = 0; rr < R; ++rr) {  // compile-time index into vv (a runtime one would go to scratch)
+      if (rr != r) continue;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const int ch = lane * CPL + j;
         if (ch < D) {
-          const float kb = kS8 * bk * kn[tt][j];
-          if (SPLIT) split_f16(kb, sKb[ch * LDT + tl], sKb[D * LDT + ch * LDT + tl]);
-          else sKb[ch * LDT + tl] = (_Float16)kb;
-          split_f16(kS8 * bv * vv[r][tt][j], sVbh[ch * LDT + tl], sVbl[ch * LDT + tl]);
-          const float qv = kS8 * sq * qn[tt][j];
-          const int qo = swz<D>(tl, pcol(ch));
-          split_f16(qv, img[I::Q_HI + qo], img[I::Q_LO + qo]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(float4*)&sVt[ch * LT + 16 * w + 4 * q] =
+                make_float4(vv[rr][4 * q][j], vv[rr][4 * q + 1][j], vv[rr][4 * q + 2][j], vv[rr][4 * q + 3][j]);
         }
       }
     }
-    // K~^T hi/lo: row = channel, 4-token runs of this wave's 16 tokens land 4 halfs apart
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int ch = lane * CPL + j;
-      if (ch < D) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f16x4 hi, lo;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int tl = 16 * w + 4 * q + e;
-            const float kv = kS8 * __expf(gC - gam[tl]) * kn[4 * q + e][j];
-            hi[e] = (_Float16)kv;
-            lo[e] = (_Float16)(kv - (float)hi[e]);
-          }
-          const int ko = swz<C64>(ch, (w >> 1) * 32 + 8 * q + 4 * (w & 1));
-          *(f16x4*)&imgB[I::K_HI + ko] = hi;
-          *(f16x4*)&imgB[I::K_LO + ko] = lo;
-        }
-      }
-    }
-    __syncthreads();
+    lds_barrier();
 
-    // T = (I + A)^-1: diagonal blocks by forward substitution (wave 0, one column per lane)
+    // T = (I + A)^-1: diagonal blocks by forward substitution (wave 0, one column per lane); the
+    // other waves write the fragments that do not need T meanwhile
     if (w == 0) {
       const int blk = lane >> 4, jj = lane & 15;
       float x[16];
@@ -391,7 +387,53 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LF + 16 * blk + jj] = x[i];
     }
-    __syncthreads();
+    {
+      // Q~ (token tile w): 2^8 scale e^{gamma_t} q_t
+      const int t = 16 * w + r16;
+      const float fq = p.scale * __expf(gam[t]);
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qfh[kk][e] + (float)qfl[kk][e]);
+        f16x8 hi, lo;
+        split8(x, hi, lo);
+        put_frag(rec, RC::Q_HI + w * KD + kk, lane, hi);
+        put_frag(rec, RC::Q_LO + w * KD + kk, lane, lo);
+      }
+      // P~ (token tile w): 2^8 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
+      const float gt = gam[t];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float x[8];
+        frag_row_f(sQK + t * LT + 32 * kk, g16, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int s = 32 * kk + kslot(g16, e);
+          x[e] = s <= t ? p.scale * __expf(gt - gam[s]) * (kInvS8 * x[e]) : 0.f;
+        }
+        f16x8 hi, lo;
+        split8(x, hi, lo);
+        put_frag(rec, RC::P_HI + w * 2 + kk, lane, hi);
+        put_frag(rec, RC::P_LO + w * 2 + kk, lane, lo);
+      }
+      // K~^T (row tiles hm = w, w+4, ...): 2^8 e^{gamma_C - gamma_s} k_s
+#pragma unroll
+      for (int hm = w; hm < HM; hm += 4) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          float x[8];
+          frag_row_f(sKt + (16 * hm + r16) * LT + 32 * kk, g16, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= kS8 * __expf(gC - gam[32 * kk + kslot(g16, e)]);
+          f16x8 hi, lo;
+          split8(x, hi, lo);
+          put_frag(rec, RC::K_HI + hm * 2 + kk, lane, hi);
+          put_frag(rec, RC::K_LO + hm * 2 + kk, lane, lo);
+        }
+      }
+    }
+    lds_barrier();
     // off-diagonal blocks by level (i - j = 1, 2, 3): T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, fp32 MFMA
     float* sXw = sX + w * 16 * 17;
     for (int lvl = 1; lvl < 4; ++lvl) {
@@ -411,7 +453,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) sTf[(16 * i + 4 * g16 + ii) * LF + 16 * j + r16] = -y[ii];
       }
-      __syncthreads();
+      lds_barrier();
     }
     for (int idx = tid; idx < C64 * C64; idx += 256) {
       const int i = idx >> 6, j = idx & 63;
@@ -419,154 +461,200 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
       if (SPLIT) split_f16(tv, sT[i * LDT + j], sT[C64 * LDT + i * LDT + j]);
       else sT[i * LDT + j] = (_Float16)tv;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // W^T = (beta e^gamma K)^T T^T  -> image rows = token (4 consecutive d_k per lane, 8-byte stores)
-    // U'  = T (beta V)               -> fragment order
+    // W and U' for token tile w. T's row fragments serve as the B operand of W^T = (beta e^gamma K)^T T^T
+    // and as the A operand of U' = T (beta V).
     {
-      float* gUp = (float*)(rec + Rec<D, SPLIT>::kUp);
-      for (int nt = w; nt < D / 16; nt += 4) {
-        // this d-tile's B fragments, reused by the four token tiles
-        f16x8 kbh[2], kbl[2], vbh[2], vbl[2];
+      f16x8 th[2], tl[2];
+      float fk[2][8], fv[2][8];  // per-token factors of this lane's fragment slots
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int rc = (16 * nt + r16) * LDT + 32 * ks + 8 * g16;
-          kbh[ks] = ld16(sKb + rc);
-          kbl[ks] = SPLIT ? ld16(sKb + D * LDT + rc) : kbh[ks];
-          vbh[ks] = ld16(sVbh + rc);
-          vbl[ks] = ld16(sVbl + rc);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-          f16x8 th[2], tl[2];
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int rt = (16 * mt + r16) * LDT + 32 * ks + 8 * g16;
-            th[ks] = ld16(sT + rt);
-            tl[ks] = SPLIT ? ld16(sT + C64 * LDT + rt) : th[ks];
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            if (SPLIT) {
-              aw = mfma16(kbl[ks], th[ks], aw);
-              aw = mfma16(kbh[ks], tl[ks], aw);
-              au = mfma16(tl[ks], vbh[ks], au);
-            }
-            aw = mfma16(kbh[ks], th[ks], aw);
-            au = mfma16(th[ks], vbl[ks], au);
-            au = mfma16(th[ks], vbh[ks], au);
-          }
-          // au = (2^8 T)(2^8 beta V) = 2^16 U'; the state pass takes 2^8 U'
-          *(f32x4*)&gUp[((long)(nt * 4 + mt) * kWave + lane) * 4] = au * kInvS8;
-          const int wo = swz<D>(16 * mt + r16, 32 * (nt >> 1) + 8 * g16 + 4 * (nt & 1));
-          f16x4 hi, lo;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float wv = -kInvS16 * aw[i];   // aw = (2^8 beta e^gamma K)^T (2^8 T)^T = 2^16 W^T
-            hi[i] = (_Float16)wv;
-            lo[i] = (_Float16)(wv - (float)hi[i]);
-          }
-          *(f16x4*)&img[I::W_HI + wo] = hi;
-          if (SPLIT) *(f16x4*)&img[I::W_LO + wo] = lo;
-        }
-      }
-    }
-    // P~ = scale * decay-masked Q K^T (s <= t), 8 permuted columns per 16-byte store
-    {
-      const int t = tid >> 2;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const int grp = 2 * (tid & 3) + pp;      // 8-column group: block grp/4, lane-group grp%4
-        const int kk = grp >> 2, gg = grp & 3;
-        f16x8 hi, lo;
+      for (int ks = 0; ks < 2; ++ks) {
+        const int rt = (16 * w + r16) * LDT + 32 * ks;
+        th[ks] = frag_row_h(sT + rt, g16);
+        tl[ks] = SPLIT ? frag_row_h(sT + C64 * LDT + rt, g16) : th[ks];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int s = 32 * kk + (e < 4 ? 4 * gg + e : 16 + 4 * gg + e - 4);
-          const float val = s <= t ? p.scale * __expf(gam[t] - gam[s]) * (kInvS8 * sQK[t * LF + s]) : 0.f;
-          hi[e] = (_Float16)val;
-          lo[e] = (_Float16)(val - (float)hi[e]);
+          const int s = 32 * ks + kslot(g16, e);
+          fv[ks][e] = kS8 * bet[s];
+          fk[ks][e] = fv[ks][e] * __expf(gam[s]);
         }
-        const int po = swz<C64>(t, 8 * grp);
-        *(f16x8*)&imgB[I::P_HI + po] = hi;
-        *(f16x8*)&imgB[I::P_LO + po] = lo;
+      }
+      // W^T tiles 2kk, 2kk+1 give lane by lane the W fragment of block kk
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        f32x4 acc[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * kk + jj;
+          acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            float x[8];
+            frag_row_f(sKt + (16 * j + r16) * LT + 32 * ks, g16, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= fk[ks][e];
+            f16x8 kbh, kbl;
+            split8(x, kbh, kbl);
+            if (SPLIT) {
+              acc[jj] = mfma16(kbl, th[ks], acc[jj]);
+              acc[jj] = mfma16(kbh, tl[ks], acc[jj]);
+            }
+            acc[jj] = mfma16(kbh, th[ks], acc[jj]);
+          }
+        }
+        // acc = (2^8 beta e^gamma K)^T (2^8 T)^T = 2^16 W^T
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = -kInvS16 * acc[0][i];
+          x[4 + i] = -kInvS16 * acc[1][i];
+        }
+        f16x8 hi, lo;
+        split8(x, hi, lo);
+        put_frag(rec, RC::W_HI + w * KD + kk, lane, hi);
+        if (SPLIT) put_frag(rec, RC::W_LO + w * KD + kk, lane, lo);
+      }
+      // U' tiles (w, nt): (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
+#pragma unroll
+      for (int nt = 0; nt < HM; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float x[8];
+          frag_row_f(sVt + (16 * nt + r16) * LT + 32 * ks, g16, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= fv[ks][e];
+          f16x8 vh, vl;
+          split8(x, vh, vl);
+          if (SPLIT) acc = mfma16(tl[ks], vh, acc);
+          acc = mfma16(th[ks], vl, acc);
+          acc = mfma16(th[ks], vh, acc);
+        }
+        *(f32x4*)(rec + (RC::UP + w * HM + nt) * 1024 + lane * 16) = acc * kInvS8;
       }
     }
-    if (tid == 0) *(float*)(rec + Rec<D, SPLIT>::kGc) = __expf(gC);
-    __syncthreads();
+    if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gC);
+    lds_barrier();
   }
 }
 
 // -------------------------------------------------------------------------------------------------
-// State pass. NW waves x NT 16-column tiles per wave = the workgroup's d_v slice.
-template <typename ActT, int D, int NW, int NT, bool SPLIT, bool FUSED>
-__global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
-  using I = Img<D, SPLIT>;
-  constexpr int HM = D / 16, KD = D / 32, CW = NW * 16 * NT, NSPLIT = D / CW;
-  static_assert(NSPLIT * CW == D, "column split");
-  static_assert(FUSED == (NSPLIT == 1), "the norm is fused exactly when one workgroup owns the head");
-  static_assert(NW * C64 * 4 <= I::B_BYTES, "norm exchange fits in a consumed part B");
-  // LDS: part A (W, Q~) single-buffered, reloaded as soon as a chunk has used it; part B (K~^T, P~)
-  // double-buffered, the next chunk's copy streaming in during the whole current chunk
-  __shared__ __attribute__((aligned(1024))) char smem[I::A_BYTES + 2 * I::B_BYTES];
+// State pass: 4 waves, a slice of CS = 16 NT value columns of one head.
+//
+// Each wave's fragments of a chunk (24 KB at d = 128) are loaded straight into registers. Memory
+// latency (records come from HBM or the last-level cache) is longer than one chunk of work, so with
+// DB the loop is unrolled by two over two register sets and the loads run two chunks ahead: the set
+// of chunk c is refilled with chunk c+2 as soon as chunk c has consumed it.
+template <int KD, int NT, int HPW, bool SPLIT, typename RawZ>
+struct PassFrags {
+  f16x8 w[KD], wl[SPLIT ? KD : 1], q[KD], ql[KD];  // part A: -W, Q~ (hi, lo) of token tile w
+  f32x4 up[NT];                                    // part A: U' of token tile w, this slice
+  f16x8 p[2], pl[2], k[HPW][2], kl[HPW][2];        // part B: P~ of token tile w, K~^T of own row tiles
+  float gc;                                        // part B: e^{gamma_C}
+  RawZ z[NT];                                      // part B: z of token tile w (fused norm)
+};
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+template <typename ActT, int D, int NT, bool SPLIT, bool FUSED, bool DB>
+__global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
+  using RC = Rec<D, SPLIT>;
+  constexpr int KD = D / 32, HM = D / 16, CS = 16 * NT, NSPLIT = D / CS;
+  constexpr int HPW = (HM + 3) / 4;       // H row tiles per wave: hm = w + 4 j
+  constexpr bool kAllOwn = HM % 4 == 0;   // every wave owns HPW tiles
+  constexpr int NG = NT >= 2 ? 2 : 1;     // column tiles per MFMA group
+  static_assert(NSPLIT * CS == D, "column split");
+  static_assert(FUSED == (NSPLIT == 1), "the norm is fused exactly when one workgroup owns the head");
+  typedef typename Raw4<ActT>::type RawZ;
+  typedef PassFrags<KD, NT, HPW, SPLIT, RawZ> Frags;
+  // H and U as MFMA operand fragments: [32-block][nt][hi, lo][lane], 16 bytes each
+  __shared__ f16x8 sH[KD * NT * 2 * kWave];
+  __shared__ f16x8 sU[2 * NT * 2 * kWave];
+
+  // workgroups of one head run on one XCD (dispatch goes round-robin over the 8 XCDs), so that the
+  // record of a chunk is fetched from HBM once and shared through that XCD's L2
+  const int nblk = gridDim.x, bid = blockIdx.x;
+  const int lid = (nblk & 7) == 0 ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
+  const int split = lid % NSPLIT, hb = lid / NSPLIT;
+  const int h = hb % p.n_v, b = hb / p.n_v;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g16 = lane >> 4, r16 = lane & 15;
   const int Lb = p.Lb, n_v = p.n_v, C = p.C;
   const int len = p.len[b];
   const int n_real = (len + C64 - 1) / C64;
-  const int cb = split * CW + w * 16 * NT;  // first d_v column of this wave
+  const int cb = split * CS;
+  auto owns = [&](int j) { return kAllOwn || w + 4 * j < HM; };
 
-  // direct global->LDS copies, 1 KB per wave instruction (lane i's 16 bytes land at 16 i)
-  // (a fixed count per wave, so the compiler can count them when it waits for later loads)
-  static_assert((I::A_BYTES / 1024) % NW == 0 && (I::B_BYTES / 1024) % NW == 0, "copies split evenly over waves");
-  char* const ldsA = smem;
-  auto ldsB = [&](int buf) { return smem + I::A_BYTES + buf * I::B_BYTES; };
-  auto prefetch_A = [&](int c) {
-    const char* src = rec_ptr<D, SPLIT>(p, b, h, c) + lane * 16;
+  auto load_a = [&](Frags& f, int c) __attribute__((always_inline)) {
+    c = c < n_real ? c : n_real - 1;  // past the end: reload the last chunk (unused, branch-free)
+    const char* rec = rec_ptr<D, SPLIT>(p, b, h, c);
 #pragma unroll
-    for (int k = 0; k < I::A_BYTES / 1024 / NW; ++k)
-      __builtin_amdgcn_global_load_lds((const void*)(src + (w + k * NW) * 1024), (lds_void*)(ldsA + (w + k * NW) * 1024), 16, 0, 0);
+    for (int kk = 0; kk < KD; ++kk) {
+      f.w[kk] = get_frag(rec, RC::W_HI + w * KD + kk, lane);
+      if (SPLIT) f.wl[kk] = get_frag(rec, RC::W_LO + w * KD + kk, lane);
+      f.q[kk] = get_frag(rec, RC::Q_HI + w * KD + kk, lane);
+      f.ql[kk] = get_frag(rec, RC::Q_LO + w * KD + kk, lane);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) f.up[nt] = *(const f32x4*)(rec + (RC::UP + w * HM + cb / 16 + nt) * 1024 + lane * 16);
   };
-  auto prefetch_B = [&](int c, int buf) {
-    const char* src = rec_ptr<D, SPLIT>(p, b, h, c) + I::A_BYTES + lane * 16;
-    char* dst = ldsB(buf);
+  auto load_b = [&](Frags& f, int c) __attribute__((always_inline)) {
+    c = c < n_real ? c : n_real - 1;
+    const char* rec = rec_ptr<D, SPLIT>(p, b, h, c);
 #pragma unroll
-    for (int k = 0; k < I::B_BYTES / 1024 / NW; ++k)
-      __builtin_amdgcn_global_load_lds((const void*)(src + (w + k * NW) * 1024), (lds_void*)(dst + (w + k * NW) * 1024), 16, 0, 0);
-  };
-  // U', e^{gamma_C} and (fused norm) z of chunk c, loaded one chunk ahead so that the wait at the top
-  // of the loop covers them
-  typedef typename Raw4<ActT>::type RawZ;
-  auto load_up = [&](int c, f32x4 (*u)[NT], float& gc, RawZ (*zr)[NT]) {
-    if (FUSED) {
+    for (int kk = 0; kk < 2; ++kk) {
+      f.p[kk] = get_frag(rec, RC::P_HI + w * 2 + kk, lane);
+      f.pl[kk] = get_frag(rec, RC::P_LO + w * 2 + kk, lane);
+    }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int t = c * C64 + 16 * mt + r16;  // rows past Lb read row Lb-1; their results are never stored
+    for (int j = 0; j < HPW; ++j) {
+      const int hm = owns(j) ? w + 4 * j : 0;  // a wave without a tile loads tile 0 and ignores it
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          zr[mt][nt] = Raw4<ActT>::load((const ActT*)p.z + (((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h) * D + cb + 16 * nt + 4 * g16);
+      for (int kk = 0; kk < 2; ++kk) {
+        f.k[j][kk] = get_frag(rec, RC::K_HI + hm * 2 + kk, lane);
+        f.kl[j][kk] = get_frag(rec, RC::K_LO + hm * 2 + kk, lane);
       }
     }
-    const char* rec = rec_ptr<D, SPLIT>(p, b, h, c);
-    const float* gUp = (const float*)(rec + Rec<D, SPLIT>::kUp);
+    f.gc = *(const float*)(rec + RC::kGc);
+    if (FUSED) {
+      const int t = c * C64 + 16 * w + r16;  // rows past Lb read row Lb-1; their results are never stored
+      const long row = ((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) u[mt][nt] = *(const f32x4*)&gUp[((long)((cb / 16 + nt) * 4 + mt) * kWave + lane) * 4];
-    gc = *(const float*)(rec + Rec<D, SPLIT>::kGc);
+      for (int nt = 0; nt < NT; ++nt) f.z[nt] = Raw4<ActT>::load((const ActT*)p.z + row * D + cb + 16 * nt + 4 * g16);
+    }
   };
 
+  // ---- the state: 2^16 H, row tiles hm = w + 4j, columns cb + 16 nt + r16 ----
   float* st = p.state + ((long)b * n_v + h) * D * D;
-  f32x4 H[HM][NT];
+  f32x4 Hacc[HPW][NT];
 #pragma unroll
-  for (int hm = 0; hm < HM; ++hm)
+  for (int j = 0; j < HPW; ++j) {
+    const int hl = owns(j) ? w + 4 * j : 0;  // a wave without this tile reads tile 0 and drops it
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) H[hm][nt][i] = 65536.f * st[(long)(16 * hm + 4 * g16 + i) * D + cb + 16 * nt + r16];
+      for (int i = 0; i < 4; ++i) {
+        const float v = st[(long)(16 * hl + 4 * g16 + i) * D + cb + 16 * nt + r16];
+        Hacc[j][nt][i] = owns(j) ? 65536.f * v : 0.f;
+      }
+  }
+  // 2^8 H hi/lo into its fragment slots: tile hm is half (hm & 1) of 32-block hm >> 1
+  auto put_H = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int hm = w + 4 * j;
+      if (owns(j)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f16x4 hi, lo;
+          split4(Hacc[j][nt] * kInvS8, hi, lo);
+          _Float16* dst = (_Float16*)&sH[(((hm >> 1) * NT + nt) * 2) * kWave + lane] + 4 * (hm & 1);
+          *(f16x4*)dst = hi;
+          *(f16x4*)(dst + 8 * kWave) = lo;
+        }
+      }
+    }
+  };
+  put_H();
 
   float nw[NT][4];
 #pragma unroll
@@ -578,215 +666,175 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
   float* oraw = (float*)((char*)p.ws + p.oraw_off);
   float* sspart = (float*)((char*)p.ws + p.ss_off);
 
-  f32x4 Upn[4][NT];
-  float gCn = 0.f;
-  RawZ zn[4][NT];
-  f32x4 res[4][NT];      // finished rows of the previous chunk, stored at the top of the next iteration
-  int res_c = -1;
-  auto store_res = [&](int c) {
+  // one chunk; f holds its fragments on entry and those of chunk c + step on return
+  auto chunk = [&](int c, Frags& f, int step) __attribute__((always_inline)) {
+    lds_barrier();  // H of this chunk is in sH
+    // ---- U = U' - W H (token tile w); O^T = H^T Q~^T ----
+    // Column tiles go in groups of NG, and each product's hi*lo terms and hi*hi term accumulate
+    // separately: consecutive MFMAs then never wait on each other's result.
+    f32x4 U[NT], OT[NT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int t = c * C64 + 16 * mt + r16;
-      if (t < Lb) {
-        const long rowb = ((long)b * Lb + t) * n_v + h;
+    for (int n0 = 0; n0 < NT; n0 += NG) {
+      f16x8 hf[KD][NG], hl[KD][NG];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = cb + 16 * nt + 4 * g16;
-          const float4 v = make_float4(res[mt][nt][0], res[mt][nt][1], res[mt][nt][2], res[mt][nt][3]);
-          if (FUSED) Act4<ActT>::store(out + rowb * D + col, v);
-          else *(float4*)(oraw + rowb * D + col) = v;
+      for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          hf[kk][g] = sH[((kk * NT + n0 + g) * 2) * kWave + lane];
+          hl[kk][g] = sH[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
         }
+      f32x4 ua[NG], ub[NG], oa[NG], ob[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        ua[g] = f.up[n0 + g];
+        ub[g] = oa[g] = ob[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) ua[g] = mfma16(f.w[kk], hl[kk][g], ua[g]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) oa[g] = mfma16(hf[kk][g], f.ql[kk], oa[g]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) ub[g] = mfma16(f.w[kk], hf[kk][g], ub[g]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) ob[g] = mfma16(hf[kk][g], f.q[kk], ob[g]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) oa[g] = mfma16(hl[kk][g], f.q[kk], oa[g]);
+        if (SPLIT) {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) ua[g] = mfma16(f.wl[kk], hf[kk][g], ua[g]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        U[n0 + g] = ua[g] + ub[g];
+        OT[n0 + g] = oa[g] + ob[g];
+      }
+    }
+    // U hi/lo into its fragment slots: token tile w is half (w & 1) of 32-block w >> 1
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f16x4 hi, lo;
+      split4(U[nt], hi, lo);
+      _Float16* dst = (_Float16*)&sU[(((w >> 1) * NT + nt) * 2) * kWave + lane] + 4 * (w & 1);
+      *(f16x4*)dst = hi;
+      *(f16x4*)(dst + 8 * kWave) = lo;
+    }
+    load_a(f, c + step);
+    lds_barrier();  // U of every token tile is in sU; every wave is done reading sH
+    // ---- H = e^{gamma_C} H + K~^T U (own row tiles); O^T += U^T P~^T ----
+    // per (block, term) one MFMA on each H tile of the group and each O^T tile: independent results
+#pragma unroll
+    for (int n0 = 0; n0 < NT; n0 += NG) {
+      f16x8 uf[2][NG], ul[2][NG];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          uf[kk][g] = sU[((kk * NT + n0 + g) * 2) * kWave + lane];
+          ul[kk][g] = sU[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
+        }
+#pragma unroll
+      for (int j = 0; j < HPW; ++j)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) Hacc[j][n0 + g] = Hacc[j][n0 + g] * f.gc;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int term = 0; term < 3; ++term) {
+#pragma unroll
+          for (int j = 0; j < HPW; ++j) {
+            if (owns(j)) {
+#pragma unroll
+              for (int g = 0; g < NG; ++g) {
+                const f16x8 ka = term == 0 ? f.kl[j][kk] : f.k[j][kk];
+                const f16x8 ub = term == 1 ? ul[kk][g] : uf[kk][g];
+                Hacc[j][n0 + g] = mfma16(ka, ub, Hacc[j][n0 + g]);
+              }
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const f16x8 ua = term == 1 ? ul[kk][g] : uf[kk][g];
+            const f16x8 pb = term == 0 ? f.pl[kk] : f.p[kk];
+            OT[n0 + g] = mfma16(ua, pb, OT[n0 + g]);
+          }
+        }
+    }
+    put_H();
+
+    // ---- output rows of token tile w: lane holds token 16w + r16, columns cb + 16 nt + 4 g16 + i ----
+    float ss = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      OT[nt] = OT[nt] * kInvS16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss += OT[nt][i] * OT[nt][i];
+    }
+    ss += __shfl_xor(ss, 16, kWave);
+    ss += __shfl_xor(ss, 32, kWave);
+    const int t = c * C64 + 16 * w + r16;
+    const long row = ((long)b * Lb + t) * n_v + h;
+    if (FUSED) {
+      const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
+      float4 res[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4 zf = Raw4<ActT>::widen(f.z[nt]);
+        res[nt] = make_float4(nw[nt][0] * (OT[nt][0] * inv) * silu(zf.x), nw[nt][1] * (OT[nt][1] * inv) * silu(zf.y),
+                              nw[nt][2] * (OT[nt][2] * inv) * silu(zf.z), nw[nt][3] * (OT[nt][3] * inv) * silu(zf.w));
+      }
+      load_b(f, c + step);
+      if (t < Lb) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) Act4<ActT>::store(out + row * D + cb + 16 * nt + 4 * g16, res[nt]);
+      }
+    } else {
+      load_b(f, c + step);
+      if (t < Lb) {
+        if (g16 == 0) sspart[row * NSPLIT + split] = ss;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          *(float4*)(oraw + row * D + cb + 16 * nt + 4 * g16) = make_float4(OT[nt][0], OT[nt][1], OT[nt][2], OT[nt][3]);
       }
     }
   };
 
   if (n_real > 0) {
-    prefetch_A(0);
-    prefetch_B(0, 0);
-    load_up(0, Upn, gCn, zn);
-  }
-  for (int c = 0; c < n_real; ++c) {
-    const int buf = c & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const _Float16* img = (const _Float16*)ldsA;
-    const _Float16* imgB = (const _Float16*)ldsB(buf);
-    if (res_c >= 0) store_res(res_c);
-    f32x4 U[4][NT];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) U[mt][nt] = Upn[mt][nt];
-    const float gC = gCn;
-    RawZ zr[4][NT];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) zr[mt][nt] = zn[mt][nt];
-    if (c + 1 < n_real) {
-      prefetch_B(c + 1, buf ^ 1);
-      load_up(c + 1, Upn, gCn, zn);
-    }
-
-    // H as an operand (rows d_k in the permuted 32-groups), hi/lo
-    f16x8 Hb[KD][NT], Hl[KD][NT];
-#pragma unroll
-    for (int kk = 0; kk < KD; ++kk)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) pack_split(H[2 * kk][nt] * kInvS8, H[2 * kk + 1][nt] * kInvS8, Hb[kk][nt], Hl[kk][nt]);
-    // U = U' - W H ; O^T = H^T Q~^T. Operand fragments are loaded a row-block at a time before the
-    // MFMAs that use them, so the LDS reads overlap instead of waiting one by one.
-    f32x4 OT[4][NT];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) OT[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      f16x8 aw[KD], bq[KD], bql[KD], awl[SPLIT ? KD : 1];
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        const int ro = swz<D>(16 * mt + r16, 32 * kk + 8 * g16);
-        aw[kk] = ld16(img + I::W_HI + ro);
-        bq[kk] = ld16(img + I::Q_HI + ro);
-        bql[kk] = ld16(img + I::Q_LO + ro);
-        if (SPLIT) awl[kk] = ld16(img + I::W_LO + ro);
+    if (DB) {
+      Frags f0, f1;
+      load_a(f0, 0);
+      load_b(f0, 0);
+      load_a(f1, 1);
+      load_b(f1, 1);
+      // the loop body has no branch, so the compiler can count the loads still in flight at its top
+      // (a conditional second chunk made it wait for all of them)
+      int c = 0;
+      for (; c + 1 < n_real; c += 2) {
+        chunk(c, f0, 2);
+        chunk(c + 1, f1, 2);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of the MFMAs
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (SPLIT) U[mt][nt] = mfma16(awl[kk], Hb[kk][nt], U[mt][nt]);
-          OT[mt][nt] = mfma16(Hb[kk][nt], bql[kk], OT[mt][nt]);
-          U[mt][nt] = mfma16(aw[kk], Hl[kk][nt], U[mt][nt]);
-          U[mt][nt] = mfma16(aw[kk], Hb[kk][nt], U[mt][nt]);
-          OT[mt][nt] = mfma16(Hl[kk][nt], bq[kk], OT[mt][nt]);
-          OT[mt][nt] = mfma16(Hb[kk][nt], bq[kk], OT[mt][nt]);
-        }
-    }
-    // every wave is done with part A: the next chunk's copy can stream in now
-    lds_barrier();
-    if (c + 1 < n_real) prefetch_A(c + 1);
-    // U as an operand (tokens in the permuted 32-groups), hi/lo
-    f16x8 Uh[2][NT], Ul[2][NT];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) pack_split(U[2 * kk][nt], U[2 * kk + 1][nt], Uh[kk][nt], Ul[kk][nt]);
-    // O^T += U^T P~^T
-    {
-      f16x8 bp[4][2], bpl[4][2];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int ro = swz<C64>(16 * mt + r16, 32 * kk + 8 * g16);
-          bp[mt][kk] = ld16(imgB + I::P_HI + ro);
-          bpl[mt][kk] = ld16(imgB + I::P_LO + ro);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            OT[mt][nt] = mfma16(Uh[kk][nt], bpl[mt][kk], OT[mt][nt]);
-            OT[mt][nt] = mfma16(Ul[kk][nt], bp[mt][kk], OT[mt][nt]);
-            OT[mt][nt] = mfma16(Uh[kk][nt], bp[mt][kk], OT[mt][nt]);
-          }
-    }
-    // H = e^{gamma_C} H + K~^T U, four 16-row blocks of K~^T per batch of loads
-    constexpr int KBAT = HM < 4 ? HM : 4;
-#pragma unroll
-    for (int hb = 0; hb < HM; hb += KBAT) {
-      f16x8 akh[KBAT][2], akl[KBAT][2];
-#pragma unroll
-      for (int q = 0; q < KBAT; ++q)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int ro = swz<C64>(16 * (hb + q) + r16, 32 * kk + 8 * g16);
-          akh[q][kk] = ld16(imgB + I::K_HI + ro);
-          akl[q][kk] = ld16(imgB + I::K_LO + ro);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < KBAT; ++q) {
-        const int hm = hb + q;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) H[hm][nt][i] *= gC;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            H[hm][nt] = mfma16(akl[q][kk], Uh[kk][nt], H[hm][nt]);
-            H[hm][nt] = mfma16(akh[q][kk], Ul[kk][nt], H[hm][nt]);
-            H[hm][nt] = mfma16(akh[q][kk], Uh[kk][nt], H[hm][nt]);
-          }
-      }
-    }
-
-    // epilogue: O^T tile (mt, nt) holds token 16mt + r16, columns cb + 16nt + 4g16 .. +3 (as 2^16 O^T)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) OT[mt][nt] = OT[mt][nt] * kInvS16;
-    float ssw[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      float ss = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ss += OT[mt][nt][i] * OT[mt][nt][i];
-      ss += __shfl_xor(ss, 16, kWave);
-      ss += __shfl_xor(ss, 32, kWave);
-      ssw[mt] = ss;
-    }
-    if (FUSED) {
-      // cross-wave sums through the image this chunk has finished with
-      lds_barrier();
-      float* sSS = (float*)ldsB(buf);
-      if (g16 == 0) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) sSS[w * C64 + 16 * mt + r16] = ssw[mt];
-      }
-      lds_barrier();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        float ss = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) ss += sSS[ww * C64 + 16 * mt + r16];
-        const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const float4 zf = Raw4<ActT>::widen(zr[mt][nt]);
-          const float zz[4] = {zf.x, zf.y, zf.z, zf.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) res[mt][nt][i] = nw[nt][i] * (OT[mt][nt][i] * inv) * silu(zz[i]);
-        }
-      }
+      if (c < n_real) chunk(c, f0, 2);
     } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int t = c * C64 + 16 * mt + r16;
-        if (g16 == 0 && t < Lb) sspart[(((long)b * Lb + t) * n_v + h) * (NSPLIT * NW) + split * NW + w] = ssw[mt];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) res[mt][nt] = OT[mt][nt];
-      }
+      Frags f0;
+      load_a(f0, 0);
+      load_b(f0, 0);
+      for (int c = 0; c < n_real; ++c) chunk(c, f0, 1);
     }
-    res_c = c;
   }
-  if (res_c >= 0) store_res(res_c);
 
   // final state, in place
 #pragma unroll
-  for (int hm = 0; hm < HM; ++hm)
+  for (int j = 0; j < HPW; ++j) {
+    const int hm = w + 4 * j;
+    if (owns(j)) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[(long)(16 * hm + 4 * g16 + i) * D + cb + 16 * nt + r16] = H[hm][nt][i] * kInvS16;
+        for (int i = 0; i < 4; ++i) st[(long)(16 * hm + 4 * g16 + i) * D + cb + 16 * nt + r16] = Hacc[j][nt][i] * kInvS16;
+    }
+  }
 
   // conv tail: rows len .. len+2 of [old tail | mixed]. Split 0 of value head h owns its v channels;
   // split 0 of the first value head of each GQA group also the q and k channels of its key head.
@@ -796,7 +844,7 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
     const ActT* mx = (const ActT*)p.mixed + (long)b * Lb * C;
     const int kh = h / R;
     const int nch = (h % R == 0) ? 3 * D : D;
-    for (int lc = tid; lc < nch; lc += 64 * NW) {
+    for (int lc = tid; lc < nch; lc += 256) {
       int gc;
       if (lc < D) gc = 2 * p.n_k * D + h * D + lc;
       else if (lc < 2 * D) gc = kh * D + (lc - D);
@@ -814,38 +862,35 @@ __global__ __launch_bounds__(64 * NW) void state_pass_kernel(PrefillArgs p) {
 }
 
 // the gated RMSNorm when a head's columns were split: out = w * o / rms(o) * silu(z)
+// (one thread per 4 columns of one (sequence, token, head) row; rows past len are left alone)
 template <typename ActT, int D, int NPART>
 __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
-  const long n = (long)p.B * p.Lb * p.n_v * (D / 4);
+  constexpr int Q = D / 4;
   const float* oraw = (const float*)((const char*)p.ws + p.oraw_off);
   const float* sspart = (const float*)((const char*)p.ws + p.ss_off);
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
-    const int cq = (int)(i % (D / 4));
-    const long row = i / (D / 4);  // (b, t, h)
-    const int bt = (int)(row / p.n_v);
-    const int b = bt / p.Lb, t = bt % p.Lb;
-    if (t >= p.len[b]) continue;
-    float ss = 0.f;
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int rr = i / Q, cq = i % Q;
+  if (rr >= p.len[b] * p.n_v) return;
+  const long row = (long)b * p.Lb * p.n_v + rr;
+  float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < NPART; ++k) ss += sspart[row * NPART + k];
-    const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
-    const float4 o = *(const float4*)(oraw + row * D + 4 * cq);
-    const float4 z = Act4<ActT>::load((const ActT*)p.z + row * D + 4 * cq);
-    const float* nw = p.norm_w + 4 * cq;
-    const float4 v = make_float4(nw[0] * (o.x * inv) * silu(z.x), nw[1] * (o.y * inv) * silu(z.y),
-                                 nw[2] * (o.z * inv) * silu(z.z), nw[3] * (o.w * inv) * silu(z.w));
-    Act4<ActT>::store((ActT*)p.out + row * D + 4 * cq, v);
-  }
+  for (int k = 0; k < NPART; ++k) ss += sspart[row * NPART + k];
+  const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
+  const float4 o = *(const float4*)(oraw + row * D + 4 * cq);
+  const float4 z = Act4<ActT>::load((const ActT*)p.z + row * D + 4 * cq);
+  const float4 nw = *(const float4*)(p.norm_w + 4 * cq);
+  const float4 v = make_float4(nw.x * (o.x * inv) * silu(z.x), nw.y * (o.y * inv) * silu(z.y),
+                               nw.z * (o.z * inv) * silu(z.z), nw.w * (o.w * inv) * silu(z.w));
+  Act4<ActT>::store((ActT*)p.out + row * D + 4 * cq, v);
 }
 
 // ---- launch configuration --------------------------------------------------------------------------
-struct PassCfg {
-  int nw, nt, nsplit;
-};
-PassCfg pass_cfg(int B, int n_v, int D, bool split_all) {
-  if (D == 128 && !split_all) return B * n_v < 128 ? PassCfg{2, 1, 4} : PassCfg{4, 2, 1};
-  if (D == 64) return PassCfg{4, 1, 1};
-  return PassCfg{2, 1, 1};
+// value columns per state-pass workgroup: the whole head when there are enough (sequence, head) pairs
+// to fill the chip, else slices, so that a short batch still spreads its chunk chains over more CUs
+int pass_nt(int B, int n_v, int D) {
+  if (D == 128) return B * n_v >= 128 ? 8 : B * n_v >= 48 ? 4 : 2;
+  return D / 16;
 }
 
 long rec_bytes(int D, bool split_all) {
@@ -853,28 +898,26 @@ long rec_bytes(int D, bool split_all) {
   return D == 32 ? Rec<32, false>::kBytes : D == 64 ? Rec<64, false>::kBytes : Rec<128, false>::kBytes;
 }
 
-template <typename ActT, int D, int R, bool SPLIT, int NW, int NT>
+template <typename ActT, int D, int R, bool SPLIT, int NT>
 hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
-  constexpr int NSPLIT = D / (NW * 16 * NT);
+  constexpr int NSPLIT = D / (16 * NT);
   hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((state_pass_kernel<ActT, D, NW, NT, SPLIT, NSPLIT == 1>), dim3(NSPLIT, p.n_v, p.B),
-                     dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NSPLIT == 1, (NT <= 4)>), dim3(NSPLIT * p.n_v * p.B), dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess || NSPLIT == 1) return e;
-  const long n = (long)p.B * p.Lb * p.n_v * (D / 4);
-  const long blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
-  hipLaunchKernelGGL((norm_kernel<ActT, D, NSPLIT * NW>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  const long per_seq = (long)p.Lb * p.n_v * (D / 4);  // < 2^31, checked by the caller
+  hipLaunchKernelGGL((norm_kernel<ActT, D, NSPLIT>), dim3((unsigned)((per_seq + 255) / 256), p.B), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-template <typename ActT, int D, bool SPLIT, int NW, int NT>
+template <typename ActT, int D, bool SPLIT, int NT>
 hipError_t launch_r(const PrefillArgs& p, int R, hipStream_t st) {
   switch (R) {
-    case 1: return launch_t<ActT, D, 1, SPLIT, NW, NT>(p, st);
-    case 2: return launch_t<ActT, D, 2, SPLIT, NW, NT>(p, st);
-    case 4: return launch_t<ActT, D, 4, SPLIT, NW, NT>(p, st);
+    case 1: return launch_t<ActT, D, 1, SPLIT, NT>(p, st);
+    case 2: return launch_t<ActT, D, 2, SPLIT, NT>(p, st);
+    case 4: return launch_t<ActT, D, 4, SPLIT, NT>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -882,11 +925,11 @@ hipError_t launch_r(const PrefillArgs& p, int R, hipStream_t st) {
 }  // namespace
 
 size_t prefill_ws_bytes(int B, int n_v, int D, int Lb, int n_chunks, bool split_all) {
-  const PassCfg cfg = pass_cfg(B, n_v, D, split_all);
+  const int nsplit = D / (16 * pass_nt(B, n_v, D));
   size_t bytes = (size_t)B * n_v * n_chunks * rec_bytes(D, split_all);
-  if (cfg.nsplit > 1) {
-    bytes += (size_t)B * Lb * n_v * D * 4;                       // unnormalised o
-    bytes += (size_t)B * Lb * n_v * cfg.nsplit * cfg.nw * 4;     // partial sums of squares
+  if (nsplit > 1) {
+    bytes += (size_t)B * Lb * n_v * D * 4;             // unnormalised o
+    bytes += (size_t)B * Lb * n_v * nsplit * 4;        // partial sums of squares
     bytes = (bytes + 255) / 256 * 256;
   }
   return bytes;
@@ -899,17 +942,18 @@ void prefill_ws_layout(PrefillArgs& p, int D, bool split_all) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hipStream_t st) {
+  const int nt = pass_nt(p.B, p.n_v, D);
   if (act_dtype == kActBf16) {
-    const PassCfg cfg = pass_cfg(p.B, p.n_v, D, false);
-    if (D == 32) return launch_r<bf16_t, 32, false, 2, 1>(p, R, st);
-    if (D == 64) return launch_r<bf16_t, 64, false, 4, 1>(p, R, st);
+    if (D == 32) return launch_r<bf16_t, 32, false, 2>(p, R, st);
+    if (D == 64) return launch_r<bf16_t, 64, false, 4>(p, R, st);
     if (D == 128) {
-      if (cfg.nsplit == 1) return launch_r<bf16_t, 128, false, 4, 2>(p, R, st);
-      return launch_r<bf16_t, 128, false, 2, 1>(p, R, st);
+      if (nt == 8) return launch_r<bf16_t, 128, false, 8>(p, R, st);
+      if (nt == 4) return launch_r<bf16_t, 128, false, 4>(p, R, st);
+      return launch_r<bf16_t, 128, false, 2>(p, R, st);
     }
   } else {
-    if (D == 32) return launch_r<float, 32, true, 2, 1>(p, R, st);
-    if (D == 64) return launch_r<float, 64, true, 4, 1>(p, R, st);
+    if (D == 32) return launch_r<float, 32, true, 2>(p, R, st);
+    if (D == 64) return launch_r<float, 64, true, 4>(p, R, st);
   }
   return hipErrorInvalidValue;
 }

@@ -99,6 +99,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc* desc, int B, int Lb);
  *   out   [B][Lb][n_v*d_v] gated-RMSNorm output; rows >= len[b] carry no meaning
  *   ws    device workspace of at least gdn_prefill_workspace_bytes(desc, B, Lb) bytes, 256-aligned;
  *         its contents on entry do not matter and are garbage on return
+ * Limits: B <= 65535 and Lb * n_v * d_v < 2^31 (GDN_EINVAL otherwise).
  * Must not alias: out with any input; state or conv_tail with anything else.
  */
 int gdn_prefill_chunk(const gdn_desc* desc, const gdn_weights* w, const void* mixed, const void* z,
