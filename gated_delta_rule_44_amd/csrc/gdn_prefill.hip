@@ -158,14 +158,29 @@ struct Act4<bf16_t> {
   }
 };
 
+// two adjacent activations (4 bytes of bf16 or 8 of fp32)
+template <typename ActT>
+struct Pair {
+  static __device__ __forceinline__ float2 load(const ActT* p) {
+    const uint32_t u = *(const uint32_t*)p;
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+  }
+};
+template <>
+struct Pair<float> {
+  static __device__ __forceinline__ float2 load(const float* p) { return *(const float2*)p; }
+};
+
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // -------------------------------------------------------------------------------------------------
 template <typename ActT, int D, int R, bool SPLIT>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   using RC = Rec<D, SPLIT>;
+  constexpr int NWV = 8, NTH = 64 * NWV;      // two waves per SIMD: one's waits overlap the other's work
+  constexpr int TPW = C64 / NWV;              // tokens per wave in the conv stage
   constexpr int KD = D / 32, HM = D / 16;
-  constexpr int CPL = D >= 64 ? D / 64 : 1;   // channels per lane in the conv stage
+  constexpr int CPL = D >= 64 ? D / 64 : 1;   // channels per lane in the conv stage (adjacent)
   constexpr int LQ = D + 8;                   // halfs per row, token-major f16 tiles
   constexpr int LT = C64 + 4;                 // floats per row, channel-major fp32 tiles and Gram results
   constexpr int LF = C64 + 1;                 // floats per row, A and T
@@ -185,6 +200,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
   constexpr int OFF_B = OFF_G + R * C64 * 4;
   constexpr int LDS = OFF_B + R * C64 * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(CPL == 1 || (CPL == 2 && D == 128), "channel layout");
   __shared__ __attribute__((aligned(16))) char smem[LDS];
   _Float16* sQh = (_Float16*)(smem + OFF_R1);
   _Float16* sQl = sQh + C64 * LQ;
@@ -205,7 +221,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
   const int t0 = c * C64;
   const int len = p.len[b];
   if (t0 >= len) return;  // all padding: the state pass stops before this chunk
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so addresses built on it stay scalar
   const int g16 = lane >> 4, r16 = lane & 15;
   const int Lb = p.Lb, C = p.C, n_k = p.n_k;
   const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
@@ -231,36 +248,47 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
     sBet[w * C64 + lane] = be;
   }
 
-  // ---- 2. conv + SiLU: wave w owns tokens 16w..16w+15, lane owns channels lane*CPL + j ------------
+  // ---- 2. conv + SiLU: wave w owns tokens TPW w .. TPW w + TPW-1, lane owns channels CPL lane + j --
   // every load below is unconditional from a clamped, in-range address and masked afterwards, so
-  // that the compiler issues them all before the first wait
-  auto conv16 = [&](int gc_base, float (*y)[CPL]) {
-    float x[19][CPL], wt[4][CPL];
+  // that the compiler issues them all before the first wait; two adjacent channels share one load
+  auto conv = [&](int gc_base, float (*y)[CPL]) {
+    float x[TPW + 3][CPL], wt[4][CPL];
+    if (CPL == 2) {
+      const int gc = gc_base + 2 * lane;
+      const float4 wa = Act4<ActT>::load(cw + gc * 4), wb = Act4<ActT>::load(cw + gc * 4 + 4);
+      wt[0][0] = wa.x; wt[1][0] = wa.y; wt[2][0] = wa.z; wt[3][0] = wa.w;
+      wt[0][CPL - 1] = wb.x; wt[1][CPL - 1] = wb.y; wt[2][CPL - 1] = wb.z; wt[3][CPL - 1] = wb.w;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int ch = lane * CPL + j;
-      const bool ok = ch < D;
-      const int gc = gc_base + (ok ? ch : 0);
+      for (int i = 0; i < TPW + 3; ++i) {
+        const int t = t0 + TPW * w - 3 + i;
+        const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
+        const float2 v = Pair<ActT>::load(src + gc);
+        x[i][0] = t < Lb ? v.x : 0.f;
+        x[i][CPL - 1] = t < Lb ? v.y : 0.f;
+      }
+    } else {
+      const bool ok = lane < D;
+      const int gc = gc_base + (ok ? lane : 0);
       const float m = ok ? 1.f : 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wt[q][j] = m * to_f32(cw[gc * 4 + q]);
+      for (int q = 0; q < 4; ++q) wt[q][0] = m * to_f32(cw[gc * 4 + q]);
 #pragma unroll
-      for (int i = 0; i < 19; ++i) {
-        const int t = t0 + 16 * w - 3 + i;
+      for (int i = 0; i < TPW + 3; ++i) {
+        const int t = t0 + TPW * w - 3 + i;
         const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
         const float v = to_f32(src[gc]);
-        x[i][j] = t < Lb ? v : 0.f;
+        x[i][0] = t < Lb ? v : 0.f;
       }
     }
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt)
+    for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
       for (int j = 0; j < CPL; ++j)
         y[tt][j] = silu(wt[0][j] * x[tt][j] + wt[1][j] * x[tt + 1][j] + wt[2][j] * x[tt + 2][j] + wt[3][j] * x[tt + 3][j]);
   };
-  auto l2norm16 = [&](float (*y)[CPL]) {
+  auto l2norm = [&](float (*y)[CPL]) {
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
+    for (int tt = 0; tt < TPW; ++tt) {
       float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) ss += y[tt][j] * y[tt][j];
@@ -270,61 +298,70 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
       for (int j = 0; j < CPL; ++j) y[tt][j] *= rn;
     }
   };
-  float qn[16][CPL], kn[16][CPL], vv[R][16][CPL];
-  conv16(kh * D, qn);
-  conv16(n_k * D + kh * D, kn);
+  float qn[TPW][CPL], kn[TPW][CPL], vv[R][TPW][CPL];
+  conv(kh * D, qn);
+  conv(n_k * D + kh * D, kn);
 #pragma unroll
-  for (int r = 0; r < R; ++r) conv16(2 * n_k * D + (kh * R + r) * D, vv[r]);
-  l2norm16(qn);
-  l2norm16(kn);
+  for (int r = 0; r < R; ++r) conv(2 * n_k * D + (kh * R + r) * D, vv[r]);
+  l2norm(qn);
+  l2norm(kn);
   // token-major 2^8 q, 2^8 k (hi/lo) for the Gram products; channel-major k in fp32
+  if (CPL * lane < D) {
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int ch = lane * CPL + j;
-    if (ch < D) {
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int o = (TPW * w + tt) * LQ + CPL * lane;
+      _Float16 qh[CPL], ql[CPL], kh_[CPL], kl[CPL];
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) {
-        const int o = (16 * w + tt) * LQ + ch;
-        split_f16(kS8 * qn[tt][j], sQh[o], sQl[o]);
-        split_f16(kS8 * kn[tt][j], sKh[o], sKl[o]);
+      for (int j = 0; j < CPL; ++j) {
+        split_f16(kS8 * qn[tt][j], qh[j], ql[j]);
+        split_f16(kS8 * kn[tt][j], kh_[j], kl[j]);
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(float4*)&sKt[ch * LT + 16 * w + 4 * q] = make_float4(kn[4 * q][j], kn[4 * q + 1][j], kn[4 * q + 2][j], kn[4 * q + 3][j]);
+      if (CPL == 2) {
+        *(f16x2*)&sQh[o] = f16x2{qh[0], qh[CPL - 1]};
+        *(f16x2*)&sQl[o] = f16x2{ql[0], ql[CPL - 1]};
+        *(f16x2*)&sKh[o] = f16x2{kh_[0], kh_[CPL - 1]};
+        *(f16x2*)&sKl[o] = f16x2{kl[0], kl[CPL - 1]};
+      } else {
+        sQh[o] = qh[0]; sQl[o] = ql[0]; sKh[o] = kh_[0]; sKl[o] = kl[0];
+      }
     }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+      for (int q = 0; q < TPW / 4; ++q)
+        *(float4*)&sKt[(CPL * lane + j) * LT + TPW * w + 4 * q] =
+            make_float4(kn[4 * q][j], kn[4 * q + 1][j], kn[4 * q + 2][j], kn[4 * q + 3][j]);
   }
   lds_barrier();
 
   // ---- 3. Gram products on the lower 16x16 tiles (split operands) --------------------------------
   // K K^T as [r][s] (for A); K Q^T computed as D[s][t] so that each lane ends up with four
-  // consecutive s of one row t of Q K^T (for P~)
-  for (int job = w; job < 20; job += 4) {
+  // consecutive s of one row t of Q K^T (for P~). The three split terms go to separate accumulators.
+  for (int job = w; job < 20; job += NWV) {
     const int prod = job / 10, tile = job % 10;       // tiles (mt, nt), nt <= mt, in row order
     const int mt = tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0;
     const int nt = tile - mt * (mt + 1) / 2;
     // KK: A = K rows 16mt, B = K rows 16nt.  KQ: A = K rows 16nt (s), B = Q rows 16mt (t)
-    const _Float16* ah = sKh;
-    const _Float16* al = sKl;
     const _Float16* bh = prod ? sQh : sKh;
     const _Float16* bl = prod ? sQl : sKl;
     const int ra0 = prod ? 16 * nt : 16 * mt, rb0 = prod ? 16 * mt : 16 * nt;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
     f16x8 fah[KD], fal[KD], fbh[KD], fbl[KD];
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) {
       const int ra = (ra0 + r16) * LQ + 32 * ks + 8 * g16, rb = (rb0 + r16) * LQ + 32 * ks + 8 * g16;
-      fah[ks] = ld16(ah + ra);
-      fal[ks] = ld16(al + ra);
+      fah[ks] = ld16(sKh + ra);
+      fal[ks] = ld16(sKl + ra);
       fbh[ks] = ld16(bh + rb);
       fbl[ks] = ld16(bl + rb);
     }
-    __builtin_amdgcn_sched_barrier(0);  // the reads go out together, then the MFMAs
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) {
-      acc = mfma16(fal[ks], fbh[ks], acc);
-      acc = mfma16(fah[ks], fbl[ks], acc);
-      acc = mfma16(fah[ks], fbh[ks], acc);
+      a0 = mfma16(fal[ks], fbh[ks], a0);
+      a1 = mfma16(fah[ks], fbl[ks], a1);
+      a2 = mfma16(fah[ks], fbh[ks], a2);
     }
+    const f32x4 acc = a2 + (a0 + a1);
     if (prod) {
       *(f32x4*)&sQK[(16 * mt + r16) * LT + 16 * nt + 4 * g16] = acc;
     } else {
@@ -332,13 +369,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
       for (int i = 0; i < 4; ++i) sKK[(16 * mt + 4 * g16 + i) * LT + 16 * nt + r16] = acc[i];
     }
   }
-  // this wave's rows of 2^8 q (token tile w) as fragments, kept in registers for every value head
-  f16x8 qfh[KD], qfl[KD];
+  // rows of 2^8 q as fragments (token tile mt = q & 3, 32-block kk = q >> 2 for q = w, w + 8, ...),
+  // kept in registers for every value head
+  constexpr int QPW = (4 * KD + NWV - 1) / NWV;
+  f16x8 qfh[QPW], qfl[QPW];
 #pragma unroll
-  for (int kk = 0; kk < KD; ++kk) {
-    const int row = (16 * w + r16) * LQ + 32 * kk;
-    qfh[kk] = frag_row_h(sQh + row, g16);
-    qfl[kk] = frag_row_h(sQl + row, g16);
+  for (int i = 0; i < QPW; ++i) {
+    const int q = w + NWV * i < 4 * KD ? w + NWV * i : 0;
+    const int row = (16 * (q & 3) + r16) * LQ + 32 * (q >> 2);
+    qfh[i] = frag_row_h(sQh + row, g16);
+    qfl[i] = frag_row_h(sQl + row, g16);
   }
   lds_barrier();
 
@@ -351,24 +391,20 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
     const float gC = gam[C64 - 1];
 
     // A (strictly lower, fp32), T's upper blocks cleared, this head's v channel-major
-    for (int idx = tid; idx < C64 * C64; idx += 256) {
+    for (int idx = tid; idx < C64 * C64; idx += NTH) {
       const int i = idx >> 6, j = idx & 63;
       sA[i * LF + j] = j < i ? bet[i] * __expf(gam[i] - gam[j]) * (kInvS16 * sKK[i * LT + j]) : 0.f;
       if ((j >> 4) > (i >> 4)) sTf[i * LF + j] = 0.f;
     }
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {  // compile-time index into vv (a runtime one would go to scratch)
-      if (rr != r) continue;
+      if (rr != r || CPL * lane >= D) continue;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int ch = lane * CPL + j;
-        if (ch < D) {
+      for (int j = 0; j < CPL; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *(float4*)&sVt[ch * LT + 16 * w + 4 * q] =
-                make_float4(vv[rr][4 * q][j], vv[rr][4 * q + 1][j], vv[rr][4 * q + 2][j], vv[rr][4 * q + 3][j]);
-        }
-      }
+        for (int q = 0; q < TPW / 4; ++q)
+          *(float4*)&sVt[(CPL * lane + j) * LT + TPW * w + 4 * q] =
+              make_float4(vv[rr][4 * q][j], vv[rr][4 * q + 1][j], vv[rr][4 * q + 2][j], vv[rr][4 * q + 3][j]);
     }
     lds_barrier();
 
@@ -388,23 +424,27 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
       for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LF + 16 * blk + jj] = x[i];
     }
     {
-      // Q~ (token tile w): 2^8 scale e^{gamma_t} q_t
-      const int t = 16 * w + r16;
-      const float fq = p.scale * __expf(gam[t]);
+      // Q~ (token tile q & 3, block q >> 2): 2^8 scale e^{gamma_t} q_t
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        float x[8];
+      for (int i = 0; i < QPW; ++i) {
+        const int q = w + NWV * i;
+        if (q < 4 * KD) {
+          const int mt = q & 3, kk = q >> 2;
+          const float fq = p.scale * __expf(gam[16 * mt + r16]);
+          float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qfh[kk][e] + (float)qfl[kk][e]);
-        f16x8 hi, lo;
-        split8(x, hi, lo);
-        put_frag(rec, RC::Q_HI + w * KD + kk, lane, hi);
-        put_frag(rec, RC::Q_LO + w * KD + kk, lane, lo);
+          for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qfh[i][e] + (float)qfl[i][e]);
+          f16x8 hi, lo;
+          split8(x, hi, lo);
+          put_frag(rec, RC::Q_HI + mt * KD + kk, lane, hi);
+          put_frag(rec, RC::Q_LO + mt * KD + kk, lane, lo);
+        }
       }
-      // P~ (token tile w): 2^8 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
-      const float gt = gam[t];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      // P~ (token tile w & 3, block w >> 2): 2^8 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
+      {
+        const int mt = w & 3, kk = w >> 2;
+        const int t = 16 * mt + r16;
+        const float gt = gam[t];
         float x[8];
         frag_row_f(sQK + t * LT + 32 * kk, g16, x);
 #pragma unroll
@@ -414,30 +454,27 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
         }
         f16x8 hi, lo;
         split8(x, hi, lo);
-        put_frag(rec, RC::P_HI + w * 2 + kk, lane, hi);
-        put_frag(rec, RC::P_LO + w * 2 + kk, lane, lo);
+        put_frag(rec, RC::P_HI + mt * 2 + kk, lane, hi);
+        put_frag(rec, RC::P_LO + mt * 2 + kk, lane, lo);
       }
-      // K~^T (row tiles hm = w, w+4, ...): 2^8 e^{gamma_C - gamma_s} k_s
+      // K~^T (row tile idx >> 1, block idx & 1 for idx = w, w + 8, ...): 2^8 e^{gamma_C - gamma_s} k_s
+      for (int idx = w; idx < 2 * HM; idx += NWV) {
+        const int hm = idx >> 1, kk = idx & 1;
+        float x[8];
+        frag_row_f(sKt + (16 * hm + r16) * LT + 32 * kk, g16, x);
 #pragma unroll
-      for (int hm = w; hm < HM; hm += 4) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          float x[8];
-          frag_row_f(sKt + (16 * hm + r16) * LT + 32 * kk, g16, x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= kS8 * __expf(gC - gam[32 * kk + kslot(g16, e)]);
-          f16x8 hi, lo;
-          split8(x, hi, lo);
-          put_frag(rec, RC::K_HI + hm * 2 + kk, lane, hi);
-          put_frag(rec, RC::K_LO + hm * 2 + kk, lane, lo);
-        }
+        for (int e = 0; e < 8; ++e) x[e] *= kS8 * __expf(gC - gam[32 * kk + kslot(g16, e)]);
+        f16x8 hi, lo;
+        split8(x, hi, lo);
+        put_frag(rec, RC::K_HI + hm * 2 + kk, lane, hi);
+        put_frag(rec, RC::K_LO + hm * 2 + kk, lane, lo);
       }
     }
     lds_barrier();
     // off-diagonal blocks by level (i - j = 1, 2, 3): T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, fp32 MFMA
-    float* sXw = sX + w * 16 * 17;
     for (int lvl = 1; lvl < 4; ++lvl) {
       if (w < 4 - lvl) {
+        float* sXw = sX + w * 16 * 17;
         const int j = w, i = w + lvl;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int k = j; k < i; ++k)
@@ -455,7 +492,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
       }
       lds_barrier();
     }
-    for (int idx = tid; idx < C64 * C64; idx += 256) {
+    for (int idx = tid; idx < C64 * C64; idx += NTH) {
       const int i = idx >> 6, j = idx & 63;
       const float tv = kS8 * sTf[i * LF + j];
       if (SPLIT) split_f16(tv, sT[i * LDT + j], sT[C64 * LDT + i * LDT + j]);
@@ -463,16 +500,21 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
     }
     lds_barrier();
 
-    // W and U' for token tile w. T's row fragments serve as the B operand of W^T = (beta e^gamma K)^T T^T
-    // and as the A operand of U' = T (beta V).
-    {
-      f16x8 th[2], tl[2];
+    // W and U'. T's row fragments (all four token tiles) serve as the B operand of
+    // W^T = (beta e^gamma K)^T T^T and as the A operand of U' = T (beta V); wave w takes d_k tiles
+    // j = w, w + 8, ... of W^T and value tiles nt = w, w + 8, ... of U', so that each operand
+    // fragment built from K or V is made once.
+    if (w < HM) {
+      f16x8 th[4][2], tl[4][2];
       float fk[2][8], fv[2][8];  // per-token factors of this lane's fragment slots
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int rt = (16 * w + r16) * LDT + 32 * ks;
-        th[ks] = frag_row_h(sT + rt, g16);
-        tl[ks] = SPLIT ? frag_row_h(sT + C64 * LDT + rt, g16) : th[ks];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int rt = (16 * mt + r16) * LDT + 32 * ks;
+          th[mt][ks] = frag_row_h(sT + rt, g16);
+          tl[mt][ks] = SPLIT ? frag_row_h(sT + C64 * LDT + rt, g16) : th[mt][ks];
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int s = 32 * ks + kslot(g16, e);
@@ -480,58 +522,69 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs p) {
           fk[ks][e] = fv[ks][e] * __expf(gam[s]);
         }
       }
-      // W^T tiles 2kk, 2kk+1 give lane by lane the W fragment of block kk
+      for (int j = w; j < HM; j += NWV) {
+        // W^T tile (j, mt) = (2^8 beta e^gamma K)^T (2^8 T)^T = 2^16 W^T; lane (g, c) holds
+        // W[16 mt + c][16 j + 4 g + i], half (j & 1) of the fragment of block j >> 1
+        f16x8 kbh[2], kbl[2];
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        f32x4 acc[2];
+        for (int ks = 0; ks < 2; ++ks) {
+          float x[8];
+          frag_row_f(sKt + (16 * j + r16) * LT + 32 * ks, g16, x);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = 2 * kk + jj;
-          acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int e = 0; e < 8; ++e) x[e] *= fk[ks][e];
+          split8(x, kbh[ks], kbl[ks]);
+        }
+        f32x4 acc[4];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            float x[8];
-            frag_row_f(sKt + (16 * j + r16) * LT + 32 * ks, g16, x);
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] *= fk[ks][e];
-            f16x8 kbh, kbl;
-            split8(x, kbh, kbl);
-            if (SPLIT) {
-              acc[jj] = mfma16(kbl, th[ks], acc[jj]);
-              acc[jj] = mfma16(kbh, tl[ks], acc[jj]);
-            }
-            acc[jj] = mfma16(kbh, th[ks], acc[jj]);
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(kbh[ks], th[mt][ks], acc[mt]);
+          if (SPLIT) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(kbl[ks], th[mt][ks], acc[mt]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(kbh[ks], tl[mt][ks], acc[mt]);
           }
         }
-        // acc = (2^8 beta e^gamma K)^T (2^8 T)^T = 2^16 W^T
-        float x[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = -kInvS16 * acc[0][i];
-          x[4 + i] = -kInvS16 * acc[1][i];
+        for (int mt = 0; mt < 4; ++mt) {
+          f16x4 hi, lo;
+          split4(acc[mt] * -kInvS16, hi, lo);
+          char* dst = rec + (RC::W_HI + mt * KD + (j >> 1)) * 1024 + lane * 16 + 8 * (j & 1);
+          *(f16x4*)dst = hi;
+          if (SPLIT) *(f16x4*)(dst + 4 * KD * 1024) = lo;
         }
-        f16x8 hi, lo;
-        split8(x, hi, lo);
-        put_frag(rec, RC::W_HI + w * KD + kk, lane, hi);
-        if (SPLIT) put_frag(rec, RC::W_LO + w * KD + kk, lane, lo);
       }
-      // U' tiles (w, nt): (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
-#pragma unroll
-      for (int nt = 0; nt < HM; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int nt = w; nt < HM; nt += NWV) {
+        // U' tile (mt, nt) = (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
+        f16x8 vh[2], vl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           float x[8];
           frag_row_f(sVt + (16 * nt + r16) * LT + 32 * ks, g16, x);
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] *= fv[ks][e];
-          f16x8 vh, vl;
-          split8(x, vh, vl);
-          if (SPLIT) acc = mfma16(tl[ks], vh, acc);
-          acc = mfma16(th[ks], vl, acc);
-          acc = mfma16(th[ks], vh, acc);
+          split8(x, vh[ks], vl[ks]);
         }
-        *(f32x4*)(rec + (RC::UP + w * HM + nt) * 1024 + lane * 16) = acc * kInvS8;
+        f32x4 a0[4], a1[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) a0[mt] = a1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) a0[mt] = mfma16(th[mt][ks], vl[ks], a0[mt]);
+          if (SPLIT) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) a0[mt] = mfma16(tl[mt][ks], vh[ks], a0[mt]);
+          }
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) a1[mt] = mfma16(th[mt][ks], vh[ks], a1[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          *(f32x4*)(rec + (RC::UP + mt * HM + nt) * 1024 + lane * 16) = (a1[mt] + a0[mt]) * kInvS8;
       }
     }
     if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gC);
@@ -576,7 +629,8 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
   const int lid = (nblk & 7) == 0 ? (bid & 7) * (nblk >> 3) + (bid >> 3) : bid;
   const int split = lid % NSPLIT, hb = lid / NSPLIT;
   const int h = hb % p.n_v, b = hb / p.n_v;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: record addresses stay scalar
   const int g16 = lane >> 4, r16 = lane & 15;
   const int Lb = p.Lb, n_v = p.n_v, C = p.C;
   const int len = p.len[b];
@@ -886,11 +940,13 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
 }
 
 // ---- launch configuration --------------------------------------------------------------------------
-// value columns per state-pass workgroup: the whole head when there are enough (sequence, head) pairs
-// to fill the chip, else slices, so that a short batch still spreads its chunk chains over more CUs
+// 16-column tiles per state-pass workgroup. A head's chain of chunks is sequential, so the only way
+// to spread a short batch over the 256 CUs is to split its value columns: NSPLIT = 256 / (B n_v)
+// slices (a power of two, at most 8), the whole head once there are 256 (sequence, head) pairs.
 int pass_nt(int B, int n_v, int D) {
-  if (D == 128) return B * n_v >= 128 ? 8 : B * n_v >= 48 ? 4 : 2;
-  return D / 16;
+  if (D != 128) return D / 16;
+  const long pairs = (long)B * n_v;
+  return pairs >= 256 ? 8 : pairs >= 128 ? 4 : pairs >= 64 ? 2 : 1;
 }
 
 long rec_bytes(int D, bool split_all) {
@@ -901,7 +957,7 @@ long rec_bytes(int D, bool split_all) {
 template <typename ActT, int D, int R, bool SPLIT, int NT>
 hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   constexpr int NSPLIT = D / (16 * NT);
-  hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NSPLIT == 1, (NT <= 4)>), dim3(NSPLIT * p.n_v * p.B), dim3(256), 0, st, p);
@@ -949,7 +1005,8 @@ hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hip
     if (D == 128) {
       if (nt == 8) return launch_r<bf16_t, 128, false, 8>(p, R, st);
       if (nt == 4) return launch_r<bf16_t, 128, false, 4>(p, R, st);
-      return launch_r<bf16_t, 128, false, 2>(p, R, st);
+      if (nt == 2) return launch_r<bf16_t, 128, false, 2>(p, R, st);
+      return launch_r<bf16_t, 128, false, 1>(p, R, st);
     }
   } else {
     if (D == 32) return launch_r<float, 32, true, 2>(p, R, st);

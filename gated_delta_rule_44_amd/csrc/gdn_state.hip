@@ -13,6 +13,26 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// kUnroll 16-byte vectors of one range per thread: every load is issued before the first store, and
+// whole blocks (all but the last of a range) take the branch-free path so that the compiler does not
+// wait on each load separately
+__device__ __forceinline__ void copy_range(const u32x4* s, u32x4* d, long n, long base) {
+  u32x4 v[kUnroll];
+  if (base + (long)(kUnroll - 1) * kThreads < n) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(s + base + (long)u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v[u], d + base + (long)u * kThreads);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const long k = base + (long)u * kThreads;
+      if (k < n) d[k] = s[k];
+    }
+  }
+}
 
 __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs p) {
   const int i = blockIdx.y;
@@ -20,40 +40,13 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs p) {
   const long di = p.dst_idx ? (long)p.dst_idx[i] : (long)i;
   const long nstate = p.src_state ? p.state_floats / 4 : 0;   // 16-byte vectors
   const long ntail = p.src_tail ? p.tail_bytes / 16 : 0;
-  const long base = ((long)blockIdx.x * kThreads * kUnroll) + threadIdx.x;
-  uint4 v[kUnroll];
-  // state part
-  if (base < nstate) {
-    const uint4* s = (const uint4*)(p.src_state + si * p.state_floats);
-    uint4* d = (uint4*)(p.dst_state + di * p.state_floats);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const long k = base + (long)u * kThreads;
-      if (k < nstate) v[u] = s[k];
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const long k = base + (long)u * kThreads;
-      if (k < nstate) d[k] = v[u];
-    }
-  }
-  // tail part (its own block range after the state's)
-  const long nsb = (nstate + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-  const long tb = (long)blockIdx.x - nsb;
-  if (tb >= 0 && ntail > 0) {
-    const long tbase = tb * kThreads * kUnroll + threadIdx.x;
-    const uint4* s = (const uint4*)((const char*)p.src_tail + si * p.tail_bytes);
-    uint4* d = (uint4*)((char*)p.dst_tail + di * p.tail_bytes);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const long k = tbase + (long)u * kThreads;
-      if (k < ntail) v[u] = s[k];
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const long k = tbase + (long)u * kThreads;
-      if (k < ntail) d[k] = v[u];
-    }
+  const long nsb = (nstate + kThreads * kUnroll - 1) / (kThreads * kUnroll);  // blocks of the state part
+  if ((long)blockIdx.x < nsb) {
+    copy_range((const u32x4*)(p.src_state + si * p.state_floats), (u32x4*)(p.dst_state + di * p.state_floats), nstate,
+               (long)blockIdx.x * kThreads * kUnroll + threadIdx.x);
+  } else if (ntail > 0) {  // the tail part takes its own block range after the state's
+    copy_range((const u32x4*)((const char*)p.src_tail + si * p.tail_bytes), (u32x4*)((char*)p.dst_tail + di * p.tail_bytes),
+               ntail, ((long)blockIdx.x - nsb) * kThreads * kUnroll + threadIdx.x);
   }
 }
 

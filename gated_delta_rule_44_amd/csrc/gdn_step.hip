@@ -1,6 +1,6 @@
 // Single-token recurrence for decode and for verify-with-checkpoints (gfx950).
 //
-// One workgroup per (key head kh, sequence b) runs T tokens one after the other: the conv on the
+// Work item = (key head kh, sequence b): T tokens one after the other through the conv on the
 // channels of key head kh (its q and k channels and the v channels of its R value heads), the q/k L2
 // norm, the gates, one delta-rule step per value head, the gated RMSNorm, and the state/tail stores.
 // Decode is T = 1 writing back to the pool row; verify writes each token's state and tail to its
@@ -12,157 +12,196 @@
 //   H <- e^g H;  u = beta (v - H^T k);  H <- H + k u^T;  o = scale H^T q
 // computed from one read of the old H:  u = beta (v - e^g H_old^T k),
 //   o = scale (e^g H_old^T q + (k.q) u),  H_new = e^g H_old + k u^T.
-// The state is HBM-streamed fp32: each thread holds a 4-column x RPT-row block of H in registers,
-// column partial sums are reduced across row groups with lane shuffles, then across waves in LDS.
+//
+// The state is HBM-streamed fp32, read and written exactly once per call. Each value head has its own
+// 256 threads (the workgroup is 256 R threads); a thread holds a 4-column x RPT-row block of its head's
+// H in registers; column partial sums are reduced across the row groups of a wave with lane shuffles
+// and across the head's waves in LDS. The register footprint is kept small enough for two workgroups
+// per CU, so that one workgroup's loads overlap another's arithmetic and stores. Keeping the q/k
+// channels of a key head in one workgroup is what lets decode update the conv tail in place without a
+// race.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
+// No implicit contraction: every fused multiply-add below is written out, so the rounding of a token
+// step is fixed by the source and identical wherever the compiler places the code (a verify token is
+// bitwise the decode step).
 #pragma clang fp contract(off)
 
 namespace gdn {
 
 namespace {
 
-constexpr int kMaxChanPerThread = 6;  // (2*128 + 4*128) / 256 = 3 with R <= 4; room to spare
+// Barrier for LDS only: __syncthreads() would also wait for the next item's state loads (vmcnt).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// 256 threads per workgroup; for R <= 2 the register budget is capped so that two workgroups share
-// a CU and one workgroup's state loads overlap the other's arithmetic and stores
-template <int D>
-struct StepThreads {
-  static constexpr int value = 256;
+template <int D, int R>
+struct StepShape {
+  static constexpr int HT = 256;                               // threads per value head
+  static constexpr int NTH = HT * R;
+  static constexpr int QD = D / 4;                             // column quads per row
+  static constexpr int RG = HT / QD;                           // row groups per head
+  static constexpr int RPT = D / RG;                           // rows per thread
 };
 
 template <typename ActT, int D, int R>
-__global__ __launch_bounds__(StepThreads<D>::value) __attribute__((amdgpu_waves_per_eu(R <= 2 ? 2 : 1))) void step_kernel(StepArgs p) {
-  constexpr int kThreads = StepThreads<D>::value;
-  constexpr int QD = D / 4;              // column quads per row
-  constexpr int RG = kThreads / QD;      // row groups
-  constexpr int RPT = D / RG;            // rows per thread (>= 1 since D*D >= 4*256 for D >= 32)
-  constexpr int NCH = 2 * D + R * D;     // channels owned by this workgroup
-  constexpr int CPT = (NCH + kThreads - 1) / kThreads;
-  static_assert(RPT >= 1 && RG * RPT == D, "thread layout");
-  static_assert(CPT <= kMaxChanPerThread, "channels per thread");
+__global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p) {
+  using S = StepShape<D, R>;
+  constexpr int HT = S::HT, NTH = S::NTH, QD = S::QD, RPT = S::RPT, HW = HT / kWave;
+  constexpr int NCH = 2 * D + R * D;         // channels owned by an item
+  constexpr int CPT = (NCH + NTH - 1) / NTH;
+  static_assert(RPT >= 1 && S::RG * RPT == D, "thread layout");
+  static_assert(QD <= kWave && kWave % QD == 0, "a wave holds whole row groups");
+  static_assert(HT >= 2 * D, "one thread per column sum");
 
-  __shared__ float sY[NCH];              // conv outputs of the current token: q | k | v(R heads)
-  __shared__ float sRed[kThreads / kWave][2][D];
+  __shared__ float sY[NCH];                  // conv outputs of the current token: q | k | v(R heads)
+  __shared__ float sRed[R][HW][2][D];        // per head, per wave: partial H^T k and H^T q
+  __shared__ __attribute__((aligned(16))) float sTot[R][2][D];  // per head: H^T k and H^T q
 
-  const int kh = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int cq = tid % QD, rg = tid / QD;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int r = tid / HT;                    // value head of the group owned by this thread
+  const int th = tid % HT;
+  const int hw = th / kWave;                 // wave inside the head's threads
+  const int cq = th % QD, rg = th / QD;
   const int n_k = p.n_k, n_v = p.n_v, C = p.C;
-  const long s = p.slot ? (long)p.slot[b] : (long)b;
-  const long SZ = (long)n_v * D * D;      // state floats per record
-  const long TZ = 3L * C;                 // tail elements per record
+  const long SZ = (long)n_v * D * D;         // state floats per record
+  const long TZ = 3L * C;                    // tail elements per record
 
   const ActT* conv_w = (const ActT*)p.conv_w;
   const ActT* mixed = (const ActT*)p.mixed;
   const ActT* zin = (const ActT*)p.z;
   const ActT* ain = (const ActT*)p.a;
   const ActT* bin = (const ActT*)p.b;
-  const ActT* tail_in = (const ActT*)p.tail_in + s * TZ;
   ActT* out = (ActT*)p.out;
 
-  // channel ownership, conv weights and tail rows in registers
-  int gch[CPT];
-  float w0[CPT], w1[CPT], w2[CPT], w3[CPT], t0[CPT], t1[CPT], t2[CPT];
+  auto slot_of = [&](int item) { const int b = item / n_k; return p.slot ? (long)p.slot[b] : (long)b; };
+  // this thread's block of its head's state: rows rg*RPT + i, columns 4 cq .. 4 cq + 3
+  auto state_src = [&](int item) {
+    const int kh = item % n_k;
+    return p.state_in + slot_of(item) * SZ + (long)(kh * R + r) * D * D + (long)(rg * RPT) * D + 4 * cq;
+  };
+  auto load_H = [&](f32x4 (&H)[RPT], int item) {
+    const float* src = state_src(item);
 #pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int lc = tid + j * kThreads;
-    int gc = -1;
-    if (lc < D) gc = kh * D + lc;
-    else if (lc < 2 * D) gc = n_k * D + kh * D + (lc - D);
-    else if (lc < NCH) gc = 2 * n_k * D + kh * R * D + (lc - 2 * D);
-    gch[j] = gc;
-    const int gl = gc >= 0 ? gc : 0;  // unconditional loads (a clamped channel for unowned slots)
-    w0[j] = to_f32(conv_w[gl * 4 + 0]);
-    w1[j] = to_f32(conv_w[gl * 4 + 1]);
-    w2[j] = to_f32(conv_w[gl * 4 + 2]);
-    w3[j] = to_f32(conv_w[gl * 4 + 3]);
-    t0[j] = to_f32(tail_in[0L * C + gl]);
-    t1[j] = to_f32(tail_in[1L * C + gl]);
-    t2[j] = to_f32(tail_in[2L * C + gl]);
-  }
+    for (int i = 0; i < RPT; ++i) H[i] = __builtin_nontemporal_load((const f32x4*)(src + (long)i * D));
+  };
 
-  // the R value heads' states in registers
-  float4 H[R][RPT];
+  // per-token activations of one item, loaded ahead of use
+  struct TokIn {
+    float x[CPT];   // pre-conv inputs of the owned channels
+    float av, bv;   // gate inputs of this thread's head
+    float z[4];     // z of this thread's output columns (row group 0 only)
+  };
+  float nw[4];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float* src = p.state_in + s * SZ + (long)(kh * R + r) * D * D;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) H[r][i] = *(const float4*)(src + (long)(rg * RPT + i) * D + 4 * cq);
-  }
+  for (int c = 0; c < 4; ++c) nw[c] = p.norm_w[4 * cq + c];
 
-  for (int t = 0; t < p.T; ++t) {
-    const long row = (long)b * p.T + t;
-    // ---- conv + SiLU on the owned channels, tail shift
+  f32x4 H[RPT];
+  {
+    const int item = blockIdx.x;
+    const int kh = item % n_k, b = item / n_k;
+    const int h = kh * R + r;
+    const long s = slot_of(item);
+    const ActT* tail_in = (const ActT*)p.tail_in + s * TZ;
+
+    // The item's small inputs are loaded before the next item's state: loads complete in issue
+    // order, so anything issued after that prefetch would wait for all of it.
+    int gch[CPT];
+    float w0[CPT], w1[CPT], w2[CPT], w3[CPT], t0[CPT], t1[CPT], t2[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int gc = gch[j];
-      const float x = to_f32(mixed[row * C + (gc >= 0 ? gc : 0)]);
-      if (gc >= 0) {
-        float pre = w0[j] * t0[j];
-        pre = pre + w1[j] * t1[j];
-        pre = pre + w2[j] * t2[j];
-        pre = pre + w3[j] * x;
-        sY[tid + j * kThreads] = silu(pre);
-        t0[j] = t1[j];
-        t1[j] = t2[j];
-        t2[j] = x;
-      }
+      const int lc = tid + j * NTH;
+      int gc = -1;
+      if (lc < D) gc = kh * D + lc;
+      else if (lc < 2 * D) gc = n_k * D + kh * D + (lc - D);
+      else if (lc < NCH) gc = 2 * n_k * D + kh * R * D + (lc - 2 * D);
+      gch[j] = gc;
+      const int gl = gc >= 0 ? gc : 0;  // unconditional loads (a clamped channel for unowned slots)
+      w0[j] = to_f32(conv_w[gl * 4 + 0]);
+      w1[j] = to_f32(conv_w[gl * 4 + 1]);
+      w2[j] = to_f32(conv_w[gl * 4 + 2]);
+      w3[j] = to_f32(conv_w[gl * 4 + 3]);
+      t0[j] = to_f32(tail_in[0L * C + gl]);
+      t1[j] = to_f32(tail_in[1L * C + gl]);
+      t2[j] = to_f32(tail_in[2L * C + gl]);
     }
-    // tail after this token: decode writes the pool row, verify the checkpoint row
-    {
-      ActT* to = (ActT*)p.tail_out + (p.verify ? row * TZ : s * TZ);
+    const float A = -__expf(p.A_log[h]), dtb = p.dt_bias[h];
+    auto load_tok = [&](TokIn& in, int t) {
+      const long row = (long)b * p.T + t;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) in.x[j] = to_f32(mixed[row * C + (gch[j] >= 0 ? gch[j] : 0)]);
+      in.av = to_f32(ain[row * n_v + h]);
+      in.bv = to_f32(bin[row * n_v + h]);
+      const long ob = row * (long)n_v * D + (long)h * D;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) in.z[c] = to_f32(zin[ob + 4 * cq + c]);
+    };
+    TokIn cur;
+    load_tok(cur, 0);
+    load_H(H, item);
+
+    for (int t = 0; t < p.T; ++t) {
+      const long row = (long)b * p.T + t;
+      TokIn in = cur;
+      if (t + 1 < p.T) load_tok(cur, t + 1);  // verify only
+      // ---- conv + SiLU on the owned channels, tail shift
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int gc = gch[j];
+        const float x = in.x[j];
         if (gc >= 0) {
-          to[0L * C + gc] = from_f32<ActT>(t0[j]);
-          to[1L * C + gc] = from_f32<ActT>(t1[j]);
-          to[2L * C + gc] = from_f32<ActT>(t2[j]);
+          float pre = w0[j] * t0[j];
+          pre = fmaf(w1[j], t1[j], pre);
+          pre = fmaf(w2[j], t2[j], pre);
+          pre = fmaf(w3[j], x, pre);
+          sY[tid + j * NTH] = silu(pre);
+          t0[j] = t1[j];
+          t1[j] = t2[j];
+          t2[j] = x;
         }
       }
-    }
-    __syncthreads();
-
-    // ---- q/k L2 norm and k.q (every wave computes them, no broadcast needed)
-    float sq = 0.f, sk = 0.f, skq = 0.f;
-    for (int i = lane; i < D; i += kWave) {
-      const float qv = sY[i], kv = sY[D + i];
-      sq = sq + qv * qv;
-      sk = sk + kv * kv;
-      skq = skq + kv * qv;
-    }
-    sq = wave_sum<kWave>(sq);
-    sk = wave_sum<kWave>(sk);
-    skq = wave_sum<kWave>(skq);
-    const float rq = rsqrt_fast(sq + p.l2_eps);
-    const float rk = rsqrt_fast(sk + p.l2_eps);
-    const float kq = (skq * rk) * rq;  // k^ . q^
-
-    float kn[RPT], qn[RPT];
+      // tail after this token: decode writes the pool row, verify the checkpoint row
+      {
+        ActT* to = (ActT*)p.tail_out + (p.verify ? row * TZ : s * TZ);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      qn[i] = sY[rg * RPT + i] * rq;
-      kn[i] = sY[D + rg * RPT + i] * rk;
-    }
+        for (int j = 0; j < CPT; ++j) {
+          const int gc = gch[j];
+          if (gc >= 0) {
+            to[0L * C + gc] = from_f32<ActT>(t0[j]);
+            to[1L * C + gc] = from_f32<ActT>(t1[j]);
+            to[2L * C + gc] = from_f32<ActT>(t2[j]);
+          }
+        }
+      }
+      const float decay = __expf(A * softplus(in.av + dtb));
+      const float beta = sigmoid(in.bv);
+      lds_barrier();
 
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int h = kh * R + r;
-      const long gi = row * n_v + h;
-      const float decay = __expf(-__expf(p.A_log[h]) * softplus(to_f32(ain[gi]) + p.dt_bias[h]));
-      const float beta = sigmoid(to_f32(bin[gi]));
+      // ---- q/k L2 norm and k.q (every wave computes them, no broadcast needed)
+      float sq = 0.f, sk = 0.f, skq = 0.f;
+      for (int i = lane; i < D; i += kWave) {
+        const float qv = sY[i], kv = sY[D + i];
+        sq = fmaf(qv, qv, sq);
+        sk = fmaf(kv, kv, sk);
+        skq = fmaf(kv, qv, skq);
+      }
+      sq = wave_sum<kWave>(sq);
+      sk = wave_sum<kWave>(sk);
+      skq = wave_sum<kWave>(skq);
+      const float rq = rsqrt_fast(sq + p.l2_eps);
+      const float rk = rsqrt_fast(sk + p.l2_eps);
+      const float kq = (skq * rk) * rq;  // k^ . q^
 
-      // column partial sums of H^T k and H^T q over this thread's rows
+      // column partial sums of H^T k and H^T q over this thread's rows (q and k re-read from LDS
+      // where used, which keeps the register footprint to the state blocks)
       float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float hv[4] = {H[r][i].x, H[r][i].y, H[r][i].z, H[r][i].w};
+        const float qn = sY[rg * RPT + i] * rq, kn = sY[D + rg * RPT + i] * rk;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          pk[c] = pk[c] + hv[c] * kn[i];
-          pq[c] = pq[c] + hv[c] * qn[i];
+          pk[c] = fmaf(H[i][c], kn, pk[c]);
+          pq[c] = fmaf(H[i][c], qn, pq[c]);
         }
       }
       // across the row groups inside the wave (lanes with the same column quad)
@@ -174,70 +213,74 @@ __global__ __launch_bounds__(StepThreads<D>::value) __attribute__((amdgpu_waves_
           pq[c] = pq[c] + __shfl_xor(pq[c], off, kWave);
         }
       }
-      __syncthreads();  // sRed free (previous head done)
       if (lane < QD) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          sRed[wave][0][4 * cq + c] = pk[c];
-          sRed[wave][1][4 * cq + c] = pq[c];
+          sRed[r][hw][0][4 * cq + c] = pk[c];
+          sRed[r][hw][1][4 * cq + c] = pq[c];
         }
       }
-      __syncthreads();
+      lds_barrier();
+      // the head's wave partials summed by 2 D of its threads (one column of H^T k or H^T q each)
+      if (th < 2 * D) {
+        const int which = th / D, col = th % D;
+        float acc = sRed[r][0][which][col];
+#pragma unroll
+        for (int ww = 1; ww < HW; ++ww) acc = acc + sRed[r][ww][which][col];
+        sTot[r][which][col] = acc;
+      }
+      lds_barrier();
+      const f32x4 hk4 = *(const f32x4*)&sTot[r][0][4 * cq], hq4 = *(const f32x4*)&sTot[r][1][4 * cq];
       float u[4], o[4];
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int col = 4 * cq + c;
-        float hk = sRed[0][0][col], hq = sRed[0][1][col];
-#pragma unroll
-        for (int w = 1; w < kThreads / kWave; ++w) {
-          hk = hk + sRed[w][0][col];
-          hq = hq + sRed[w][1][col];
-        }
-        const float v = sY[2 * D + r * D + col];
-        u[c] = beta * (v - decay * hk);
-        o[c] = p.scale * (decay * hq + kq * u[c]);
-        ss = ss + o[c] * o[c];
+        const float v = sY[2 * D + r * D + 4 * cq + c];
+        u[c] = beta * (v - decay * hk4[c]);
+        o[c] = p.scale * fmaf(kq, u[c], decay * hq4[c]);
+        ss = fmaf(o[c], o[c], ss);
       }
       // new state
       float* dst = p.state_out + (p.verify ? row * SZ : s * SZ) + (long)h * D * D;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        float4 nh;
-        nh.x = decay * H[r][i].x + kn[i] * u[0];
-        nh.y = decay * H[r][i].y + kn[i] * u[1];
-        nh.z = decay * H[r][i].z + kn[i] * u[2];
-        nh.w = decay * H[r][i].w + kn[i] * u[3];
-        H[r][i] = nh;
-        *(float4*)(dst + (long)(rg * RPT + i) * D + 4 * cq) = nh;
+        const float kn = sY[D + rg * RPT + i] * rk;
+        f32x4 nh;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) nh[c] = fmaf(kn, u[c], decay * H[i][c]);
+        H[i] = nh;
+        __builtin_nontemporal_store(nh, (f32x4*)(dst + (long)(rg * RPT + i) * D + 4 * cq));
       }
-      // gated RMSNorm over the D columns held by the QD lanes of this row group
+      // gated RMSNorm over the D columns held by the QD lanes of row group 0
       ss = wave_sum<QD>(ss);
-      if (tid < QD) {
+      if (th < QD) {
         const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
         const long ob = row * (long)n_v * D + (long)h * D;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int col = 4 * cq + c;
-          const float zz = to_f32(zin[ob + col]);
-          out[ob + col] = from_f32<ActT>(p.norm_w[col] * (o[c] * inv) * silu(zz));
-        }
+        for (int c = 0; c < 4; ++c) out[ob + 4 * cq + c] = from_f32<ActT>(nw[c] * (o[c] * inv) * silu(in.z[c]));
       }
+      lds_barrier();  // sY, sRed and sTot reused by the next token or item
     }
-    __syncthreads();  // sY reused by the next token
   }
+}
+
+// one workgroup per (key head, sequence): many small independent workgroups keep every CU's memory
+// pipe busy, one finishing its stores while the next loads
+template <typename ActT, int D, int R>
+hipError_t launch_step_r(const StepArgs& p, hipStream_t st) {
+  using S = StepShape<D, R>;
+  hipLaunchKernelGGL((step_kernel<ActT, D, R>), dim3(p.n_k * p.B), dim3(S::NTH), 0, st, p);
+  return hipGetLastError();
 }
 
 template <typename ActT, int D>
 hipError_t launch_step_d(const StepArgs& p, int R, hipStream_t st) {
-  dim3 grid(p.n_k, p.B), block(StepThreads<D>::value);
   switch (R) {
-    case 1: hipLaunchKernelGGL((step_kernel<ActT, D, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((step_kernel<ActT, D, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((step_kernel<ActT, D, 4>), grid, block, 0, st, p); break;
+    case 1: return launch_step_r<ActT, D, 1>(p, st);
+    case 2: return launch_step_r<ActT, D, 2>(p, st);
+    case 4: return launch_step_r<ActT, D, 4>(p, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace

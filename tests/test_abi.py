@@ -67,9 +67,10 @@ def test_sizes():
     lib = gdn.load_library()
     d = gdn.GdnDesc(n_k=16, n_v=32, d_k=128, d_v=128)
     assert gdn.state_record_bytes(d) == 32 * 128 * 128 * 4 + 3 * 8192 * 2
-    n = gdn.prefill_workspace_bytes(d, 4, 100)
+    # 8 x 32 (sequence, head) pairs fill the chip with whole heads: only the chunk records count
+    n = gdn.prefill_workspace_bytes(d, 8, 100)
     assert n > 0 and n % 256 == 0
-    assert gdn.prefill_workspace_bytes(d, 4, 128) == n  # 100 and 128 tokens both take two chunks
+    assert gdn.prefill_workspace_bytes(d, 8, 128) == n  # 100 and 128 tokens both take two chunks
     # few (sequence, head) pairs: heads are split over workgroups and o is staged per token
     assert gdn.prefill_workspace_bytes(d, 1, 128) > gdn.prefill_workspace_bytes(d, 1, 100) > 0
     assert gdn.prefill_workspace_bytes(gdn.GdnDesc(n_k=2, n_v=4, d_k=128, d_v=128, act_dtype=gdn.GDN_F32), 1, 64) == 0

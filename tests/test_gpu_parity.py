@@ -65,9 +65,12 @@ def test_prefill_ragged_multichunk(D, R):
     _prefill_case(dims, 3, 3, 300, [300, 171, 1], state_std=0.05, tail_rand=True)
 
 
-def test_prefill_fused_norm_d128():
-    """Enough (sequence, value head) pairs that one workgroup owns each head's columns (fused norm)."""
-    _prefill_case(NEXT, 11, 4, 150, [150, 64, 1, 100], state_std=0.05, tail_rand=True)
+@pytest.mark.parametrize("B", [2, 4, 8])
+def test_prefill_column_splits_d128(B):
+    """32 value heads x B sequences: 64, 128 and 256 (sequence, head) pairs give 4, 2 and 1 workgroups
+    per head (the last with the gated RMSNorm fused into the state pass)."""
+    lens = [150, 64, 1, 100, 129, 0, 150, 37][:B]
+    _prefill_case(NEXT, 11, B, 150, lens, state_std=0.05, tail_rand=True)
 
 
 def test_prefill_fp32_multichunk():
