@@ -1,21 +1,27 @@
 """Benchmark of the Gated DeltaNet layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|verify|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|copy]
 
 Headline (`value`): prefill tokens/s of one layer on one sequence of 4096 tokens, 16 key / 16 value
 heads, d_k = d_v = 128, bf16 activations, fp32 state, continued from a saved state (one step = one
 gdn_prefill_chunk call: conv, gates, L2 norms, chunked delta rule, gated RMSNorm, state and tail
 write-back). Input sets rotate so that the 256 MB last-level cache does not hold the step's inputs.
+`ms_per_step` is the median of per-call HIP-event times on the launch stream.
+
+`roofline` is that of the dominant launch of the call, timed live through the library's per-launch
+event session (gdn_timing_begin/end) on the launch stream: the state pass, priced against the dense
+f16 MFMA peak with the algorithmic FLOP of the inter-chunk step (6 d_k d_v per token and value head),
+or chunk_prep with the intra-chunk contractions (Gram, W, U', P). `call` prices the whole call: its
+algorithmic bytes against HBM (the call's bound: 141 FLOP/B is below the ~312 FLOP/B ridge) and its
+algorithmic FLOP against MFMA. `traffic` is the counter-measured HBM bytes of that launch when the
+committed counter summary was taken on the current sources, else null.
 
 The same run also measures, each as a sub-object of the one JSON line:
+  prefill_stack - one layer of the 9B-like stack: 8 x 8192 tokens, 16 key / 32 value heads
   decode  - 36 GDN layers x 256 sequences x 1 token (one step = 36 gdn_decode_step calls), state GB/s
   verify  - 64 sequences x (1+4) tokens with checkpoints, then accept and the commit copy
   copy    - the O(1) state bridge: 256 records {fp32 state, conv tail} of one layer
   cpu_baseline - the fp64 oracle on the host cores on the prefill workload
-
-Roofline: HBM-bound by algorithmic intensity (141 FLOP/B against a ridge of ~312 FLOP/B), so the
-prefill call is priced against 8 TB/s with algorithmic bytes; the counted MFMA fraction (bf16/f16
-dense peak 2.5 PFLOP/s) is reported beside it.
 """
 from __future__ import annotations
 
@@ -50,26 +56,54 @@ def decode_bytes(dims):
         dims.conv_dim + 2 * dims.n_v * dims.d_v + 2 * dims.n_v)
 
 
-def kernel_hash() -> str:
+KERNEL_SOURCES = {
+    "chunk_prep": ("gdn_prefill.hip", "gdn_common.h", "gdn_kernels.h"),
+    "state_pass": ("gdn_prefill.hip", "gdn_common.h", "gdn_kernels.h"),
+    "norm": ("gdn_prefill.hip", "gdn_common.h", "gdn_kernels.h"),
+    "step_decode": ("gdn_step.hip", "gdn_common.h", "gdn_kernels.h"),
+    "step_verify": ("gdn_step.hip", "gdn_common.h", "gdn_kernels.h"),
+    "copy": ("gdn_state.hip", "gdn_common.h", "gdn_kernels.h"),
+    "accept": ("gdn_state.hip", "gdn_common.h", "gdn_kernels.h"),
+    "conv": ("gdn_conv.hip", "gdn_common.h", "gdn_kernels.h"),
+}
+
+
+def kernel_hash(kernel=None) -> str:
+    """Hash of the sources a kernel is built from (all of csrc when kernel is None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_44_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    files = KERNEL_SOURCES[kernel] if kernel else sorted(os.listdir(csrc))
+    for f in files:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name: str):
-    """HBM bytes per call from the committed PMC summary, if it was taken on the current kernels."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, if taken on the current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(name)
+        rec = json.load(open(path)).get(workload, {}).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_hash") != kernel_hash():
+    if not rec or rec.get("source_hash") != kernel_hash(kernel):
         return None
-    return rec.get("bytes_per_call")
+    return rec.get("bytes_per_launch")
+
+
+def launch_breakdown(torch, gdn, fn, n):
+    """Per-launch durations over n calls of fn, from the library's event-timing session on the launch
+    stream; returns {kernel: (launches per call, mean ms per launch)}."""
+    torch.cuda.synchronize()
+    gdn.timing_begin(64 * n)
+    for i in range(n):
+        fn(i)
+    recs = gdn.timing_end(64 * n)
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    return {k: (len(v) / n, float(np.mean(v))) for k, v in per.items()}
 
 
 class Timer:
@@ -93,45 +127,88 @@ class Timer:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         per = [s.elapsed_time(e) for s, e in self.ev[:steps]]
-        return float(np.mean(per)), wall * 1e3 / steps
+        return float(np.median(per)), wall * 1e3 / steps
 
 
-def bench_prefill(torch, gdn, args):
-    from gdn_inputs import SMALL, make_layer, random_state
+def prefill_kernel_flop(dims, T: int, C: int = 64):
+    """Algorithmic FLOP of one prefill call split by the launch that does it: the intra-chunk WY/UT
+    contractions (Gram, W, U', P) in chunk_prep, the inter-chunk state pass (U, O, H) in state_pass."""
+    nk, nv, dk, dv = dims.n_k, dims.n_v, dims.d_k, dims.d_v
+    return {"chunk_prep": T * (nv * 2 * C * (dk + 2 * dv) + nk * 4 * C * dk),
+            "state_pass": T * nv * 6 * dk * dv}
+
+
+def kernel_roofline(workload, kernel, ms, flop=None, nbytes=None):
+    """Roofline object of one launch: algorithmic work per launch over its measured duration."""
+    sec = ms / 1e3
+    if flop is not None:
+        ach = flop / sec / 1e12
+        r = {"bound": "mfma", "achieved": ach, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": ach / MFMA_PEAK_TFLOPS, "algorithmic_flop_per_launch": flop}
+    else:
+        ach = nbytes / sec / 1e9
+        r = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes}
+    r.update(traffic=measured_traffic(workload, kernel), kernel=kernel, ms_per_launch=ms)
+    return r
+
+
+def _prefill_sets(torch, gdn, dims, B, T, nsets, seed0):
+    from gdn_inputs import make_layer, random_state
     from tests.gpu_helpers import act, desc_of, f32, i32, weights
-    dims = SMALL
-    T = 4096
-    nsets = 4
     d = desc_of(dims)
     sets = []
     for k in range(nsets):
-        w, x, rng = make_layer(100 + k, dims, 1, T)
-        S0, tail0 = random_state(rng, dims, 1)
+        w, x, rng = make_layer(seed0 + k, dims, B, T)
+        S0, tail0 = random_state(rng, dims, B)
         sets.append(dict(w=weights(w, dims), mixed=act(x.mixed, dims), z=act(x.z, dims), a=act(x.a, dims),
                          b=act(x.b, dims), lens=i32(x.lens), tail=act(tail0, dims), state=f32(S0),
-                         out=torch.empty(1, T, dims.value_dim, dtype=torch.bfloat16, device="cuda"),
-                         ws=gdn.prefill_workspace(d, 1, T)))
+                         out=torch.empty(B, T, dims.value_dim, dtype=torch.bfloat16, device="cuda"),
+                         ws=gdn.prefill_workspace(d, B, T)))
 
     def step(i):
         s = sets[i % nsets]
         gdn.prefill_chunk(d, s["w"], s["mixed"], s["z"], s["a"], s["b"], s["lens"], s["tail"], s["state"],
                           s["out"], s["ws"])
+    return step
 
-    ms_event, ms_wall = Timer(torch, args.steps).run(step, args.steps, args.warmup)
+
+def _prefill_measure(torch, gdn, args, dims, B, T, nsets, seed0, workload, steps, warmup):
+    step = _prefill_sets(torch, gdn, dims, B, T, nsets, seed0)
+    ms_event, ms_wall = Timer(torch, steps).run(step, steps, warmup)
+    kern = launch_breakdown(torch, gdn, step, steps)
     flop, nbytes = prefill_work(dims, T)
+    flop, nbytes = flop * B, nbytes * B
+    kflop = {k: v * B for k, v in prefill_kernel_flop(dims, T).items()}
     sec = ms_event / 1e3
-    achieved = nbytes / sec / 1e9
-    traffic = measured_traffic("prefill_4k")
+    dominant = max(kern, key=lambda k: kern[k][0] * kern[k][1])
+    roof = kernel_roofline(workload, dominant, kern[dominant][1],
+                           flop=kflop.get(dominant), nbytes=None if dominant in kflop else nbytes)
     res = {
-        "tokens_per_s": T / sec, "ms_per_call": ms_event, "ms_wall_per_step": ms_wall,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdn_prefill_chunk (chunk_prep + state_pass launches)",
-                     "algorithmic_bytes_per_call": nbytes, "algorithmic_flop_per_call": flop},
-        "mfma": {"achieved_tflops": flop / sec / 1e12, "peak_tflops": MFMA_PEAK_TFLOPS,
-                 "frac": flop / sec / 1e12 / MFMA_PEAK_TFLOPS},
+        "tokens_per_s": B * T / sec, "ms_per_call": ms_event, "ms_wall_per_step": ms_wall,
+        "roofline": roof,
+        "call": {"hbm_achieved_GBs": nbytes / sec / 1e9, "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                 "mfma_achieved_TFLOPs": flop / sec / 1e12, "mfma_frac": flop / sec / 1e12 / MFMA_PEAK_TFLOPS,
+                 "algorithmic_bytes": nbytes, "algorithmic_flop": flop},
+        "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()},
     }
-    return res, dims, T
+    return res
+
+
+def bench_prefill(torch, gdn, args):
+    from gdn_inputs import SMALL
+    T = 4096
+    # 4 input sets (with their workspaces, ~850 MB) rotate past the 256 MB last-level cache
+    return _prefill_measure(torch, gdn, args, SMALL, 1, T, 4, 100, "prefill_4k", args.steps, args.warmup), SMALL, T
+
+
+def bench_prefill_stack(torch, gdn, args):
+    """One GDN layer of the 9B-like stack: 8 sequences x 8192 tokens, 16 key / 32 value heads."""
+    from gdn_inputs import NEXT
+    res = _prefill_measure(torch, gdn, args, NEXT, 8, 8192, 2, 400, "prefill_stack_layer",
+                           max(3, args.steps // 5), max(1, args.warmup // 2))
+    res["workload"] = "one layer of the 36-GDN-layer stack: 8 x 8192 tokens, 16/32 heads, d=128, bf16"
+    return res
 
 
 def bench_decode(torch, gdn, args):
@@ -157,14 +234,13 @@ def bench_decode(torch, gdn, args):
 
     steps = max(3, args.steps // 5)
     ms, _ = Timer(torch, steps).run(step, steps, max(1, args.warmup // 2))
-    nbytes = L * B * decode_bytes(dims)
-    gbs = nbytes / (ms / 1e3) / 1e9
-    traffic = measured_traffic("decode_layer_b256")
+    kern = launch_breakdown(torch, gdn, step, 2)
+    per_launch = B * decode_bytes(dims)
+    roof = kernel_roofline("decode_layer_b256", "step_decode", kern["step_decode"][1], nbytes=per_launch)
+    gbs = L * per_launch / (ms / 1e3) / 1e9
     return {"workload": "36 GDN layers x 256 sequences x 1 token, 16/32 heads, d=128, fp32 state",
             "tokens_per_s": B / (ms / 1e3), "ms_per_step": ms, "ms_per_layer": ms / L,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "kernel": "step_kernel (decode, T=1)",
-                         "algorithmic_bytes_per_call": nbytes / L}}
+            "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "roofline": roof}
 
 
 def bench_verify(torch, gdn, args):
@@ -193,12 +269,17 @@ def bench_verify(torch, gdn, args):
         gdn.state_copy(d, sp, tp, slots, ck_s, ck_t, ci, B)
 
     ms, _ = Timer(torch, args.steps).run(step, args.steps, args.warmup)
+    kern = launch_breakdown(torch, gdn, step, 4)
     rec = dims.n_v * dims.d_k * dims.d_v * 4
     tail_b = 3 * dims.conv_dim * 2
-    nbytes = B * (rec * (1 + T) + T * tail_b + 2 * (rec + tail_b))
+    io = B * T * 2 * (dims.conv_dim + 2 * dims.value_dim + 2 * dims.n_v)
+    verify_bytes = B * (rec * (1 + T) + T * tail_b) + io
+    nbytes = verify_bytes + B * 2 * (rec + tail_b)
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"workload": "64 sequences x (1+4) tokens, 16/32 heads, d=128: verify + accept + commit",
-            "ms_per_step": ms, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}
+            "ms_per_step": ms, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+            "roofline": kernel_roofline("verify_b64_k4", "step_verify", kern["step_verify"][1], nbytes=verify_bytes),
+            "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()}}
 
 
 def bench_copy(torch, gdn, args):
@@ -221,7 +302,8 @@ def bench_copy(torch, gdn, args):
     nbytes = 2 * n * gdn.state_record_bytes(d)
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"workload": "256 state records (fp32 state + bf16 conv tail) of one 16/32-head layer",
-            "ms_per_call": ms, "mib": nbytes / 2 / 2 ** 20, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+            "ms_per_call": ms, "mib": nbytes / 2 / 2 ** 20, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "roofline": kernel_roofline("state_copy_256", "copy", ms, nbytes=nbytes)}
 
 
 def cpu_baseline():
@@ -271,8 +353,12 @@ def main():
         line["config"] = {"workload": "prefill_4k: 1 sequence x 4096 tokens, 16 key / 16 value heads, d=128",
                           "global_batch": 1, "seq_len": T, "chunk": 64, "parallelism": "single GPU"}
         line["roofline"] = pre["roofline"]
-        line["mfma"] = pre["mfma"]
+        line["call"] = pre["call"]
+        line["kernels_ms"] = pre["kernels_ms"]
         line["ms_wall_per_step"] = pre["ms_wall_per_step"]
+    if only in ("all", "stack"):
+        line["prefill_stack"] = bench_prefill_stack(torch, gdn, args)
+        torch.cuda.empty_cache()
     if only in ("all", "decode"):
         line["decode"] = bench_decode(torch, gdn, args)
         torch.cuda.empty_cache()

@@ -50,7 +50,7 @@ class _Weights(ctypes.Structure):
 _lib = None
 EXPORTS = ("gdn_last_error", "gdn_version", "gdn_conv_chunk", "gdn_prefill_workspace_bytes", "gdn_prefill_chunk",
            "gdn_decode_step", "gdn_verify_with_checkpoints", "gdn_accept", "gdn_state_copy",
-           "gdn_state_record_bytes")
+           "gdn_state_record_bytes", "gdn_timing_begin", "gdn_timing_end")
 
 
 def load_library(path: str = LIB_PATH):
@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_state_copy.argtypes = [D, P, P, P, P, P, P, I, P]
     lib.gdn_state_record_bytes.argtypes = [D]
     lib.gdn_state_record_bytes.restype = Z
+    lib.gdn_timing_begin.argtypes = [I]
+    lib.gdn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), I]
     for name in ("gdn_conv_chunk", "gdn_prefill_chunk", "gdn_decode_step", "gdn_verify_with_checkpoints",
                  "gdn_accept", "gdn_state_copy"):
         getattr(lib, name).restype = I
@@ -329,3 +331,19 @@ def state_copy(desc: GdnDesc, dst_state, dst_tail, dst_idx, src_state, src_tail,
 
 def state_record_bytes(desc: GdnDesc) -> int:
     return int(load_library().gdn_state_record_bytes(ctypes.byref(desc.c())))
+
+
+def timing_begin(capacity: int = 1024) -> None:
+    """Open a per-launch timing session on this thread (see gdn_timing_begin)."""
+    _check("gdn_timing_begin", load_library().gdn_timing_begin(int(capacity)))
+
+
+def timing_end(cap: int = 1024):
+    """Close the session; returns [(kernel name, milliseconds)] in launch order."""
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = load_library().gdn_timing_end(names, ms, int(cap))
+    if n < 0:
+        _check("gdn_timing_end", n)
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
+

@@ -1,8 +1,11 @@
 // The C ABI of libgdn.so (declared in include/gdn.h): argument checks, then kernel launches on the
-// caller's stream. Nothing here allocates device memory or synchronises with the host.
+// caller's stream. Nothing here allocates device memory; only gdn_timing_end (a measurement aid)
+// synchronises with the host.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <new>
 
 #include "gdn.h"
 #include "gdn_kernels.h"
@@ -56,9 +59,81 @@ int check_weights(const gdn_weights* w) {
   return GDN_OK;
 }
 
+// ---- per-launch timing session (diagnostics) ----
+struct TimedLaunch {
+  const char* kernel;
+  hipEvent_t start, stop;
+};
+thread_local TimedLaunch* t_launch = nullptr;  // open session: capacity t_cap, t_used recorded
+thread_local int t_cap = 0, t_used = 0;
+
 }  // namespace
 
+namespace gdn {
+void timing_before(const char* kernel, hipStream_t st) {
+  if (!t_launch || t_used >= t_cap) return;
+  t_launch[t_used].kernel = kernel;
+  (void)hipEventRecord(t_launch[t_used].start, st);
+}
+void timing_after(hipStream_t st) {
+  if (!t_launch || t_used >= t_cap) return;
+  (void)hipEventRecord(t_launch[t_used].stop, st);
+  ++t_used;
+}
+}  // namespace gdn
+
 extern "C" {
+
+int gdn_timing_begin(int capacity) {
+  if (t_launch) return fail(GDN_EINVAL, "gdn_timing_begin: a session is already open");
+  if (capacity <= 0 || capacity > 65536) return fail(GDN_EINVAL, "gdn_timing_begin: capacity=%d", capacity);
+  TimedLaunch* rec = new (std::nothrow) TimedLaunch[capacity];
+  if (!rec) return fail(GDN_EINVAL, "gdn_timing_begin: out of host memory");
+  for (int i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&rec[i].start);
+    if (e == hipSuccess) e = hipEventCreate(&rec[i].stop);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) {
+        (void)hipEventDestroy(rec[j].start);
+        (void)hipEventDestroy(rec[j].stop);
+      }
+      delete[] rec;
+      return hip_status(e, "gdn_timing_begin");
+    }
+  }
+  t_launch = rec;
+  t_cap = capacity;
+  t_used = 0;
+  g_err[0] = 0;
+  return GDN_OK;
+}
+
+int gdn_timing_end(const char** kernels, float* ms, int cap) {
+  if (!t_launch) return fail(GDN_EINVAL, "gdn_timing_end: no open session");
+  hipError_t err = hipSuccess;
+  const int n = t_used;
+  for (int i = 0; i < n; ++i) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(t_launch[i].stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, t_launch[i].start, t_launch[i].stop);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    if (i < cap) {
+      if (kernels) kernels[i] = t_launch[i].kernel;
+      if (ms) ms[i] = t;
+    }
+  }
+  for (int i = 0; i < t_cap; ++i) {
+    (void)hipEventDestroy(t_launch[i].start);
+    (void)hipEventDestroy(t_launch[i].stop);
+  }
+  delete[] t_launch;
+  t_launch = nullptr;
+  t_cap = t_used = 0;
+  if (err != hipSuccess) return hip_status(err, "gdn_timing_end");
+  g_err[0] = 0;
+  return n;
+}
+
 
 const char* gdn_last_error(void) { return g_err; }
 

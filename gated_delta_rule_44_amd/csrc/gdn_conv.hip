@@ -97,8 +97,10 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(ConvArgs p) {
 
 hipError_t launch_conv(const ConvArgs& p, int act_dtype, hipStream_t st) {
   dim3 grid((p.C / 4 + kThreads - 1) / kThreads, (p.Lb + kTok - 1) / kTok, p.B), block(kThreads);
+  timing_before("conv", st);
   if (act_dtype == kActBf16) hipLaunchKernelGGL(conv_kernel<bf16_t>, grid, block, 0, st, p);
   else hipLaunchKernelGGL(conv_kernel<float>, grid, block, 0, st, p);
+  timing_after(st);
   return hipGetLastError();
 }
 

@@ -6,6 +6,11 @@
 
 namespace gdn {
 
+// Optional per-launch timing (gdn_timing_begin / gdn_timing_end): every launch site brackets its kernel
+// with these; they record HIP events on the launch stream only while a timing session is open.
+void timing_before(const char* kernel, hipStream_t st);
+void timing_after(hipStream_t st);
+
 constexpr int kActBf16 = 0;
 constexpr int kActF32 = 1;
 

@@ -957,14 +957,20 @@ long rec_bytes(int D, bool split_all) {
 template <typename ActT, int D, int R, bool SPLIT, int NT>
 hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   constexpr int NSPLIT = D / (16 * NT);
+  timing_before("chunk_prep", st);
   hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+  timing_after(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  timing_before("state_pass", st);
   hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NSPLIT == 1, (NT <= 4)>), dim3(NSPLIT * p.n_v * p.B), dim3(256), 0, st, p);
+  timing_after(st);
   e = hipGetLastError();
   if (e != hipSuccess || NSPLIT == 1) return e;
   const long per_seq = (long)p.Lb * p.n_v * (D / 4);  // < 2^31, checked by the caller
+  timing_before("norm", st);
   hipLaunchKernelGGL((norm_kernel<ActT, D, NSPLIT>), dim3((unsigned)((per_seq + 255) / 256), p.B), dim3(256), 0, st, p);
+  timing_after(st);
   return hipGetLastError();
 }
 

@@ -74,13 +74,17 @@ hipError_t launch_copy(const CopyArgs& p, hipStream_t st) {
   const long ntail = p.src_tail ? p.tail_bytes / 16 : 0;
   const long blocks = (nstate + per_block - 1) / per_block + (ntail + per_block - 1) / per_block;
   if (blocks <= 0 || p.n <= 0) return hipSuccess;
+  timing_before("copy", st);
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks, p.n), dim3(kThreads), 0, st, p);
+  timing_after(st);
   return hipGetLastError();
 }
 
 hipError_t launch_accept(const AcceptArgs& p, hipStream_t st) {
   if (p.B <= 0) return hipSuccess;
+  timing_before("accept", st);
   hipLaunchKernelGGL(accept_kernel, dim3((p.B + 127) / 128), dim3(128), 0, st, p);
+  timing_after(st);
   return hipGetLastError();
 }
 

@@ -269,7 +269,9 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
 template <typename ActT, int D, int R>
 hipError_t launch_step_r(const StepArgs& p, hipStream_t st) {
   using S = StepShape<D, R>;
+  timing_before(p.verify ? "step_verify" : "step_decode", st);
   hipLaunchKernelGGL((step_kernel<ActT, D, R>), dim3(p.n_k * p.B), dim3(S::NTH), 0, st, p);
+  timing_after(st);
   return hipGetLastError();
 }
 

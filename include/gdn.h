@@ -164,6 +164,21 @@ int gdn_state_copy(const gdn_desc* desc, float* dst_state, void* dst_tail, const
  * cache_payload_bytes per sequence per layer). */
 size_t gdn_state_record_bytes(const gdn_desc* desc);
 
+/*
+ * Per-launch timing, for measurement (not part of the method). gdn_timing_begin opens a session on the
+ * calling thread: until gdn_timing_end, every kernel the library launches from this thread is
+ * bracketed by two HIP events recorded on the launch stream (at most `capacity` launches, 1..65536;
+ * later ones are not timed). The events are created here, on the host side of the runtime; no
+ * device memory is allocated and nothing synchronises until the end.
+ * gdn_timing_end waits for the recorded events, writes the first `cap` launches in launch order as
+ * (static kernel name, milliseconds) into kernels[] and ms[] (either may be NULL), closes the session
+ * and returns the number of launches recorded, or a negative status (GDN_EINVAL: no open session,
+ * GDN_EHIP: an event failed). Kernel names: "conv", "chunk_prep", "state_pass", "norm",
+ * "step_decode", "step_verify", "copy", "accept".
+ */
+int gdn_timing_begin(int capacity);
+int gdn_timing_end(const char** kernels, float* ms, int cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -83,3 +83,11 @@ def test_python_layer_rejects_cpu_tensors():
     with pytest.raises(RuntimeError):
         gdn.conv_chunk(d, torch.zeros(d.conv_dim, 4, dtype=torch.bfloat16), x, torch.ones(1, dtype=torch.int32),
                        torch.zeros(1, 3, d.conv_dim, dtype=torch.bfloat16))
+
+
+def test_timing_session_errors():
+    """Session misuse is rejected before any HIP call."""
+    lib = gdn.load_library()
+    assert lib.gdn_timing_begin(0) == -1 and b"capacity" in lib.gdn_last_error()
+    assert lib.gdn_timing_end(None, None, 0) == -1 and b"no open session" in lib.gdn_last_error()
+

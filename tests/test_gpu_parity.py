@@ -290,3 +290,27 @@ def test_state_copy_gather_scatter():
     gdn.state_copy(d, dst2, None, None, src_s, None, None, n_src)
     torch.cuda.synchronize()
     assert torch.equal(dst2, src_s)
+
+
+def test_timing_session_names_every_launch():
+    """The per-launch timing session sees each kernel a call launches, in order, with its time."""
+    dims = LayerDims(n_k=2, n_v=4, d_k=128, d_v=128)
+    _say("timing session: prefill (split heads) then decode")
+    w, x, rng = make_layer(5, dims, 1, 128)
+    d = desc_of(dims)
+    W = weights(w, dims)
+    tail = act(np.zeros(dims.tail_shape(1), np.float32), dims)
+    st = f32(np.zeros(dims.state_shape(1), np.float32))
+    out = torch.empty(1, 128, dims.value_dim, dtype=torch.bfloat16, device="cuda")
+    ws = gdn.prefill_workspace(d, 1, 128)
+    gdn.timing_begin(16)
+    gdn.prefill_chunk(d, W, act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims), i32(x.lens),
+                      tail, st, out, ws)
+    gdn.decode_step(d, W, act(x.mixed[:, 0], dims), act(x.z[:, 0], dims), act(x.a[:, 0], dims),
+                    act(x.b[:, 0], dims), None, tail, st, torch.empty(1, dims.value_dim, dtype=torch.bfloat16,
+                                                                      device="cuda"))
+    recs = gdn.timing_end(16)
+    assert [n for n, _ in recs] == ["chunk_prep", "state_pass", "norm", "step_decode"]
+    assert all(ms > 0 for _, ms in recs)
+    with pytest.raises(gdn.GdnError):
+        gdn.timing_end(16)  # no open session
