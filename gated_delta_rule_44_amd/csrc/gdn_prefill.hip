@@ -677,6 +677,41 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
     }
   };
 
+  // single fragments of chunk c, for refilling a register right after its last use in the current
+  // chunk: the refills then interleave with the MFMAs instead of queueing behind each other
+  auto rec_of = [&](int c) { return (const char*)rec_ptr<D, SPLIT>(p, b, h, c < n_real ? c : n_real - 1); };
+  auto ld_wq = [&](Frags& f, int c, int kk) __attribute__((always_inline)) {
+    const char* rec = rec_of(c);
+    f.w[kk] = get_frag(rec, RC::W_HI + w * KD + kk, lane);
+    if (SPLIT) f.wl[kk] = get_frag(rec, RC::W_LO + w * KD + kk, lane);
+    f.q[kk] = get_frag(rec, RC::Q_HI + w * KD + kk, lane);
+    f.ql[kk] = get_frag(rec, RC::Q_LO + w * KD + kk, lane);
+  };
+  auto ld_up = [&](Frags& f, int c, int nt) __attribute__((always_inline)) {
+    f.up[nt] = *(const f32x4*)(rec_of(c) + (RC::UP + w * HM + cb / 16 + nt) * 1024 + lane * 16);
+  };
+  auto ld_pk = [&](Frags& f, int c, int kk) __attribute__((always_inline)) {
+    const char* rec = rec_of(c);
+    f.p[kk] = get_frag(rec, RC::P_HI + w * 2 + kk, lane);
+    f.pl[kk] = get_frag(rec, RC::P_LO + w * 2 + kk, lane);
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int hm = owns(j) ? w + 4 * j : 0;
+      f.k[j][kk] = get_frag(rec, RC::K_HI + hm * 2 + kk, lane);
+      f.kl[j][kk] = get_frag(rec, RC::K_LO + hm * 2 + kk, lane);
+    }
+  };
+  auto ld_gc = [&](Frags& f, int c) __attribute__((always_inline)) { f.gc = *(const float*)(rec_of(c) + RC::kGc); };
+  auto ld_z = [&](Frags& f, int c) __attribute__((always_inline)) {
+    if (FUSED) {
+      const int cc = c < n_real ? c : n_real - 1;
+      const int t = cc * C64 + 16 * w + r16;  // rows past Lb read row Lb-1; their results are never stored
+      const long row = ((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) f.z[nt] = Raw4<ActT>::load((const ActT*)p.z + row * D + cb + 16 * nt + 4 * g16);
+    }
+  };
+
   // ---- the state: 2^16 H, row tiles hm = w + 4j, columns cb + 16 nt + r16 ----
   float* st = p.state + ((long)b * n_v + h) * D * D;
   f32x4 Hacc[HPW][NT];
@@ -722,6 +757,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
 
   // one chunk; f holds its fragments on entry and those of chunk c + step on return
   auto chunk = [&](int c, Frags& f, int step) __attribute__((always_inline)) {
+    const int cn = c + step;  // the chunk whose fragments refill f
     lds_barrier();  // H of this chunk is in sH
     // ---- U = U' - W H (token tile w); O^T = H^T Q~^T ----
     // Column tiles go in groups of NG, and each product's hi*lo terms and hi*hi term accumulate
@@ -742,6 +778,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
       for (int g = 0; g < NG; ++g) {
         ua[g] = f.up[n0 + g];
         ub[g] = oa[g] = ob[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ld_up(f, cn, n0 + g);
       }
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) {
@@ -759,6 +796,8 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
 #pragma unroll
           for (int g = 0; g < NG; ++g) ua[g] = mfma16(f.wl[kk], hf[kk][g], ua[g]);
         }
+        if (n0 + NG >= NT) ld_wq(f, cn, kk);  // last use of this block's W and Q~ in the chunk
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -775,7 +814,6 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
       *(f16x4*)dst = hi;
       *(f16x4*)(dst + 8 * kWave) = lo;
     }
-    load_a(f, c + step);
     lds_barrier();  // U of every token tile is in sU; every wave is done reading sH
     // ---- H = e^{gamma_C} H + K~^T U (own row tiles); O^T += U^T P~^T ----
     // per (block, term) one MFMA on each H tile of the group and each O^T tile: independent results
@@ -793,8 +831,9 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
       for (int j = 0; j < HPW; ++j)
 #pragma unroll
         for (int g = 0; g < NG; ++g) Hacc[j][n0 + g] = Hacc[j][n0 + g] * f.gc;
+      if (n0 + NG >= NT) ld_gc(f, cn);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int term = 0; term < 3; ++term) {
 #pragma unroll
@@ -815,6 +854,9 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
             OT[n0 + g] = mfma16(ua, pb, OT[n0 + g]);
           }
         }
+        if (n0 + NG >= NT) ld_pk(f, cn, kk);  // last use of this block's P~ and K~ in the chunk
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     put_H();
 
@@ -839,13 +881,12 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
         res[nt] = make_float4(nw[nt][0] * (OT[nt][0] * inv) * silu(zf.x), nw[nt][1] * (OT[nt][1] * inv) * silu(zf.y),
                               nw[nt][2] * (OT[nt][2] * inv) * silu(zf.z), nw[nt][3] * (OT[nt][3] * inv) * silu(zf.w));
       }
-      load_b(f, c + step);
+      ld_z(f, cn);
       if (t < Lb) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) Act4<ActT>::store(out + row * D + cb + 16 * nt + 4 * g16, res[nt]);
       }
     } else {
-      load_b(f, c + step);
       if (t < Lb) {
         if (g16 == 0) sspart[row * NSPLIT + split] = ss;
 #pragma unroll
