@@ -36,6 +36,8 @@
 // must stay >= 2^-14: operands of unit scale are carried multiplied by 2^8 (exact), and the scales are
 // chosen so that every product lands in a consistent domain: the state pass keeps H as 2^16 H, U as
 // 2^8 U and O^T as 2^16 O^T, with 2^8 Q~, 2^8 P~, 2^8 K~, 2^8 U' and unscaled -W in the record.
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -112,11 +114,13 @@ template <int D, bool SPLIT>
 __device__ __forceinline__ char* rec_ptr(const PrefillArgs& p, int b, int h, int c) {
   return (char*)p.ws + (((long)b * p.n_v + h) * p.n_chunks + c) * Rec<D, SPLIT>::kBytes;
 }
+// (the lane offset is an unsigned 32-bit value added to a wave-uniform base, which the compiler can
+// encode as a scalar base plus vector offset instead of a per-lane 64-bit address)
 __device__ __forceinline__ void put_frag(char* rec, int blk, int lane, f16x8 v) {
-  *(f16x8*)(rec + blk * 1024 + lane * 16) = v;
+  *(f16x8*)(rec + blk * 1024 + (uint32_t)(lane * 16)) = v;
 }
 __device__ __forceinline__ f16x8 get_frag(const char* rec, int blk, int lane) {
-  return *(const f16x8*)(rec + blk * 1024 + lane * 16);
+  return *(const f16x8*)(rec + blk * 1024 + (uint32_t)(lane * 16));
 }
 
 // four activations as stored (8 bytes of bf16 or 16 of fp32), widened when used
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
         for (int mt = 0; mt < 4; ++mt) {
           f16x4 hi, lo;
           split4(acc[mt] * -kInvS16, hi, lo);
-          char* dst = rec + (RC::W_HI + mt * KD + (j >> 1)) * 1024 + lane * 16 + 8 * (j & 1);
+          char* dst = rec + (RC::W_HI + mt * KD + (j >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (j & 1));
           *(f16x4*)dst = hi;
           if (SPLIT) *(f16x4*)(dst + 4 * KD * 1024) = lo;
         }
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
         }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          *(f32x4*)(rec + (RC::UP + mt * HM + nt) * 1024 + lane * 16) = (a1[mt] + a0[mt]) * kInvS8;
+          *(f32x4*)(rec + (RC::UP + mt * HM + nt) * 1024 + (uint32_t)(lane * 16)) = (a1[mt] + a0[mt]) * kInvS8;
       }
     }
     if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gC);
@@ -593,32 +597,44 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 }
 
 // -------------------------------------------------------------------------------------------------
-// State pass: 4 waves, a slice of CS = 16 NT value columns of one head.
+// State pass: 8 waves, a slice of CS = 16 NT value columns of one head. Wave w works on token tile
+// w & 3 and owns H row tile w (when w < d_k/16). Waves 0-3 carry the chain: U = U' - W H for their
+// token tile. Waves 4-7 carry the output: O^T = H^T Q~^T + U^T P~^T for their token tile. Every wave
+// then updates its own H row tile, H = e^{gamma_C} H + K~^T U. Each SIMD runs one chain wave and one
+// output wave, so the output work fills the gaps of the chain.
 //
-// Each wave's fragments of a chunk (24 KB at d = 128) are loaded straight into registers. Memory
-// latency (records come from HBM or the last-level cache) is longer than one chunk of work, so with
-// DB the loop is unrolled by two over two register sets and the loads run two chunks ahead: the set
-// of chunk c is refilled with chunk c+2 as soon as chunk c has consumed it.
-template <int KD, int NT, int HPW, bool SPLIT, typename RawZ>
-struct PassFrags {
-  f16x8 w[KD], wl[SPLIT ? KD : 1], q[KD], ql[KD];  // part A: -W, Q~ (hi, lo) of token tile w
-  f32x4 up[NT];                                    // part A: U' of token tile w, this slice
-  f16x8 p[2], pl[2], k[HPW][2], kl[HPW][2];        // part B: P~ of token tile w, K~^T of own row tiles
-  float gc;                                        // part B: e^{gamma_C}
-  RawZ z[NT];                                      // part B: z of token tile w (fused norm)
+// Each wave's fragments of a chunk are loaded straight into registers. Memory latency is longer than
+// one chunk of work, so with DB the loop is unrolled by two over two register sets and the loads run
+// two chunks ahead: each fragment of chunk c is refilled with chunk c+2 right after its last use.
+// The two roles keep separate fragment sets (and run separate copies of the chunk loop), so that the
+// registers of one role are never live in the other's code.
+template <int KD, int NT, bool SPLIT>
+struct ChainFrags {
+  f16x8 w[KD], wl[SPLIT ? KD : 1];  // -W of the token tile
+  f32x4 up[NT];                     // U' of the token tile, this slice
+  f16x8 k[2], kl[2];                // K~^T of the own H tile
+  float gc;                         // e^{gamma_C}
+};
+template <int KD, int NT, typename RawZ>
+struct OutFrags {
+  f16x8 q[KD], ql[KD];              // Q~ of the token tile
+  f16x8 p[2], pl[2];                // P~ of the token tile
+  f16x8 k[2], kl[2];                // K~^T of the own H tile
+  float gc;                         // e^{gamma_C}
+  RawZ z[NT];                       // z of the token tile (fused norm)
 };
 
 template <typename ActT, int D, int NT, bool SPLIT, bool FUSED, bool DB>
-__global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
+__global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
   using RC = Rec<D, SPLIT>;
   constexpr int KD = D / 32, HM = D / 16, CS = 16 * NT, NSPLIT = D / CS;
-  constexpr int HPW = (HM + 3) / 4;       // H row tiles per wave: hm = w + 4 j
-  constexpr bool kAllOwn = HM % 4 == 0;   // every wave owns HPW tiles
-  constexpr int NG = NT >= 2 ? 2 : 1;     // column tiles per MFMA group
+  constexpr int NG = (NT == 2 || NT == 4) ? 2 : 1;  // column tiles per MFMA group (registers cap NT = 8 at 1)
   static_assert(NSPLIT * CS == D, "column split");
+  static_assert(HM <= 8, "one H row tile per wave");
   static_assert(FUSED == (NSPLIT == 1), "the norm is fused exactly when one workgroup owns the head");
   typedef typename Raw4<ActT>::type RawZ;
-  typedef PassFrags<KD, NT, HPW, SPLIT, RawZ> Frags;
+  typedef ChainFrags<KD, NT, SPLIT> CF;
+  typedef OutFrags<KD, NT, RawZ> OF;
   // H and U as MFMA operand fragments: [32-block][nt][hi, lo][lane], 16 bytes each
   __shared__ f16x8 sH[KD * NT * 2 * kWave];
   __shared__ f16x8 sU[2 * NT * 2 * kWave];
@@ -631,192 +647,185 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
   const int h = hb % p.n_v, b = hb / p.n_v;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: record addresses stay scalar
+  const int tt = w & 3;                      // token tile
+  const bool chain = w < 4;                  // chain wave (U) or output wave (O)
+  const bool owner = w < HM;                 // owns H row tile w
   const int g16 = lane >> 4, r16 = lane & 15;
   const int Lb = p.Lb, n_v = p.n_v, C = p.C;
   const int len = p.len[b];
   const int n_real = (len + C64 - 1) / C64;
   const int cb = split * CS;
-  auto owns = [&](int j) { return kAllOwn || w + 4 * j < HM; };
 
-  auto load_a = [&](Frags& f, int c) __attribute__((always_inline)) {
-    c = c < n_real ? c : n_real - 1;  // past the end: reload the last chunk (unused, branch-free)
-    const char* rec = rec_ptr<D, SPLIT>(p, b, h, c);
-#pragma unroll
-    for (int kk = 0; kk < KD; ++kk) {
-      f.w[kk] = get_frag(rec, RC::W_HI + w * KD + kk, lane);
-      if (SPLIT) f.wl[kk] = get_frag(rec, RC::W_LO + w * KD + kk, lane);
-      f.q[kk] = get_frag(rec, RC::Q_HI + w * KD + kk, lane);
-      f.ql[kk] = get_frag(rec, RC::Q_LO + w * KD + kk, lane);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) f.up[nt] = *(const f32x4*)(rec + (RC::UP + w * HM + cb / 16 + nt) * 1024 + lane * 16);
-  };
-  auto load_b = [&](Frags& f, int c) __attribute__((always_inline)) {
-    c = c < n_real ? c : n_real - 1;
-    const char* rec = rec_ptr<D, SPLIT>(p, b, h, c);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      f.p[kk] = get_frag(rec, RC::P_HI + w * 2 + kk, lane);
-      f.pl[kk] = get_frag(rec, RC::P_LO + w * 2 + kk, lane);
-    }
-#pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int hm = owns(j) ? w + 4 * j : 0;  // a wave without a tile loads tile 0 and ignores it
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        f.k[j][kk] = get_frag(rec, RC::K_HI + hm * 2 + kk, lane);
-        f.kl[j][kk] = get_frag(rec, RC::K_LO + hm * 2 + kk, lane);
-      }
-    }
-    f.gc = *(const float*)(rec + RC::kGc);
-    if (FUSED) {
-      const int t = c * C64 + 16 * w + r16;  // rows past Lb read row Lb-1; their results are never stored
-      const long row = ((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) f.z[nt] = Raw4<ActT>::load((const ActT*)p.z + row * D + cb + 16 * nt + 4 * g16);
-    }
-  };
-
-  // single fragments of chunk c, for refilling a register right after its last use in the current
-  // chunk: the refills then interleave with the MFMAs instead of queueing behind each other
+  // single fragments of chunk c (past the end: the last chunk, loaded and unused, branch-free)
   auto rec_of = [&](int c) { return (const char*)rec_ptr<D, SPLIT>(p, b, h, c < n_real ? c : n_real - 1); };
-  auto ld_wq = [&](Frags& f, int c, int kk) __attribute__((always_inline)) {
+  auto ld_w = [&](CF& f, int c, int kk) __attribute__((always_inline)) {
     const char* rec = rec_of(c);
-    f.w[kk] = get_frag(rec, RC::W_HI + w * KD + kk, lane);
-    if (SPLIT) f.wl[kk] = get_frag(rec, RC::W_LO + w * KD + kk, lane);
-    f.q[kk] = get_frag(rec, RC::Q_HI + w * KD + kk, lane);
-    f.ql[kk] = get_frag(rec, RC::Q_LO + w * KD + kk, lane);
+    f.w[kk] = get_frag(rec, RC::W_HI + tt * KD + kk, lane);
+    if (SPLIT) f.wl[kk] = get_frag(rec, RC::W_LO + tt * KD + kk, lane);
   };
-  auto ld_up = [&](Frags& f, int c, int nt) __attribute__((always_inline)) {
-    f.up[nt] = *(const f32x4*)(rec_of(c) + (RC::UP + w * HM + cb / 16 + nt) * 1024 + lane * 16);
-  };
-  auto ld_pk = [&](Frags& f, int c, int kk) __attribute__((always_inline)) {
+  auto ld_q = [&](OF& f, int c, int kk) __attribute__((always_inline)) {
     const char* rec = rec_of(c);
-    f.p[kk] = get_frag(rec, RC::P_HI + w * 2 + kk, lane);
-    f.pl[kk] = get_frag(rec, RC::P_LO + w * 2 + kk, lane);
-#pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int hm = owns(j) ? w + 4 * j : 0;
-      f.k[j][kk] = get_frag(rec, RC::K_HI + hm * 2 + kk, lane);
-      f.kl[j][kk] = get_frag(rec, RC::K_LO + hm * 2 + kk, lane);
-    }
+    f.q[kk] = get_frag(rec, RC::Q_HI + tt * KD + kk, lane);
+    f.ql[kk] = get_frag(rec, RC::Q_LO + tt * KD + kk, lane);
   };
-  auto ld_gc = [&](Frags& f, int c) __attribute__((always_inline)) { f.gc = *(const float*)(rec_of(c) + RC::kGc); };
-  auto ld_z = [&](Frags& f, int c) __attribute__((always_inline)) {
+  auto ld_up = [&](CF& f, int c, int nt) __attribute__((always_inline)) {
+    f.up[nt] = *(const f32x4*)(rec_of(c) + (RC::UP + tt * HM + cb / 16 + nt) * 1024 + (uint32_t)(lane * 16));
+  };
+  auto ld_p = [&](OF& f, int c, int kk) __attribute__((always_inline)) {
+    const char* rec = rec_of(c);
+    f.p[kk] = get_frag(rec, RC::P_HI + tt * 2 + kk, lane);
+    f.pl[kk] = get_frag(rec, RC::P_LO + tt * 2 + kk, lane);
+  };
+  auto ld_k = [&](auto& f, int c, int kk) __attribute__((always_inline)) {
+    const char* rec = rec_of(c);
+    const int hm = owner ? w : 0;  // a wave without a tile loads tile 0 and ignores it
+    f.k[kk] = get_frag(rec, RC::K_HI + hm * 2 + kk, lane);
+    f.kl[kk] = get_frag(rec, RC::K_LO + hm * 2 + kk, lane);
+  };
+  auto ld_gc = [&](auto& f, int c) __attribute__((always_inline)) { f.gc = *(const float*)(rec_of(c) + RC::kGc); };
+  auto ld_z = [&](OF& f, int c) __attribute__((always_inline)) {
     if (FUSED) {
       const int cc = c < n_real ? c : n_real - 1;
-      const int t = cc * C64 + 16 * w + r16;  // rows past Lb read row Lb-1; their results are never stored
+      const int t = cc * C64 + 16 * tt + r16;  // rows past Lb read row Lb-1; their results are never stored
       const long row = ((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) f.z[nt] = Raw4<ActT>::load((const ActT*)p.z + row * D + cb + 16 * nt + 4 * g16);
     }
   };
-
-  // ---- the state: 2^16 H, row tiles hm = w + 4j, columns cb + 16 nt + r16 ----
-  float* st = p.state + ((long)b * n_v + h) * D * D;
-  f32x4 Hacc[HPW][NT];
+  auto load_all = [&](auto& f, int c) __attribute__((always_inline)) {
+    if constexpr (std::is_same<std::decay_t<decltype(f)>, CF>::value) {
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const int hl = owns(j) ? w + 4 * j : 0;  // a wave without this tile reads tile 0 and drops it
+      for (int kk = 0; kk < KD; ++kk) ld_w(f, c, kk);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) ld_up(f, c, nt);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) ld_q(f, c, kk);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) ld_p(f, c, kk);
+      ld_z(f, c);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ld_k(f, c, kk);
+    ld_gc(f, c);
+  };
+
+  // ---- the state: 2^16 H of row tile w, columns cb + 16 nt + r16 ----
+  float* st = p.state + ((long)b * n_v + h) * D * D;
+  f32x4 Hacc[NT];
+  {
+    const int hl = owner ? w : 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float v = st[(long)(16 * hl + 4 * g16 + i) * D + cb + 16 * nt + r16];
-        Hacc[j][nt][i] = owns(j) ? 65536.f * v : 0.f;
+        Hacc[nt][i] = owner ? 65536.f * v : 0.f;
       }
   }
-  // 2^8 H hi/lo into its fragment slots: tile hm is half (hm & 1) of 32-block hm >> 1
+  // 2^8 H hi/lo into its fragment slots: tile w is half (w & 1) of 32-block w >> 1
   auto put_H = [&]() __attribute__((always_inline)) {
+    if (owner) {
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int hm = w + 4 * j;
-      if (owns(j)) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          f16x4 hi, lo;
-          split4(Hacc[j][nt] * kInvS8, hi, lo);
-          _Float16* dst = (_Float16*)&sH[(((hm >> 1) * NT + nt) * 2) * kWave + lane] + 4 * (hm & 1);
-          *(f16x4*)dst = hi;
-          *(f16x4*)(dst + 8 * kWave) = lo;
-        }
+      for (int nt = 0; nt < NT; ++nt) {
+        f16x4 hi, lo;
+        split4(Hacc[nt] * kInvS8, hi, lo);
+        _Float16* dst = (_Float16*)&sH[(((w >> 1) * NT + nt) * 2) * kWave + lane] + 4 * (w & 1);
+        *(f16x4*)dst = hi;
+        *(f16x4*)(dst + 8 * kWave) = lo;
       }
     }
   };
   put_H();
 
-  float nw[NT][4];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nw[nt][i] = p.norm_w[cb + 16 * nt + 4 * g16 + i];
+  // the norm weights of this slice, read from LDS in the epilogue (registers are the scarce resource)
+  __shared__ __attribute__((aligned(16))) float sNW[CS];
+  if (tid < CS) sNW[tid] = p.norm_w[cb + tid];
 
   ActT* out = (ActT*)p.out;
   float* oraw = (float*)((char*)p.ws + p.oraw_off);
   float* sspart = (float*)((char*)p.ws + p.ss_off);
 
-  // one chunk; f holds its fragments on entry and those of chunk c + step on return
-  auto chunk = [&](int c, Frags& f, int step) __attribute__((always_inline)) {
+  auto chunk = [&](int c, auto& f, int step) __attribute__((always_inline)) {
+    constexpr bool kChain = std::is_same<std::decay_t<decltype(f)>, CF>::value;
     const int cn = c + step;  // the chunk whose fragments refill f
+    f32x4 OT[NT];
     lds_barrier();  // H of this chunk is in sH
-    // ---- U = U' - W H (token tile w); O^T = H^T Q~^T ----
-    // Column tiles go in groups of NG, and each product's hi*lo terms and hi*hi term accumulate
-    // separately: consecutive MFMAs then never wait on each other's result.
-    f32x4 U[NT], OT[NT];
+    if constexpr (kChain) {
+      // ---- U = U' - W H (token tile tt); the hi*lo and hi*hi terms accumulate separately ----
+      f32x4 U[NT];
 #pragma unroll
-    for (int n0 = 0; n0 < NT; n0 += NG) {
-      f16x8 hf[KD][NG], hl[KD][NG];
+      for (int n0 = 0; n0 < NT; n0 += NG) {
+        f16x8 hf[KD][NG], hl[KD][NG];
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk)
+        for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            hf[kk][g] = sH[((kk * NT + n0 + g) * 2) * kWave + lane];
+            hl[kk][g] = sH[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
+          }
+        f32x4 ua[NG], ub[NG];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          hf[kk][g] = sH[((kk * NT + n0 + g) * 2) * kWave + lane];
-          hl[kk][g] = sH[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
+          ua[g] = f.up[n0 + g];
+          ub[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ld_up(f, cn, n0 + g);
         }
-      f32x4 ua[NG], ub[NG], oa[NG], ob[NG];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        ua[g] = f.up[n0 + g];
-        ub[g] = oa[g] = ob[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        ld_up(f, cn, n0 + g);
-      }
+        for (int kk = 0; kk < KD; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
+          for (int g = 0; g < NG; ++g) ua[g] = mfma16(f.w[kk], hl[kk][g], ua[g]);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) ua[g] = mfma16(f.w[kk], hl[kk][g], ua[g]);
+          for (int g = 0; g < NG; ++g) ub[g] = mfma16(f.w[kk], hf[kk][g], ub[g]);
+          if (SPLIT) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) oa[g] = mfma16(hf[kk][g], f.ql[kk], oa[g]);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) ub[g] = mfma16(f.w[kk], hf[kk][g], ub[g]);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) ob[g] = mfma16(hf[kk][g], f.q[kk], ob[g]);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) oa[g] = mfma16(hl[kk][g], f.q[kk], oa[g]);
-        if (SPLIT) {
-#pragma unroll
-          for (int g = 0; g < NG; ++g) ua[g] = mfma16(f.wl[kk], hf[kk][g], ua[g]);
+            for (int g = 0; g < NG; ++g) ua[g] = mfma16(f.wl[kk], hf[kk][g], ua[g]);
+          }
+          if (n0 + NG >= NT) ld_w(f, cn, kk);  // last use of this block's W in the chunk
         }
-        if (n0 + NG >= NT) ld_wq(f, cn, kk);  // last use of this block's W and Q~ in the chunk
-        __builtin_amdgcn_sched_barrier(0);
-      }
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        U[n0 + g] = ua[g] + ub[g];
-        OT[n0 + g] = oa[g] + ob[g];
+        for (int g = 0; g < NG; ++g) U[n0 + g] = ua[g] + ub[g];
       }
-    }
-    // U hi/lo into its fragment slots: token tile w is half (w & 1) of 32-block w >> 1
+      // U hi/lo into its fragment slots: token tile tt is half (tt & 1) of 32-block tt >> 1
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f16x4 hi, lo;
-      split4(U[nt], hi, lo);
-      _Float16* dst = (_Float16*)&sU[(((w >> 1) * NT + nt) * 2) * kWave + lane] + 4 * (w & 1);
-      *(f16x4*)dst = hi;
-      *(f16x4*)(dst + 8 * kWave) = lo;
+      for (int nt = 0; nt < NT; ++nt) {
+        f16x4 hi, lo;
+        split4(U[nt], hi, lo);
+        _Float16* dst = (_Float16*)&sU[(((tt >> 1) * NT + nt) * 2) * kWave + lane] + 4 * (tt & 1);
+        *(f16x4*)dst = hi;
+        *(f16x4*)(dst + 8 * kWave) = lo;
+      }
+    } else {
+      // ---- O^T = H^T Q~^T (token tile tt) ----
+#pragma unroll
+      for (int n0 = 0; n0 < NT; n0 += NG) {
+        f16x8 hf[KD][NG], hl[KD][NG];
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            hf[kk][g] = sH[((kk * NT + n0 + g) * 2) * kWave + lane];
+            hl[kk][g] = sH[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
+          }
+        f32x4 oa[NG], ob[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) oa[g] = ob[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) oa[g] = mfma16(hf[kk][g], f.ql[kk], oa[g]);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) ob[g] = mfma16(hf[kk][g], f.q[kk], ob[g]);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) oa[g] = mfma16(hl[kk][g], f.q[kk], oa[g]);
+          if (n0 + NG >= NT) ld_q(f, cn, kk);  // last use of this block's Q~ in the chunk
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) OT[n0 + g] = oa[g] + ob[g];
+      }
     }
     lds_barrier();  // U of every token tile is in sU; every wave is done reading sH
-    // ---- H = e^{gamma_C} H + K~^T U (own row tiles); O^T += U^T P~^T ----
-    // per (block, term) one MFMA on each H tile of the group and each O^T tile: independent results
+    // ---- own H tile: H = e^{gamma_C} H + K~^T U; output waves also O^T += U^T P~^T ----
 #pragma unroll
     for (int n0 = 0; n0 < NT; n0 += NG) {
       f16x8 uf[2][NG], ul[2][NG];
@@ -828,66 +837,66 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
           ul[kk][g] = sU[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
         }
 #pragma unroll
-      for (int j = 0; j < HPW; ++j)
-#pragma unroll
-        for (int g = 0; g < NG; ++g) Hacc[j][n0 + g] = Hacc[j][n0 + g] * f.gc;
+      for (int g = 0; g < NG; ++g) Hacc[n0 + g] = Hacc[n0 + g] * f.gc;
       if (n0 + NG >= NT) ld_gc(f, cn);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int term = 0; term < 3; ++term) {
+          if (owner) {
 #pragma unroll
-          for (int j = 0; j < HPW; ++j) {
-            if (owns(j)) {
-#pragma unroll
-              for (int g = 0; g < NG; ++g) {
-                const f16x8 ka = term == 0 ? f.kl[j][kk] : f.k[j][kk];
-                const f16x8 ub = term == 1 ? ul[kk][g] : uf[kk][g];
-                Hacc[j][n0 + g] = mfma16(ka, ub, Hacc[j][n0 + g]);
-              }
+            for (int g = 0; g < NG; ++g) {
+              const f16x8 ka = term == 0 ? f.kl[kk] : f.k[kk];
+              const f16x8 ub = term == 1 ? ul[kk][g] : uf[kk][g];
+              Hacc[n0 + g] = mfma16(ka, ub, Hacc[n0 + g]);
             }
           }
+          if constexpr (!kChain) {
 #pragma unroll
-          for (int g = 0; g < NG; ++g) {
-            const f16x8 ua = term == 1 ? ul[kk][g] : uf[kk][g];
-            const f16x8 pb = term == 0 ? f.pl[kk] : f.p[kk];
-            OT[n0 + g] = mfma16(ua, pb, OT[n0 + g]);
+            for (int g = 0; g < NG; ++g) {
+              const f16x8 ua = term == 1 ? ul[kk][g] : uf[kk][g];
+              const f16x8 pb = term == 0 ? f.pl[kk] : f.p[kk];
+              OT[n0 + g] = mfma16(ua, pb, OT[n0 + g]);
+            }
           }
         }
-        if (n0 + NG >= NT) ld_pk(f, cn, kk);  // last use of this block's P~ and K~ in the chunk
-        __builtin_amdgcn_sched_barrier(0);
+        if (n0 + NG >= NT) {  // last use of this block's K~ (and P~) in the chunk
+          ld_k(f, cn, kk);
+          if constexpr (!kChain) ld_p(f, cn, kk);
+        }
       }
     }
     put_H();
 
-    // ---- output rows of token tile w: lane holds token 16w + r16, columns cb + 16 nt + 4 g16 + i ----
-    float ss = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      OT[nt] = OT[nt] * kInvS16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ss += OT[nt][i] * OT[nt][i];
-    }
-    ss += __shfl_xor(ss, 16, kWave);
-    ss += __shfl_xor(ss, 32, kWave);
-    const int t = c * C64 + 16 * w + r16;
-    const long row = ((long)b * Lb + t) * n_v + h;
-    if (FUSED) {
-      const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
-      float4 res[NT];
+    // ---- output waves: token 16 tt + r16, columns cb + 16 nt + 4 g16 + i ----
+    if constexpr (!kChain) {
+      float ss = 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float4 zf = Raw4<ActT>::widen(f.z[nt]);
-        res[nt] = make_float4(nw[nt][0] * (OT[nt][0] * inv) * silu(zf.x), nw[nt][1] * (OT[nt][1] * inv) * silu(zf.y),
-                              nw[nt][2] * (OT[nt][2] * inv) * silu(zf.z), nw[nt][3] * (OT[nt][3] * inv) * silu(zf.w));
-      }
-      ld_z(f, cn);
-      if (t < Lb) {
+        OT[nt] = OT[nt] * kInvS16;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) Act4<ActT>::store(out + row * D + cb + 16 * nt + 4 * g16, res[nt]);
+        for (int i = 0; i < 4; ++i) ss += OT[nt][i] * OT[nt][i];
       }
-    } else {
-      if (t < Lb) {
+      ss += __shfl_xor(ss, 16, kWave);
+      ss += __shfl_xor(ss, 32, kWave);
+      const int t = c * C64 + 16 * tt + r16;
+      const long row = ((long)b * Lb + t) * n_v + h;
+      if (FUSED) {
+        const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
+        float4 res[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float4 zf = Raw4<ActT>::widen(f.z[nt]);
+          const float4 nw = *(const float4*)&sNW[16 * nt + 4 * g16];
+          res[nt] = make_float4(nw.x * (OT[nt][0] * inv) * silu(zf.x), nw.y * (OT[nt][1] * inv) * silu(zf.y),
+                                nw.z * (OT[nt][2] * inv) * silu(zf.z), nw.w * (OT[nt][3] * inv) * silu(zf.w));
+        }
+        ld_z(f, cn);
+        if (t < Lb) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) Act4<ActT>::store(out + row * D + cb + 16 * nt + 4 * g16, res[nt]);
+        }
+      } else if (t < Lb) {
         if (g16 == 0) sspart[row * NSPLIT + split] = ss;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -896,13 +905,11 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
     }
   };
 
-  if (n_real > 0) {
+  // every wave runs the same number of chunks and barriers, whichever copy of the loop it is in
+  auto run = [&](auto& f0, auto& f1) __attribute__((always_inline)) {
     if (DB) {
-      Frags f0, f1;
-      load_a(f0, 0);
-      load_b(f0, 0);
-      load_a(f1, 1);
-      load_b(f1, 1);
+      load_all(f0, 0);
+      load_all(f1, 1);
       // the loop body has no branch, so the compiler can count the loads still in flight at its top
       // (a conditional second chunk made it wait for all of them)
       int c = 0;
@@ -912,23 +919,26 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
       }
       if (c < n_real) chunk(c, f0, 2);
     } else {
-      Frags f0;
-      load_a(f0, 0);
-      load_b(f0, 0);
+      load_all(f0, 0);
       for (int c = 0; c < n_real; ++c) chunk(c, f0, 1);
+    }
+  };
+  if (n_real > 0) {
+    if (chain) {
+      CF f0, f1;
+      run(f0, f1);
+    } else {
+      OF f0, f1;
+      run(f0, f1);
     }
   }
 
   // final state, in place
+  if (owner) {
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const int hm = w + 4 * j;
-    if (owns(j)) {
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[(long)(16 * hm + 4 * g16 + i) * D + cb + 16 * nt + r16] = Hacc[j][nt][i] * kInvS16;
-    }
+      for (int i = 0; i < 4; ++i) st[(long)(16 * w + 4 * g16 + i) * D + cb + 16 * nt + r16] = Hacc[nt][i] * kInvS16;
   }
 
   // conv tail: rows len .. len+2 of [old tail | mixed]. Split 0 of value head h owns its v channels;
@@ -939,7 +949,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(PrefillArgs p) {
     const ActT* mx = (const ActT*)p.mixed + (long)b * Lb * C;
     const int kh = h / R;
     const int nch = (h % R == 0) ? 3 * D : D;
-    for (int lc = tid; lc < nch; lc += 256) {
+    for (int lc = tid; lc < nch; lc += 512) {
       int gc;
       if (lc < D) gc = 2 * p.n_k * D + h * D + lc;
       else if (lc < 2 * D) gc = kh * D + (lc - D);
@@ -1004,7 +1014,7 @@ hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timing_before("state_pass", st);
-  hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NSPLIT == 1, (NT <= 4)>), dim3(NSPLIT * p.n_v * p.B), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NSPLIT == 1, (NT <= 4)>), dim3(NSPLIT * p.n_v * p.B), dim3(512), 0, st, p);
   timing_after(st);
   e = hipGetLastError();
   if (e != hipSuccess || NSPLIT == 1) return e;
