@@ -162,17 +162,20 @@ struct Act4<bf16_t> {
   }
 };
 
-// two adjacent activations (4 bytes of bf16 or 8 of fp32)
+// two adjacent activations (4 bytes of bf16 or 8 of fp32), loaded as stored and widened when used
 template <typename ActT>
 struct Pair {
-  static __device__ __forceinline__ float2 load(const ActT* p) {
-    const uint32_t u = *(const uint32_t*)p;
+  typedef uint32_t type;
+  static __device__ __forceinline__ type load(const ActT* p) { return *(const uint32_t*)p; }
+  static __device__ __forceinline__ float2 widen(type u) {
     return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
   }
 };
 template <>
 struct Pair<float> {
-  static __device__ __forceinline__ float2 load(const float* p) { return *(const float2*)p; }
+  typedef float2 type;
+  static __device__ __forceinline__ type load(const float* p) { return *(const float2*)p; }
+  static __device__ __forceinline__ float2 widen(type u) { return u; }
 };
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
@@ -199,10 +202,11 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   constexpr int OFF_KK = OFF_KT + SZ_CHF;           // 2^16 K K^T [r][s]
   constexpr int OFF_QK = OFF_KK + C64 * LT * 4;     // 2^16 Q K^T [t][s]
   constexpr int OFF_T = OFF_QK + C64 * LT * 4;      // 2^8 T as f16 hi (then lo)
-  constexpr int OFF_X = OFF_T + (SPLIT ? 2 : 1) * C64 * LDT * 2;
-  constexpr int OFF_G = OFF_X + 4 * 16 * 17 * 4;
+  constexpr int OFF_X = OFF_T;                      // level products, only while T is still fp32
+  constexpr int OFF_G = OFF_T + (SPLIT ? 2 : 1) * C64 * LDT * 2;
   constexpr int OFF_B = OFF_G + R * C64 * 4;
   constexpr int LDS = OFF_B + R * C64 * 4;
+  static_assert(4 * 16 * 17 * 4 <= (SPLIT ? 2 : 1) * C64 * LDT * 2, "level products fit the T tile");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(CPL == 1 || (CPL == 2 && D == 128), "channel layout");
   __shared__ __attribute__((aligned(16))) char smem[LDS];
@@ -233,16 +237,40 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   const ActT* tail = (const ActT*)p.tail + (long)b * 3 * C;
   const ActT* cw = (const ActT*)p.conv_w;
 
-  // ---- 1. gates of the R value heads: wave r, lane = token; inclusive scan of g over the chunk -----
+  // ---- 1. every global load of this stage first, then the arithmetic: gate inputs (lane = token),
+  // conv inputs and taps of q, k and the R value heads (wave w: rows TPW w - 3 .. TPW w + TPW - 1, lane:
+  // channels CPL lane + j, two adjacent channels per load). Addresses are clamped into range and the
+  // values masked when widened, so that all loads are in flight before the first wait.
+  constexpr int NCV = 2 + R;  // convolutions: q, k, then the value heads
+  typedef typename std::conditional<CPL == 2, typename Pair<ActT>::type, ActT>::type XRaw;
+  typedef typename Raw4<ActT>::type WRaw;
+  const int hg = kh * R + (w < R ? w : 0);
+  const int tg = t0 + lane;
+  const long gi = ((long)b * Lb + (tg < len ? tg : len - 1)) * p.n_v + hg;  // len >= 1 here
+  const ActT a_raw = ((const ActT*)p.a)[gi], b_raw = ((const ActT*)p.b)[gi];
+  XRaw xr[NCV][TPW + 3];
+  WRaw wr[NCV][CPL];
+#pragma unroll
+  for (int j = 0; j < NCV; ++j) {
+    const int base = j == 0 ? kh * D : j == 1 ? (n_k + kh) * D : (2 * n_k + kh * R + j - 2) * D;
+    const int gc = base + (CPL == 2 ? 2 * lane : (lane < D ? lane : 0));
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) wr[j][i] = Raw4<ActT>::load(cw + (gc + i) * 4);
+#pragma unroll
+    for (int i = 0; i < TPW + 3; ++i) {
+      const int t = t0 + TPW * w - 3 + i;
+      const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
+      if constexpr (CPL == 2) xr[j][i] = Pair<ActT>::load(src + gc);
+      else xr[j][i] = src[gc];
+    }
+  }
+
+  // ---- 2. gates of the R value heads: wave r, lane = token; inclusive scan of g over the chunk -----
   if (w < R) {
-    const int h = kh * R + w;
-    const int t = t0 + lane;
-    const long gi = ((long)b * Lb + (t < len ? t : len - 1)) * p.n_v + h;  // len >= 1 here
-    const float av = to_f32(((const ActT*)p.a)[gi]), bv = to_f32(((const ActT*)p.b)[gi]);
-    const float g0 = -__expf(p.A_log[h]) * softplus(av + p.dt_bias[h]);
-    const float b0 = sigmoid(bv);
-    float g = t < len ? g0 : 0.f;
-    const float be = t < len ? b0 : 0.f;
+    const float g0 = -__expf(p.A_log[hg]) * softplus(to_f32(a_raw) + p.dt_bias[hg]);
+    const float b0 = sigmoid(to_f32(b_raw));
+    float g = tg < len ? g0 : 0.f;
+    const float be = tg < len ? b0 : 0.f;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const float o = __shfl_up(g, off, kWave);
@@ -252,43 +280,31 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     sBet[w * C64 + lane] = be;
   }
 
-  // ---- 2. conv + SiLU: wave w owns tokens TPW w .. TPW w + TPW-1, lane owns channels CPL lane + j --
-  // every load below is unconditional from a clamped, in-range address and masked afterwards, so
-  // that the compiler issues them all before the first wait; two adjacent channels share one load
-  auto conv = [&](int gc_base, float (*y)[CPL]) {
+  // ---- 3. conv + SiLU of convolution j: y[tt][i] for token TPW w + tt, channel CPL lane + i ---------
+  auto conv = [&](int j, float (*y)[CPL]) {
     float x[TPW + 3][CPL], wt[4][CPL];
-    if (CPL == 2) {
-      const int gc = gc_base + 2 * lane;
-      const float4 wa = Act4<ActT>::load(cw + gc * 4), wb = Act4<ActT>::load(cw + gc * 4 + 4);
-      wt[0][0] = wa.x; wt[1][0] = wa.y; wt[2][0] = wa.z; wt[3][0] = wa.w;
-      wt[0][CPL - 1] = wb.x; wt[1][CPL - 1] = wb.y; wt[2][CPL - 1] = wb.z; wt[3][CPL - 1] = wb.w;
+    const float m = CPL == 2 || lane < D ? 1.f : 0.f;  // lanes past d (d = 32) produce zeros
 #pragma unroll
-      for (int i = 0; i < TPW + 3; ++i) {
-        const int t = t0 + TPW * w - 3 + i;
-        const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
-        const float2 v = Pair<ActT>::load(src + gc);
-        x[i][0] = t < Lb ? v.x : 0.f;
-        x[i][CPL - 1] = t < Lb ? v.y : 0.f;
-      }
-    } else {
-      const bool ok = lane < D;
-      const int gc = gc_base + (ok ? lane : 0);
-      const float m = ok ? 1.f : 0.f;
+    for (int i = 0; i < CPL; ++i) {
+      const float4 wf = Raw4<ActT>::widen(wr[j][i]);
+      wt[0][i] = m * wf.x; wt[1][i] = m * wf.y; wt[2][i] = m * wf.z; wt[3][i] = m * wf.w;
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wt[q][0] = m * to_f32(cw[gc * 4 + q]);
-#pragma unroll
-      for (int i = 0; i < TPW + 3; ++i) {
-        const int t = t0 + TPW * w - 3 + i;
-        const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
-        const float v = to_f32(src[gc]);
-        x[i][0] = t < Lb ? v : 0.f;
+    for (int i = 0; i < TPW + 3; ++i) {
+      const bool in = t0 + TPW * w - 3 + i < Lb;
+      if constexpr (CPL == 2) {
+        const float2 v = Pair<ActT>::widen(xr[j][i]);
+        x[i][0] = in ? v.x : 0.f;
+        x[i][CPL - 1] = in ? v.y : 0.f;
+      } else {
+        x[i][0] = in ? to_f32(xr[j][i]) : 0.f;
       }
     }
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-      for (int j = 0; j < CPL; ++j)
-        y[tt][j] = silu(wt[0][j] * x[tt][j] + wt[1][j] * x[tt + 1][j] + wt[2][j] * x[tt + 2][j] + wt[3][j] * x[tt + 3][j]);
+      for (int i = 0; i < CPL; ++i)
+        y[tt][i] = silu(wt[0][i] * x[tt][i] + wt[1][i] * x[tt + 1][i] + wt[2][i] * x[tt + 2][i] + wt[3][i] * x[tt + 3][i]);
   };
   auto l2norm = [&](float (*y)[CPL]) {
 #pragma unroll
@@ -303,10 +319,10 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     }
   };
   float qn[TPW][CPL], kn[TPW][CPL], vv[R][TPW][CPL];
-  conv(kh * D, qn);
-  conv(n_k * D + kh * D, kn);
+  conv(0, qn);
+  conv(1, kn);
 #pragma unroll
-  for (int r = 0; r < R; ++r) conv(2 * n_k * D + (kh * R + r) * D, vv[r]);
+  for (int r = 0; r < R; ++r) conv(2 + r, vv[r]);
   l2norm(qn);
   l2norm(kn);
   // token-major 2^8 q, 2^8 k (hi/lo) for the Gram products; channel-major k in fp32
@@ -338,7 +354,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   }
   lds_barrier();
 
-  // ---- 3. Gram products on the lower 16x16 tiles (split operands) --------------------------------
+  // ---- 4. Gram products on the lower 16x16 tiles (split operands) --------------------------------
   // K K^T as [r][s] (for A); K Q^T computed as D[s][t] so that each lane ends up with four
   // consecutive s of one row t of Q K^T (for P~). The three split terms go to separate accumulators.
   for (int job = w; job < 20; job += NWV) {
@@ -386,7 +402,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   }
   lds_barrier();
 
-  // ---- 4. per value head of the group ------------------------------------------------------------
+  // ---- 5. per value head of the group ------------------------------------------------------------
   for (int r = 0; r < R; ++r) {
     const int h = kh * R + r;
     const float* gam = sGam + r * C64;
