@@ -55,6 +55,7 @@ def _load():
         _lib.oracle_verify.argtypes = [ctypes.POINTER(_Dims), I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, I]
         _lib.oracle_verify.restype = I
         _lib.oracle_accept.argtypes = [I, I, P, P, P, P, P]
+        _lib.oracle_accept_paths.argtypes = [I, I, I, P, P, P, P, P, P]
     return _lib
 
 
@@ -200,3 +201,30 @@ def accept(drafts, preds):
     ne = np.empty(B, np.int32)
     _load().oracle_accept(B, K, _p(drafts), _p(preds), _p(m), _p(em), _p(ne))
     return m, em, ne
+
+
+def verify_paths(dims: Dims, weights, mixed, z, a, b, tail0, H0, threads=None):
+    """P candidate paths per sequence, each T tokens from the sequence's (tail0, H0) (mtp/generate.py
+    page, tree_verify_step: the cache is tiled into one row per path and every row runs as an ordinary
+    sequence). mixed [B,P,T,C], z [B,P,T,n_v*d_v], a and b [B,P,T,n_v]; tail0 [B,Kc,C], H0 [B,n_v,d_k,d_v].
+    Returns dict(ckpt_H [B,P,T,n_v,d_k,d_v], ckpt_tail [B,P,T,Kc,C], out [B,P,T,n_v*d_v])."""
+    mixed, z, a, b = _f64(mixed), _f64(z), _f64(a), _f64(b)
+    B, P, T = mixed.shape[:3]
+    flat = lambda x: x.reshape((B * P,) + x.shape[2:])
+    rows = lambda x: np.repeat(_f64(x), P, axis=0)  # row b*P + p starts from sequence b's state
+    r = verify(dims, weights, flat(mixed), flat(z), flat(a), flat(b), rows(tail0), rows(H0), threads)
+    return {k: v.reshape((B, P) + v.shape[1:]) for k, v in r.items()}
+
+
+def accept_paths(drafts, preds):
+    """drafts [B,P,K], preds [B,P,K+1] int. Returns (m [B], path [B], emitted [B,K+1], n_emitted [B]):
+    the first path with the longest accepted prefix, and its emitted tokens."""
+    drafts, preds = _i32(drafts), _i32(preds)
+    B, P, K = drafts.shape
+    assert preds.shape == (B, P, K + 1)
+    m = np.empty(B, np.int32)
+    path = np.empty(B, np.int32)
+    em = np.empty((B, K + 1), np.int32)
+    ne = np.empty(B, np.int32)
+    _load().oracle_accept_paths(B, P, K, _p(drafts), _p(preds), _p(m), _p(path), _p(em), _p(ne))
+    return m, path, em, ne

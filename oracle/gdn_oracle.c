@@ -223,3 +223,30 @@ void oracle_accept(int B, int K, const int* drafts, const int* preds, int* m, in
     n_emitted[s] = j + 1;
   }
 }
+
+/*
+ * Winner of a batch-of-paths verify (mtp/generate.py page, tree_verify_step): every one of the P
+ * paths of a sequence gets its accepted prefix m_p by the rule of oracle_accept, and the winner is
+ * the first path with the largest m_p (a later path wins only by matching strictly more drafts). The
+ * emitted tokens are the winner's, formed as in oracle_accept.
+ * drafts [B][P][K], preds [B][P][K+1]; m, path, n_emitted [B]; emitted [B][K+1].
+ */
+void oracle_accept_paths(int B, int P, int K, const int* drafts, const int* preds, int* m, int* path, int* emitted,
+                         int* n_emitted) {
+  for (int s = 0; s < B; ++s) {
+    int best = 0, best_m = -1;
+    for (int p = 0; p < P; ++p) {
+      const int* dr = drafts + ((size_t)s * P + p) * K;
+      const int* pr = preds + ((size_t)s * P + p) * (K + 1);
+      int j = 0;
+      while (j < K && pr[j] == dr[j]) ++j;
+      if (j > best_m) {
+        best_m = j;
+        best = p;
+      }
+    }
+    oracle_accept(1, K, drafts + ((size_t)s * P + best) * K, preds + ((size_t)s * P + best) * (K + 1), m + s,
+                  emitted + (size_t)s * (K + 1), n_emitted + s);
+    path[s] = best;
+  }
+}

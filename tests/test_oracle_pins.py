@@ -79,6 +79,17 @@ def test_golden_accept():
     np.testing.assert_array_equal(ne, c["n_emitted"])
 
 
+def test_golden_accept_paths():
+    c = GOLD["accept_paths"]
+    m, path, em, ne = oracle.accept_paths(c["drafts"], c["preds"])
+    np.testing.assert_array_equal(m, c["m"])
+    np.testing.assert_array_equal(path, c["path"])
+    np.testing.assert_array_equal(em, c["emitted"])
+    np.testing.assert_array_equal(ne, c["n_emitted"])
+    P, K = np.array(c["drafts"]).shape[1:]
+    np.testing.assert_array_equal((np.arange(len(m)) * P + path) * (K + 1) + m, c["ckpt_index"])
+
+
 # ---- P1: brute force (dense closed form, one triangular solve) ----------------------------------
 
 @pytest.mark.parametrize("L,strong,h0", [(1, False, False), (7, False, True), (33, True, True), (64, False, True)])
@@ -305,6 +316,58 @@ def test_accept_exhaustive_k4_vocab3():
         mm = m_ref[i]
         exp = list(D[i, :mm]) + [P[i, mm]] + [0] * (K - mm)
         np.testing.assert_array_equal(em[i], exp)
+
+
+def test_accept_paths_exhaustive_p2_k2_vocab2():
+    """Every pair of paths over a vocabulary of 2 with K = 2: the winner is the first maximum of the
+    per-path match counts (numpy's argmax), and P = 1 is the single-path rule."""
+    K, P = 2, 2
+    dr1 = np.array(list(itertools.product(range(2), repeat=K)), np.int32)
+    pr1 = np.array(list(itertools.product(range(2), repeat=K + 1)), np.int32)
+    one = [(d, q) for d in dr1 for q in pr1]                     # every (drafts, preds) of one path
+    pairs = list(itertools.product(range(len(one)), repeat=P))   # every assignment of two paths
+    D = np.array([[one[i][0] for i in pr] for pr in pairs])
+    Q = np.array([[one[i][1] for i in pr] for pr in pairs])
+    m, path, em, ne = oracle.accept_paths(D, Q)
+    mp = np.cumprod(Q[:, :, :K] == D, axis=2).sum(axis=2)       # [cases, P]
+    np.testing.assert_array_equal(m, mp.max(axis=1))
+    np.testing.assert_array_equal(path, np.argmax(mp, axis=1))
+    win = np.arange(len(pairs))
+    m1, em1, ne1 = oracle.accept(D[win, path], Q[win, path])
+    np.testing.assert_array_equal(em, em1)
+    np.testing.assert_array_equal(ne, ne1)
+    # one path: the same as accept
+    m2, path2, em2, ne2 = oracle.accept_paths(D[:, :1], Q[:, :1])
+    m3, em3, ne3 = oracle.accept(D[:, 0], Q[:, 0])
+    assert not path2.any()
+    np.testing.assert_array_equal(m2, m3)
+    np.testing.assert_array_equal(em2, em3)
+
+
+def test_verify_paths_rows_start_from_their_sequence():
+    """Path p of sequence b is an ordinary verify from sequence b's state and tail; paths with the same
+    tokens give the same checkpoints."""
+    dims = LayerDims(n_k=1, n_v=2, d_k=4, d_v=6, act=ACT_F32)
+    od = oracle.Dims.of(dims)
+    B, P, T = 2, 3, 4
+    w, x, rng = make_layer(29, dims, B * P, T)
+    shape = lambda a: a.reshape((B, P) + a.shape[1:])
+    mixed, z, a, b = shape(x.mixed).copy(), shape(x.z), shape(x.a), shape(x.b)
+    mixed[1, 2] = mixed[1, 0]  # sequence 1: path 2 repeats path 0's tokens
+    z, a, b = z.copy(), a.copy(), b.copy()
+    z[1, 2], a[1, 2], b[1, 2] = z[1, 0], a[1, 0], b[1, 0]
+    H0 = rng.standard_normal((B, 2, 4, 6)) * 0.3
+    t0 = rng.standard_normal((B, 3, dims.conv_dim))
+    r = oracle.verify_paths(od, w, mixed, z, a, b, t0, H0)
+    for s in range(B):
+        for p in range(P):
+            one = oracle.verify(od, w, mixed[s, p:p + 1], z[s, p:p + 1], a[s, p:p + 1], b[s, p:p + 1], t0[s:s + 1],
+                                H0[s:s + 1])
+            for k in ("ckpt_H", "ckpt_tail", "out"):
+                np.testing.assert_array_equal(r[k][s, p], one[k][0])
+    for k in ("ckpt_H", "ckpt_tail", "out"):
+        np.testing.assert_array_equal(r[k][1, 2], r[k][1, 0])
+        assert not np.array_equal(r[k][0, 1], r[k][0, 0])
 
 
 def test_verify_checkpoints_equal_repeated_decode():
