@@ -1,6 +1,6 @@
 """Benchmark of the Gated DeltaNet layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|verify_paths|copy]
 
 Headline (`value`): prefill tokens/s of one layer on one sequence of 4096 tokens, 16 key / 16 value
 heads, d_k = d_v = 128, bf16 activations, fp32 state, continued from a saved state (one step = one
@@ -283,6 +283,47 @@ def bench_verify(torch, gdn, args):
             "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()}}
 
 
+def bench_verify_paths(torch, gdn, args):
+    from gdn_inputs import NEXT, make_layer, path_inputs, random_state, verify_path_draws
+    from tests.gpu_helpers import act, desc_of, f32, i32, weights
+    dims = NEXT
+    B, P, K = 64, 4, 4
+    T = K + 1
+    d = desc_of(dims)
+    w, _, rng = make_layer(301, dims, 1, 1)
+    x = path_inputs(rng, dims, B, P, T)
+    S0, tail0 = random_state(rng, dims, B)
+    drafts, preds, _ = verify_path_draws(rng, B, P, K)
+    W = weights(w, dims)
+    pools = [(f32(S0), act(tail0, dims)) for _ in range(3)]  # 3 x 128 MiB rotate past the LLC
+    mx, zz, aa, bb = act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims)
+    ck_s = torch.empty(B, P, T, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda")
+    ck_t = torch.empty(B, P, T, 3, dims.conv_dim, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(B, P, T, dims.value_dim, dtype=torch.bfloat16, device="cuda")
+    dr, pr = i32(drafts), i32(preds)
+    slots = i32(np.arange(B))
+
+    def step(i):
+        sp, tp = pools[i % len(pools)]
+        gdn.verify_paths(d, W, mx, zz, aa, bb, None, tp, sp, ck_s, ck_t, out)
+        ci = gdn.accept_paths(dr, pr)[4]
+        gdn.state_copy(d, sp, tp, slots, ck_s, ck_t, ci, B)
+
+    ms, _ = Timer(torch, args.steps).run(step, args.steps, args.warmup)
+    kern = launch_breakdown(torch, gdn, step, 4)
+    rec = dims.n_v * dims.d_k * dims.d_v * 4
+    tail_b = 3 * dims.conv_dim * 2
+    io = B * P * T * 2 * (dims.conv_dim + 2 * dims.value_dim + 2 * dims.n_v)
+    verify_bytes = B * (rec + tail_b) + B * P * T * (rec + tail_b) + io  # shared state read once per sequence
+    nbytes = verify_bytes + B * 2 * (rec + tail_b)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "64 sequences x 4 paths x (1+4) tokens, 16/32 heads, d=128: verify + accept + commit",
+            "ms_per_step": ms, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+            "roofline": kernel_roofline("verify_paths_b64_p4_k4", "step_verify", kern["step_verify"][1],
+                                        nbytes=verify_bytes),
+            "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()}}
+
+
 def bench_copy(torch, gdn, args):
     from gdn_inputs import NEXT
     from tests.gpu_helpers import desc_of
@@ -365,6 +406,8 @@ def main():
         torch.cuda.empty_cache()
     if only in ("all", "verify"):
         line["verify"] = bench_verify(torch, gdn, args)
+    if only in ("all", "verify_paths"):
+        line["verify_paths"] = bench_verify_paths(torch, gdn, args)
     if only in ("all", "copy"):
         line["copy"] = bench_copy(torch, gdn, args)
     if not args.no_cpu and only in ("all", "prefill"):

@@ -49,7 +49,8 @@ class _Weights(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("gdn_last_error", "gdn_version", "gdn_conv_chunk", "gdn_prefill_workspace_bytes", "gdn_prefill_chunk",
-           "gdn_decode_step", "gdn_verify_with_checkpoints", "gdn_accept", "gdn_state_copy",
+           "gdn_decode_step", "gdn_verify_with_checkpoints", "gdn_verify_paths", "gdn_accept", "gdn_accept_paths",
+           "gdn_state_copy",
            "gdn_state_record_bytes", "gdn_timing_begin", "gdn_timing_end")
 
 
@@ -72,14 +73,16 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_prefill_chunk.argtypes = [D, W, P, P, P, P, P, P, P, P, I, I, P, Z, P]
     lib.gdn_decode_step.argtypes = [D, W, P, P, P, P, P, P, P, P, I, P]
     lib.gdn_verify_with_checkpoints.argtypes = [D, W, P, P, P, P, I, P, P, P, P, P, P, I, P]
+    lib.gdn_verify_paths.argtypes = [D, W, P, P, P, P, I, I, P, P, P, P, P, P, I, P]
     lib.gdn_accept.argtypes = [P, P, I, I, P, P, P, P, P]
+    lib.gdn_accept_paths.argtypes = [P, P, I, I, I, P, P, P, P, P, P]
     lib.gdn_state_copy.argtypes = [D, P, P, P, P, P, P, I, P]
     lib.gdn_state_record_bytes.argtypes = [D]
     lib.gdn_state_record_bytes.restype = Z
     lib.gdn_timing_begin.argtypes = [I]
     lib.gdn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), I]
     for name in ("gdn_conv_chunk", "gdn_prefill_chunk", "gdn_decode_step", "gdn_verify_with_checkpoints",
-                 "gdn_accept", "gdn_state_copy"):
+                 "gdn_verify_paths", "gdn_accept", "gdn_accept_paths", "gdn_state_copy"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -281,6 +284,60 @@ def verify_with_checkpoints(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, slot, 
     _check("gdn_verify_with_checkpoints",
            lib.gdn_verify_with_checkpoints(ctypes.byref(desc.c()), ctypes.byref(cw), *args, T, *rest, B, _stream()))
     return ckpt_state, ckpt_tail, out
+
+
+def verify_paths(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, slot, conv_tail_pool, state_pool,
+                 ckpt_state=None, ckpt_tail=None, out=None, check_slots: bool = False):
+    """P candidate paths of T tokens per sequence (mixed [B,P,T,C_ch]), every path of sequence b from pool
+    row slot[b] (unchanged). Returns (ckpt_state [B,P,T,n_v,d_k,d_v], ckpt_tail [B,P,T,Kc,C_ch],
+    out [B,P,T,n_v*d_v])."""
+    lib = load_library()
+    B, P, T, _ = mixed.shape
+    dev = mixed.device
+    nvd = desc.n_v * desc.d_v
+    npool = state_pool.shape[0]
+    if ckpt_state is None:
+        ckpt_state = torch.empty(B, P, T, desc.n_v, desc.d_k, desc.d_v, dtype=torch.float32, device=dev)
+    if ckpt_tail is None:
+        ckpt_tail = torch.empty(B, P, T, desc.kc, desc.conv_dim, dtype=desc.act, device=dev)
+    if out is None:
+        out = torch.empty(B, P, T, nvd, dtype=desc.act, device=dev)
+    if slot is not None and check_slots:
+        _check_index(slot, "slot", npool, False)
+    cw = _weights(desc, w, dev)
+    args = (_dev(mixed, "mixed", (B, P, T, desc.conv_dim), desc.act, dev),
+            _dev(z, "z", (B, P, T, nvd), desc.act, dev),
+            _dev(a, "a", (B, P, T, desc.n_v), desc.act, dev),
+            _dev(b, "b", (B, P, T, desc.n_v), desc.act, dev))
+    rest = (_opt(slot, "slot", (B,), torch.int32, dev),
+            _dev(conv_tail_pool, "conv_tail_pool", (npool, desc.kc, desc.conv_dim), desc.act, dev),
+            _dev(state_pool, "state_pool", (npool, desc.n_v, desc.d_k, desc.d_v), torch.float32, dev),
+            _dev(ckpt_state, "ckpt_state", (B, P, T, desc.n_v, desc.d_k, desc.d_v), torch.float32, dev),
+            _dev(ckpt_tail, "ckpt_tail", (B, P, T, desc.kc, desc.conv_dim), desc.act, dev),
+            _dev(out, "out", (B, P, T, nvd), desc.act, dev))
+    _check("gdn_verify_paths",
+           lib.gdn_verify_paths(ctypes.byref(desc.c()), ctypes.byref(cw), *args, T, P, *rest, B, _stream()))
+    return ckpt_state, ckpt_tail, out
+
+
+def accept_paths(drafts, preds, want_ckpt_index: bool = True):
+    """Winner of P paths per sequence (drafts [B,P,K], preds [B,P,K+1]). Returns (m [B], path [B],
+    emitted [B,K+1], n_emitted [B], ckpt_index [B] or None)."""
+    lib = load_library()
+    B, P, K = drafts.shape
+    dev = drafts.device
+    m = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty(B, dtype=torch.int32, device=dev)
+    em = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ne = torch.empty(B, dtype=torch.int32, device=dev)
+    ci = torch.empty(B, dtype=torch.int32, device=dev) if want_ckpt_index else None
+    _check("gdn_accept_paths",
+           lib.gdn_accept_paths(_dev(drafts, "drafts", (B, P, K), torch.int32, dev),
+                                _dev(preds, "preds", (B, P, K + 1), torch.int32, dev), B, P, K,
+                                _dev(m, "m", (B,), torch.int32, dev), _dev(path, "path", (B,), torch.int32, dev),
+                                _dev(em, "emitted", None, torch.int32, dev), _dev(ne, "n_emitted", None, torch.int32, dev),
+                                _opt(ci, "ckpt_index", (B,), torch.int32, dev), _stream()))
+    return m, path, em, ne, ci
 
 
 def accept(drafts, preds, want_ckpt_index: bool = True):

@@ -175,6 +175,8 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
   if (B > 65535) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d exceeds 65535", B);
   if ((long)Lb * d->n_v * d->d_v >= (1L << 31))
     return fail(GDN_EINVAL, "gdn_prefill_chunk: Lb * n_v * d_v = %ld must stay below 2^31", (long)Lb * d->n_v * d->d_v);
+  if ((long)B * ((Lb + gdn::kChunk - 1) / gdn::kChunk) * d->n_k >= (1L << 31))
+    return fail(GDN_EINVAL, "gdn_prefill_chunk: B * chunks * n_k must stay below 2^31");
   if (d->act_dtype == GDN_F32 && d->d_k > 64)
     return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunk: fp32 activations are built for d <= 64 (got %d)", d->d_k);
   const size_t need = gdn_prefill_workspace_bytes(d, B, Lb);
@@ -197,20 +199,20 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
 
 static int step_common(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
                        const void* b, int T, const int32_t* slot, const void* tail_in, const float* state_in,
-                       void* tail_out, float* state_out, void* out, int B, int verify, gdn_stream_t stream,
+                       void* tail_out, float* state_out, void* out, int B, int P, int verify, gdn_stream_t stream,
                        const char* name) {
   if (int rc = check_desc(d)) return rc;
   if (int rc = check_weights(w)) return rc;
   if (!mixed || !z || !a || !b || !tail_in || !state_in || !tail_out || !state_out || !out)
     return fail(GDN_EINVAL, "%s: NULL pointer", name);
-  if (B <= 0 || T <= 0) return fail(GDN_EINVAL, "%s: B=%d T=%d must be positive", name, B, T);
-  if (B > 65535) return fail(GDN_EINVAL, "%s: B=%d exceeds 65535", name, B);
+  if (B <= 0 || T <= 0 || P <= 0) return fail(GDN_EINVAL, "%s: B=%d T=%d P=%d must be positive", name, B, T, P);
+  if ((long)B * P > 65535) return fail(GDN_EINVAL, "%s: B*P=%ld exceeds 65535", name, (long)B * P);
   if (!aligned16(state_in) || !aligned16(state_out)) return fail(GDN_EINVAL, "%s: states must be 16-byte aligned", name);
   gdn::StepArgs p{};
   p.conv_w = w->conv_w; p.A_log = w->A_log; p.dt_bias = w->dt_bias; p.norm_w = w->norm_w;
   p.mixed = mixed; p.z = z; p.a = a; p.b = b; p.slot = slot; p.tail_in = tail_in; p.state_in = state_in;
   p.tail_out = tail_out; p.state_out = state_out; p.out = out;
-  p.B = B; p.T = T; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d); p.verify = verify;
+  p.B = B; p.T = T; p.P = P; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d); p.verify = verify;
   p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
   return hip_status(gdn::launch_step(p, d->act_dtype, d->d_k, d->n_v / d->n_k, (hipStream_t)stream), name);
 }
@@ -219,7 +221,7 @@ int gdn_decode_step(const gdn_desc* d, const gdn_weights* w, const void* mixed, 
                     const void* b, const int32_t* slot, void* conv_tail_pool, float* state_pool, void* out, int B,
                     gdn_stream_t stream) {
   return step_common(d, w, mixed, z, a, b, 1, slot, conv_tail_pool, state_pool, conv_tail_pool, state_pool, out, B,
-                     0, stream, "gdn_decode_step");
+                     1, 0, stream, "gdn_decode_step");
 }
 
 int gdn_verify_with_checkpoints(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z,
@@ -228,16 +230,38 @@ int gdn_verify_with_checkpoints(const gdn_desc* d, const gdn_weights* w, const v
                                 gdn_stream_t stream) {
   if (ckpt_state == state_pool || ckpt_tail == conv_tail_pool)
     return fail(GDN_EINVAL, "gdn_verify_with_checkpoints: checkpoints alias the pools");
-  return step_common(d, w, mixed, z, a, b, T, slot, conv_tail_pool, state_pool, ckpt_tail, ckpt_state, out, B, 1,
+  return step_common(d, w, mixed, z, a, b, T, slot, conv_tail_pool, state_pool, ckpt_tail, ckpt_state, out, B, 1, 1,
                      stream, "gdn_verify_with_checkpoints");
+}
+
+int gdn_verify_paths(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
+                     const void* b, int T, int P, const int32_t* slot, const void* conv_tail_pool,
+                     const float* state_pool, float* ckpt_state, void* ckpt_tail, void* out, int B,
+                     gdn_stream_t stream) {
+  if (ckpt_state == state_pool || ckpt_tail == conv_tail_pool)
+    return fail(GDN_EINVAL, "gdn_verify_paths: checkpoints alias the pools");
+  return step_common(d, w, mixed, z, a, b, T, slot, conv_tail_pool, state_pool, ckpt_tail, ckpt_state, out, B, P, 1,
+                     stream, "gdn_verify_paths");
 }
 
 int gdn_accept(const int32_t* drafts, const int32_t* preds, int B, int K, int32_t* m, int32_t* emitted,
                int32_t* n_emitted, int32_t* ckpt_index, gdn_stream_t stream) {
   if (!drafts || !preds || !m || !emitted || !n_emitted) return fail(GDN_EINVAL, "gdn_accept: NULL pointer");
   if (B <= 0 || K < 0) return fail(GDN_EINVAL, "gdn_accept: B=%d K=%d", B, K);
-  gdn::AcceptArgs p{drafts, preds, m, emitted, n_emitted, ckpt_index, B, K};
+  if ((long)B * (K + 1) >= (1L << 31)) return fail(GDN_EINVAL, "gdn_accept: B*(K+1) must stay below 2^31");
+  gdn::AcceptArgs p{drafts, preds, m, emitted, n_emitted, ckpt_index, nullptr, B, K, 1};
   return hip_status(gdn::launch_accept(p, (hipStream_t)stream), "gdn_accept");
+}
+
+int gdn_accept_paths(const int32_t* drafts, const int32_t* preds, int B, int P, int K, int32_t* m, int32_t* path,
+                     int32_t* emitted, int32_t* n_emitted, int32_t* ckpt_index, gdn_stream_t stream) {
+  if (!drafts || !preds || !m || !path || !emitted || !n_emitted)
+    return fail(GDN_EINVAL, "gdn_accept_paths: NULL pointer");
+  if (B <= 0 || P <= 0 || K < 0) return fail(GDN_EINVAL, "gdn_accept_paths: B=%d P=%d K=%d", B, P, K);
+  if ((long)B * P * (K + 1) >= (1L << 31))
+    return fail(GDN_EINVAL, "gdn_accept_paths: B*P*(K+1) must stay below 2^31");
+  gdn::AcceptArgs p{drafts, preds, m, emitted, n_emitted, ckpt_index, path, B, K, P};
+  return hip_status(gdn::launch_accept(p, (hipStream_t)stream), "gdn_accept_paths");
 }
 
 int gdn_state_copy(const gdn_desc* d, float* dst_state, void* dst_tail, const int32_t* dst_idx,

@@ -20,17 +20,18 @@ struct StepArgs {
   const float* A_log;
   const float* dt_bias;
   const float* norm_w;
-  const void* mixed;    // [B][T][C]
-  const void* z;        // [B][T][n_v*D]
-  const void* a;        // [B][T][n_v]
-  const void* b;        // [B][T][n_v]
+  const void* mixed;    // [B*P][T][C]
+  const void* z;        // [B*P][T][n_v*D]
+  const void* a;        // [B*P][T][n_v]
+  const void* b;        // [B*P][T][n_v]
   const int32_t* slot;  // [B] or null
   const void* tail_in;  // pool [*][3][C]
   const float* state_in;  // pool [*][n_v][D][D]
-  void* tail_out;       // decode: the pool; verify: [B*T][3][C]
-  float* state_out;     // decode: the pool; verify: [B*T][n_v][D][D]
-  void* out;            // [B][T][n_v*D]
+  void* tail_out;       // decode: the pool; verify: [B*P*T][3][C]
+  float* state_out;     // decode: the pool; verify: [B*P*T][n_v][D][D]
+  void* out;            // [B*P][T][n_v*D]
   int B, T, n_k, n_v, C;
+  int P;                // rows per sequence: 1, or the paths of a batch-of-paths verify
   int verify;
   float scale, l2_eps, rms_eps;
 };
@@ -88,13 +89,14 @@ struct CopyArgs {
 hipError_t launch_copy(const CopyArgs& p, hipStream_t st);
 
 struct AcceptArgs {
-  const int32_t* drafts;
-  const int32_t* preds;
+  const int32_t* drafts;  // [B][P][K]
+  const int32_t* preds;   // [B][P][K+1]
   int32_t* m;
   int32_t* emitted;
   int32_t* n_emitted;
   int32_t* ckpt_index;
-  int B, K;
+  int32_t* path;          // winning path per sequence, or null (P = 1)
+  int B, K, P;
 };
 hipError_t launch_accept(const AcceptArgs& p, hipStream_t st);
 

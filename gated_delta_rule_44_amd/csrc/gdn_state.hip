@@ -50,20 +50,31 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs p) {
   }
 }
 
-// the "mtp/generate.py" page's accept_prefix, one sequence per thread
+// the "mtp/generate.py" page's accept_prefix, one sequence per thread. With P paths per sequence
+// (its tree_verify_step) every path's prefix is measured and the first path with the longest one wins.
 __global__ void accept_kernel(AcceptArgs p) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= p.B) return;
-  const int K = p.K;
-  const int32_t* dr = p.drafts + (long)b * K;
-  const int32_t* pr = p.preds + (long)b * (K + 1);
-  int m = 0;
-  while (m < K && pr[m] == dr[m]) ++m;
+  const int K = p.K, P = p.P;
+  int m = -1, win = 0;
+  for (int q = 0; q < P; ++q) {
+    const int32_t* dr = p.drafts + ((long)b * P + q) * K;
+    const int32_t* pr = p.preds + ((long)b * P + q) * (K + 1);
+    int j = 0;
+    while (j < K && pr[j] == dr[j]) ++j;
+    if (j > m) {
+      m = j;
+      win = q;
+    }
+  }
+  const int32_t* dr = p.drafts + ((long)b * P + win) * K;
+  const int32_t* pr = p.preds + ((long)b * P + win) * (K + 1);
   int32_t* em = p.emitted + (long)b * (K + 1);
   for (int i = 0; i <= K; ++i) em[i] = i < m ? dr[i] : (i == m ? pr[m] : 0);
   p.m[b] = m;
   p.n_emitted[b] = m + 1;
-  if (p.ckpt_index) p.ckpt_index[b] = b * (K + 1) + m;
+  if (p.path) p.path[b] = win;
+  if (p.ckpt_index) p.ckpt_index[b] = (b * P + win) * (K + 1) + m;
 }
 
 }  // namespace

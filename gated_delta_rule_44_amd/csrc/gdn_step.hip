@@ -1,10 +1,13 @@
 // Single-token recurrence for decode and for verify-with-checkpoints (gfx950).
 //
-// Work item = (key head kh, sequence b): T tokens one after the other through the conv on the
+// Work item = (key head kh, row bp = b P + p): T tokens one after the other through the conv on the
 // channels of key head kh (its q and k channels and the v channels of its R value heads), the q/k L2
 // norm, the gates, one delta-rule step per value head, the gated RMSNorm, and the state/tail stores.
 // Decode is T = 1 writing back to the pool row; verify writes each token's state and tail to its
-// checkpoint row and leaves the pool untouched. Both run this one kernel, so checkpoint i is bitwise
+// checkpoint row and leaves the pool untouched. A batch-of-paths verify has P rows per sequence b,
+// every one starting from b's pool row (the "mtp/generate.py" page tiles the cache into one row per
+// candidate path); the P workgroups of one (sequence, key head) are n_k apart in the grid and read
+// the same state block, which the second and later ones find in the cache. Both run this one kernel, so checkpoint i is bitwise
 // what i+1 decode calls produce (the multistate verify of the "mtp/generate.py" page claims the same
 // bit-identity against its per-token kernel).
 //
@@ -74,7 +77,7 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
   const ActT* bin = (const ActT*)p.b;
   ActT* out = (ActT*)p.out;
 
-  auto slot_of = [&](int item) { const int b = item / n_k; return p.slot ? (long)p.slot[b] : (long)b; };
+  auto slot_of = [&](int item) { const int b = item / n_k / p.P; return p.slot ? (long)p.slot[b] : (long)b; };
   // this thread's block of its head's state: rows rg*RPT + i, columns 4 cq .. 4 cq + 3
   auto state_src = [&](int item) {
     const int kh = item % n_k;
@@ -99,7 +102,7 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
   f32x4 H[RPT];
   {
     const int item = blockIdx.x;
-    const int kh = item % n_k, b = item / n_k;
+    const int kh = item % n_k, bp = item / n_k;  // row: sequence bp / P, path bp % P
     const int h = kh * R + r;
     const long s = slot_of(item);
     const ActT* tail_in = (const ActT*)p.tail_in + s * TZ;
@@ -127,7 +130,7 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
     }
     const float A = -__expf(p.A_log[h]), dtb = p.dt_bias[h];
     auto load_tok = [&](TokIn& in, int t) {
-      const long row = (long)b * p.T + t;
+      const long row = (long)bp * p.T + t;
 #pragma unroll
       for (int j = 0; j < CPT; ++j) in.x[j] = to_f32(mixed[row * C + (gch[j] >= 0 ? gch[j] : 0)]);
       in.av = to_f32(ain[row * n_v + h]);
@@ -141,7 +144,7 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
     load_H(H, item);
 
     for (int t = 0; t < p.T; ++t) {
-      const long row = (long)b * p.T + t;
+      const long row = (long)bp * p.T + t;
       TokIn in = cur;
       if (t + 1 < p.T) load_tok(cur, t + 1);  // verify only
       // ---- conv + SiLU on the owned channels, tail shift
@@ -270,7 +273,7 @@ template <typename ActT, int D, int R>
 hipError_t launch_step_r(const StepArgs& p, hipStream_t st) {
   using S = StepShape<D, R>;
   timing_before(p.verify ? "step_verify" : "step_decode", st);
-  hipLaunchKernelGGL((step_kernel<ActT, D, R>), dim3(p.n_k * p.B), dim3(S::NTH), 0, st, p);
+  hipLaunchKernelGGL((step_kernel<ActT, D, R>), dim3(p.n_k * p.B * p.P), dim3(S::NTH), 0, st, p);
   timing_after(st);
   return hipGetLastError();
 }

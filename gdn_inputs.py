@@ -176,6 +176,25 @@ def verify_draws(rng: np.random.Generator, B: int, K: int, vocab: int = 1000):
     return drafts, preds, m
 
 
+def verify_path_draws(rng: np.random.Generator, B: int, P: int, K: int, vocab: int = 1000):
+    """P candidate paths per sequence: drafts [B,P,K], a prefix length m ~ U{0..K} per path, and
+    predictions [B,P,K+1] that agree with that path's drafts on exactly its first m positions."""
+    d, p, m = verify_draws(rng, B * P, K, vocab)
+    return d.reshape(B, P, K), p.reshape(B, P, K + 1), m.reshape(B, P)
+
+
+def path_inputs(rng: np.random.Generator, dims: LayerDims, B: int, P: int, T: int) -> LayerInputs:
+    """Projected inputs of P paths of T tokens per sequence ([B,P,T,...]); the paths of a sequence share
+    their first token (the root every candidate path continues from)."""
+    x = make_inputs(rng, dims, B * P, T)
+    out = []
+    for a in (x.mixed, x.z, x.a, x.b):
+        a = a.reshape((B, P) + a.shape[1:]).copy()
+        a[:, 1:, 0] = a[:, :1, 0]
+        out.append(a)
+    return LayerInputs(*out, np.full(B, T, np.int32))
+
+
 # ---- the workloads -----------------------------------------------------------------------------------
 
 TINY = LayerDims(n_k=2, n_v=4, d_k=32, d_v=32, act=ACT_F32)            # T=64, chunk 16

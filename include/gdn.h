@@ -99,7 +99,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc* desc, int B, int Lb);
  *   out   [B][Lb][n_v*d_v] gated-RMSNorm output; rows >= len[b] carry no meaning
  *   ws    device workspace of at least gdn_prefill_workspace_bytes(desc, B, Lb) bytes, 256-aligned;
  *         its contents on entry do not matter and are garbage on return
- * Limits: B <= 65535 and Lb * n_v * d_v < 2^31 (GDN_EINVAL otherwise).
+ * Limits: B <= 65535, Lb * n_v * d_v < 2^31 and B * ceil(Lb / 64) * n_k < 2^31 (GDN_EINVAL otherwise).
  * Must not alias: out with any input; state or conv_tail with anything else.
  */
 int gdn_prefill_chunk(const gdn_desc* desc, const gdn_weights* w, const void* mixed, const void* z,
@@ -146,6 +146,37 @@ int gdn_verify_with_checkpoints(const gdn_desc* desc, const gdn_weights* w, cons
  */
 int gdn_accept(const int32_t* drafts, const int32_t* preds, int B, int K, int32_t* m, int32_t* emitted,
                int32_t* n_emitted, int32_t* ckpt_index, gdn_stream_t stream);
+
+/*
+ * Batch-of-paths (tree) verify (mtp/generate.py page, tree_verify_step: P candidate paths per
+ * sequence, the cache tiled into one row per path, every row an ordinary linear sequence). Row
+ * bp = b*P + p runs path p of sequence b: T tokens one at a time from pool row slot[b] (or b), which
+ * every path of b shares and which is read, never written; the kernel is the one
+ * gdn_verify_with_checkpoints runs, so each row is bitwise that call on the row's tokens.
+ *   mixed [B][P][T][C_ch], z [B][P][T][n_v*d_v], a and b [B][P][T][n_v]
+ *   ckpt_state [B][P][T][n_v][d_k][d_v], ckpt_tail [B][P][T][Kc][C_ch]: record bp*T + t holds the
+ *              state and tail after token t of row bp
+ *   out [B][P][T][n_v*d_v]
+ * Limits: B * P <= 65535. Checkpoints must not alias the pools (GDN_EINVAL).
+ */
+int gdn_verify_paths(const gdn_desc* desc, const gdn_weights* w, const void* mixed, const void* z,
+                     const void* a, const void* b, int T, int P, const int32_t* slot,
+                     const void* conv_tail_pool, const float* state_pool, float* ckpt_state, void* ckpt_tail,
+                     void* out, int B, gdn_stream_t stream);
+
+/*
+ * Winner of a batch-of-paths verify (mtp/generate.py page, tree_verify_step): every path's accepted
+ * prefix as in gdn_accept; the winner is the first path with the longest one (ties go to the earlier
+ * path). Integer work, bit-exact.
+ *   drafts [B][P][K], preds [B][P][K+1] (device)
+ *   m [B], path [B]   the winner's prefix length and index
+ *   emitted [B][K+1]  the winner's drafts[:m], then its preds[m], then zeros; n_emitted [B] = m + 1
+ *   ckpt_index [B]    (b*P + path)*(K+1) + m: the checkpoint record of gdn_verify_paths (run with
+ *                     T = K+1) to commit with gdn_state_copy; may be NULL
+ * Limits: B * P * (K+1) < 2^31.
+ */
+int gdn_accept_paths(const int32_t* drafts, const int32_t* preds, int B, int P, int K, int32_t* m, int32_t* path,
+                     int32_t* emitted, int32_t* n_emitted, int32_t* ckpt_index, gdn_stream_t stream);
 
 /*
  * Copy n fixed-size state records {fp32 state [n_v][d_k][d_v], conv tail [Kc][C_ch]} — O(1) in

@@ -54,6 +54,9 @@ def test_null_and_size_errors():
     p = ctypes.c_void_p(256)
     assert lib.gdn_conv_chunk(ctypes.byref(d), p, p, p, ctypes.c_void_p(512), ctypes.c_void_p(768), 0, 4, None) == -1
     assert lib.gdn_accept(None, None, 4, 4, None, None, None, None, None) == -1
+    assert lib.gdn_accept_paths(p, p, 4, 2, 4, p, None, p, p, None, None) == -1
+    assert b"NULL" in lib.gdn_last_error()
+    assert lib.gdn_accept_paths(p, p, 4, 0, 4, p, p, p, p, None, None) == -1 and b"P=0" in lib.gdn_last_error()
     assert lib.gdn_state_copy(ctypes.byref(d), None, None, None, None, None, None, 1, None) == -1
     assert lib.gdn_state_copy(ctypes.byref(d), p, None, None, p, None, None, 1, None) == -1  # aliasing
     w = gdn._Weights(256, 512, 768, 1024)
@@ -61,6 +64,16 @@ def test_null_and_size_errors():
     rc = lib.gdn_prefill_chunk(ctypes.byref(d), ctypes.byref(w), p, p, p, p, p, p, ctypes.c_void_p(4096),
                                ctypes.c_void_p(8192), 1, 64, ctypes.c_void_p(1 << 20), 16, None)
     assert rc == -1 and b"workspace" in lib.gdn_last_error()
+    # verify over paths: checkpoints aliasing the pool, P out of range, B*P over the grid limit
+    assert lib.gdn_verify_paths(ctypes.byref(d), ctypes.byref(w), p, p, p, p, 5, 2, None, p, p, p,
+                                ctypes.c_void_p(4096), p, 1, None) == -1
+    assert b"alias" in lib.gdn_last_error()
+    q = ctypes.c_void_p(1 << 24)
+    assert lib.gdn_verify_paths(ctypes.byref(d), ctypes.byref(w), p, p, p, p, 5, 0, None, p, p, q, q, p, 1, None) == -1
+    assert b"P=0" in lib.gdn_last_error()
+    assert lib.gdn_verify_paths(ctypes.byref(d), ctypes.byref(w), p, p, p, p, 5, 4, None, p, p, q, q, p, 20000,
+                                None) == -1
+    assert b"65535" in lib.gdn_last_error()
 
 
 def test_sizes():

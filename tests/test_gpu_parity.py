@@ -8,8 +8,8 @@ import torch
 
 import oracle
 import gated_delta_rule_44_amd as gdn
-from gdn_inputs import (ACT_BF16, ACT_F32, NEXT, SMALL, TINY, LayerDims, chunk_lengths, make_layer, random_state,
-                        verify_draws)
+from gdn_inputs import (ACT_BF16, ACT_F32, NEXT, SMALL, TINY, LayerDims, chunk_lengths, make_layer, path_inputs,
+                        random_state, verify_draws, verify_path_draws)
 from tests.gpu_helpers import (act, assert_out_close, assert_state_close, desc_of, f32, host, i32, out_excess,
                                state_rel_err, weights)
 
@@ -250,6 +250,90 @@ def test_verify_checkpoints_and_commit():
         assert torch.equal(sp[s], ck_s[s, m_ref[s]])
         assert torch.equal(tp[s], ck_t[s, m_ref[s]])
     assert_state_close(host(sp), ref["ckpt_H"][np.arange(B), m_ref])
+
+
+def test_verify_paths_and_commit():
+    """Batch-of-paths verify: 6 sequences x 4 paths x (1+4) tokens from permuted pool rows, against the
+    oracle; every row bitwise equal to a single-path verify of its tokens; the winner by the first
+    longest accepted prefix (bit-exact) committed through the state copy."""
+    dims, B, P, K = NEXT, 6, 4, 4
+    T = K + 1
+    _say(f"verify paths B={B} P={P} K={K}")
+    w, _, rng = make_layer(13, dims, 1, 1)
+    H0, T0 = _saved_states(dims, w, rng, B)
+    x = path_inputs(rng, dims, B, P, T)
+    drafts, preds, _ = verify_path_draws(rng, B, P, K)
+    preds[1, 3, :K] = drafts[1, 3]          # a full match on the last path, which the others miss
+    preds[1, :3, 0] = drafts[1, :3, 0] + 1
+    preds[2, 1:3, :2] = drafts[2, 1:3, :2]  # a tie between paths 1 and 2 ...
+    preds[2, 1:3, 2] = drafts[2, 1:3, 2] + 1
+    preds[2, 0, 0], preds[2, 3, 0] = drafts[2, 0, 0] + 1, drafts[2, 3, 0] + 1  # ... that no other path beats
+    d = desc_of(dims)
+    W = weights(w, dims)
+    npool = B + 2
+    slots = rng.permutation(npool)[:B].astype(np.int32)
+    poolH = np.zeros(dims.state_shape(npool), np.float32)
+    poolT = np.zeros(dims.tail_shape(npool), np.float32)
+    poolH[slots], poolT[slots] = H0, T0
+    sp, tp = f32(poolH), act(poolT, dims)
+    mx, zz, aa, bb = act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims)
+    ck_s, ck_t, out = gdn.verify_paths(d, W, mx, zz, aa, bb, i32(slots), tp, sp, check_slots=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sp), poolH), "verify modified the pool"
+    ref = oracle.verify_paths(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, T0, H0)
+    assert_out_close(host(out), ref["out"], dims, "verify_paths out")
+    cks = host(ck_s)
+    for p in range(P):
+        for i in range(T):
+            assert_state_close(cks[:, p, i], ref["ckpt_H"][:, p, i], f"path {p} checkpoint {i}")
+    np.testing.assert_array_equal(host(ck_t), ref["ckpt_tail"].astype(np.float32))
+    for p in range(1, P):  # the shared first token leaves every path in the same state
+        assert torch.equal(ck_s[:, p, 0], ck_s[:, 0, 0]) and torch.equal(out[:, p, 0], out[:, 0, 0])
+    # each row bitwise a single-path verify of its tokens
+    for p in range(P):
+        s1, t1, o1 = gdn.verify_with_checkpoints(d, W, mx[:, p].contiguous(), zz[:, p].contiguous(),
+                                                 aa[:, p].contiguous(), bb[:, p].contiguous(), i32(slots), tp, sp)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, ck_s[:, p]) and torch.equal(t1, ck_t[:, p]) and torch.equal(o1, out[:, p]), f"path {p}"
+    # winner and commit
+    m, path, em, ne, ci = gdn.accept_paths(i32(drafts), i32(preds))
+    torch.cuda.synchronize()
+    m_ref, path_ref, em_ref, ne_ref = oracle.accept_paths(drafts, preds)
+    assert path_ref[1] == 3 and m_ref[1] == K and path_ref[2] == 1 and m_ref[2] == 2
+    np.testing.assert_array_equal(m.cpu().numpy(), m_ref)
+    np.testing.assert_array_equal(path.cpu().numpy(), path_ref)
+    np.testing.assert_array_equal(em.cpu().numpy(), em_ref)
+    np.testing.assert_array_equal(ne.cpu().numpy(), ne_ref)
+    np.testing.assert_array_equal(ci.cpu().numpy(), (np.arange(B) * P + path_ref) * T + m_ref)
+    gdn.state_copy(d, sp, tp, i32(slots), ck_s, ck_t, ci, B)
+    torch.cuda.synchronize()
+    for s in range(B):
+        assert torch.equal(sp[int(slots[s])], ck_s[s, path_ref[s], m_ref[s]])
+        assert torch.equal(tp[int(slots[s])], ck_t[s, path_ref[s], m_ref[s]])
+
+
+def test_accept_paths_exhaustive():
+    """Every pair of paths over a vocabulary of 2 with K = 2, and a random batch of 4 paths with K = 4."""
+    import itertools
+    K, P = 2, 2
+    dr1 = np.array(list(itertools.product(range(2), repeat=K)), np.int32)
+    pr1 = np.array(list(itertools.product(range(2), repeat=K + 1)), np.int32)
+    one = [(a, b) for a in dr1 for b in pr1]
+    pairs = list(itertools.product(range(len(one)), repeat=P))
+    D = np.array([[one[i][0] for i in pr] for pr in pairs], np.int32)
+    Q = np.array([[one[i][1] for i in pr] for pr in pairs], np.int32)
+    rng = np.random.default_rng(31)
+    D4, Q4, _ = verify_path_draws(rng, 500, 4, 4, vocab=3)
+    for dr, pr in ((D, Q), (D4, Q4)):
+        m, path, em, ne, ci = gdn.accept_paths(i32(dr), i32(pr))
+        torch.cuda.synchronize()
+        m_ref, path_ref, em_ref, ne_ref = oracle.accept_paths(dr, pr)
+        np.testing.assert_array_equal(m.cpu().numpy(), m_ref)
+        np.testing.assert_array_equal(path.cpu().numpy(), path_ref)
+        np.testing.assert_array_equal(em.cpu().numpy(), em_ref)
+        np.testing.assert_array_equal(ne.cpu().numpy(), ne_ref)
+        Bn, Pn, Kn = dr.shape
+        np.testing.assert_array_equal(ci.cpu().numpy(), (np.arange(Bn) * Pn + path_ref) * (Kn + 1) + m_ref)
 
 
 def test_accept_exhaustive():
