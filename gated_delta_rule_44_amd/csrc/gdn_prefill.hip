@@ -36,7 +36,6 @@
 // must stay >= 2^-14: operands of unit scale are carried multiplied by 2^8 (exact), and the scales are
 // chosen so that every product lands in a consistent domain: the state pass keeps H as 2^16 H, U as
 // 2^8 U and O^T as 2^16 O^T, with 2^8 Q~, 2^8 P~, 2^8 K~, 2^8 U' and unscaled -W in the record.
-#include <atomic>
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -226,68 +225,45 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   float* sGam = (float*)(smem + OFF_G);
   float* sBet = (float*)(smem + OFF_B);
 
-  const int lane0 = threadIdx.x & 63;
-  const int w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: addresses built on it stay scalar
-  const int Lb = p.Lb, C = p.C, n_k = p.n_k, n_chunks = p.n_chunks;
+  const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  const int t0 = c * C64;
+  const int len = p.len[b];
+  if (t0 >= len) return;  // all padding: the state pass stops before this chunk
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so addresses built on it stay scalar
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int Lb = p.Lb, C = p.C, n_k = p.n_k;
+  const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
+  const ActT* tail = (const ActT*)p.tail + (long)b * 3 * C;
   const ActT* cw = (const ActT*)p.conv_w;
-  const int n_units = n_chunks * n_k * p.B;  // unit u: chunk u % n_chunks of key head (u / n_chunks) % n_k
 
-  // ---- 1. raw inputs of a unit, all loads issued before any is used: gate inputs (lane = token),
+  // ---- 1. every global load of this stage first, then the arithmetic: gate inputs (lane = token),
   // conv inputs and taps of q, k and the R value heads (wave w: rows TPW w - 3 .. TPW w + TPW - 1, lane:
   // channels CPL lane + j, two adjacent channels per load). Addresses are clamped into range and the
-  // values masked when widened. Each workgroup walks units u = blockIdx.x, + gridDim.x, ...; the
-  // next unit's loads go out as soon as the current unit's convolutions have consumed the registers,
-  // so that they are in flight while the rest of the current unit computes.
+  // values masked when widened, so that all loads are in flight before the first wait.
   constexpr int NCV = 2 + R;  // convolutions: q, k, then the value heads
   typedef typename std::conditional<CPL == 2, typename Pair<ActT>::type, ActT>::type XRaw;
   typedef typename Raw4<ActT>::type WRaw;
-  XRaw xr[NCV][TPW + 3];
-  WRaw wr[NCV][CPL];
-  ActT a_raw, b_raw;
-  auto load_raw = [&](int u) __attribute__((always_inline)) {
-    const int c = u % n_chunks, kh = (u / n_chunks) % n_k, b = u / (n_chunks * n_k);
-    const int t0 = c * C64;
-    const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
-    const ActT* tail = (const ActT*)p.tail + (long)b * 3 * C;
-    const int tg = t0 + lane0;
-    const long gi = ((long)b * Lb + (tg < Lb ? tg : Lb - 1)) * p.n_v + kh * R + (w0 < R ? w0 : 0);
-    a_raw = ((const ActT*)p.a)[gi];
-    b_raw = ((const ActT*)p.b)[gi];
-#pragma unroll
-    for (int j = 0; j < NCV; ++j) {
-      const int base = j == 0 ? kh * D : j == 1 ? (n_k + kh) * D : (2 * n_k + kh * R + j - 2) * D;
-      const int gc = base + (CPL == 2 ? 2 * lane0 : (lane0 < D ? lane0 : 0));
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) wr[j][i] = Raw4<ActT>::load(cw + (gc + i) * 4);
-#pragma unroll
-      for (int i = 0; i < TPW + 3; ++i) {
-        const int t = t0 + TPW * w0 - 3 + i;
-        const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
-        if constexpr (CPL == 2) xr[j][i] = Pair<ActT>::load(src + gc);
-        else xr[j][i] = src[gc];
-      }
-    }
-  };
-  if ((int)blockIdx.x < n_units) load_raw(blockIdx.x);
-
-  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-  // the lane-dependent LDS offsets of the unit's stages are recomputed in every pass of the loop (an
-  // opaque copy of the thread index): hoisted out of it they would hold registers all the time
-  int tid_u = threadIdx.x;
-  asm volatile("" : "+v"(tid_u));
-  const int tid = tid_u, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g16 = lane >> 4, r16 = lane & 15;
-  const int c = u % n_chunks, kh = (u / n_chunks) % n_k, b = u / (n_chunks * n_k);
-  const int t0 = c * C64;
-  const int len = p.len[b];
-  const int un = u + gridDim.x;  // this workgroup's next unit
-  if (t0 >= len) {  // all padding: the state pass stops before this chunk
-    if (un < n_units) load_raw(un);
-    continue;
-  }
   const int hg = kh * R + (w < R ? w : 0);
   const int tg = t0 + lane;
+  const long gi = ((long)b * Lb + (tg < len ? tg : len - 1)) * p.n_v + hg;  // len >= 1 here
+  const ActT a_raw = ((const ActT*)p.a)[gi], b_raw = ((const ActT*)p.b)[gi];
+  XRaw xr[NCV][TPW + 3];
+  WRaw wr[NCV][CPL];
+#pragma unroll
+  for (int j = 0; j < NCV; ++j) {
+    const int base = j == 0 ? kh * D : j == 1 ? (n_k + kh) * D : (2 * n_k + kh * R + j - 2) * D;
+    const int gc = base + (CPL == 2 ? 2 * lane : (lane < D ? lane : 0));
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) wr[j][i] = Raw4<ActT>::load(cw + (gc + i) * 4);
+#pragma unroll
+    for (int i = 0; i < TPW + 3; ++i) {
+      const int t = t0 + TPW * w - 3 + i;
+      const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
+      if constexpr (CPL == 2) xr[j][i] = Pair<ActT>::load(src + gc);
+      else xr[j][i] = src[gc];
+    }
+  }
 
   // ---- 2. gates of the R value heads: wave r, lane = token; inclusive scan of g over the chunk -----
   if (w < R) {
@@ -347,7 +323,6 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   conv(1, kn);
 #pragma unroll
   for (int r = 0; r < R; ++r) conv(2 + r, vv[r]);
-  if (un < n_units) load_raw(un);
   l2norm(qn);
   l2norm(kn);
   // token-major 2^8 q, 2^8 k (hi/lo) for the Gram products; channel-major k in fp32
@@ -635,7 +610,6 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gC);
     lds_barrier();
   }
-  }  // units
 }
 
 // -------------------------------------------------------------------------------------------------
@@ -1047,29 +1021,11 @@ long rec_bytes(int D, bool split_all) {
   return D == 32 ? Rec<32, false>::kBytes : D == 64 ? Rec<64, false>::kBytes : Rec<128, false>::kBytes;
 }
 
-// compute units of the stream's device (chunk_prep runs one persistent workgroup per CU: its LDS
-// leaves room for no second one)
-int cu_count(hipStream_t st) {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 template <typename ActT, int D, int R, bool SPLIT, int NT>
 hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   constexpr int NSPLIT = D / (16 * NT);
   timing_before("chunk_prep", st);
-  const long units = (long)p.n_chunks * p.n_k * p.B;  // < 2^31, checked by the caller
-  const int cus = cu_count(st);
-  if (cus <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3((unsigned)(units < cus ? units : cus)), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
   timing_after(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
