@@ -388,3 +388,40 @@ def test_verify_checkpoints_equal_repeated_decode():
     # and the whole T-token run equals one multi-token call
     full = oracle.layer_forward(od, w, x.mixed, x.z, x.a, x.b, None, t0, H0)
     np.testing.assert_allclose(ver["ckpt_H"][:, -1], full["H"], rtol=1e-12, atol=1e-13)
+
+
+# ---- the prefix-state cache's bookkeeping (qev_fast/statecache.py page), worked by hand ----------
+
+def test_prefix_model_bounds_hand_worked():
+    from oracle.prefix_cache import PrefixCacheModel
+    m = PrefixCacheModel(8, stride=2048, tail=16, align=64)
+    # stride multiples below p = 4992, p - tail = 4984 rounded down to 4928, and p
+    assert m._bounds(0, 5000) == [2048, 4096, 4928, 4992]
+    assert m._bounds(4096, 5000) == [4928, 4992]
+    # p - tail rounds down to 0, not past the start: only p
+    assert m._bounds(0, 64) == [64]
+    # no stride, no tail: p alone, cut into chunks of at most 2048
+    assert PrefixCacheModel(8, stride=0, tail=0, max_chunk=2048)._bounds(0, 5000) == [2048, 4096, 4992]
+
+
+def test_prefix_model_lookup_and_lru_hand_worked():
+    from oracle.prefix_cache import PrefixCacheModel
+    m = PrefixCacheModel(2, stride=2048, tail=16, align=64, min_prefix=256)
+    A = np.arange(1000)
+    B = np.concatenate([A[:500], -np.arange(1, 501)])
+    D = np.arange(5000, 6000)
+    # A: cold, one checkpoint at p = 960 (p - tail = 984 also rounds down to 960)
+    assert m.row(A, 1000) == (-1, 0, 960, [960], [0])
+    # B shares 500 tokens with A: checkpoint 0 (at 960) is past that, so cold again
+    assert m.row(B, 1000) == (-1, 0, 960, [960], [1])
+    # A again: a hit on checkpoint 0, which becomes the most recently used
+    assert m.row(A, 1000) == (0, 960, 960, [], [])
+    # D: cold; three checkpoints for two slots, so B's (the least recently used) goes
+    assert m.row(D, 1000) == (-1, 0, 960, [960], [2])
+    assert m.alive() == [0, 2]
+    # B once more: its checkpoint is gone
+    assert m.row(B, 1000)[:2] == (-1, 0)
+    # a row below min_prefix takes the plain path
+    assert m.row(A[:200], 200) == (-1, 0, 192, [], [])
+    assert m.stats == dict(rows=5, hits=1, partial=0, cold=4, plain=1, tokens_reused=960,
+                           tokens_computed=4 * 1000 + 40 + 200, ckpts_made=4, evicted=2)
