@@ -1,6 +1,6 @@
 """Benchmark of the Gated DeltaNet layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|verify_paths|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|verify_paths|prefix_cache|copy]
 
 Headline (`value`): prefill tokens/s of one layer on one sequence of 4096 tokens, 16 key / 16 value
 heads, d_k = d_v = 128, bf16 activations, fp32 state, continued from a saved state (one step = one
@@ -324,6 +324,43 @@ def bench_verify_paths(torch, gdn, args):
             "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()}}
 
 
+def bench_prefix_cache(torch, gdn, args):
+    """Rows of 8192 tokens that share a 6144-token prefix (a system prompt) and differ in their last 2048,
+    through the prefix-state cache (restore, 2048-token chunks, snapshots) and through the plain path
+    (every row from zero). Throughput counts every row token, computed or reused."""
+    from gdn_inputs import NEXT, make_layer
+    from tests.gpu_helpers import act, desc_of, weights
+    dims = NEXT
+    rows_n, n, shared, vocab = 8, 8192, 6144, 512
+    d = desc_of(dims)
+    w, table, rng = make_layer(302, dims, 1, vocab)
+    W = weights(w, dims)
+    tab = [act(f, dims)[0] for f in (table.mixed, table.z, table.a, table.b)]  # per token id
+    stem = rng.integers(0, vocab, size=shared)
+    rows = [np.concatenate([stem, rng.integers(0, vocab, size=n - shared)]).astype(np.int32) for _ in range(rows_n)]
+    inputs = [[t[torch.as_tensor(r, device="cuda").long()][None].contiguous() for t in tab] for r in rows]
+    state = torch.empty(1, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda")
+    tail = torch.empty(1, 3, dims.conv_dim, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(1, n, dims.value_dim, dtype=torch.bfloat16, device="cuda")
+
+    def run(cached):
+        cache = gdn.PrefixStateCache(d, slots=16, min_prefix=256 if cached else n + 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for r, x in zip(rows, inputs):
+            cache.run_row(W, r, *x, state, tail, out, shared)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3, cache.stats()
+
+    run(True), run(False)  # warm-up
+    ms_c, st = min((run(True) for _ in range(max(1, args.steps // 10))), key=lambda r: r[0])
+    ms_p, _ = min((run(False) for _ in range(max(1, args.steps // 10))), key=lambda r: r[0])
+    tok = rows_n * n
+    return {"workload": "8 rows x 8192 tokens sharing a 6144-token prefix, 16/32 heads, d=128, one layer",
+            "ms_cached": ms_c, "ms_plain": ms_p, "tokens_per_s_cached": tok / (ms_c / 1e3),
+            "tokens_per_s_plain": tok / (ms_p / 1e3), "speedup": ms_p / ms_c, "stats": st}
+
+
 def bench_copy(torch, gdn, args):
     from gdn_inputs import NEXT
     from tests.gpu_helpers import desc_of
@@ -408,6 +445,8 @@ def main():
         line["verify"] = bench_verify(torch, gdn, args)
     if only in ("all", "verify_paths"):
         line["verify_paths"] = bench_verify_paths(torch, gdn, args)
+    if only in ("all", "prefix_cache"):
+        line["prefix_cache"] = bench_prefix_cache(torch, gdn, args)
     if only in ("all", "copy"):
         line["copy"] = bench_copy(torch, gdn, args)
     if not args.no_cpu and only in ("all", "prefill"):

@@ -14,6 +14,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,7 +52,8 @@ _lib = None
 EXPORTS = ("gdn_last_error", "gdn_version", "gdn_conv_chunk", "gdn_prefill_workspace_bytes", "gdn_prefill_chunk",
            "gdn_decode_step", "gdn_verify_with_checkpoints", "gdn_verify_paths", "gdn_accept", "gdn_accept_paths",
            "gdn_state_copy",
-           "gdn_state_record_bytes", "gdn_timing_begin", "gdn_timing_end")
+           "gdn_state_record_bytes", "gdn_state_zero", "gdn_pcache_create", "gdn_pcache_destroy", "gdn_pcache_row",
+           "gdn_pcache_stats", "gdn_pcache_alive", "gdn_timing_begin", "gdn_timing_end")
 
 
 def load_library(path: str = LIB_PATH):
@@ -79,10 +81,20 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_state_copy.argtypes = [D, P, P, P, P, P, P, I, P]
     lib.gdn_state_record_bytes.argtypes = [D]
     lib.gdn_state_record_bytes.restype = Z
+    lib.gdn_state_zero.argtypes = [D, P, P, P, I, P]
+    L = ctypes.c_int64
+    lib.gdn_pcache_create.argtypes = [I, I, I, I, I, I, ctypes.POINTER(P)]
+    lib.gdn_pcache_destroy.argtypes = [P]
+    lib.gdn_pcache_destroy.restype = None
+    lib.gdn_pcache_row.argtypes = [P, ctypes.POINTER(ctypes.c_int32), I, I, I, ctypes.POINTER(ctypes.c_int32),
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(L)]
+    lib.gdn_pcache_stats.argtypes = [P, ctypes.POINTER(L)]
+    lib.gdn_pcache_alive.argtypes = [P, I, ctypes.POINTER(L)]
     lib.gdn_timing_begin.argtypes = [I]
     lib.gdn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), I]
     for name in ("gdn_conv_chunk", "gdn_prefill_chunk", "gdn_decode_step", "gdn_verify_with_checkpoints",
-                 "gdn_verify_paths", "gdn_accept", "gdn_accept_paths", "gdn_state_copy"):
+                 "gdn_verify_paths", "gdn_accept", "gdn_accept_paths", "gdn_state_copy", "gdn_state_zero",
+                 "gdn_pcache_create", "gdn_pcache_row", "gdn_pcache_stats", "gdn_pcache_alive"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -384,6 +396,100 @@ def state_copy(desc: GdnDesc, dst_state, dst_tail, dst_idx, src_state, src_tail,
     di = _opt(dst_idx, "dst_idx", (n,), torch.int32, dev)
     si = _opt(src_idx, "src_idx", (n,), torch.int32, dev)
     _check("gdn_state_copy", lib.gdn_state_copy(ctypes.byref(desc.c()), ds, dt, di, ss, st, si, n, _stream()))
+
+
+def state_zero(desc: GdnDesc, state, tail, idx=None, n: int = None):
+    """Zero n records (idx[i], or i) of a state pool and / or a tail pool (either may be None)."""
+    lib = load_library()
+    dev = (state if state is not None else tail).device
+    if n is None:
+        n = (state if state is not None else tail).shape[0] if idx is None else idx.numel()
+    sp = _opt(state, "state", None, torch.float32, dev)
+    tp = _opt(tail, "tail", None, desc.act, dev)
+    _check("gdn_state_zero", lib.gdn_state_zero(ctypes.byref(desc.c()), sp, tp, _opt(idx, "idx", (n,), torch.int32, dev),
+                                                n, _stream()))
+
+
+PCACHE_STATS = ("rows", "hits", "partial", "cold", "plain", "tokens_reused", "tokens_computed", "ckpts_made",
+                "evicted")
+
+
+class PrefixStateCache:
+    """The prefix-state cache of one GDN layer: bookkeeping in libgdn (gdn_pcache_*), the checkpoint pool
+    on the GPU, and the row executor (restore or zero, chunked prefill, snapshots), all on the current
+    stream in the plan's order."""
+
+    def __init__(self, desc: GdnDesc, slots: int, stride: int = 2048, tail: int = 16, align: int = 64,
+                 max_chunk: int = 2048, min_prefix: int = 256, device="cuda"):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check("gdn_pcache_create", lib.gdn_pcache_create(slots, stride, tail, align, max_chunk, min_prefix,
+                                                          ctypes.byref(h)))
+        self._h, self._lib = h, lib
+        self.desc, self.max_chunk = desc, max_chunk
+        self.state_pool = torch.empty(max(slots, 1), desc.n_v, desc.d_k, desc.d_v, dtype=torch.float32, device=device)
+        self.tail_pool = torch.empty(max(slots, 1), desc.kc, desc.conv_dim, dtype=desc.act, device=device)
+        self.ws = prefill_workspace(desc, 1, max_chunk, device)
+        # 0, 1, 2, ...: one-element views of it serve as chunk lengths and slot indices without a host copy
+        self._ramp = torch.arange(max(max_chunk, slots) + 1, dtype=torch.int32, device=device)
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            self._lib.gdn_pcache_destroy(self._h)
+            self._h = None
+
+    def plan(self, ids, p_state: int) -> dict:
+        """Book one row (ids: its tokens) and return its plan."""
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        n = len(ids)
+        cap = 16
+        while True:
+            info = (ctypes.c_int32 * 4)()
+            bounds = (ctypes.c_int32 * cap)()
+            snap = (ctypes.c_int32 * cap)()
+            ck = (ctypes.c_int64 * (cap + 1))()
+            nb = self._lib.gdn_pcache_row(self._h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n, int(p_state),
+                                          cap, info, bounds, snap, ck)
+            if nb >= 0:
+                break
+            if cap > n + 16:
+                _check("gdn_pcache_row", nb)
+            cap *= 4
+        return {"restore_slot": info[0], "c0": info[1], "p": info[2], "bounds": list(bounds[:nb]),
+                "snap_slot": list(snap[:nb]), "restored": ck[0], "new": list(ck[1:nb + 1]), "n": n}
+
+    def run_row(self, w: GdnWeights, ids, mixed, z, a, b, state, tail, out, p_state: int) -> dict:
+        """One row through the layer: mixed [1,n,C_ch], z [1,n,n_v*d_v], a and b [1,n,n_v]; state [1,n_v,d_k,d_v]
+        and tail [1,Kc,C_ch] end as the row's final state; out [1,n,n_v*d_v] is written for tokens [c0, n)."""
+        d = self.desc
+        plan = self.plan(ids, p_state)
+        one = lambda v: self._ramp[v:v + 1]
+        if plan["restore_slot"] >= 0:
+            state_copy(d, state, tail, None, self.state_pool, self.tail_pool, one(plan["restore_slot"]), 1)
+        else:
+            state_zero(d, state, tail)
+        ends = plan["bounds"] + [plan["n"]]
+        s = plan["c0"]
+        for i, e in enumerate(ends):
+            while s < e:
+                t = min(e, s + self.max_chunk)
+                prefill_chunk(d, w, mixed[:, s:t], z[:, s:t], a[:, s:t], b[:, s:t], one(t - s), tail, state,
+                              out[:, s:t], self.ws)
+                s = t
+            if i < len(plan["bounds"]) and plan["snap_slot"][i] >= 0:
+                state_copy(d, self.state_pool, self.tail_pool, one(plan["snap_slot"][i]), state, tail, None, 1)
+        return plan
+
+    def stats(self) -> dict:
+        v = (ctypes.c_int64 * len(PCACHE_STATS))()
+        _check("gdn_pcache_stats", self._lib.gdn_pcache_stats(self._h, v))
+        return dict(zip(PCACHE_STATS, list(v)))
+
+    def alive(self) -> list:
+        n = self._lib.gdn_pcache_alive(self._h, 0, None)
+        v = (ctypes.c_int64 * max(n, 1))()
+        self._lib.gdn_pcache_alive(self._h, n, v)
+        return list(v[:n])
 
 
 def state_record_bytes(desc: GdnDesc) -> int:

@@ -287,4 +287,19 @@ int gdn_state_copy(const gdn_desc* d, float* dst_state, void* dst_tail, const in
   return hip_status(gdn::launch_copy(p, (hipStream_t)stream), "gdn_state_copy");
 }
 
+int gdn_state_zero(const gdn_desc* d, float* state, void* tail, const int32_t* idx, int n, gdn_stream_t stream) {
+  if (int rc = check_desc(d)) return rc;
+  if (n <= 0 || n > 65535) return fail(GDN_EINVAL, "gdn_state_zero: n=%d (1..65535)", n);
+  if (!state && !tail) return fail(GDN_EINVAL, "gdn_state_zero: nothing to zero");
+  if (!aligned16(state) || !aligned16(tail)) return fail(GDN_EINVAL, "gdn_state_zero: buffers must be 16-byte aligned");
+  const long act = d->act_dtype == GDN_BF16 ? 2 : 4;
+  gdn::CopyArgs p{};
+  p.dst_state = state; p.dst_tail = tail; p.dst_idx = idx;
+  p.state_floats = (long)d->n_v * d->d_k * d->d_v;
+  p.tail_bytes = (long)(d->conv_k - 1) * conv_channels(d) * act;
+  p.n = n;
+  if (p.tail_bytes % 16) return fail(GDN_EUNSUPPORTED, "gdn_state_zero: tail record of %ld bytes", p.tail_bytes);
+  return hip_status(gdn::launch_zero(p, (hipStream_t)stream), "gdn_state_zero");
+}
+
 }  // extern "C"

@@ -87,6 +87,7 @@ struct CopyArgs {
   int n;
 };
 hipError_t launch_copy(const CopyArgs& p, hipStream_t st);
+hipError_t launch_zero(const CopyArgs& p, hipStream_t st);  // dst pointers and dst_idx only
 
 struct AcceptArgs {
   const int32_t* drafts;  // [B][P][K]

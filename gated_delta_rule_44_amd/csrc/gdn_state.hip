@@ -50,6 +50,32 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs p) {
   }
 }
 
+// zeros into record dst_idx[i] (or i): the same tiling as copy_kernel, src pointers unused
+__global__ __launch_bounds__(kThreads) void zero_kernel(CopyArgs p) {
+  const int i = blockIdx.y;
+  const long di = p.dst_idx ? (long)p.dst_idx[i] : (long)i;
+  const long nstate = p.dst_state ? p.state_floats / 4 : 0;
+  const long ntail = p.dst_tail ? p.tail_bytes / 16 : 0;
+  const long nsb = (nstate + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  u32x4* d;
+  long n, base;
+  if ((long)blockIdx.x < nsb) {
+    d = (u32x4*)(p.dst_state + di * p.state_floats);
+    n = nstate;
+    base = (long)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+  } else {
+    d = (u32x4*)((char*)p.dst_tail + di * p.tail_bytes);
+    n = ntail;
+    base = ((long)blockIdx.x - nsb) * kThreads * kUnroll + threadIdx.x;
+  }
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const long k = base + (long)u * kThreads;
+    if (k < n) d[k] = z;
+  }
+}
+
 // the "mtp/generate.py" page's accept_prefix, one sequence per thread. With P paths per sequence
 // (its tree_verify_step) every path's prefix is measured and the first path with the longest one wins.
 __global__ void accept_kernel(AcceptArgs p) {
@@ -87,6 +113,18 @@ hipError_t launch_copy(const CopyArgs& p, hipStream_t st) {
   if (blocks <= 0 || p.n <= 0) return hipSuccess;
   timing_before("copy", st);
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks, p.n), dim3(kThreads), 0, st, p);
+  timing_after(st);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(const CopyArgs& p, hipStream_t st) {
+  const long per_block = (long)kThreads * kUnroll;
+  const long nstate = p.dst_state ? p.state_floats / 4 : 0;
+  const long ntail = p.dst_tail ? p.tail_bytes / 16 : 0;
+  const long blocks = (nstate + per_block - 1) / per_block + (ntail + per_block - 1) / per_block;
+  if (blocks <= 0 || p.n <= 0) return hipSuccess;
+  timing_before("zero", st);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks, p.n), dim3(kThreads), 0, st, p);
   timing_after(st);
   return hipGetLastError();
 }

@@ -196,6 +196,56 @@ int gdn_state_copy(const gdn_desc* desc, float* dst_state, void* dst_tail, const
 size_t gdn_state_record_bytes(const gdn_desc* desc);
 
 /*
+ * Prefix-state cache ("qev_fast/statecache.py" page, StateCache): host bookkeeping only, no HIP call.
+ * A checkpoint is the fp32 state and conv tail of one sequence after the first `pos` tokens of an
+ * earlier row, held in one slot of a caller-owned record pool (slots 0 .. slots-1; one slot may hold a
+ * record per GDN layer). For each new row the cache finds the deepest checkpoint whose tokens the row
+ * shares, and books checkpoints at the chunk ends the page places: multiples of `stride`, p - tail and
+ * p (p = the row's checkpointable prefix, min(p_state, n) rounded down to `align`), no chunk longer than
+ * `max_chunk`. With more checkpoints than slots, the least recently used ones go (starting a row from a
+ * checkpoint counts as a use). Rows with p < min_prefix take the plain path: no lookup, no checkpoints.
+ * Only the recurrent state is cached; the attention K / V of the page's cache belongs to other layers.
+ *
+ * gdn_pcache_row plans and books one row (ids: its n tokens, host memory). It writes
+ *   info[4]       = {restore slot or -1 (start from zero), c0 = tokens the restore covers, p, n_bounds}
+ *   bounds[i]     chunk ends in (c0, p], ascending: run [c0, bounds[0]), [bounds[0], bounds[1]), ...,
+ *                 then [p, n); after the chunk ending at bounds[i], copy the state into snap_slot[i]
+ *                 (-1: that checkpoint was evicted at once, skip the copy)
+ *   ckpt[1 + cap] (may be NULL) the restored checkpoint's number, then the new checkpoints' numbers
+ *                 (numbers count checkpoints in the order they are made; -1 for none / evicted)
+ * and returns n_bounds, or GDN_EINVAL (nothing booked) for bad arguments or n_bounds > cap. The restore
+ * must be issued before the snapshots: the restored slot may be handed to a new checkpoint of the row.
+ * The plan holds for GPU work issued in order on one stream. Not thread-safe.
+ * gdn_pcache_stats copies the GDN_PCACHE_NSTATS counters; gdn_pcache_alive writes the numbers of the
+ * live checkpoints (ascending, at most cap) and returns how many there are.
+ */
+typedef struct gdn_pcache gdn_pcache;
+enum {
+  GDN_PCACHE_ROWS = 0,          /* rows that looked the cache up */
+  GDN_PCACHE_HITS,              /* ... that found a checkpoint at p */
+  GDN_PCACHE_PARTIAL,           /* ... that found one before p */
+  GDN_PCACHE_COLD,              /* ... that found none */
+  GDN_PCACHE_PLAIN,             /* rows too short to checkpoint */
+  GDN_PCACHE_TOKENS_REUSED,
+  GDN_PCACHE_TOKENS_COMPUTED,
+  GDN_PCACHE_CKPTS_MADE,
+  GDN_PCACHE_EVICTED,
+  GDN_PCACHE_NSTATS
+};
+int gdn_pcache_create(int slots, int stride, int tail, int align, int max_chunk, int min_prefix, gdn_pcache** out);
+void gdn_pcache_destroy(gdn_pcache* cache);
+int gdn_pcache_row(gdn_pcache* cache, const int32_t* ids, int n, int p_state, int cap, int32_t* info, int32_t* bounds,
+                   int32_t* snap_slot, int64_t* ckpt);
+int gdn_pcache_stats(const gdn_pcache* cache, int64_t* stats);
+int gdn_pcache_alive(const gdn_pcache* cache, int cap, int64_t* nums);
+
+/*
+ * Zero n state records {fp32 state [n_v][d_k][d_v], conv tail [Kc][C_ch]}: record idx[i] (or i when idx
+ * is NULL) of each pool. Either pool may be NULL. The start of a row that no checkpoint covers.
+ */
+int gdn_state_zero(const gdn_desc* desc, float* state, void* tail, const int32_t* idx, int n, gdn_stream_t stream);
+
+/*
  * Per-launch timing, for measurement (not part of the method). gdn_timing_begin opens a session on the
  * calling thread: until gdn_timing_end, every kernel the library launches from this thread is
  * bracketed by two HIP events recorded on the launch stream (at most `capacity` launches, 1..65536;
@@ -204,7 +254,7 @@ size_t gdn_state_record_bytes(const gdn_desc* desc);
  * gdn_timing_end waits for the recorded events, writes the first `cap` launches in launch order as
  * (static kernel name, milliseconds) into kernels[] and ms[] (either may be NULL), closes the session
  * and returns the number of launches recorded, or a negative status (GDN_EINVAL: no open session,
- * GDN_EHIP: an event failed). Kernel names: "conv", "chunk_prep", "state_pass", "norm",
+ * GDN_EHIP: an event failed). Kernel names: "conv", "chunk_prep", "state_pass", "norm", "zero",
  * "step_decode", "step_verify", "copy", "accept".
  */
 int gdn_timing_begin(int capacity);
