@@ -1,6 +1,6 @@
 """Benchmark of the Gated DeltaNet layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|verify_paths|prefix_cache|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|verify_paths|prefix_cache|spec_loop|copy]
 
 Headline (`value`): prefill tokens/s of one layer on one sequence of 4096 tokens, 16 key / 16 value
 heads, d_k = d_v = 128, bf16 activations, fp32 state, continued from a saved state (one step = one
@@ -361,6 +361,39 @@ def bench_prefix_cache(torch, gdn, args):
             "tokens_per_s_plain": tok / (ms_p / 1e3), "speedup": ms_p / ms_c, "stats": st}
 
 
+def bench_spec_loop(torch, gdn, args):
+    """The speculative-decoding loop (verify + accept + commit per step, the host reading m back each
+    step) over 64 sequences with K = 4 and drafts that match the synthetic verifier with probability 0.7,
+    committing verify checkpoints directly and, for comparison, replaying the accepted prefix."""
+    from gated_delta_rule_44_amd import spec
+    from gdn_inputs import NEXT, SpecStream, make_layer, random_state
+    from tests.gpu_helpers import act, desc_of, f32, weights
+    dims, B, K, vocab, steps = NEXT, 64, 4, 1024, 24
+    d = desc_of(dims)
+    w, table, rng = make_layer(303, dims, 1, vocab)
+    W = weights(w, dims)
+    tab = [act(f, dims)[0] for f in (table.mixed, table.z, table.a, table.b)]
+    S0, tail0 = random_state(rng, dims, B)
+    res = {}
+    for mode in ("direct", "replay"):
+        sp, tp = f32(S0), act(tail0, dims)
+        loop = spec.SpecDecodeLoop(d, W, tab, K, np.arange(B), sp, tp, mode=mode)
+        stream = SpecStream(np.random.default_rng(9), B, 8 * steps * (K + 1), vocab, 0.7)
+        for _ in range(3):  # warm-up steps
+            stream.advance(loop.step(*stream.draw(K))[0])
+        loop.stats = spec.LoopStats(K, B)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            stream.advance(loop.step(*stream.draw(K))[0])
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        res[mode] = {"tokens_per_s": loop.stats.tokens / sec, "ms_per_step": sec / steps * 1e3,
+                     "acceptance_rate": loop.stats.report().acceptance_rate, **loop.stats.as_dict()}
+    return {"workload": "64 sequences, K=4 drafts per step, synthetic drafts matching with p=0.7, 24 steps, one layer",
+            **res}
+
+
 def bench_copy(torch, gdn, args):
     from gdn_inputs import NEXT
     from tests.gpu_helpers import desc_of
@@ -447,6 +480,8 @@ def main():
         line["verify_paths"] = bench_verify_paths(torch, gdn, args)
     if only in ("all", "prefix_cache"):
         line["prefix_cache"] = bench_prefix_cache(torch, gdn, args)
+    if only in ("all", "spec_loop"):
+        line["spec_loop"] = bench_spec_loop(torch, gdn, args)
     if only in ("all", "copy"):
         line["copy"] = bench_copy(torch, gdn, args)
     if not args.no_cpu and only in ("all", "prefill"):

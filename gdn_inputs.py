@@ -195,6 +195,33 @@ def path_inputs(rng: np.random.Generator, dims: LayerDims, B: int, P: int, T: in
     return LayerInputs(*out, np.full(B, T, np.int32))
 
 
+class SpecStream:
+    """Synthetic speculative decoding for B sequences: a seeded ground-truth token stream per sequence
+    stands for the verifier's greedy continuation, and each draft equals the ground truth at its position
+    with probability q (else another token)."""
+
+    def __init__(self, rng: np.random.Generator, B: int, length: int, vocab: int, q: float):
+        self.rng, self.vocab, self.q = rng, vocab, q
+        self.truth = rng.integers(0, vocab, size=(B, length)).astype(np.int32)
+        self.pos = np.zeros(B, np.int64)  # index of each sequence's last emitted token (not yet consumed)
+
+    def draw(self, K: int):
+        """-> (x [B], drafts [B,K], preds [B,K+1]) for the next step."""
+        B = len(self.pos)
+        idx = self.pos[:, None] + np.arange(K + 2)[None, :]
+        if idx.max() >= self.truth.shape[1]:
+            raise ValueError("ground-truth stream exhausted")
+        t = np.take_along_axis(self.truth, idx, axis=1)
+        x, preds = t[:, 0], t[:, 1:K + 2]
+        drafts = preds[:, :K].copy()
+        miss = self.rng.random((B, K)) >= self.q
+        drafts[miss] = (drafts[miss] + 1 + self.rng.integers(0, self.vocab - 1, size=int(miss.sum()))) % self.vocab
+        return x.astype(np.int32), drafts.astype(np.int32), preds.astype(np.int32)
+
+    def advance(self, m: np.ndarray):
+        self.pos += np.asarray(m, np.int64) + 1
+
+
 # ---- the workloads -----------------------------------------------------------------------------------
 
 TINY = LayerDims(n_k=2, n_v=4, d_k=32, d_v=32, act=ACT_F32)            # T=64, chunk 16
