@@ -161,7 +161,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc* d, int B, int Lb) {
   if (check_desc(d) || B <= 0 || Lb <= 0) return 0;
   if (d->act_dtype == GDN_F32 && d->d_k > 64) return 0;
   const int n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
-  return gdn::prefill_ws_bytes(B, d->n_v, d->d_k, Lb, n_chunks, d->act_dtype == GDN_F32);
+  return gdn::prefill_ws_bytes(B, d->n_k, d->n_v, d->d_k, Lb, n_chunks, d->act_dtype == GDN_F32);
 }
 
 int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,

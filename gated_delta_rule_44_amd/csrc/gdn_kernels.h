@@ -64,13 +64,14 @@ struct PrefillArgs {
   void* tail;           // [B][3][C] in/out
   float* state;         // [B][n_v][D][D] in/out
   void* out;            // [B][Lb][n_v*D]
-  void* ws;             // workspace: chunk records, then (split heads only) unnormalised o and partial sums
-  long oraw_off, ss_off;  // byte offsets inside ws
+  void* ws;             // workspace: value records, key records (n_v > n_k), then (split heads only)
+                        // unnormalised o and partial sums
+  long key_off, oraw_off, ss_off;  // byte offsets inside ws: key records, unnormalised o, partial sums
   int B, Lb, n_k, n_v, C, n_chunks;
   float scale, l2_eps, rms_eps;
 };
 // fp32 activations run every MFMA operand as a hi/lo pair (split_all) and are built for d <= 64
-size_t prefill_ws_bytes(int B, int n_v, int D, int Lb, int n_chunks, bool split_all);
+size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool split_all);
 void prefill_ws_layout(PrefillArgs& p, int D, bool split_all);
 hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hipStream_t st);
 

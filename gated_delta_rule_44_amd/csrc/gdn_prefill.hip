@@ -90,29 +90,47 @@ __device__ __forceinline__ void split4(f32x4 x, f16x4& hi, f16x4& lo) {
   }
 }
 
-// ---- the per-chunk record (one per sequence x value head x chunk) -------------------------------
+// ---- the per-chunk records -----------------------------------------------------------------------
 // Fragment blocks of 1 KB: lane l's 16 bytes at 16 l. Token tile mt = 16 tokens, H row tile hm = 16
 // rows of d_k, kk = 32-block of the contraction index, hi/lo halves in separate blocks.
-template <int D, bool SPLIT>
+// One record per sequence x value head x chunk. With one value head per key head (SH false) it holds
+// the decayed Q~ and K~ too. With several (SH true), q and k, which are per key head, go once into a
+// key record per sequence x key head x chunk, undecayed, and the value record carries the per-token
+// decays instead: the state pass scales the columns of Q H by scale e^{gamma_t} and decays U by
+// e^{gamma_C - gamma_t} before the state update.
+template <int D, bool SPLIT, bool SH>
 struct Rec {
   static constexpr int KD = D / 32, HM = D / 16;
   static constexpr int W_HI = 0;                               // [mt][kk]: -W[token][d_k]
   static constexpr int W_LO = W_HI + 4 * KD;                   // (fp32 activations only)
-  static constexpr int Q_HI = W_LO + (SPLIT ? 4 * KD : 0);     // [mt][kk]: 2^8 Q~[token][d_k]
+  static constexpr int Q_HI = W_LO + (SPLIT ? 4 * KD : 0);     // [mt][kk]: 2^8 Q~[token][d_k] (SH false)
   static constexpr int Q_LO = Q_HI + 4 * KD;
-  static constexpr int P_HI = Q_LO + 4 * KD;                   // [mt][kk]: 2^8 P~[token t][token s]
+  static constexpr int P_HI = SH ? Q_HI : Q_LO + 4 * KD;       // [mt][kk]: 2^8 P~[token t][token s]
   static constexpr int P_LO = P_HI + 8;
-  static constexpr int K_HI = P_LO + 8;                        // [hm][kk]: 2^8 K~^T[d_k][token]
+  static constexpr int K_HI = P_LO + 8;                        // [hm][kk]: 2^8 K~^T[d_k][token] (SH false)
   static constexpr int K_LO = K_HI + 2 * HM;
-  static constexpr int UP = K_LO + 2 * HM;                     // [mt][nt]: 2^8 U' in accumulator order
+  static constexpr int UP = SH ? K_HI : K_LO + 2 * HM;         // [mt][nt]: 2^8 U' in accumulator order
   static constexpr int NBLK = UP + 4 * HM;
   static constexpr long kGc = NBLK * 1024L;                    // e^{gamma_C}
-  static constexpr long kBytes = kGc + 256;
+  static constexpr long kEg = kGc + 256;                       // SH: scale e^{gamma_t}, t = 0..63
+  static constexpr long kEd = kEg + 256;                       // SH: e^{gamma_C - gamma_t}
+  static constexpr long kBytes = kGc + (SH ? 768 : 256);
+};
+// the key record (SH): 2^8 q and 2^8 k^T of one key head, hi/lo, as the Q~ / K~ blocks above
+template <int D>
+struct KeyRec {
+  static constexpr int KD = D / 32, HM = D / 16;
+  static constexpr int Q_HI = 0, Q_LO = 4 * KD, K_HI = 8 * KD, K_LO = 8 * KD + 2 * HM;
+  static constexpr long kBytes = (8 * KD + 4 * HM) * 1024L;
 };
 
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool SH>
 __device__ __forceinline__ char* rec_ptr(const PrefillArgs& p, int b, int h, int c) {
-  return (char*)p.ws + (((long)b * p.n_v + h) * p.n_chunks + c) * Rec<D, SPLIT>::kBytes;
+  return (char*)p.ws + (((long)b * p.n_v + h) * p.n_chunks + c) * Rec<D, SPLIT, SH>::kBytes;
+}
+template <int D>
+__device__ __forceinline__ char* key_ptr(const PrefillArgs& p, int b, int kh, int c) {
+  return (char*)p.ws + p.key_off + (((long)b * p.n_k + kh) * p.n_chunks + c) * KeyRec<D>::kBytes;
 }
 // (the lane offset is an unsigned 32-bit value added to a wave-uniform base, which the compiler can
 // encode as a scalar base plus vector offset instead of a per-lane 64-bit address)
@@ -183,7 +201,8 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // -------------------------------------------------------------------------------------------------
 template <typename ActT, int D, int R, bool SPLIT>
 __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
-  using RC = Rec<D, SPLIT>;
+  constexpr bool SH = R > 1;
+  using RC = Rec<D, SPLIT, SH>;
   constexpr int NWV = 8, NTH = 64 * NWV;      // two waves per SIMD: one's waits overlap the other's work
   constexpr int TPW = C64 / NWV;              // tokens per wave in the conv stage
   constexpr int KD = D / 32, HM = D / 16;
@@ -400,6 +419,31 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     qfh[i] = frag_row_h(sQh + row, g16);
     qfl[i] = frag_row_h(sQl + row, g16);
   }
+  if constexpr (SH) {
+    // the key record: 2^8 q (token tile q & 3, block q >> 2) and 2^8 k^T (row tile idx >> 1, block
+    // idx & 1), once for all value heads of the group
+    using KR = KeyRec<D>;
+    char* krec = key_ptr<D>(p, b, kh, c);
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int q = w + NWV * i;
+      if (q < 4 * KD) {
+        put_frag(krec, KR::Q_HI + (q & 3) * KD + (q >> 2), lane, qfh[i]);
+        put_frag(krec, KR::Q_LO + (q & 3) * KD + (q >> 2), lane, qfl[i]);
+      }
+    }
+    for (int idx = w; idx < 2 * HM; idx += NWV) {
+      const int hm = idx >> 1, kk = idx & 1;
+      float x[8];
+      frag_row_f(sKt + (16 * hm + r16) * LT + 32 * kk, g16, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= kS8;
+      f16x8 hi, lo;
+      split8(x, hi, lo);
+      put_frag(krec, KR::K_HI + hm * 2 + kk, lane, hi);
+      put_frag(krec, KR::K_LO + hm * 2 + kk, lane, lo);
+    }
+  }
   lds_barrier();
 
   // ---- 5. per value head of the group ------------------------------------------------------------
@@ -407,7 +451,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     const int h = kh * R + r;
     const float* gam = sGam + r * C64;
     const float* bet = sBet + r * C64;
-    char* rec = rec_ptr<D, SPLIT>(p, b, h, c);
+    char* rec = rec_ptr<D, SPLIT, SH>(p, b, h, c);
     const float gC = gam[C64 - 1];
 
     // A (strictly lower, fp32), T's upper blocks cleared, this head's v channel-major
@@ -448,7 +492,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 #pragma unroll
       for (int i = 0; i < QPW; ++i) {
         const int q = w + NWV * i;
-        if (q < 4 * KD) {
+        if (!SH && q < 4 * KD) {
           const int mt = q & 3, kk = q >> 2;
           const float fq = p.scale * __expf(gam[16 * mt + r16]);
           float x[8];
@@ -477,8 +521,13 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
         put_frag(rec, RC::P_HI + mt * 2 + kk, lane, hi);
         put_frag(rec, RC::P_LO + mt * 2 + kk, lane, lo);
       }
-      // K~^T (row tile idx >> 1, block idx & 1 for idx = w, w + 8, ...): 2^8 e^{gamma_C - gamma_s} k_s
-      for (int idx = w; idx < 2 * HM; idx += NWV) {
+      // K~^T (row tile idx >> 1, block idx & 1 for idx = w, w + 8, ...): 2^8 e^{gamma_C - gamma_s} k_s;
+      // with a key record, the per-token decays instead
+      if (SH && tid < C64) {
+        *(float*)(rec + RC::kEg + 4 * tid) = p.scale * __expf(gam[tid]);
+        *(float*)(rec + RC::kEd + 4 * tid) = __expf(gC - gam[tid]);
+      }
+      for (int idx = SH ? 2 * HM : w; idx < 2 * HM; idx += NWV) {
         const int hm = idx >> 1, kk = idx & 1;
         float x[8];
         frag_row_f(sKt + (16 * hm + r16) * LT + 32 * kk, g16, x);
@@ -630,6 +679,7 @@ struct ChainFrags {
   f32x4 up[NT];                     // U' of the token tile, this slice
   f16x8 k[2], kl[2];                // K~^T of the own H tile
   float gc;                         // e^{gamma_C}
+  f32x4 ed;                         // with a key record: e^{gamma_C - gamma_t} of this lane's U rows
 };
 template <int KD, int NT, typename RawZ>
 struct OutFrags {
@@ -637,12 +687,14 @@ struct OutFrags {
   f16x8 p[2], pl[2];                // P~ of the token tile
   f16x8 k[2], kl[2];                // K~^T of the own H tile
   float gc;                         // e^{gamma_C}
+  float eg;                         // with a key record: scale e^{gamma_t} of this lane's token
   RawZ z[NT];                       // z of the token tile (fused norm)
 };
 
-template <typename ActT, int D, int NT, bool SPLIT, bool FUSED, bool DB>
+template <typename ActT, int D, int NT, bool SPLIT, bool FUSED, bool DB, bool SH>
 __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
-  using RC = Rec<D, SPLIT>;
+  using RC = Rec<D, SPLIT, SH>;
+  using KR = KeyRec<D>;
   constexpr int KD = D / 32, HM = D / 16, CS = 16 * NT, NSPLIT = D / CS;
   constexpr int NG = (NT == 2 || NT == 4) ? 2 : 1;  // column tiles per MFMA group (registers cap NT = 8 at 1)
   static_assert(NSPLIT * CS == D, "column split");
@@ -654,6 +706,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
   // H and U as MFMA operand fragments: [32-block][nt][hi, lo][lane], 16 bytes each
   __shared__ f16x8 sH[KD * NT * 2 * kWave];
   __shared__ f16x8 sU[2 * NT * 2 * kWave];
+  __shared__ f16x8 sUd[SH ? 2 * NT * 2 * kWave : 1];  // with a key record: diag(e^{gamma_C - gamma}) U
 
   // workgroups of one head run on one XCD (dispatch goes round-robin over the 8 XCDs), so that the
   // record of a chunk is fetched from HBM once and shared through that XCD's L2
@@ -673,16 +726,23 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
   const int cb = split * CS;
 
   // single fragments of chunk c (past the end: the last chunk, loaded and unused, branch-free)
-  auto rec_of = [&](int c) { return (const char*)rec_ptr<D, SPLIT>(p, b, h, c < n_real ? c : n_real - 1); };
+  auto rec_of = [&](int c) { return (const char*)rec_ptr<D, SPLIT, SH>(p, b, h, c < n_real ? c : n_real - 1); };
+  auto key_of = [&](int c) { return (const char*)key_ptr<D>(p, b, h / (n_v / p.n_k), c < n_real ? c : n_real - 1); };
   auto ld_w = [&](CF& f, int c, int kk) __attribute__((always_inline)) {
     const char* rec = rec_of(c);
     f.w[kk] = get_frag(rec, RC::W_HI + tt * KD + kk, lane);
     if (SPLIT) f.wl[kk] = get_frag(rec, RC::W_LO + tt * KD + kk, lane);
   };
   auto ld_q = [&](OF& f, int c, int kk) __attribute__((always_inline)) {
-    const char* rec = rec_of(c);
-    f.q[kk] = get_frag(rec, RC::Q_HI + tt * KD + kk, lane);
-    f.ql[kk] = get_frag(rec, RC::Q_LO + tt * KD + kk, lane);
+    if constexpr (SH) {
+      const char* rec = key_of(c);
+      f.q[kk] = get_frag(rec, KR::Q_HI + tt * KD + kk, lane);
+      f.ql[kk] = get_frag(rec, KR::Q_LO + tt * KD + kk, lane);
+    } else {
+      const char* rec = rec_of(c);
+      f.q[kk] = get_frag(rec, RC::Q_HI + tt * KD + kk, lane);
+      f.ql[kk] = get_frag(rec, RC::Q_LO + tt * KD + kk, lane);
+    }
   };
   auto ld_up = [&](CF& f, int c, int nt) __attribute__((always_inline)) {
     f.up[nt] = *(const f32x4*)(rec_of(c) + (RC::UP + tt * HM + cb / 16 + nt) * 1024 + (uint32_t)(lane * 16));
@@ -693,12 +753,26 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
     f.pl[kk] = get_frag(rec, RC::P_LO + tt * 2 + kk, lane);
   };
   auto ld_k = [&](auto& f, int c, int kk) __attribute__((always_inline)) {
-    const char* rec = rec_of(c);
     const int hm = owner ? w : 0;  // a wave without a tile loads tile 0 and ignores it
-    f.k[kk] = get_frag(rec, RC::K_HI + hm * 2 + kk, lane);
-    f.kl[kk] = get_frag(rec, RC::K_LO + hm * 2 + kk, lane);
+    if constexpr (SH) {
+      const char* rec = key_of(c);
+      f.k[kk] = get_frag(rec, KR::K_HI + hm * 2 + kk, lane);
+      f.kl[kk] = get_frag(rec, KR::K_LO + hm * 2 + kk, lane);
+    } else {
+      const char* rec = rec_of(c);
+      f.k[kk] = get_frag(rec, RC::K_HI + hm * 2 + kk, lane);
+      f.kl[kk] = get_frag(rec, RC::K_LO + hm * 2 + kk, lane);
+    }
   };
   auto ld_gc = [&](auto& f, int c) __attribute__((always_inline)) { f.gc = *(const float*)(rec_of(c) + RC::kGc); };
+  // the per-token decays of a record with a key record: rows 16 tt + 4 g16 + i of U (chain), token
+  // 16 tt + r16 of O (output)
+  auto ld_ed = [&](CF& f, int c) __attribute__((always_inline)) {
+    if constexpr (SH) f.ed = *(const f32x4*)(rec_of(c) + RC::kEd + 4 * (16 * tt + 4 * g16));
+  };
+  auto ld_eg = [&](OF& f, int c) __attribute__((always_inline)) {
+    if constexpr (SH) f.eg = *(const float*)(rec_of(c) + RC::kEg + 4 * (16 * tt + r16));
+  };
   auto ld_z = [&](OF& f, int c) __attribute__((always_inline)) {
     if (FUSED) {
       const int cc = c < n_real ? c : n_real - 1;
@@ -714,11 +788,13 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
       for (int kk = 0; kk < KD; ++kk) ld_w(f, c, kk);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) ld_up(f, c, nt);
+      ld_ed(f, c);
     } else {
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) ld_q(f, c, kk);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) ld_p(f, c, kk);
+      ld_eg(f, c);
       ld_z(f, c);
     }
 #pragma unroll
@@ -802,15 +878,24 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) U[n0 + g] = ua[g] + ub[g];
       }
-      // U hi/lo into its fragment slots: token tile tt is half (tt & 1) of 32-block tt >> 1
+      // U hi/lo into its fragment slots: token tile tt is half (tt & 1) of 32-block tt >> 1 (and, with a
+      // key record, the decayed U the state update takes)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f16x4 hi, lo;
         split4(U[nt], hi, lo);
-        _Float16* dst = (_Float16*)&sU[(((tt >> 1) * NT + nt) * 2) * kWave + lane] + 4 * (tt & 1);
+        const int slot = (((tt >> 1) * NT + nt) * 2) * kWave + lane;
+        _Float16* dst = (_Float16*)&sU[slot] + 4 * (tt & 1);
         *(f16x4*)dst = hi;
         *(f16x4*)(dst + 8 * kWave) = lo;
+        if constexpr (SH) {
+          split4(U[nt] * f.ed, hi, lo);
+          _Float16* dd = (_Float16*)&sUd[slot] + 4 * (tt & 1);
+          *(f16x4*)dd = hi;
+          *(f16x4*)(dd + 8 * kWave) = lo;
+        }
       }
+      ld_ed(f, cn);
     } else {
       // ---- O^T = H^T Q~^T (token tile tt) ----
 #pragma unroll
@@ -837,48 +922,102 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
           if (n0 + NG >= NT) ld_q(f, cn, kk);  // last use of this block's Q~ in the chunk
         }
 #pragma unroll
-        for (int g = 0; g < NG; ++g) OT[n0 + g] = oa[g] + ob[g];
+        for (int g = 0; g < NG; ++g) OT[n0 + g] = SH ? (oa[g] + ob[g]) * f.eg : oa[g] + ob[g];
       }
+      ld_eg(f, cn);
     }
     lds_barrier();  // U of every token tile is in sU; every wave is done reading sH
     // ---- own H tile: H = e^{gamma_C} H + K~^T U; output waves also O^T += U^T P~^T ----
+    if constexpr (!SH) {
+      // both products read the same U fragments: interleaved, so that the MFMA pipe stays full
 #pragma unroll
-    for (int n0 = 0; n0 < NT; n0 += NG) {
-      f16x8 uf[2][NG], ul[2][NG];
+      for (int n0 = 0; n0 < NT; n0 += NG) {
+        f16x8 uf[2][NG], ul[2][NG];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          uf[kk][g] = sU[((kk * NT + n0 + g) * 2) * kWave + lane];
-          ul[kk][g] = sU[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
+          for (int g = 0; g < NG; ++g) {
+            uf[kk][g] = sU[((kk * NT + n0 + g) * 2) * kWave + lane];
+            ul[kk][g] = sU[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
+          }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) Hacc[n0 + g] = Hacc[n0 + g] * f.gc;
+        if (n0 + NG >= NT) ld_gc(f, cn);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int term = 0; term < 3; ++term) {
+            if (owner) {
+#pragma unroll
+              for (int g = 0; g < NG; ++g) {
+                const f16x8 ka = term == 0 ? f.kl[kk] : f.k[kk];
+                const f16x8 ub = term == 1 ? ul[kk][g] : uf[kk][g];
+                Hacc[n0 + g] = mfma16(ka, ub, Hacc[n0 + g]);
+              }
+            }
+            if constexpr (!kChain) {
+#pragma unroll
+              for (int g = 0; g < NG; ++g) {
+                const f16x8 ua = term == 1 ? ul[kk][g] : uf[kk][g];
+                const f16x8 pb = term == 0 ? f.pl[kk] : f.p[kk];
+                OT[n0 + g] = mfma16(ua, pb, OT[n0 + g]);
+              }
+            }
+          }
+          if (n0 + NG >= NT) {  // last use of this block's K~ (and P~) in the chunk
+            ld_k(f, cn, kk);
+            if constexpr (!kChain) ld_p(f, cn, kk);
+          }
         }
+      }
+    } else {
+      // the state update takes the decayed U, O^T the plain one: one after the other, so that only one
+      // set of U fragments is held at a time
 #pragma unroll
-      for (int g = 0; g < NG; ++g) Hacc[n0 + g] = Hacc[n0 + g] * f.gc;
-      if (n0 + NG >= NT) ld_gc(f, cn);
+      for (int n0 = 0; n0 < NT; n0 += NG) {
+        f16x8 df[2][NG], dl[2][NG];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int term = 0; term < 3; ++term) {
+          for (int g = 0; g < NG; ++g) {
+            df[kk][g] = sUd[((kk * NT + n0 + g) * 2) * kWave + lane];
+            dl[kk][g] = sUd[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
+          }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) Hacc[n0 + g] = Hacc[n0 + g] * f.gc;
+        if (n0 + NG >= NT) ld_gc(f, cn);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
           if (owner) {
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-              const f16x8 ka = term == 0 ? f.kl[kk] : f.k[kk];
-              const f16x8 ub = term == 1 ? ul[kk][g] : uf[kk][g];
-              Hacc[n0 + g] = mfma16(ka, ub, Hacc[n0 + g]);
-            }
+            for (int term = 0; term < 3; ++term)
+#pragma unroll
+              for (int g = 0; g < NG; ++g)
+                Hacc[n0 + g] = mfma16(term == 0 ? f.kl[kk] : f.k[kk], term == 1 ? dl[kk][g] : df[kk][g], Hacc[n0 + g]);
           }
-          if constexpr (!kChain) {
+          if (n0 + NG >= NT) ld_k(f, cn, kk);  // last use of this block's K in the chunk
+        }
+      }
+      if constexpr (!kChain) {
+#pragma unroll
+        for (int n0 = 0; n0 < NT; n0 += NG) {
+          f16x8 uf[2][NG], ul[2][NG];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-              const f16x8 ua = term == 1 ? ul[kk][g] : uf[kk][g];
-              const f16x8 pb = term == 0 ? f.pl[kk] : f.p[kk];
-              OT[n0 + g] = mfma16(ua, pb, OT[n0 + g]);
+              uf[kk][g] = sU[((kk * NT + n0 + g) * 2) * kWave + lane];
+              ul[kk][g] = sU[((kk * NT + n0 + g) * 2 + 1) * kWave + lane];
             }
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int term = 0; term < 3; ++term)
+#pragma unroll
+              for (int g = 0; g < NG; ++g)
+                OT[n0 + g] = mfma16(term == 1 ? ul[kk][g] : uf[kk][g], term == 0 ? f.pl[kk] : f.p[kk], OT[n0 + g]);
+            if (n0 + NG >= NT) ld_p(f, cn, kk);  // last use of this block's P~ in the chunk
           }
-        }
-        if (n0 + NG >= NT) {  // last use of this block's K~ (and P~) in the chunk
-          ld_k(f, cn, kk);
-          if constexpr (!kChain) ld_p(f, cn, kk);
         }
       }
     }
@@ -1016,9 +1155,23 @@ int pass_nt(int B, int n_v, int D) {
   return pairs >= 256 ? 8 : pairs >= 128 ? 4 : pairs >= 64 ? 2 : 1;
 }
 
-long rec_bytes(int D, bool split_all) {
-  if (split_all) return D == 32 ? Rec<32, true>::kBytes : Rec<64, true>::kBytes;
-  return D == 32 ? Rec<32, false>::kBytes : D == 64 ? Rec<64, false>::kBytes : Rec<128, false>::kBytes;
+// bytes of one value record and of one key record (zero without key records)
+template <int D, bool SPLIT>
+void rec_sizes_t(bool sh, long& vrec, long& krec) {
+  vrec = sh ? Rec<D, SPLIT, true>::kBytes : Rec<D, SPLIT, false>::kBytes;
+  krec = sh ? KeyRec<D>::kBytes : 0;
+}
+void rec_sizes(int D, bool split_all, bool sh, long& vrec, long& krec) {
+  if (split_all) {
+    if (D == 32) rec_sizes_t<32, true>(sh, vrec, krec);
+    else rec_sizes_t<64, true>(sh, vrec, krec);
+  } else if (D == 32) {
+    rec_sizes_t<32, false>(sh, vrec, krec);
+  } else if (D == 64) {
+    rec_sizes_t<64, false>(sh, vrec, krec);
+  } else {
+    rec_sizes_t<128, false>(sh, vrec, krec);
+  }
 }
 
 template <typename ActT, int D, int R, bool SPLIT, int NT>
@@ -1030,7 +1183,7 @@ hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timing_before("state_pass", st);
-  hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NSPLIT == 1, (NT <= 4)>), dim3(NSPLIT * p.n_v * p.B), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NSPLIT == 1, (NT <= 4), (R > 1)>), dim3(NSPLIT * p.n_v * p.B), dim3(512), 0, st, p);
   timing_after(st);
   e = hipGetLastError();
   if (e != hipSuccess || NSPLIT == 1) return e;
@@ -1053,9 +1206,11 @@ hipError_t launch_r(const PrefillArgs& p, int R, hipStream_t st) {
 
 }  // namespace
 
-size_t prefill_ws_bytes(int B, int n_v, int D, int Lb, int n_chunks, bool split_all) {
+size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool split_all) {
   const int nsplit = D / (16 * pass_nt(B, n_v, D));
-  size_t bytes = (size_t)B * n_v * n_chunks * rec_bytes(D, split_all);
+  long vrec, krec;
+  rec_sizes(D, split_all, n_v > n_k, vrec, krec);
+  size_t bytes = (size_t)B * n_chunks * ((size_t)n_v * vrec + (size_t)n_k * krec);
   if (nsplit > 1) {
     bytes += (size_t)B * Lb * n_v * D * 4;             // unnormalised o
     bytes += (size_t)B * Lb * n_v * nsplit * 4;        // partial sums of squares
@@ -1065,7 +1220,10 @@ size_t prefill_ws_bytes(int B, int n_v, int D, int Lb, int n_chunks, bool split_
 }
 
 void prefill_ws_layout(PrefillArgs& p, int D, bool split_all) {
-  const size_t rec = (size_t)p.B * p.n_v * p.n_chunks * rec_bytes(D, split_all);
+  long vrec, krec;
+  rec_sizes(D, split_all, p.n_v > p.n_k, vrec, krec);
+  p.key_off = (long)p.B * p.n_v * p.n_chunks * vrec;
+  const size_t rec = (size_t)p.key_off + (size_t)p.B * p.n_k * p.n_chunks * krec;
   p.oraw_off = (long)rec;
   p.ss_off = (long)(rec + (size_t)p.B * p.Lb * p.n_v * D * 4);
 }
