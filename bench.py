@@ -1,6 +1,6 @@
 """Benchmark of the Gated DeltaNet layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|verify_paths|prefix_cache|spec_loop|copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|verify_paths|prefix_cache|spec_loop|copy|peaks]
 
 Headline (`value`): prefill tokens/s of one layer on one sequence of 4096 tokens, 16 key / 16 value
 heads, d_k = d_v = 128, bf16 activations, fp32 state, continued from a saved state (one step = one
@@ -20,7 +20,11 @@ The same run also measures, each as a sub-object of the one JSON line:
   prefill_stack - one layer of the 9B-like stack: 8 x 8192 tokens, 16 key / 32 value heads
   decode  - 36 GDN layers x 256 sequences x 1 token (one step = 36 gdn_decode_step calls), state GB/s
   verify  - 64 sequences x (1+4) tokens with checkpoints, then accept and the commit copy
+  verify_paths - the same with 4 candidate paths per sequence (tree verify), accept over paths, commit
+  prefix_cache - 8 rows of 8192 tokens sharing 6144 through the prefix-state cache, against no cache
+  spec_loop - the speculative-decoding loop (verify, accept, commit or replay) over 64 sequences
   copy    - the O(1) state bridge: 256 records {fp32 state, conv tail} of one layer
+  measured_peaks - the MFMA probe's dense f16 TFLOP/s and the copy leg's GB/s beside the published peaks
   cpu_baseline - the fp64 oracle on the host cores on the prefill workload
 """
 from __future__ import annotations
@@ -484,6 +488,13 @@ def main():
         line["spec_loop"] = bench_spec_loop(torch, gdn, args)
     if only in ("all", "copy"):
         line["copy"] = bench_copy(torch, gdn, args)
+    if only in ("all", "peaks"):
+        # the peaks the rooflines are quoted against, re-derived on this GPU: dense f16 MFMA from the
+        # probe kernel (best of 5), HBM streaming from the state-copy leg when it ran
+        tf = max(gdn.mfma_probe() for _ in range(5))
+        line["measured_peaks"] = {"mfma_f16_TFLOPs": tf, "mfma_frac_of_published": tf / MFMA_PEAK_TFLOPS,
+                                  "hbm_copy_GBs": line.get("copy", {}).get("GB_per_s"),
+                                  "published": {"mfma_bf16_f16_TFLOPs": MFMA_PEAK_TFLOPS, "hbm_GBs": HBM_PEAK_GBS}}
     if not args.no_cpu and only in ("all", "prefill"):
         line["cpu_baseline"] = cpu_baseline()
     line["kernel_hash"] = kernel_hash()

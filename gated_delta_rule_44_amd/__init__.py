@@ -53,7 +53,7 @@ EXPORTS = ("gdn_last_error", "gdn_version", "gdn_conv_chunk", "gdn_prefill_works
            "gdn_decode_step", "gdn_verify_with_checkpoints", "gdn_verify_paths", "gdn_accept", "gdn_accept_paths",
            "gdn_state_copy",
            "gdn_state_record_bytes", "gdn_state_zero", "gdn_pcache_create", "gdn_pcache_destroy", "gdn_pcache_row",
-           "gdn_pcache_stats", "gdn_pcache_alive", "gdn_timing_begin", "gdn_timing_end")
+           "gdn_pcache_stats", "gdn_pcache_alive", "gdn_mfma_probe", "gdn_timing_begin", "gdn_timing_end")
 
 
 def load_library(path: str = LIB_PATH):
@@ -90,6 +90,7 @@ def load_library(path: str = LIB_PATH):
                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(L)]
     lib.gdn_pcache_stats.argtypes = [P, ctypes.POINTER(L)]
     lib.gdn_pcache_alive.argtypes = [P, I, ctypes.POINTER(L)]
+    lib.gdn_mfma_probe.argtypes = [P, I, I, P]
     lib.gdn_timing_begin.argtypes = [I]
     lib.gdn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), I]
     for name in ("gdn_conv_chunk", "gdn_prefill_chunk", "gdn_decode_step", "gdn_verify_with_checkpoints",
@@ -494,6 +495,20 @@ class PrefixStateCache:
 
 def state_record_bytes(desc: GdnDesc) -> int:
     return int(load_library().gdn_state_record_bytes(ctypes.byref(desc.c())))
+
+
+def mfma_probe(blocks: int = 2048, iters: int = 1024) -> float:
+    """Run the MFMA throughput probe once and return its achieved dense f16 TFLOP/s (timed by a
+    timing session on the current stream)."""
+    lib = load_library()
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    timing_begin(4)
+    try:
+        _check("gdn_mfma_probe", lib.gdn_mfma_probe(_dev(sink, "sink", None, torch.float32), blocks, iters, _stream()))
+    finally:
+        rec = timing_end(4)
+    ms = rec[0][1]
+    return blocks * 4 * 2 * iters * 2 * 32 * 32 * 16 / (ms / 1e3) / 1e12
 
 
 def timing_begin(capacity: int = 1024) -> None:

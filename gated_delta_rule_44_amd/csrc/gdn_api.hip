@@ -287,6 +287,12 @@ int gdn_state_copy(const gdn_desc* d, float* dst_state, void* dst_tail, const in
   return hip_status(gdn::launch_copy(p, (hipStream_t)stream), "gdn_state_copy");
 }
 
+int gdn_mfma_probe(float* sink, int blocks, int iters, gdn_stream_t stream) {
+  if (!sink || blocks <= 0 || iters <= 0) return fail(GDN_EINVAL, "gdn_mfma_probe: sink=%p blocks=%d iters=%d",
+                                                      (void*)sink, blocks, iters);
+  return hip_status(gdn::launch_mfma_probe(sink, blocks, iters, (hipStream_t)stream), "gdn_mfma_probe");
+}
+
 int gdn_state_zero(const gdn_desc* d, float* state, void* tail, const int32_t* idx, int n, gdn_stream_t stream) {
   if (int rc = check_desc(d)) return rc;
   if (n <= 0 || n > 65535) return fail(GDN_EINVAL, "gdn_state_zero: n=%d (1..65535)", n);

@@ -102,4 +102,8 @@ struct AcceptArgs {
 };
 hipError_t launch_accept(const AcceptArgs& p, hipStream_t st);
 
+// ---- measurement aid ------------------------------------------------------------------------------
+// blocks x 256 threads, each wave 2 chains x iters f16 MFMAs of 32x32x16; sink [blocks * 256] floats
+hipError_t launch_mfma_probe(float* sink, int blocks, int iters, hipStream_t st);
+
 }  // namespace gdn

@@ -255,9 +255,16 @@ int gdn_state_zero(const gdn_desc* desc, float* state, void* tail, const int32_t
  * (static kernel name, milliseconds) into kernels[] and ms[] (either may be NULL), closes the session
  * and returns the number of launches recorded, or a negative status (GDN_EINVAL: no open session,
  * GDN_EHIP: an event failed). Kernel names: "conv", "chunk_prep", "state_pass", "norm", "zero",
- * "step_decode", "step_verify", "copy", "accept".
+ * "step_decode", "step_verify", "copy", "accept", "mfma_probe".
  */
 int gdn_timing_begin(int capacity);
+/*
+ * MFMA throughput probe, for measurement (not part of the method): blocks x 256 threads, every wave
+ * issuing 2 independent chains of `iters` f16 32x32x16 MFMAs (2 * 32 * 32 * 16 FLOP each), so a run
+ * does blocks * 4 * 2 * iters * 32768 FLOP. sink: device buffer of blocks * 256 floats (written).
+ * Time it with the timing session (kernel name "mfma_probe") or the caller's events.
+ */
+int gdn_mfma_probe(float* sink, int blocks, int iters, gdn_stream_t stream);
 int gdn_timing_end(const char** kernels, float* ms, int cap);
 
 #ifdef __cplusplus
