@@ -224,7 +224,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   constexpr int OFF_X = OFF_T;                      // level products, only while T is still fp32
   constexpr int OFF_G = OFF_T + (SPLIT ? 2 : 1) * C64 * LDT * 2;
   constexpr int OFF_B = OFF_G + R * C64 * 4;
-  constexpr int LDS = OFF_B + R * C64 * 4;
+  constexpr int OFF_E = OFF_B + R * C64 * 4;        // per head: e^{gamma_t}, then e^{gamma_C - gamma_t}
+  constexpr int LDS = OFF_E + 2 * C64 * 4;
   static_assert(4 * 16 * 17 * 4 <= (SPLIT ? 2 : 1) * C64 * LDT * 2, "level products fit the T tile");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(CPL == 1 || (CPL == 2 && D == 128), "channel layout");
@@ -243,6 +244,8 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   float* sX = (float*)(smem + OFF_X);
   float* sGam = (float*)(smem + OFF_G);
   float* sBet = (float*)(smem + OFF_B);
+  float* sEg = (float*)(smem + OFF_E);
+  float* sEd = sEg + C64;
 
   const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int t0 = c * C64;
@@ -454,7 +457,12 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     char* rec = rec_ptr<D, SPLIT, SH>(p, b, h, c);
     const float gC = gam[C64 - 1];
 
-    // A (strictly lower, fp32), T's upper blocks cleared, this head's v channel-major
+    // A (strictly lower, fp32), T's upper blocks cleared, this head's v channel-major, and the
+    // per-token decays e^{gamma_t}, e^{gamma_C - gamma_t} (each exponential taken once per head)
+    if (tid < C64) {
+      sEg[tid] = __expf(gam[tid]);
+      sEd[tid] = __expf(gC - gam[tid]);
+    }
     for (int idx = tid; idx < C64 * C64; idx += NTH) {
       const int i = idx >> 6, j = idx & 63;
       sA[i * LF + j] = j < i ? bet[i] * __expf(gam[i] - gam[j]) * (kInvS16 * sKK[i * LT + j]) : 0.f;
@@ -494,7 +502,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
         const int q = w + NWV * i;
         if (!SH && q < 4 * KD) {
           const int mt = q & 3, kk = q >> 2;
-          const float fq = p.scale * __expf(gam[16 * mt + r16]);
+          const float fq = p.scale * sEg[16 * mt + r16];
           float x[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qfh[i][e] + (float)qfl[i][e]);
@@ -524,15 +532,15 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
       // K~^T (row tile idx >> 1, block idx & 1 for idx = w, w + 8, ...): 2^8 e^{gamma_C - gamma_s} k_s;
       // with a key record, the per-token decays instead
       if (SH && tid < C64) {
-        *(float*)(rec + RC::kEg + 4 * tid) = p.scale * __expf(gam[tid]);
-        *(float*)(rec + RC::kEd + 4 * tid) = __expf(gC - gam[tid]);
+        *(float*)(rec + RC::kEg + 4 * tid) = p.scale * sEg[tid];
+        *(float*)(rec + RC::kEd + 4 * tid) = sEd[tid];
       }
       for (int idx = SH ? 2 * HM : w; idx < 2 * HM; idx += NWV) {
         const int hm = idx >> 1, kk = idx & 1;
         float x[8];
         frag_row_f(sKt + (16 * hm + r16) * LT + 32 * kk, g16, x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= kS8 * __expf(gC - gam[32 * kk + kslot(g16, e)]);
+        for (int e = 0; e < 8; ++e) x[e] *= kS8 * sEd[32 * kk + kslot(g16, e)];
         f16x8 hi, lo;
         split8(x, hi, lo);
         put_frag(rec, RC::K_HI + hm * 2 + kk, lane, hi);
@@ -588,7 +596,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
         for (int e = 0; e < 8; ++e) {
           const int s = 32 * ks + kslot(g16, e);
           fv[ks][e] = kS8 * bet[s];
-          fk[ks][e] = fv[ks][e] * __expf(gam[s]);
+          fk[ks][e] = fv[ks][e] * sEg[s];
         }
       }
       for (int j = w; j < HM; j += NWV) {
