@@ -202,6 +202,55 @@ def test_decode_step_vs_oracle(dims, B):
     assert np.all(hp[others] == 0)
 
 
+def test_decode_full_batch_sampled():
+    """The decode leg's launch: 256 sequences, 16 key / 32 value heads, d=128, states like the benchmark's;
+    sequences 0, 77 and 255 against the oracle, and every output finite."""
+    dims, B = NEXT, 256
+    _say("decode B=256 (bench launch)")
+    w, _, rng = make_layer(61, dims, 1, 1)
+    H0, T0 = random_state(rng, dims, B)
+    x = _decode_inputs(dims, rng, B, 1)
+    d = desc_of(dims)
+    sp, tp = f32(H0), act(T0, dims)
+    out = gdn.decode_step(d, weights(w, dims), act(x.mixed[:, 0], dims), act(x.z[:, 0], dims), act(x.a[:, 0], dims),
+                          act(x.b[:, 0], dims), None, tp, sp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    od = oracle.Dims.of(dims)
+    for s in (0, 77, 255):
+        sl = slice(s, s + 1)
+        ref = oracle.layer_forward(od, w, x.mixed[sl], x.z[sl], x.a[sl], x.b[sl], None, T0[sl], H0[sl])
+        assert_out_close(host(out[s]), ref["out"][0, 0], dims, f"decode seq {s}")
+        assert_state_close(host(sp[s]), ref["H"][0], f"decode state {s}")
+        np.testing.assert_array_equal(host(tp[s]), ref["tail"][0].astype(np.float32))
+
+
+def test_verify_paths_full_size_sampled():
+    """The tree-verify leg's launch: 64 sequences x 4 paths x (1+4) tokens, 16/32 heads, d=128; sequences
+    5 and 63 (every path) against the oracle."""
+    dims, B, P, K = NEXT, 64, 4, 4
+    T = K + 1
+    _say("verify paths B=64 P=4 (bench launch)")
+    w, _, rng = make_layer(62, dims, 1, 1)
+    H0, T0 = random_state(rng, dims, B)
+    x = path_inputs(rng, dims, B, P, T)
+    d = desc_of(dims)
+    sp, tp = f32(H0), act(T0, dims)
+    ck_s, ck_t, out = gdn.verify_paths(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims),
+                                       act(x.b, dims), None, tp, sp)
+    torch.cuda.synchronize()
+    od = oracle.Dims.of(dims)
+    for s in (5, 63):
+        sl = slice(s, s + 1)
+        ref = oracle.verify_paths(od, w, x.mixed[sl], x.z[sl], x.a[sl], x.b[sl], T0[sl], H0[sl])
+        assert_out_close(host(out[s]), ref["out"][0], dims, f"paths out seq {s}")
+        cks = host(ck_s[s])
+        for p in range(P):
+            for i in range(T):
+                assert_state_close(cks[p, i], ref["ckpt_H"][0, p, i], f"seq {s} path {p} checkpoint {i}")
+        np.testing.assert_array_equal(host(ck_t[s]), ref["ckpt_tail"][0].astype(np.float32))
+
+
 def test_verify_checkpoints_and_commit():
     """Verify batch: 64 sequences x (1+4) tokens with per-token checkpoints; accept with m ~ U{0..4};
     restore the checkpoint; compare with the oracle and, bitwise, with repeated GPU decode."""
