@@ -1,6 +1,6 @@
 """Benchmark of the Gated DeltaNet layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|decode|verify|verify_paths|prefix_cache|spec_loop|copy|peaks]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|continuation|decode|verify|verify_paths|prefix_cache|spec_loop|copy|peaks]
 
 Headline (`value`): prefill tokens/s of one layer on one sequence of 4096 tokens, 16 key / 16 value
 heads, d_k = d_v = 128, bf16 activations, fp32 state, continued from a saved state (one step = one
@@ -20,6 +20,7 @@ The same run also measures, each as a sub-object of the one JSON line:
   prefill_stack - one layer of the 9B-like stack: 8 x 8192 tokens, 16 key / 32 value heads
   decode  - 36 GDN layers x 256 sequences x 1 token (one step = 36 gdn_decode_step calls), state GB/s
   verify  - 64 sequences x (1+4) tokens with checkpoints, then accept and the commit copy
+  continuation - a 32768-token prompt in bucketed chunks, each continuing from the saved state
   verify_paths - the same with 4 candidate paths per sequence (tree verify), accept over paths, commit
   prefix_cache - 8 rows of 8192 tokens sharing 6144 through the prefix-state cache, against no cache
   spec_loop - the speculative-decoding loop (verify, accept, commit or replay) over 64 sequences
@@ -328,6 +329,54 @@ def bench_verify_paths(torch, gdn, args):
             "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()}}
 
 
+def bench_continuation(torch, gdn, args):
+    """A 32768-token prompt in bucketed chunks (16/32 heads, d=128): each chunk one gdn_prefill_chunk call
+    padded to its bucket, continuing from the previous call's fp32 state and conv tail. Throughput counts
+    real tokens only."""
+    from gdn_inputs import NEXT, chunk_lengths, make_layer
+    from tests.gpu_helpers import act, desc_of, i32, weights
+    dims, total = NEXT, 32768
+    d = desc_of(dims)
+    w, x, rng = make_layer(304, dims, 1, total)
+    W = weights(w, dims)
+    parts = chunk_lengths(rng, total)
+    calls, t0 = [], 0
+    for n, bucket in parts:
+        def pad(a):
+            seg = a[:, t0:t0 + n]
+            fill = rng.standard_normal((1, bucket - n, a.shape[2])).astype(np.float32)
+            return act(np.concatenate([seg, fill], 1), dims)
+        calls.append((pad(x.mixed), pad(x.z), pad(x.a), pad(x.b), i32([n]),
+                      torch.empty(1, bucket, dims.value_dim, dtype=torch.bfloat16, device="cuda")))
+        t0 += n
+    ws = gdn.prefill_workspace(d, 1, max(b for _, b in parts))
+    tail = torch.zeros(1, 3, dims.conv_dim, dtype=torch.bfloat16, device="cuda")
+    state = torch.zeros(1, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda")
+
+    def step(i):
+        for mx, zz, aa, bb, ln, out in calls:
+            gdn.prefill_chunk(d, W, mx, zz, aa, bb, ln, tail, state, out, ws)
+
+    reps = max(2, args.steps // 10)
+    ms, _ = Timer(torch, reps).run(step, reps, 1)
+    # the same calls captured once into a HIP graph and replayed (the library allocates nothing and never
+    # synchronises inside a call, so a caller can capture it)
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cs):
+            step(0)
+    torch.cuda.current_stream().wait_stream(cs)
+    ms_g, _ = Timer(torch, reps).run(lambda i: g.replay(), reps, 1)
+    padded = sum(b for _, b in parts)
+    return {"workload": "1 x 32768 tokens in %d bucketed chunks, 16/32 heads, d=128" % len(parts),
+            "ms_per_prompt": ms, "tokens_per_s": total / (ms / 1e3), "chunks": len(parts),
+            "padded_tokens": padded, "ms_per_chunk": ms / len(parts),
+            "graph": {"ms_per_prompt": ms_g, "tokens_per_s": total / (ms_g / 1e3)}}
+
+
 def bench_prefix_cache(torch, gdn, args):
     """Rows of 8192 tokens that share a 6144-token prefix (a system prompt) and differ in their last 2048,
     through the prefix-state cache (restore, 2048-token chunks, snapshots) and through the plain path
@@ -482,6 +531,8 @@ def main():
         line["verify"] = bench_verify(torch, gdn, args)
     if only in ("all", "verify_paths"):
         line["verify_paths"] = bench_verify_paths(torch, gdn, args)
+    if only in ("all", "continuation"):
+        line["continuation"] = bench_continuation(torch, gdn, args)
     if only in ("all", "prefix_cache"):
         line["prefix_cache"] = bench_prefix_cache(torch, gdn, args)
     if only in ("all", "spec_loop"):

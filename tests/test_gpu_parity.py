@@ -447,3 +447,57 @@ def test_timing_session_names_every_launch():
     assert all(ms > 0 for _, ms in recs)
     with pytest.raises(gdn.GdnError):
         gdn.timing_end(16)  # no open session
+
+
+def test_continuation_graph_replay_equals_eager():
+    """A prompt of bucketed chunks captured once into a HIP graph (torch.cuda.CUDAGraph around the library
+    calls): three replays, each after resetting the state and tail eagerly, give the eager run's outputs
+    and final state bit for bit."""
+    dims, total = NEXT, 4096
+    _say("continuation graph replay")
+    w, x, rng = make_layer(63, dims, 1, total)
+    parts = chunk_lengths(rng, total)
+    d = desc_of(dims)
+    W = weights(w, dims)
+    calls, t0 = [], 0
+    for n, bucket in parts:
+        def pad(a):
+            seg = a[:, t0:t0 + n]
+            fill = rng.standard_normal((1, bucket - n, a.shape[2])).astype(np.float32)
+            return act(np.concatenate([seg, fill], 1), dims)
+        calls.append((pad(x.mixed), pad(x.z), pad(x.a), pad(x.b), i32([n]),
+                      torch.empty(1, bucket, dims.value_dim, dtype=torch.bfloat16, device="cuda"), n))
+        t0 += n
+    ws = gdn.prefill_workspace(d, 1, max(b for _, b in parts))
+    tail = torch.zeros(1, 3, dims.conv_dim, dtype=torch.bfloat16, device="cuda")
+    state = torch.zeros(1, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda")
+
+    def run():
+        for mx, zz, aa, bb, ln, out, _ in calls:
+            gdn.prefill_chunk(d, W, mx, zz, aa, bb, ln, tail, state, out, ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref_out = [c[5][0, :c[6]].clone() for c in calls]
+    ref_state, ref_tail = state.clone(), tail.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        state.zero_()
+        tail.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        state.zero_()
+        tail.zero_()
+        for c in calls:
+            c[5].fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, c in enumerate(calls):
+            assert torch.equal(c[5][0, :c[6]], ref_out[i]), f"replay {rep}: chunk {i} output differs"
+        assert torch.equal(state, ref_state) and torch.equal(tail, ref_tail), f"replay {rep}: state differs"
