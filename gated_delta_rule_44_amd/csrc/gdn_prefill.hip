@@ -13,15 +13,18 @@
 //   conv + SiLU over [saved tail | chunk], q/k L2 norm, gates with the padding mask, the Gram products
 //   K K^T and K Q^T (f16 MFMA, hi/lo-split operands), then for each value head of the GQA group the UT
 //   inverse T (fp32: diagonal 16x16 blocks by substitution, off-diagonal blocks on fp32 MFMA), W and U'
-//   (f16 MFMA), P~ = scale P, Q~ = scale diag(e^gamma) Q and K~ = diag(e^{gamma_C - gamma}) K. Every
-//   operand the state pass needs is written as a ready MFMA fragment: 1 KB blocks in which lane l's
-//   16 bytes are exactly what lane l of the consuming wave loads, so each store and each load is one
-//   fully coalesced 1 KB wave access.
+//   (f16 MFMA), P~ = scale P, Q~ = scale diag(e^gamma) Q and K~ = diag(e^{gamma_C - gamma}) K (with
+//   several value heads per key head, q and k once per key head and the decays as per-token factors;
+//   see the records below). Every operand the state pass needs is written as a ready MFMA fragment:
+//   1 KB blocks in which lane l's 16 bytes are exactly what lane l of the consuming wave loads, so each
+//   store and each load is one fully coalesced 1 KB wave access.
 // Launch 2, state_pass_kernel (one workgroup per column slice x value head x sequence, chunks in order;
-//   wave w owns token tile w of U and O and the H row tiles w, w+4, ...):
-//   U = U' - W H  (wave w: tokens 16w..16w+15, H read as fragments from LDS)
-//   O^T = H^T Q~^T + U^T P~^T, H = e^{gamma_C} H + K~^T U  (U read back as fragments from LDS)
-//   Only H and U cross waves, through LDS; each wave loads its own fragments of the next chunk into
+//   eight waves in two roles, one of each on every SIMD; wave w works on token tile w & 3 and owns H
+//   row tile w):
+//   chain waves 0-3:  U = U' - W H for their token tile (H read as fragments from LDS)
+//   output waves 4-7: O^T = H^T Q~^T + U^T P~^T for their token tile
+//   every wave:       its row tile of H = e^{gamma_C} H + K~^T U (U read back as fragments from LDS)
+//   Only H and U cross waves, through LDS; each wave loads its own fragments of the next chunks into
 //   registers while the current chunk computes. The gated RMSNorm is fused when one workgroup owns all
 //   d_v columns of the head, otherwise norm_kernel finishes it from the saved partial sums.
 //

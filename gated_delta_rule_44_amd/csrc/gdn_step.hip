@@ -4,12 +4,12 @@
 // channels of key head kh (its q and k channels and the v channels of its R value heads), the q/k L2
 // norm, the gates, one delta-rule step per value head, the gated RMSNorm, and the state/tail stores.
 // Decode is T = 1 writing back to the pool row; verify writes each token's state and tail to its
-// checkpoint row and leaves the pool untouched. A batch-of-paths verify has P rows per sequence b,
-// every one starting from b's pool row (the "mtp/generate.py" page tiles the cache into one row per
-// candidate path); the P workgroups of one (sequence, key head) are n_k apart in the grid and read
-// the same state block, which the second and later ones find in the cache. Both run this one kernel, so checkpoint i is bitwise
+// checkpoint row and leaves the pool untouched. Both run this one kernel, so checkpoint i is bitwise
 // what i+1 decode calls produce (the multistate verify of the "mtp/generate.py" page claims the same
-// bit-identity against its per-token kernel).
+// bit-identity against its per-token kernel). A batch-of-paths verify has P rows per sequence b, every
+// one starting from b's pool row (that page tiles the cache into one row per candidate path); the P
+// workgroups of one (sequence, key head) are n_k apart in the grid and read the same state block,
+// which the second and later ones find in the cache.
 //
 // The step (H = S^T, [d_k][d_v] per value head, k and q L2-normalised):
 //   H <- e^g H;  u = beta (v - H^T k);  H <- H + k u^T;  o = scale H^T q
@@ -19,8 +19,9 @@
 // The state is HBM-streamed fp32, read and written exactly once per call. Each value head has its own
 // 256 threads (the workgroup is 256 R threads); a thread holds a 4-column x RPT-row block of its head's
 // H in registers; column partial sums are reduced across the row groups of a wave with lane shuffles
-// and across the head's waves in LDS. The register footprint is kept small enough for two workgroups
-// per CU, so that one workgroup's loads overlap another's arithmetic and stores. Keeping the q/k
+// and across the head's waves in LDS. The register footprint is kept small (three waves per SIMD at
+// d = 128), so that the waves of different workgroups overlap one's loads with another's arithmetic
+// and stores. Keeping the q/k
 // channels of a key head in one workgroup is what lets decode update the conv tail in place without a
 // race.
 #include "gdn_common.h"
