@@ -460,16 +460,22 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     char* rec = rec_ptr<D, SPLIT, SH>(p, b, h, c);
     const float gC = gam[C64 - 1];
 
-    // A (strictly lower, fp32), T's upper blocks cleared, this head's v channel-major, and the
+    // A (strictly lower, fp32), this head's v channel-major, and the
     // per-token decays e^{gamma_t}, e^{gamma_C - gamma_t} (each exponential taken once per head)
     if (tid < C64) {
       sEg[tid] = __expf(gam[tid]);
       sEd[tid] = __expf(gC - gam[tid]);
     }
-    for (int idx = tid; idx < C64 * C64; idx += NTH) {
-      const int i = idx >> 6, j = idx & 63;
-      sA[i * LF + j] = j < i ? bet[i] * __expf(gam[i] - gam[j]) * (kInvS16 * sKK[i * LT + j]) : 0.f;
-      if ((j >> 4) > (i >> 4)) sTf[i * LF + j] = 0.f;
+    // (only the strictly lower part is ever read: rows p and 63 - p share 16 threads, 63 entries a pair)
+    static_assert(NTH == 32 * 16 && C64 == 64, "row pairs of the A fill");
+    {
+      const int pr = tid >> 4, q = tid & 15;
+#pragma unroll
+      for (int e = q; e < C64 - 1; e += 16) {
+        const int i = e < pr ? pr : C64 - 1 - pr;
+        const int j = e < pr ? e : e - pr;
+        sA[i * LF + j] = bet[i] * __expf(gam[i] - gam[j]) * (kInvS16 * sKK[i * LT + j]);
+      }
     }
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {  // compile-time index into vv (a runtime one would go to scratch)
@@ -574,7 +580,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     }
     for (int idx = tid; idx < C64 * C64; idx += NTH) {
       const int i = idx >> 6, j = idx & 63;
-      const float tv = kS8 * sTf[i * LF + j];
+      const float tv = (j >> 4) > (i >> 4) ? 0.f : kS8 * sTf[i * LF + j];  // T's upper blocks are zero
       if (SPLIT) split_f16(tv, sT[i * LDT + j], sT[C64 * LDT + i * LDT + j]);
       else sT[i * LDT + j] = (_Float16)tv;
     }
