@@ -176,6 +176,7 @@ def _decode_inputs(dims, rng, B, T):
 
 
 @pytest.mark.parametrize("dims,B", [(NEXT, 8), (SMALL, 4), (LayerDims(n_k=2, n_v=8, d_k=64, d_v=64), 3),
+                                    (LayerDims(n_k=2, n_v=8, d_k=128, d_v=128), 5),
                                     (LayerDims(n_k=2, n_v=4, d_k=32, d_v=32, act=ACT_F32), 2)])
 def test_decode_step_vs_oracle(dims, B):
     _say(f"decode B={B} dims={dims}")
