@@ -98,6 +98,30 @@ def test_python_layer_rejects_cpu_tensors():
                        torch.zeros(1, 3, d.conv_dim, dtype=torch.bfloat16))
 
 
+def test_new_entry_points_reject_bad_arguments():
+    """State zero, the MFMA probe and the prefix cache check their arguments before any HIP call."""
+    lib = gdn.load_library()
+    d = _desc()
+    assert lib.gdn_state_zero(ctypes.byref(d), None, None, None, 1, None) == -1 and b"nothing" in lib.gdn_last_error()
+    p = ctypes.c_void_p(256)
+    assert lib.gdn_state_zero(ctypes.byref(d), p, None, None, 0, None) == -1 and b"n=0" in lib.gdn_last_error()
+    assert lib.gdn_state_zero(ctypes.byref(d), ctypes.c_void_p(260), None, None, 1, None) == -1
+    assert b"aligned" in lib.gdn_last_error()
+    assert lib.gdn_mfma_probe(None, 4, 4, None) == -1 and b"gdn_mfma_probe" in lib.gdn_last_error()
+    assert lib.gdn_mfma_probe(p, 0, 4, None) == -1
+    h = ctypes.c_void_p()
+    assert lib.gdn_pcache_create(4, 512, 16, 64, 0, 0, ctypes.byref(h)) == -1  # max_chunk must be positive
+    assert lib.gdn_pcache_create(4, 512, 16, 64, 256, 0, None) == -1
+    assert lib.gdn_pcache_create(4, 512, 16, 64, 256, 0, ctypes.byref(h)) == 0
+    info = (ctypes.c_int32 * 4)()
+    assert lib.gdn_pcache_row(h, None, 5, 5, 0, info, None, None, None) == -1   # ids NULL with n > 0
+    assert lib.gdn_pcache_row(h, None, 0, 0, 0, info, None, None, None) == 0    # an empty row: plain
+    st = (ctypes.c_int64 * len(gdn.PCACHE_STATS))()
+    assert lib.gdn_pcache_stats(h, st) == 0 and st[gdn.PCACHE_STATS.index("plain")] == 1
+    assert lib.gdn_pcache_stats(None, st) == -1 and lib.gdn_pcache_alive(h, 0, None) == 0
+    lib.gdn_pcache_destroy(h)
+
+
 def test_timing_session_errors():
     """Session misuse is rejected before any HIP call."""
     lib = gdn.load_library()
