@@ -1,6 +1,6 @@
 """Benchmark of the Gated DeltaNet layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|continuation|decode|verify|verify_paths|prefix_cache|spec_loop|copy|peaks]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|stack|continuation|decode|verify|verify_paths|prefix_cache|spec_loop|conv|copy|peaks]
 
 Headline (`value`): prefill tokens/s of one layer on one sequence of 4096 tokens, 16 key / 16 value
 heads, d_k = d_v = 128, bf16 activations, fp32 state, continued from a saved state (one step = one
@@ -24,6 +24,7 @@ The same run also measures, each as a sub-object of the one JSON line:
   verify_paths - the same with 4 candidate paths per sequence (tree verify), accept over paths, commit
   prefix_cache - 8 rows of 8192 tokens sharing 6144 through the prefix-state cache, against no cache
   spec_loop - the speculative-decoding loop (verify, accept, commit or replay) over 64 sequences
+  conv    - the standalone causal conv + SiLU over 8 x 8192 tokens of the stack layer's channels
   copy    - the O(1) state bridge: 256 records {fp32 state, conv tail} of one layer
   measured_peaks - the MFMA probe's dense f16 TFLOP/s and the copy leg's GB/s beside the published peaks
   cpu_baseline - the fp64 oracle on the host cores on the prefill workload
@@ -447,6 +448,34 @@ def bench_spec_loop(torch, gdn, args):
             **res}
 
 
+def bench_conv(torch, gdn, args):
+    """The standalone causal conv + SiLU (gdn_conv_chunk) over the stack layer's inputs: 8 x 8192 tokens
+    of 8192 bf16 channels, with the conv tail rolled forward. Algorithmic bytes: mixed read once, y
+    written once, tails read and written."""
+    from gdn_inputs import NEXT
+    from tests.gpu_helpers import desc_of
+    dims, B, L = NEXT, 8, 8192
+    d = desc_of(dims)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    C = dims.conv_dim
+    sets = [torch.empty(B, L, C, device="cuda").normal_(generator=g).bfloat16() for _ in range(2)]
+    w = torch.empty(C, 4, device="cuda").normal_(0, 0.5, generator=g).bfloat16()
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    tail = torch.zeros(B, 3, C, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(B, L, C, dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        gdn.conv_chunk(d, w, sets[i % 2], lens, tail, y)
+
+    ms, _ = Timer(torch, args.steps).run(step, args.steps, args.warmup)
+    nbytes = 2 * B * L * C * 2 + 2 * B * 3 * C * 2 + C * 4 * 2
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "8 x 8192 tokens x 8192 bf16 channels (16/32 heads, d=128)", "ms_per_call": ms,
+            "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "roofline": kernel_roofline("conv_8x8192", "conv", ms, nbytes=nbytes)}
+
+
 def bench_copy(torch, gdn, args):
     from gdn_inputs import NEXT
     from tests.gpu_helpers import desc_of
@@ -537,6 +566,8 @@ def main():
         line["prefix_cache"] = bench_prefix_cache(torch, gdn, args)
     if only in ("all", "spec_loop"):
         line["spec_loop"] = bench_spec_loop(torch, gdn, args)
+    if only in ("all", "conv"):
+        line["conv"] = bench_conv(torch, gdn, args)
     if only in ("all", "copy"):
         line["copy"] = bench_copy(torch, gdn, args)
     if only in ("all", "peaks"):

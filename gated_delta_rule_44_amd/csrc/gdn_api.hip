@@ -153,6 +153,8 @@ int gdn_conv_chunk(const gdn_desc* d, const void* conv_w, const void* mixed, con
   if (!aligned16(conv_w) || !aligned16(mixed) || !aligned16(conv_tail) || !aligned16(y))
     return fail(GDN_EINVAL, "gdn_conv_chunk: buffers must be 16-byte aligned");
   if (y == mixed || y == conv_tail) return fail(GDN_EINVAL, "gdn_conv_chunk: y aliases an input");
+  if ((conv_channels(d) + 1023) / 1024 * ((Lb + 63L) / 64) * B >= (1L << 31))
+    return fail(GDN_EINVAL, "gdn_conv_chunk: ceil(C/1024) * ceil(Lb/64) * B must stay below 2^31");
   gdn::ConvArgs p{conv_w, mixed, len, conv_tail, y, B, Lb, (int)conv_channels(d)};
   return hip_status(gdn::launch_conv(p, d->act_dtype, (hipStream_t)stream), "gdn_conv_chunk");
 }

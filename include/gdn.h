@@ -81,6 +81,7 @@ const char* gdn_version(void);
  *                             i.e. the last Kc real inputs, old rows kept when len[b] < Kc
  *   y         [B][Lb][C_ch]   y[t][c] = silu(sum_j conv_w[c][j] * xin[t+j][c]); rows >= len[b] are
  *                             computed like the others and carry no meaning
+ * Limits: ceil(C_ch / 1024) * ceil(Lb / 64) * B < 2^31 (GDN_EINVAL otherwise).
  * Must not alias: y with mixed or conv_tail.
  */
 int gdn_conv_chunk(const gdn_desc* desc, const void* conv_w, const void* mixed, const int32_t* len,

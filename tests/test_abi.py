@@ -53,6 +53,10 @@ def test_null_and_size_errors():
     assert b"NULL" in lib.gdn_last_error()
     p = ctypes.c_void_p(256)
     assert lib.gdn_conv_chunk(ctypes.byref(d), p, p, p, ctypes.c_void_p(512), ctypes.c_void_p(768), 0, 4, None) == -1
+    # the conv's flattened grid: ceil(C/1024) * ceil(Lb/64) * B workgroups must fit in 2^31
+    assert lib.gdn_conv_chunk(ctypes.byref(d), p, p, p, ctypes.c_void_p(512), ctypes.c_void_p(768), 1 << 16,
+                              1 << 28, None) == -1
+    assert b"2^31" in lib.gdn_last_error()
     assert lib.gdn_accept(None, None, 4, 4, None, None, None, None, None) == -1
     assert lib.gdn_accept_paths(p, p, 4, 2, 4, p, None, p, p, None, None) == -1
     assert b"NULL" in lib.gdn_last_error()

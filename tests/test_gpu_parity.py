@@ -143,7 +143,9 @@ def test_continuation_equals_single_pass():
 # ---------------------------------------------------------------------------------------------------
 # conv
 
-@pytest.mark.parametrize("dims,B,L,lens", [(TINY, 1, 64, [64]), (NEXT, 3, 70, [70, 2, 0]), (SMALL, 2, 33, [33, 17])])
+# the kernel walks 64-token spans in 8-token groups: 203 and 131 tokens end mid-group in a later span
+@pytest.mark.parametrize("dims,B,L,lens", [(TINY, 1, 64, [64]), (NEXT, 3, 70, [70, 2, 0]), (SMALL, 2, 33, [33, 17]),
+                                           (SMALL, 2, 203, [203, 130]), (NEXT, 3, 131, [131, 1, 64])])
 def test_conv_chunk(dims, B, L, lens):
     _say(f"conv B={B} L={L}")
     w, x, rng = make_layer(7, dims, B, L, lens)
