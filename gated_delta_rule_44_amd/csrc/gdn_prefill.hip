@@ -679,6 +679,399 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 }
 
 // -------------------------------------------------------------------------------------------------
+// chunk_prep for one value head per key head with bf16 activations: the same records as
+// chunk_prep_kernel, built in less than half its LDS, so that two workgroups share a CU and one's
+// memory waits and barriers overlap the other's work. k is staged only token-major (K~ and the W
+// operand gather their d-major fragments from it), the Gram products go from the accumulators straight
+// into P~ (record) and A (LDS), and the W and U' operands wait in registers while T is formed.
+template <typename ActT, int D>
+__global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
+  using RC = Rec<D, false, false>;
+  constexpr int NWV = 8;
+  constexpr int TPW = C64 / NWV;
+  constexpr int KD = D / 32, HM = D / 16;
+  constexpr int CPL = D / 64;                 // channels per lane in the conv stage (adjacent)
+  constexpr int LQ = D + 8, LT = C64 + 4, LF = C64 + 1, LDT = C64 + 8;
+  constexpr int SZ_TOK = C64 * LQ * 2;        // one token-major f16 tile
+  constexpr int SZ_AF = C64 * LF * 4;         // one fp32 64 x 64 tile
+  constexpr int SZ_RQ = cmax(2 * SZ_TOK, 2 * SZ_AF);                   // q hi|lo, then A | T (fp32)
+  constexpr int SZ_RK = cmax(2 * SZ_TOK, cmax(D * LT * 4, C64 * LDT * 2));  // k hi|lo, then v^T, then T (f16)
+  constexpr int OFF_RK = SZ_RQ, OFF_G = OFF_RK + SZ_RK;
+  constexpr int LDS = OFF_G + 4 * C64 * 4;
+  static_assert(D == 64 || D == 128, "channel layout");
+  static_assert(4 * 16 * 17 * 4 <= C64 * LDT * 2, "level products fit the T tile");
+  static_assert(2 * LDS <= 160 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  _Float16* sQh = (_Float16*)smem;
+  _Float16* sQl = sQh + C64 * LQ;
+  float* sA = (float*)smem;                    // after the Gram products
+  float* sTf = sA + C64 * LF;
+  _Float16* sKh = (_Float16*)(smem + OFF_RK);
+  _Float16* sKl = sKh + C64 * LQ;
+  float* sVt = (float*)(smem + OFF_RK);        // after K~ and the W operand are built
+  float* sX = (float*)(smem + OFF_RK);         // level products, after the v operand is built
+  _Float16* sT = (_Float16*)(smem + OFF_RK);   // after the levels
+  float* sGam = (float*)(smem + OFF_G);
+  float* sBet = sGam + C64;
+  float* sEg = sBet + C64;
+  float* sEd = sEg + C64;
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;  // key head = value head
+  const int t0 = c * C64;
+  const int len = p.len[b];
+  if (t0 >= len) return;  // all padding: the state pass stops before this chunk
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, r16 = lane & 15;
+  const int Lb = p.Lb, C = p.C, n_k = p.n_k;
+  const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
+  const ActT* tail = (const ActT*)p.tail + (long)b * 3 * C;
+  const ActT* cw = (const ActT*)p.conv_w;
+  char* rec = rec_ptr<D, false, false>(p, b, h, c);
+
+  // ---- 1. every global load first: gate inputs (lane = token), conv inputs and taps of q, k, v -----
+  typedef typename std::conditional<CPL == 2, typename Pair<ActT>::type, ActT>::type XRaw;
+  typedef typename Raw4<ActT>::type WRaw;
+  const int tg = t0 + lane;
+  const long gi = ((long)b * Lb + (tg < len ? tg : len - 1)) * p.n_v + h;
+  const ActT a_raw = ((const ActT*)p.a)[gi], b_raw = ((const ActT*)p.b)[gi];
+  XRaw xr[3][TPW + 3];
+  WRaw wr[3][CPL];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int gc = (j == 0 ? h : j == 1 ? n_k + h : 2 * n_k + h) * D + CPL * lane;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) wr[j][i] = Raw4<ActT>::load(cw + (gc + i) * 4);
+#pragma unroll
+    for (int i = 0; i < TPW + 3; ++i) {
+      const int t = t0 + TPW * w - 3 + i;
+      const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
+      if constexpr (CPL == 2) xr[j][i] = Pair<ActT>::load(src + gc);
+      else xr[j][i] = src[gc];
+    }
+  }
+
+  // ---- 2. gates (wave 0, lane = token): inclusive scan of g, and the two per-token decays ---------
+  if (w == 0) {
+    const float g0 = -__expf(p.A_log[h]) * softplus(to_f32(a_raw) + p.dt_bias[h]);
+    const float b0 = sigmoid(to_f32(b_raw));
+    float g = tg < len ? g0 : 0.f;
+    const float be = tg < len ? b0 : 0.f;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float o = __shfl_up(g, off, kWave);
+      if (lane >= off) g += o;
+    }
+    const float gC = __shfl(g, C64 - 1, kWave);
+    sGam[lane] = g;
+    sBet[lane] = be;
+    sEg[lane] = __expf(g);
+    sEd[lane] = __expf(gC - g);
+  }
+
+  // ---- 3. conv + SiLU (token TPW w + tt, channel CPL lane + i), L2 norms of q and k ---------------
+  auto conv = [&](int j, float (*y)[CPL]) {
+    float x[TPW + 3][CPL], wt[4][CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const float4 wf = Raw4<ActT>::widen(wr[j][i]);
+      wt[0][i] = wf.x; wt[1][i] = wf.y; wt[2][i] = wf.z; wt[3][i] = wf.w;
+    }
+#pragma unroll
+    for (int i = 0; i < TPW + 3; ++i) {
+      const bool in = t0 + TPW * w - 3 + i < Lb;
+      if constexpr (CPL == 2) {
+        const float2 v = Pair<ActT>::widen(xr[j][i]);
+        x[i][0] = in ? v.x : 0.f;
+        x[i][CPL - 1] = in ? v.y : 0.f;
+      } else {
+        x[i][0] = in ? to_f32(xr[j][i]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        y[tt][i] = silu(wt[0][i] * x[tt][i] + wt[1][i] * x[tt + 1][i] + wt[2][i] * x[tt + 2][i] + wt[3][i] * x[tt + 3][i]);
+  };
+  auto l2norm = [&](float (*y)[CPL]) {
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) ss += y[tt][j] * y[tt][j];
+      ss = wave_sum<kWave>(ss);
+      const float rn = rsqrt_fast(ss + p.l2_eps);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) y[tt][j] *= rn;
+    }
+  };
+  float qn[TPW][CPL], kn[TPW][CPL], vv[TPW][CPL];
+  conv(0, qn);
+  conv(1, kn);
+  conv(2, vv);
+  l2norm(qn);
+  l2norm(kn);
+  // token-major 2^8 q and 2^8 k (hi/lo)
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int o = (TPW * w + tt) * LQ + CPL * lane;
+    _Float16 qh[CPL], ql[CPL], kh_[CPL], kl[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      split_f16(kS8 * qn[tt][j], qh[j], ql[j]);
+      split_f16(kS8 * kn[tt][j], kh_[j], kl[j]);
+    }
+    if constexpr (CPL == 2) {
+      *(f16x2*)&sQh[o] = f16x2{qh[0], qh[CPL - 1]};
+      *(f16x2*)&sQl[o] = f16x2{ql[0], ql[CPL - 1]};
+      *(f16x2*)&sKh[o] = f16x2{kh_[0], kh_[CPL - 1]};
+      *(f16x2*)&sKl[o] = f16x2{kl[0], kl[CPL - 1]};
+    } else {
+      sQh[o] = qh[0]; sQl[o] = ql[0]; sKh[o] = kh_[0]; sKl[o] = kl[0];
+    }
+  }
+  lds_barrier();
+
+  // ---- 4. Gram products (split operands, three accumulators) --------------------------------------
+  // D[i][j] = X rows ra0 + i . Y rows rb0 + j over d; lane (g, c) gets i = 4 g + e, j = c
+  auto gram = [&](const _Float16* xh, const _Float16* xl, int ra0, const _Float16* yh, const _Float16* yl,
+                  int rb0) __attribute__((always_inline)) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+    f16x8 fah[KD], fal[KD], fbh[KD], fbl[KD];
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      const int ra = (ra0 + r16) * LQ + 32 * ks + 8 * g16, rb = (rb0 + r16) * LQ + 32 * ks + 8 * g16;
+      fah[ks] = ld16(xh + ra);
+      fal[ks] = ld16(xl + ra);
+      fbh[ks] = ld16(yh + rb);
+      fbl[ks] = ld16(yl + rb);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      a0 = mfma16(fal[ks], fbh[ks], a0);
+      a1 = mfma16(fah[ks], fbl[ks], a1);
+      a2 = mfma16(fah[ks], fbh[ks], a2);
+    }
+    return a2 + (a0 + a1);
+  };
+  // lower 16x16 tiles (mt, nt), nt <= mt, in row order
+  auto tile_mt = [](int tile) { return tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0; };
+
+  // Q~ (token tile q & 3, 32-block q >> 2 for q = w, w + 8, ...): 2^8 scale e^{gamma_t} q_t
+  constexpr int QPW = (4 * KD + NWV - 1) / NWV;
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int q = w + NWV * i;
+    if (q < 4 * KD) {
+      const int mt = q & 3, kk = q >> 2;
+      const int row = (16 * mt + r16) * LQ + 32 * kk;
+      const f16x8 qh = frag_row_h(sQh + row, g16), ql = frag_row_h(sQl + row, g16);
+      const float fq = p.scale * sEg[16 * mt + r16];
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qh[e] + (float)ql[e]);
+      f16x8 hi, lo;
+      split8(x, hi, lo);
+      put_frag(rec, RC::Q_HI + mt * KD + kk, lane, hi);
+      put_frag(rec, RC::Q_LO + mt * KD + kk, lane, lo);
+    }
+  }
+  // P~ (token tile w & 3, block w >> 2) from the K Q^T tiles of s tiles 2 kk and 2 kk + 1, whose
+  // accumulators hold exactly this lane's fragment slots: 2^8 scale e^{gamma_t - gamma_s} q_t.k_s, s <= t
+  {
+    const int mt = w & 3, kk = w >> 2;
+    f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pb = pa;
+    if (2 * kk <= mt) pa = gram(sKh, sKl, 32 * kk, sQh, sQl, 16 * mt);
+    if (2 * kk + 1 <= mt) pb = gram(sKh, sKl, 32 * kk + 16, sQh, sQl, 16 * mt);
+    const int t = 16 * mt + r16;
+    const float gt = sGam[t];
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = pa[e];
+      x[4 + e] = pb[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int s = 32 * kk + kslot(g16, e);
+      x[e] = s <= t ? p.scale * __expf(gt - sGam[s]) * (kInvS8 * x[e]) : 0.f;
+    }
+    f16x8 hi, lo;
+    split8(x, hi, lo);
+    put_frag(rec, RC::P_HI + mt * 2 + kk, lane, hi);
+    put_frag(rec, RC::P_LO + mt * 2 + kk, lane, lo);
+  }
+  // K K^T tiles, two for the waves without P~ tiles: waves 0-3 tiles 0-3, 4: 4-5, 5: 6-7, 6: 8, 7: 9
+  const int kt0 = w < 4 ? w : w == 4 ? 4 : w == 5 ? 6 : w + 2;
+  const bool two = w == 4 || w == 5;
+  f32x4 kka, kkb = {0.f, 0.f, 0.f, 0.f};
+  {
+    const int mt = tile_mt(kt0), nt = kt0 - mt * (mt + 1) / 2;
+    kka = gram(sKh, sKl, 16 * mt, sKh, sKl, 16 * nt);
+  }
+  if (two) {
+    const int mt = tile_mt(kt0 + 1), nt = kt0 + 1 - mt * (mt + 1) / 2;
+    kkb = gram(sKh, sKl, 16 * mt, sKh, sKl, 16 * nt);
+  }
+  lds_barrier();  // q is dead: A goes into its region
+
+  // ---- 5. A (strictly lower, fp32) from the accumulators; K~ and the W operand from token-major k ---
+  auto put_A = [&](int tile, f32x4 acc) __attribute__((always_inline)) {
+    const int mt = tile_mt(tile), nt = tile - mt * (mt + 1) / 2;
+    const int j = 16 * nt + r16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * mt + 4 * g16 + e;
+      if (j < i) sA[i * LF + j] = sBet[i] * __expf(sGam[i] - sGam[j]) * (kInvS16 * acc[e]);
+    }
+  };
+  put_A(kt0, kka);
+  if (two) put_A(kt0 + 1, kkb);
+  // 2^8 k[s][d] for d = 16 hm + r16 and the fragment slots s of this lane (hi + lo recombined)
+  auto k_col = [&](int hm, int kk, float (&x)[8]) __attribute__((always_inline)) {
+    const int d = 16 * hm + r16;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int s = 32 * kk + kslot(g16, e);
+      x[e] = (float)sKh[s * LQ + d] + (float)sKl[s * LQ + d];
+    }
+  };
+  // K~^T (row tile idx >> 1, block idx & 1): 2^8 e^{gamma_C - gamma_s} k_s
+  for (int idx = w; idx < 2 * HM; idx += NWV) {
+    const int hm = idx >> 1, kk = idx & 1;
+    float x[8];
+    k_col(hm, kk, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= sEd[32 * kk + kslot(g16, e)];
+    f16x8 hi, lo;
+    split8(x, hi, lo);
+    put_frag(rec, RC::K_HI + hm * 2 + kk, lane, hi);
+    put_frag(rec, RC::K_LO + hm * 2 + kk, lane, lo);
+  }
+  // the W operand of wave w (d tile w): 2^8 beta_s e^{gamma_s} k_s as f16
+  f16x8 kb[2];
+  if (w < HM) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float x[8];
+      k_col(w, ks, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int s = 32 * ks + kslot(g16, e);
+        kb[ks][e] = (_Float16)(sBet[s] * sEg[s] * x[e]);
+      }
+    }
+  }
+  lds_barrier();  // A is complete; k is dead: v^T goes into its region
+
+  // ---- 6. v channel-major; T's diagonal blocks by forward substitution (wave 0, one column per lane) --
+#pragma unroll
+  for (int j = 0; j < CPL; ++j)
+#pragma unroll
+    for (int q = 0; q < TPW / 4; ++q)
+      *(float4*)&sVt[(CPL * lane + j) * LT + TPW * w + 4 * q] =
+          make_float4(vv[4 * q][j], vv[4 * q + 1][j], vv[4 * q + 2][j], vv[4 * q + 3][j]);
+  if (w == 0) {
+    const int blk = lane >> 4, jj = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = i == jj ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s -= sA[(16 * blk + i) * LF + 16 * blk + m] * x[m];
+      x[i] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LF + 16 * blk + jj] = x[i];
+  }
+  lds_barrier();
+  // the U' operand of wave w (value tile w): 2^8 beta_s v_s, hi/lo
+  f16x8 vh[2], vl[2];
+  if (w < HM) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float x[8];
+      frag_row_f(sVt + (16 * w + r16) * LT + 32 * ks, g16, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= kS8 * sBet[32 * ks + kslot(g16, e)];
+      split8(x, vh[ks], vl[ks]);
+    }
+  }
+  lds_barrier();  // v^T is dead: the level products go into its region
+
+  // ---- 7. T's off-diagonal blocks by level (i - j = 1, 2, 3): T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj --
+  for (int lvl = 1; lvl < 4; ++lvl) {
+    if (w < 4 - lvl) {
+      float* sXw = sX + w * 16 * 17;
+      const int j = w, i = w + lvl;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k = j; k < i; ++k)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc = mfma_f32(sA[(16 * i + r16) * LF + 16 * k + 4 * ks + g16], sTf[(16 * k + 4 * ks + g16) * LF + 16 * j + r16], acc);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sXw[(4 * g16 + ii) * 17 + r16] = acc[ii];
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        y = mfma_f32(sTf[(16 * i + r16) * LF + 16 * i + 4 * ks + g16], sXw[(4 * ks + g16) * 17 + r16], y);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sTf[(16 * i + 4 * g16 + ii) * LF + 16 * j + r16] = -y[ii];
+    }
+    lds_barrier();
+  }
+  for (int idx = tid; idx < C64 * C64; idx += 64 * NWV) {
+    const int i = idx >> 6, j = idx & 63;
+    sT[i * LDT + j] = (_Float16)((j >> 4) > (i >> 4) ? 0.f : kS8 * sTf[i * LF + j]);  // upper blocks are zero
+  }
+  lds_barrier();
+
+  // ---- 8. W^T = (beta e^gamma K)^T T^T (d tile w) and U' = T (beta V) (value tile w) -------------
+  if (w < HM) {
+    f16x8 th[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) th[mt][ks] = frag_row_h(sT + (16 * mt + r16) * LDT + 32 * ks, g16);
+    {
+      // W^T tile (w, mt) = 2^16 W^T; lane (g, c) holds W[16 mt + c][16 w + 4 g + i], half (w & 1) of
+      // the fragment of block w >> 1
+      f32x4 acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(kb[ks], th[mt][ks], acc[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f16x4 hi, lo;
+        split4(acc[mt] * -kInvS16, hi, lo);
+        *(f16x4*)(rec + (RC::W_HI + mt * KD + (w >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (w & 1))) = hi;
+      }
+    }
+    {
+      // U' tile (mt, w) = (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
+      f32x4 a0[4], a1[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a0[mt] = a1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) a0[mt] = mfma16(th[mt][ks], vl[ks], a0[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) a1[mt] = mfma16(th[mt][ks], vh[ks], a1[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        *(f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)) = (a1[mt] + a0[mt]) * kInvS8;
+    }
+  }
+  if (tid == 0) *(float*)(rec + RC::kGc) = __expf(sGam[C64 - 1]);
+}
+
+// -------------------------------------------------------------------------------------------------
 // State pass: 8 waves, a slice of CS = 16 NT value columns of one head. Wave w works on token tile
 // w & 3 and owns H row tile w (when w < d_k/16). Waves 0-3 carry the chain: U = U' - W H for their
 // token tile. Waves 4-7 carry the output: O^T = H^T Q~^T + U^T P~^T for their token tile. Every wave
@@ -1195,7 +1588,10 @@ template <typename ActT, int D, int R, bool SPLIT, int NT>
 hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   constexpr int NSPLIT = D / (16 * NT);
   timing_before("chunk_prep", st);
-  hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+  if constexpr (R == 1 && !SPLIT && (D == 64 || D == 128))
+    hipLaunchKernelGGL((chunk_prep1_kernel<ActT, D>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
   timing_after(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
