@@ -679,14 +679,17 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 }
 
 // -------------------------------------------------------------------------------------------------
-// chunk_prep for one value head per key head with bf16 activations: the same records as
-// chunk_prep_kernel, built in less than half its LDS, so that two workgroups share a CU and one's
-// memory waits and barriers overlap the other's work. k is staged only token-major (K~ and the W
-// operand gather their d-major fragments from it), the Gram products go from the accumulators straight
-// into P~ (record) and A (LDS), and the W and U' operands wait in registers while T is formed.
-template <typename ActT, int D>
-__global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
-  using RC = Rec<D, false, false>;
+// chunk_prep with bf16 activations in less than half the LDS of chunk_prep_kernel (the same records),
+// so that two workgroups share a CU and one's memory waits and barriers overlap the other's work.
+// k is staged only token-major (K~, the key record and the W operands gather their d-major fragments
+// from it); the Gram accumulators stay in registers and become P~ (record) and A (LDS) per value head;
+// the W operands of every value head are built while k is staged, and the U' operand of a head waits
+// in registers while its T is formed.
+template <typename ActT, int D, int R>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void chunk_prep2_kernel(PrefillArgs p) {
+  constexpr bool SH = R > 1;
+  using RC = Rec<D, false, SH>;
+  using KR = KeyRec<D>;
   constexpr int NWV = 8;
   constexpr int TPW = C64 / NWV;
   constexpr int KD = D / 32, HM = D / 16;
@@ -697,7 +700,7 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
   constexpr int SZ_RQ = cmax(2 * SZ_TOK, 2 * SZ_AF);                   // q hi|lo, then A | T (fp32)
   constexpr int SZ_RK = cmax(2 * SZ_TOK, cmax(D * LT * 4, C64 * LDT * 2));  // k hi|lo, then v^T, then T (f16)
   constexpr int OFF_RK = SZ_RQ, OFF_G = OFF_RK + SZ_RK;
-  constexpr int LDS = OFF_G + 4 * C64 * 4;
+  constexpr int LDS = OFF_G + 4 * R * C64 * 4;
   static_assert(D == 64 || D == 128, "channel layout");
   static_assert(4 * 16 * 17 * 4 <= C64 * LDT * 2, "level products fit the T tile");
   static_assert(2 * LDS <= 160 * 1024, "two workgroups per CU");
@@ -712,11 +715,11 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
   float* sX = (float*)(smem + OFF_RK);         // level products, after the v operand is built
   _Float16* sT = (_Float16*)(smem + OFF_RK);   // after the levels
   float* sGam = (float*)(smem + OFF_G);
-  float* sBet = sGam + C64;
-  float* sEg = sBet + C64;
-  float* sEd = sEg + C64;
+  float* sBet = sGam + R * C64;               // per value head of the group: [r][token]
+  float* sEg = sBet + R * C64;
+  float* sEd = sEg + R * C64;
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;  // key head = value head
+  const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int t0 = c * C64;
   const int len = p.len[b];
   if (t0 >= len) return;  // all padding: the state pass stops before this chunk
@@ -727,19 +730,21 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
   const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
   const ActT* tail = (const ActT*)p.tail + (long)b * 3 * C;
   const ActT* cw = (const ActT*)p.conv_w;
-  char* rec = rec_ptr<D, false, false>(p, b, h, c);
 
-  // ---- 1. every global load first: gate inputs (lane = token), conv inputs and taps of q, k, v -----
+  // ---- 1. every global load first: gate inputs (lane = token), conv inputs and taps of q, k and the
+  // R value heads (wave w: rows TPW w - 3 .. TPW w + TPW - 1, lane: channels CPL lane + i) ---------
+  constexpr int NCV = 2 + R;
   typedef typename std::conditional<CPL == 2, typename Pair<ActT>::type, ActT>::type XRaw;
   typedef typename Raw4<ActT>::type WRaw;
+  const int hg = kh * R + (w < R ? w : 0);
   const int tg = t0 + lane;
-  const long gi = ((long)b * Lb + (tg < len ? tg : len - 1)) * p.n_v + h;
+  const long gi = ((long)b * Lb + (tg < len ? tg : len - 1)) * p.n_v + hg;
   const ActT a_raw = ((const ActT*)p.a)[gi], b_raw = ((const ActT*)p.b)[gi];
-  XRaw xr[3][TPW + 3];
-  WRaw wr[3][CPL];
+  XRaw xr[NCV][TPW + 3];
+  WRaw wr[NCV][CPL];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int gc = (j == 0 ? h : j == 1 ? n_k + h : 2 * n_k + h) * D + CPL * lane;
+  for (int j = 0; j < NCV; ++j) {
+    const int gc = (j == 0 ? kh : j == 1 ? n_k + kh : 2 * n_k + kh * R + j - 2) * D + CPL * lane;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) wr[j][i] = Raw4<ActT>::load(cw + (gc + i) * 4);
 #pragma unroll
@@ -751,9 +756,9 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
     }
   }
 
-  // ---- 2. gates (wave 0, lane = token): inclusive scan of g, and the two per-token decays ---------
-  if (w == 0) {
-    const float g0 = -__expf(p.A_log[h]) * softplus(to_f32(a_raw) + p.dt_bias[h]);
+  // ---- 2. gates of value head r (wave r, lane = token): inclusive scan of g, the per-token decays ---
+  if (w < R) {
+    const float g0 = -__expf(p.A_log[hg]) * softplus(to_f32(a_raw) + p.dt_bias[hg]);
     const float b0 = sigmoid(to_f32(b_raw));
     float g = tg < len ? g0 : 0.f;
     const float be = tg < len ? b0 : 0.f;
@@ -763,10 +768,10 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
       if (lane >= off) g += o;
     }
     const float gC = __shfl(g, C64 - 1, kWave);
-    sGam[lane] = g;
-    sBet[lane] = be;
-    sEg[lane] = __expf(g);
-    sEd[lane] = __expf(gC - g);
+    sGam[w * C64 + lane] = g;
+    sBet[w * C64 + lane] = be;
+    sEg[w * C64 + lane] = __expf(g);
+    sEd[w * C64 + lane] = __expf(gC - g);
   }
 
   // ---- 3. conv + SiLU (token TPW w + tt, channel CPL lane + i), L2 norms of q and k ---------------
@@ -806,10 +811,11 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
       for (int j = 0; j < CPL; ++j) y[tt][j] *= rn;
     }
   };
-  float qn[TPW][CPL], kn[TPW][CPL], vv[TPW][CPL];
+  float qn[TPW][CPL], kn[TPW][CPL], vv[R][TPW][CPL];
   conv(0, qn);
   conv(1, kn);
-  conv(2, vv);
+#pragma unroll
+  for (int r = 0; r < R; ++r) conv(2 + r, vv[r]);
   l2norm(qn);
   l2norm(kn);
   // token-major 2^8 q and 2^8 k (hi/lo)
@@ -838,28 +844,24 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
   auto gram = [&](const _Float16* xh, const _Float16* xl, int ra0, const _Float16* yh, const _Float16* yl,
                   int rb0) __attribute__((always_inline)) {
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
-    f16x8 fah[KD], fal[KD], fbh[KD], fbl[KD];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) {
+    for (int ks = 0; ks < KD; ++ks) {  // operands one 32-block at a time (registers are the limit here)
       const int ra = (ra0 + r16) * LQ + 32 * ks + 8 * g16, rb = (rb0 + r16) * LQ + 32 * ks + 8 * g16;
-      fah[ks] = ld16(xh + ra);
-      fal[ks] = ld16(xl + ra);
-      fbh[ks] = ld16(yh + rb);
-      fbl[ks] = ld16(yl + rb);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KD; ++ks) {
-      a0 = mfma16(fal[ks], fbh[ks], a0);
-      a1 = mfma16(fah[ks], fbl[ks], a1);
-      a2 = mfma16(fah[ks], fbh[ks], a2);
+      const f16x8 fah = ld16(xh + ra), fal = ld16(xl + ra), fbh = ld16(yh + rb), fbl = ld16(yl + rb);
+      a0 = mfma16(fal, fbh, a0);
+      a1 = mfma16(fah, fbl, a1);
+      a2 = mfma16(fah, fbh, a2);
     }
     return a2 + (a0 + a1);
   };
   // lower 16x16 tiles (mt, nt), nt <= mt, in row order
   auto tile_mt = [](int tile) { return tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0; };
 
-  // Q~ (token tile q & 3, 32-block q >> 2 for q = w, w + 8, ...): 2^8 scale e^{gamma_t} q_t
+  // q: with one value head, Q~ = 2^8 scale e^{gamma_t} q_t into the value record; with several, 2^8 q
+  // into the key record (fragment (token tile q & 3, 32-block q >> 2) for q = w, w + 8, ...)
   constexpr int QPW = (4 * KD + NWV - 1) / NWV;
+  char* krec = SH ? key_ptr<D>(p, b, kh, c) : nullptr;
+  char* rec0 = rec_ptr<D, false, SH>(p, b, kh * R, c);
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
     const int q = w + NWV * i;
@@ -867,42 +869,28 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
       const int mt = q & 3, kk = q >> 2;
       const int row = (16 * mt + r16) * LQ + 32 * kk;
       const f16x8 qh = frag_row_h(sQh + row, g16), ql = frag_row_h(sQl + row, g16);
-      const float fq = p.scale * sEg[16 * mt + r16];
-      float x[8];
+      if constexpr (SH) {
+        put_frag(krec, KR::Q_HI + mt * KD + kk, lane, qh);
+        put_frag(krec, KR::Q_LO + mt * KD + kk, lane, ql);
+      } else {
+        const float fq = p.scale * sEg[16 * mt + r16];
+        float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qh[e] + (float)ql[e]);
-      f16x8 hi, lo;
-      split8(x, hi, lo);
-      put_frag(rec, RC::Q_HI + mt * KD + kk, lane, hi);
-      put_frag(rec, RC::Q_LO + mt * KD + kk, lane, lo);
+        for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qh[e] + (float)ql[e]);
+        f16x8 hi, lo;
+        split8(x, hi, lo);
+        put_frag(rec0, RC::Q_HI + mt * KD + kk, lane, hi);
+        put_frag(rec0, RC::Q_LO + mt * KD + kk, lane, lo);
+      }
     }
   }
-  // P~ (token tile w & 3, block w >> 2) from the K Q^T tiles of s tiles 2 kk and 2 kk + 1, whose
-  // accumulators hold exactly this lane's fragment slots: 2^8 scale e^{gamma_t - gamma_s} q_t.k_s, s <= t
-  {
-    const int mt = w & 3, kk = w >> 2;
-    f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pb = pa;
-    if (2 * kk <= mt) pa = gram(sKh, sKl, 32 * kk, sQh, sQl, 16 * mt);
-    if (2 * kk + 1 <= mt) pb = gram(sKh, sKl, 32 * kk + 16, sQh, sQl, 16 * mt);
-    const int t = 16 * mt + r16;
-    const float gt = sGam[t];
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = pa[e];
-      x[4 + e] = pb[e];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int s = 32 * kk + kslot(g16, e);
-      x[e] = s <= t ? p.scale * __expf(gt - sGam[s]) * (kInvS8 * x[e]) : 0.f;
-    }
-    f16x8 hi, lo;
-    split8(x, hi, lo);
-    put_frag(rec, RC::P_HI + mt * 2 + kk, lane, hi);
-    put_frag(rec, RC::P_LO + mt * 2 + kk, lane, lo);
-  }
-  // K K^T tiles, two for the waves without P~ tiles: waves 0-3 tiles 0-3, 4: 4-5, 5: 6-7, 6: 8, 7: 9
+  // K Q^T tiles of s tiles 2 kk and 2 kk + 1 for the P~ fragment (token tile w & 3, block w >> 2):
+  // lane (g, c) of the two accumulators holds exactly that fragment's slots
+  const int pmt = w & 3, pkk = w >> 2;
+  f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pb = pa;
+  if (2 * pkk <= pmt) pa = gram(sKh, sKl, 32 * pkk, sQh, sQl, 16 * pmt);
+  if (2 * pkk + 1 <= pmt) pb = gram(sKh, sKl, 32 * pkk + 16, sQh, sQl, 16 * pmt);
+  // K K^T tiles, two for the waves without K Q^T tiles: waves 0-3 tiles 0-3, 4: 4-5, 5: 6-7, 6: 8, 7: 9
   const int kt0 = w < 4 ? w : w == 4 ? 4 : w == 5 ? 6 : w + 2;
   const bool two = w == 4 || w == 5;
   f32x4 kka, kkb = {0.f, 0.f, 0.f, 0.f};
@@ -914,161 +902,204 @@ __global__ __launch_bounds__(512, 2) void chunk_prep1_kernel(PrefillArgs p) {
     const int mt = tile_mt(kt0 + 1), nt = kt0 + 1 - mt * (mt + 1) / 2;
     kkb = gram(sKh, sKl, 16 * mt, sKh, sKl, 16 * nt);
   }
-  lds_barrier();  // q is dead: A goes into its region
+  lds_barrier();  // q is dead
 
-  // ---- 5. A (strictly lower, fp32) from the accumulators; K~ and the W operand from token-major k ---
-  auto put_A = [&](int tile, f32x4 acc) __attribute__((always_inline)) {
-    const int mt = tile_mt(tile), nt = tile - mt * (mt + 1) / 2;
-    const int j = 16 * nt + r16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * mt + 4 * g16 + e;
-      if (j < i) sA[i * LF + j] = sBet[i] * __expf(sGam[i] - sGam[j]) * (kInvS16 * acc[e]);
-    }
-  };
-  put_A(kt0, kka);
-  if (two) put_A(kt0 + 1, kkb);
-  // 2^8 k[s][d] for d = 16 hm + r16 and the fragment slots s of this lane (hi + lo recombined)
-  auto k_col = [&](int hm, int kk, float (&x)[8]) __attribute__((always_inline)) {
+  // ---- 5. k^T fragments from token-major k: K~ (one value head) or the key record's k; W operands --
+  // slots s of this lane for d = 16 hm + r16, hi and lo as staged
+  auto k_col = [&](int hm, int kk, f16x8& hi, f16x8& lo) __attribute__((always_inline)) {
     const int d = 16 * hm + r16;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int s = 32 * kk + kslot(g16, e);
-      x[e] = (float)sKh[s * LQ + d] + (float)sKl[s * LQ + d];
+      hi[e] = sKh[s * LQ + d];
+      lo[e] = sKl[s * LQ + d];
     }
   };
-  // K~^T (row tile idx >> 1, block idx & 1): 2^8 e^{gamma_C - gamma_s} k_s
   for (int idx = w; idx < 2 * HM; idx += NWV) {
     const int hm = idx >> 1, kk = idx & 1;
-    float x[8];
-    k_col(hm, kk, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= sEd[32 * kk + kslot(g16, e)];
     f16x8 hi, lo;
-    split8(x, hi, lo);
-    put_frag(rec, RC::K_HI + hm * 2 + kk, lane, hi);
-    put_frag(rec, RC::K_LO + hm * 2 + kk, lane, lo);
+    k_col(hm, kk, hi, lo);
+    if constexpr (SH) {
+      put_frag(krec, KR::K_HI + hm * 2 + kk, lane, hi);
+      put_frag(krec, KR::K_LO + hm * 2 + kk, lane, lo);
+    } else {  // K~^T: 2^8 e^{gamma_C - gamma_s} k_s
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = sEd[32 * kk + kslot(g16, e)] * ((float)hi[e] + (float)lo[e]);
+      split8(x, hi, lo);
+      put_frag(rec0, RC::K_HI + hm * 2 + kk, lane, hi);
+      put_frag(rec0, RC::K_LO + hm * 2 + kk, lane, lo);
+    }
   }
-  // the W operand of wave w (d tile w): 2^8 beta_s e^{gamma_s} k_s as f16
-  f16x8 kb[2];
+  // the W operand of wave w (d tile w) for every value head: 2^8 beta_s e^{gamma_s} k_s as f16
+  f16x8 kb[R][2];
   if (w < HM) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      f16x8 hi, lo;
+      k_col(w, ks, hi, lo);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int s = r * C64 + 32 * ks + kslot(g16, e);
+          kb[r][ks][e] = (_Float16)(sBet[s] * sEg[s] * ((float)hi[e] + (float)lo[e]));
+        }
+    }
+  }
+  lds_barrier();  // k is dead
+
+  // ---- 6. per value head of the group ------------------------------------------------------------
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float* gam = sGam + r * C64;
+    const float* bet = sBet + r * C64;
+    char* rec = rec_ptr<D, false, SH>(p, b, kh * R + r, c);
+    // P~ (token tile pmt, block pkk): 2^8 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
+    {
+      const int t = 16 * pmt + r16;
+      const float gt = gam[t];
       float x[8];
-      k_col(w, ks, x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = pa[e];
+        x[4 + e] = pb[e];
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int s = 32 * ks + kslot(g16, e);
-        kb[ks][e] = (_Float16)(sBet[s] * sEg[s] * x[e]);
+        const int s = 32 * pkk + kslot(g16, e);
+        x[e] = s <= t ? p.scale * __expf(gt - gam[s]) * (kInvS8 * x[e]) : 0.f;
+      }
+      f16x8 hi, lo;
+      split8(x, hi, lo);
+      put_frag(rec, RC::P_HI + pmt * 2 + pkk, lane, hi);
+      put_frag(rec, RC::P_LO + pmt * 2 + pkk, lane, lo);
+    }
+    // A (strictly lower, fp32) from the K K^T accumulators, into the q region
+    auto put_A = [&](int tile, f32x4 acc) __attribute__((always_inline)) {
+      const int mt = tile_mt(tile), nt = tile - mt * (mt + 1) / 2;
+      const int j = 16 * nt + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * mt + 4 * g16 + e;
+        if (j < i) sA[i * LF + j] = bet[i] * __expf(gam[i] - gam[j]) * (kInvS16 * acc[e]);
+      }
+    };
+    put_A(kt0, kka);
+    if (two) put_A(kt0 + 1, kkb);
+    // with a key record: the per-token decays the state pass applies
+    if (SH && tid < C64) {
+      *(float*)(rec + RC::kEg + 4 * tid) = p.scale * sEg[r * C64 + tid];
+      *(float*)(rec + RC::kEd + 4 * tid) = sEd[r * C64 + tid];
+    }
+    // v of this head channel-major, into the k region
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+      for (int q = 0; q < TPW / 4; ++q)
+        *(float4*)&sVt[(CPL * lane + j) * LT + TPW * w + 4 * q] =
+            make_float4(vv[r][4 * q][j], vv[r][4 * q + 1][j], vv[r][4 * q + 2][j], vv[r][4 * q + 3][j]);
+    lds_barrier();
+
+    // T's diagonal blocks by forward substitution (wave 0, one column per lane); the U' operand of
+    // wave w (value tile w): 2^8 beta_s v_s, hi/lo
+    if (w == 0) {
+      const int blk = lane >> 4, jj = lane & 15;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = i == jj ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) s -= sA[(16 * blk + i) * LF + 16 * blk + m] * x[m];
+        x[i] = s;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LF + 16 * blk + jj] = x[i];
+    }
+    f16x8 vh[2], vl[2];
+    if (w < HM) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
+        frag_row_f(sVt + (16 * w + r16) * LT + 32 * ks, g16, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= kS8 * bet[32 * ks + kslot(g16, e)];
+        split8(x, vh[ks], vl[ks]);
       }
     }
-  }
-  lds_barrier();  // A is complete; k is dead: v^T goes into its region
+    lds_barrier();  // v^T is dead: the level products go into its region
 
-  // ---- 6. v channel-major; T's diagonal blocks by forward substitution (wave 0, one column per lane) --
+    // T's off-diagonal blocks by level (i - j = 1, 2, 3): T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+    for (int lvl = 1; lvl < 4; ++lvl) {
+      if (w < 4 - lvl) {
+        float* sXw = sX + w * 16 * 17;
+        const int j = w, i = w + lvl;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k = j; k < i; ++k)
 #pragma unroll
-  for (int j = 0; j < CPL; ++j)
+          for (int ks = 0; ks < 4; ++ks)
+            acc = mfma_f32(sA[(16 * i + r16) * LF + 16 * k + 4 * ks + g16], sTf[(16 * k + 4 * ks + g16) * LF + 16 * j + r16], acc);
 #pragma unroll
-    for (int q = 0; q < TPW / 4; ++q)
-      *(float4*)&sVt[(CPL * lane + j) * LT + TPW * w + 4 * q] =
-          make_float4(vv[4 * q][j], vv[4 * q + 1][j], vv[4 * q + 2][j], vv[4 * q + 3][j]);
-  if (w == 0) {
-    const int blk = lane >> 4, jj = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = i == jj ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) s -= sA[(16 * blk + i) * LF + 16 * blk + m] * x[m];
-      x[i] = s;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LF + 16 * blk + jj] = x[i];
-  }
-  lds_barrier();
-  // the U' operand of wave w (value tile w): 2^8 beta_s v_s, hi/lo
-  f16x8 vh[2], vl[2];
-  if (w < HM) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      float x[8];
-      frag_row_f(sVt + (16 * w + r16) * LT + 32 * ks, g16, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= kS8 * sBet[32 * ks + kslot(g16, e)];
-      split8(x, vh[ks], vl[ks]);
-    }
-  }
-  lds_barrier();  // v^T is dead: the level products go into its region
-
-  // ---- 7. T's off-diagonal blocks by level (i - j = 1, 2, 3): T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj --
-  for (int lvl = 1; lvl < 4; ++lvl) {
-    if (w < 4 - lvl) {
-      float* sXw = sX + w * 16 * 17;
-      const int j = w, i = w + lvl;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k = j; k < i; ++k)
+        for (int ii = 0; ii < 4; ++ii) sXw[(4 * g16 + ii) * 17 + r16] = acc[ii];
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          acc = mfma_f32(sA[(16 * i + r16) * LF + 16 * k + 4 * ks + g16], sTf[(16 * k + 4 * ks + g16) * LF + 16 * j + r16], acc);
+          y = mfma_f32(sTf[(16 * i + r16) * LF + 16 * i + 4 * ks + g16], sXw[(4 * ks + g16) * 17 + r16], y);
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sXw[(4 * g16 + ii) * 17 + r16] = acc[ii];
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        y = mfma_f32(sTf[(16 * i + r16) * LF + 16 * i + 4 * ks + g16], sXw[(4 * ks + g16) * 17 + r16], y);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) sTf[(16 * i + 4 * g16 + ii) * LF + 16 * j + r16] = -y[ii];
+        for (int ii = 0; ii < 4; ++ii) sTf[(16 * i + 4 * g16 + ii) * LF + 16 * j + r16] = -y[ii];
+      }
+      lds_barrier();
+    }
+    for (int idx = tid; idx < C64 * C64; idx += 64 * NWV) {
+      const int i = idx >> 6, j = idx & 63;
+      sT[i * LDT + j] = (_Float16)((j >> 4) > (i >> 4) ? 0.f : kS8 * sTf[i * LF + j]);  // upper blocks are zero
     }
     lds_barrier();
-  }
-  for (int idx = tid; idx < C64 * C64; idx += 64 * NWV) {
-    const int i = idx >> 6, j = idx & 63;
-    sT[i * LDT + j] = (_Float16)((j >> 4) > (i >> 4) ? 0.f : kS8 * sTf[i * LF + j]);  // upper blocks are zero
-  }
-  lds_barrier();
 
-  // ---- 8. W^T = (beta e^gamma K)^T T^T (d tile w) and U' = T (beta V) (value tile w) -------------
-  if (w < HM) {
-    f16x8 th[4][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) th[mt][ks] = frag_row_h(sT + (16 * mt + r16) * LDT + 32 * ks, g16);
-    {
-      // W^T tile (w, mt) = 2^16 W^T; lane (g, c) holds W[16 mt + c][16 w + 4 g + i], half (w & 1) of
-      // the fragment of block w >> 1
-      f32x4 acc[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // W^T = (beta e^gamma K)^T T^T (d tile w) and U' = T (beta V) (value tile w)
+    if (w < HM) {
+      f16x8 th[4][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(kb[ks], th[mt][ks], acc[mt]);
+        for (int mt = 0; mt < 4; ++mt) th[mt][ks] = frag_row_h(sT + (16 * mt + r16) * LDT + 32 * ks, g16);
+      {
+        // W^T tile (w, mt) = 2^16 W^T; lane (g, c) holds W[16 mt + c][16 w + 4 g + i], half (w & 1)
+        // of the fragment of block w >> 1
+        f32x4 acc[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f16x4 hi, lo;
-        split4(acc[mt] * -kInvS16, hi, lo);
-        *(f16x4*)(rec + (RC::W_HI + mt * KD + (w >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (w & 1))) = hi;
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(kb[r][ks], th[mt][ks], acc[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f16x4 hi, lo;
+          split4(acc[mt] * -kInvS16, hi, lo);
+          *(f16x4*)(rec + (RC::W_HI + mt * KD + (w >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (w & 1))) = hi;
+        }
+      }
+      {
+        // U' tile (mt, w) = (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
+        f32x4 a0[4], a1[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) a0[mt] = a1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) a0[mt] = mfma16(th[mt][ks], vl[ks], a0[mt]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) a1[mt] = mfma16(th[mt][ks], vh[ks], a1[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          *(f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)) = (a1[mt] + a0[mt]) * kInvS8;
       }
     }
-    {
-      // U' tile (mt, w) = (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
-      f32x4 a0[4], a1[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a0[mt] = a1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) a0[mt] = mfma16(th[mt][ks], vl[ks], a0[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) a1[mt] = mfma16(th[mt][ks], vh[ks], a1[mt]);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        *(f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)) = (a1[mt] + a0[mt]) * kInvS8;
-    }
+    if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gam[C64 - 1]);
+    if (r + 1 < R) lds_barrier();  // T of this head is read; A, T and v of the next head overwrite it
   }
-  if (tid == 0) *(float*)(rec + RC::kGc) = __expf(sGam[C64 - 1]);
 }
 
 // -------------------------------------------------------------------------------------------------
@@ -1588,8 +1619,8 @@ template <typename ActT, int D, int R, bool SPLIT, int NT>
 hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   constexpr int NSPLIT = D / (16 * NT);
   timing_before("chunk_prep", st);
-  if constexpr (R == 1 && !SPLIT && (D == 64 || D == 128))
-    hipLaunchKernelGGL((chunk_prep1_kernel<ActT, D>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+  if constexpr (R <= 2 && !SPLIT && (D == 64 || D == 128))
+    hipLaunchKernelGGL((chunk_prep2_kernel<ActT, D, R>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
   else
     hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
   timing_after(st);
