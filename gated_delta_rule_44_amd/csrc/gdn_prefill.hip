@@ -890,6 +890,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pb = pa;
   if (2 * pkk <= pmt) pa = gram(sKh, sKl, 32 * pkk, sQh, sQl, 16 * pmt);
   if (2 * pkk + 1 <= pmt) pb = gram(sKh, sKl, 32 * pkk + 16, sQh, sQl, 16 * pmt);
+  // P~ of every value head: 2^8 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float* gam = sGam + r * C64;
+    const int t = 16 * pmt + r16;
+    const float gt = gam[t];
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = pa[e];
+      x[4 + e] = pb[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int s = 32 * pkk + kslot(g16, e);
+      x[e] = s <= t ? p.scale * __expf(gt - gam[s]) * (kInvS8 * x[e]) : 0.f;
+    }
+    f16x8 hi, lo;
+    split8(x, hi, lo);
+    char* rec = rec_ptr<D, false, SH>(p, b, kh * R + r, c);
+    put_frag(rec, RC::P_HI + pmt * 2 + pkk, lane, hi);
+    put_frag(rec, RC::P_LO + pmt * 2 + pkk, lane, lo);
+  }
   // K K^T tiles, two for the waves without K Q^T tiles: waves 0-3 tiles 0-3, 4: 4-5, 5: 6-7, 6: 8, 7: 9
   const int kt0 = w < 4 ? w : w == 4 ? 4 : w == 5 ? 6 : w + 2;
   const bool two = w == 4 || w == 5;
@@ -955,26 +978,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const float* gam = sGam + r * C64;
     const float* bet = sBet + r * C64;
     char* rec = rec_ptr<D, false, SH>(p, b, kh * R + r, c);
-    // P~ (token tile pmt, block pkk): 2^8 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
-    {
-      const int t = 16 * pmt + r16;
-      const float gt = gam[t];
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = pa[e];
-        x[4 + e] = pb[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int s = 32 * pkk + kslot(g16, e);
-        x[e] = s <= t ? p.scale * __expf(gt - gam[s]) * (kInvS8 * x[e]) : 0.f;
-      }
-      f16x8 hi, lo;
-      split8(x, hi, lo);
-      put_frag(rec, RC::P_HI + pmt * 2 + pkk, lane, hi);
-      put_frag(rec, RC::P_LO + pmt * 2 + pkk, lane, lo);
-    }
     // A (strictly lower, fp32) from the K K^T accumulators, into the q region
     auto put_A = [&](int tile, f32x4 acc) __attribute__((always_inline)) {
       const int mt = tile_mt(tile), nt = tile - mt * (mt + 1) / 2;
@@ -1056,45 +1059,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     lds_barrier();
 
-    // W^T = (beta e^gamma K)^T T^T (d tile w) and U' = T (beta V) (value tile w)
+    // W^T = (beta e^gamma K)^T T^T (d tile w) and U' = T (beta V) (value tile w), one token tile mt at
+    // a time (the operands of the next value head are live here too)
     if (w < HM) {
-      f16x8 th[4][2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int mt = 0; mt < 4; ++mt) {
+        f16x8 th[2];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) th[mt][ks] = frag_row_h(sT + (16 * mt + r16) * LDT + 32 * ks, g16);
-      {
+        for (int ks = 0; ks < 2; ++ks) th[ks] = frag_row_h(sT + (16 * mt + r16) * LDT + 32 * ks, g16);
         // W^T tile (w, mt) = 2^16 W^T; lane (g, c) holds W[16 mt + c][16 w + 4 g + i], half (w & 1)
         // of the fragment of block w >> 1
-        f32x4 acc[4];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(kb[r][ks], th[mt][ks], acc[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          f16x4 hi, lo;
-          split4(acc[mt] * -kInvS16, hi, lo);
-          *(f16x4*)(rec + (RC::W_HI + mt * KD + (w >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (w & 1))) = hi;
-        }
-      }
-      {
+        for (int ks = 0; ks < 2; ++ks) acc = mfma16(kb[r][ks], th[ks], acc);
+        f16x4 hi, lo;
+        split4(acc * -kInvS16, hi, lo);
+        *(f16x4*)(rec + (RC::W_HI + mt * KD + (w >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (w & 1))) = hi;
         // U' tile (mt, w) = (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
-        f32x4 a0[4], a1[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) a0[mt] = a1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) a0[mt] = mfma16(th[mt][ks], vl[ks], a0[mt]);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) a1[mt] = mfma16(th[mt][ks], vh[ks], a1[mt]);
+          a0 = mfma16(th[ks], vl[ks], a0);
+          a1 = mfma16(th[ks], vh[ks], a1);
         }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          *(f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)) = (a1[mt] + a0[mt]) * kInvS8;
+        *(f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)) = (a1 + a0) * kInvS8;
       }
     }
     if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gam[C64 - 1]);
