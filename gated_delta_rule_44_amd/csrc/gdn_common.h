@@ -25,12 +25,17 @@ template <typename T>
 __device__ __forceinline__ T from_f32(float x);
 template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// fp32 -> bf16 rounds to nearest even with NaNs kept quiet: gfx950's v_cvt_pk_bf16_f32, one instruction
+// for a pair (the integer-rounding form costs a dozen instructions and a branch per value)
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return bf16_t{(uint16_t)((u >> 16) | 0x40)};
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t{(uint16_t)(u >> 16)};
+  return bf16_t{__builtin_bit_cast(uint16_t, (__bf16)x)};
+}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// bf16(a) in the low half, bf16(b) in the high half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // ---- scalar maths (fp32) --------------------------------------------------------------------------

@@ -39,8 +39,8 @@ struct Vec4<bf16_t> {
   }
   static __device__ __forceinline__ void store(bf16_t* p, float4 v) {
     uint2 u;
-    u.x = (uint32_t)from_f32<bf16_t>(v.x).bits | ((uint32_t)from_f32<bf16_t>(v.y).bits << 16);
-    u.y = (uint32_t)from_f32<bf16_t>(v.z).bits | ((uint32_t)from_f32<bf16_t>(v.w).bits << 16);
+    u.x = pack_bf16x2(v.x, v.y);
+    u.y = pack_bf16x2(v.z, v.w);
     *(uint2*)p = u;
   }
 };
