@@ -65,9 +65,12 @@ struct PrefillArgs {
   float* state;         // [B][n_v][D][D] in/out
   void* out;            // [B][Lb][n_v*D]
   void* ws;             // workspace: value records, key records (n_v > n_k), then (split heads only)
-                        // unnormalised o and partial sums
-  long key_off, oraw_off, ss_off;  // byte offsets inside ws: key records, unnormalised o, partial sums
+                        // the partial sums of squares of every (sequence, head, token) row, one per
+                        // slice, and, when a norm pass finishes the rows, the unnormalised o
+  long key_off, ss_off, oraw_off;  // byte offsets inside ws: key records, partial sums, unnormalised o
   int B, Lb, n_k, n_v, C, n_chunks;
+  int nsplit;           // column slices per head in the state pass (1: the whole head)
+  int exchange;         // split heads: 1 = the slices exchange row sums, 0 = a norm pass finishes
   float scale, l2_eps, rms_eps;
 };
 // fp32 activations run every MFMA operand as a hi/lo pair (split_all) and are built for d <= 64

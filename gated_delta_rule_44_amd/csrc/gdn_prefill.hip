@@ -1,5 +1,4 @@
-// Chunked prefill of the gated delta rule (gfx950): two launches, plus a norm pass when one value
-// head's columns are split over several workgroups.
+// Chunked prefill of the gated delta rule (gfx950): two launches.
 //
 // Chunk form (chunk of C = 64 tokens, entering state H0 = S0^T, gamma_r = sum_{i<=r} g_i inside the
 // chunk; from the recurrence S_t = e^{g_t} S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T by the
@@ -25,8 +24,12 @@
 //   output waves 4-7: O^T = H^T Q~^T + U^T P~^T for their token tile
 //   every wave:       its row tile of H = e^{gamma_C} H + K~^T U (U read back as fragments from LDS)
 //   Only H and U cross waves, through LDS; each wave loads its own fragments of the next chunks into
-//   registers while the current chunk computes. The gated RMSNorm is fused when one workgroup owns all
-//   d_v columns of the head, otherwise norm_kernel finishes it from the saved partial sums.
+//   registers while the current chunk computes. The gated RMSNorm: when one workgroup owns all d_v
+//   columns of the head it normalises each row at once. When the columns are split over 2 or 4 slices
+//   on a long call, each slice posts its partial sum of squares of the row, keeps w o silu(z) of its
+//   columns in LDS and scales them by 1/rms a few chunks later, once every slice of the head has
+//   posted (chunk_prep marks those sums pending first; all slices of a head are resident together, one
+//   workgroup per CU). Otherwise the slices save o and their sums and norm_kernel finishes the rows.
 //
 // Fragment convention (f16 16x16x32 MFMA, lane l = 16 g + c): a 32-wide k-block is split so that lane
 // group g holds k = {4g..4g+3, 16+4g..16+4g+3}. With that grouping the two 16x16 accumulator tiles of a
@@ -52,6 +55,10 @@ constexpr int C64 = kChunk;
 constexpr float kS8 = 256.f;              // 2^8 operand scale
 constexpr float kInvS8 = 1.f / 256.f;
 constexpr float kInvS16 = 1.f / 65536.f;
+// a split head's partial sum of squares not posted yet (a posted sum is >= 0 or NaN, never -1)
+constexpr float kSsPending = -1.f;
+// bound of a slice's wait for the other slices' sums, in ticks of the 100 MHz constant clock (1 s)
+constexpr uint64_t kSpinTicks = 100000000ull;
 
 // Barrier for LDS reads and writes only. __syncthreads() also waits for this wave's outstanding global
 // loads and stores (vmcnt), which would stall on the record stores of chunk_prep and serialise the
@@ -202,6 +209,20 @@ struct Pair<float> {
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // -------------------------------------------------------------------------------------------------
+// With a head's columns split over state-pass slices: mark the partial sums of squares of this chunk's
+// rows (every value head of key head kh) pending; each slice overwrites its own when it posts it.
+// Layout [sequence][value head][token][slice].
+__device__ __forceinline__ void mark_sums_pending(const PrefillArgs& p, int b, int kh, int R, int t0, int tid) {
+  const int ns = p.nsplit;
+  if (ns <= 1 || !p.exchange) return;
+  float* ss = (float*)((char*)p.ws + p.ss_off);
+  for (int i = tid; i < R * C64 * ns; i += 512) {
+    const int hr = i / (C64 * ns), t = t0 + (i / ns) % C64;
+    if (t < p.Lb) ss[(((long)b * p.n_v + kh * R + hr) * p.Lb + t) * ns + i % ns] = kSsPending;
+  }
+}
+
+// -------------------------------------------------------------------------------------------------
 template <typename ActT, int D, int R, bool SPLIT>
 __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   constexpr bool SH = R > 1;
@@ -256,6 +277,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   if (t0 >= len) return;  // all padding: the state pass stops before this chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so addresses built on it stay scalar
+  mark_sums_pending(p, b, kh, R, t0, tid);
   const int g16 = lane >> 4, r16 = lane & 15;
   const int Lb = p.Lb, C = p.C, n_k = p.n_k;
   const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
@@ -726,6 +748,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g16 = lane >> 4, r16 = lane & 15;
+  mark_sums_pending(p, b, kh, R, t0, tid);
   const int Lb = p.Lb, C = p.C, n_k = p.n_k;
   const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
   const ActT* tail = (const ActT*)p.tail + (long)b * 3 * C;
@@ -1102,36 +1125,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 // two chunks ahead: each fragment of chunk c is refilled with chunk c+2 right after its last use.
 // The two roles keep separate fragment sets (and run separate copies of the chunk loop), so that the
 // registers of one role are never live in the other's code.
-template <int KD, int NT, bool SPLIT>
+template <int KD, int NT, bool SPLIT, typename RawZ>
 struct ChainFrags {
   f16x8 w[KD], wl[SPLIT ? KD : 1];  // -W of the token tile
   f32x4 up[NT];                     // U' of the token tile, this slice
   f16x8 k[2], kl[2];                // K~^T of the own H tile
   float gc;                         // e^{gamma_C}
   f32x4 ed;                         // with a key record: e^{gamma_C - gamma_t} of this lane's U rows
+  RawZ z[NT];                       // split head: z of the token tile, handed to the output wave
 };
-template <int KD, int NT, typename RawZ>
+template <int KD, int NT, typename RawZ, int NS>
 struct OutFrags {
   f16x8 q[KD], ql[KD];              // Q~ of the token tile
   f16x8 p[2], pl[2];                // P~ of the token tile
   f16x8 k[2], kl[2];                // K~^T of the own H tile
   float gc;                         // e^{gamma_C}
   float eg;                         // with a key record: scale e^{gamma_t} of this lane's token
-  RawZ z[NT];                       // z of the token tile (fused norm)
+  RawZ z[NT];                       // z of the token tile (gated norm)
+  float sums[NS];                   // split head: a pair of the slices' row sums of an earlier chunk, in flight
 };
 
-template <typename ActT, int D, int NT, bool SPLIT, bool FUSED, bool DB, bool SH>
+// how the gated RMSNorm of a row is finished: in the epilogue (one workgroup owns the head), by the
+// slices' exchange of row sums, or by norm_kernel from the saved unnormalised o and partial sums
+constexpr int kNormFused = 0, kNormExchange = 1, kNormPass = 2;
+
+template <typename ActT, int D, int NT, bool SPLIT, int NM, bool DB, bool SH>
 __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
+  constexpr bool FUSED = NM == kNormFused, XCH = NM == kNormExchange;
   using RC = Rec<D, SPLIT, SH>;
   using KR = KeyRec<D>;
   constexpr int KD = D / 32, HM = D / 16, CS = 16 * NT, NSPLIT = D / CS;
   constexpr int NG = (NT == 2 || NT == 4) ? 2 : 1;  // column tiles per MFMA group (registers cap NT = 8 at 1)
   static_assert(NSPLIT * CS == D, "column split");
   static_assert(HM <= 8, "one H row tile per wave");
-  static_assert(FUSED == (NSPLIT == 1), "the norm is fused exactly when one workgroup owns the head");
+  static_assert(FUSED == (NSPLIT == 1), "FUSED: one workgroup owns every column of the head");
+  static_assert(NSPLIT == 1 || NSPLIT % 2 == 0, "row sums are read in pairs");
+  static_assert(!XCH || (DB && (NT == 2 || NT == 4)), "the row-sum exchange: 32- or 64-column slices, two fragment sets");
+  // row-sum exchange: the rows of chunk c are normalised at the end of chunk c + kDelay. With 32
+  // columns the row sums are loaded at the start of chunk c + 2 into the fragment set of that chunk
+  // and used a whole chunk later (the uncached round trip is longer than one chunk); with 64 columns,
+  // where registers are scarce, they are loaded after the state update of chunk c + 2 and used at its
+  // end.
+  constexpr bool kDeep = NT == 2;
+  constexpr int kDelay = kDeep ? 3 : 2, kRing = kDelay + 1;
   typedef typename Raw4<ActT>::type RawZ;
-  typedef ChainFrags<KD, NT, SPLIT> CF;
-  typedef OutFrags<KD, NT, RawZ> OF;
+  typedef ChainFrags<KD, NT, SPLIT, RawZ> CF;
+  typedef OutFrags<KD, NT, RawZ, 2> OF;
   // H and U as MFMA operand fragments: [32-block][nt][hi, lo][lane], 16 bytes each
   __shared__ f16x8 sH[KD * NT * 2 * kWave];
   __shared__ f16x8 sU[2 * NT * 2 * kWave];
@@ -1202,8 +1241,10 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
   auto ld_eg = [&](OF& f, int c) __attribute__((always_inline)) {
     if constexpr (SH) f.eg = *(const float*)(rec_of(c) + RC::kEg + 4 * (16 * tt + r16));
   };
-  auto ld_z = [&](OF& f, int c) __attribute__((always_inline)) {
-    if (FUSED) {
+  // z of token 16 tt + r16, columns cb + 16 nt + 4 g16 .. +3: loaded by the output wave when one
+  // workgroup owns the head, by the chain wave of the token tile (registers to spare) when it is split
+  auto ld_z = [&](auto& f, int c) __attribute__((always_inline)) {
+    {
       const int cc = c < n_real ? c : n_real - 1;
       const int t = cc * C64 + 16 * tt + r16;  // rows past Lb read row Lb-1; their results are never stored
       const long row = ((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h;
@@ -1218,13 +1259,14 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) ld_up(f, c, nt);
       ld_ed(f, c);
+      if (XCH) ld_z(f, c);
     } else {
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) ld_q(f, c, kk);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) ld_p(f, c, kk);
       ld_eg(f, c);
-      ld_z(f, c);
+      if (FUSED) ld_z(f, c);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) ld_k(f, c, kk);
@@ -1262,15 +1304,77 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
   // the norm weights of this slice, read from LDS in the epilogue (registers are the scarce resource)
   __shared__ __attribute__((aligned(16))) float sNW[CS];
   if (tid < CS) sNW[tid] = p.norm_w[cb + tid];
+  // split head: w o silu(z) of the last kRing chunks, [chunk % kRing][token tile][nt][lane], until
+  // the row's 1/rms is known; z of the last two chunks from the chain waves, [chunk & 1][token tile][nt][lane]
+  __shared__ float4 sY[XCH ? kRing * 4 * NT * kWave : 1];
+  __shared__ RawZ sZ[XCH ? 2 * 4 * NT * kWave : 1];
 
   ActT* out = (ActT*)p.out;
-  float* oraw = (float*)((char*)p.ws + p.oraw_off);
   float* sspart = (float*)((char*)p.ws + p.ss_off);
+  float* oraw = (float*)((char*)p.ws + p.oraw_off);
 
-  auto chunk = [&](int c, auto& f, int step) __attribute__((always_inline)) {
+  // split head: the partial sums of squares that every slice posted for the row of token
+  // 16 tt + r16 of chunk cc, [sequence][head][token][slice], read past the caches (agent scope: the
+  // slices may sit on different L2s). Lane group g16 loads pair g16 % NP of its row's sums, so a wave
+  // reads 16 consecutive rows in one contiguous sweep; finish_rows combines the groups' pairs.
+  constexpr int NP = NSPLIT > 1 ? NSPLIT / 2 : 1;
+  float* ssrow = sspart + ((long)b * n_v + h) * Lb * NSPLIT;  // this head's rows
+  auto load_sums = [&](int cc, float (&sums)[2]) __attribute__((always_inline)) {
+    // unconditional (a row past Lb reads row Lb - 1 and is ignored), so that nothing waits here
+    const int t = cc * C64 + 16 * tt + r16;
+    const uint64_t* src = (const uint64_t*)(ssrow + (long)(t < Lb ? t : Lb - 1) * NSPLIT) + (g16 % NP);
+    const uint64_t u = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sums[0] = __uint_as_float((uint32_t)u);
+    sums[1] = __uint_as_float((uint32_t)(u >> 32));
+  };
+  // scale this slice's w o silu(z) of the row by 1/rms and store it. A slice posts chunk c before it
+  // waits for chunk c - kDelay and every slice of the head is resident, so a sum still pending
+  // arrives; the time bound only guarantees that the kernel ends even if that were not so.
+  auto finish_rows = [&](int cc, const float (&in)[2]) __attribute__((always_inline)) {
+    const int t = cc * C64 + 16 * tt + r16;
+    float sums[2] = {in[0], in[1]};  // a copy: re-reading into the fragment set kept it out of registers
+    // the row's total over every slice and whether one is still pending, in all four lane groups
+    auto combine = [&](float& tot) __attribute__((always_inline)) {
+      tot = sums[0] + sums[1];
+      int pend = (sums[0] == kSsPending || sums[1] == kSsPending) ? 1 : 0;
+#pragma unroll
+      for (int m = 1; m < NP; m *= 2) {
+        tot += __shfl_xor(tot, 16 * m, kWave);
+        pend |= __shfl_xor(pend, 16 * m, kWave);
+      }
+      return pend == 0 || t >= Lb;
+    };
+    float tot;
+    if (!__all(combine(tot))) {
+      const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+      do {
+        __builtin_amdgcn_s_sleep(2);
+        load_sums(cc, sums);
+      } while (!__all(combine(tot)) && __builtin_amdgcn_s_memrealtime() - t_start < kSpinTicks);
+    }
+    const float inv = rsqrt_fast(tot / (float)D + p.rms_eps);
+    const long row = ((long)b * Lb + t) * n_v + h;
+    if (t < Lb) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4 y = sY[(((cc % kRing) * 4 + tt) * NT + nt) * kWave + lane];
+        Act4<ActT>::store(out + row * D + cb + 16 * nt + 4 * g16, make_float4(y.x * inv, y.y * inv, y.z * inv, y.w * inv));
+      }
+    }
+  };
+
+  // f: the fragment set of chunk c; g: the other set (split heads, output waves: its row sums, loaded
+  // at the start of chunk c - 1, are those of chunk c - 3)
+  auto chunk = [&](int c, auto& f, auto& g, int step) __attribute__((always_inline)) {
     constexpr bool kChain = std::is_same<std::decay_t<decltype(f)>, CF>::value;
     const int cn = c + step;  // the chunk whose fragments refill f
     f32x4 OT[NT];
+    // split head, output waves: the row sums of chunk c - 2 (a spill of these with 64 columns would be
+    // reloaded behind the whole queue of fragment prefetches, hence the later load there)
+    float sums[2];
+    if constexpr (!kChain && XCH && kDeep) {
+      if (c >= 2) load_sums(c - 2, f.sums);
+    }
     lds_barrier();  // H of this chunk is in sH
     if constexpr (kChain) {
       // ---- U = U' - W H (token tile tt); the hi*lo and hi*hi terms accumulate separately ----
@@ -1325,6 +1429,11 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
         }
       }
       ld_ed(f, cn);
+      if constexpr (XCH) {  // read by the output wave of the token tile after the next barrier
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sZ[(((c & 1) * 4 + tt) * NT + nt) * kWave + lane] = f.z[nt];
+        ld_z(f, cn);
+      }
     } else {
       // ---- O^T = H^T Q~^T (token tile tt) ----
 #pragma unroll
@@ -1450,6 +1559,9 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
         }
       }
     }
+    if constexpr (!kChain && XCH && !kDeep) {
+      if (c >= 2) load_sums(c - 2, sums);
+    }
     put_H();
 
     // ---- output waves: token 16 tt + r16, columns cb + 16 nt + 4 g16 + i ----
@@ -1465,7 +1577,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
       ss += __shfl_xor(ss, 32, kWave);
       const int t = c * C64 + 16 * tt + r16;
       const long row = ((long)b * Lb + t) * n_v + h;
-      if (FUSED) {
+      if constexpr (FUSED) {
         const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
         float4 res[NT];
 #pragma unroll
@@ -1480,8 +1592,24 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) Act4<ActT>::store(out + row * D + cb + 16 * nt + 4 * g16, res[nt]);
         }
-      } else if (t < Lb) {
-        if (g16 == 0) sspart[row * NSPLIT + split] = ss;
+      } else if constexpr (XCH) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float4 zf = Raw4<ActT>::widen(sZ[(((c & 1) * 4 + tt) * NT + nt) * kWave + lane]);
+          const float4 nw = *(const float4*)&sNW[16 * nt + 4 * g16];
+          sY[((((c % kRing) * 4 + tt) * NT + nt) * kWave) + lane] =
+              make_float4(nw.x * OT[nt][0] * silu(zf.x), nw.y * OT[nt][1] * silu(zf.y),
+                          nw.z * OT[nt][2] * silu(zf.z), nw.w * OT[nt][3] * silu(zf.w));
+        }
+        if (t < Lb && g16 == 0)
+          __hip_atomic_store(ssrow + (long)t * NSPLIT + split, ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (kDeep) {
+          if (c >= 3) finish_rows(c - 3, g.sums);
+        } else {
+          if (c >= 2) finish_rows(c - 2, sums);
+        }
+      } else if (t < Lb) {  // norm pass: this slice's sum of squares and its unnormalised o
+        if (g16 == 0) ssrow[(long)t * NSPLIT + split] = ss;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           *(float4*)(oraw + row * D + cb + 16 * nt + 4 * g16) = make_float4(OT[nt][0], OT[nt][1], OT[nt][2], OT[nt][3]);
@@ -1491,20 +1619,20 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
 
   // every wave runs the same number of chunks and barriers, whichever copy of the loop it is in
   auto run = [&](auto& f0, auto& f1) __attribute__((always_inline)) {
-    if (DB) {
+    if constexpr (DB) {
       load_all(f0, 0);
       load_all(f1, 1);
       // the loop body has no branch, so the compiler can count the loads still in flight at its top
       // (a conditional second chunk made it wait for all of them)
       int c = 0;
       for (; c + 1 < n_real; c += 2) {
-        chunk(c, f0, 2);
-        chunk(c + 1, f1, 2);
+        chunk(c, f0, f1, 2);
+        chunk(c + 1, f1, f0, 2);
       }
-      if (c < n_real) chunk(c, f0, 2);
+      if (c < n_real) chunk(c, f0, f1, 2);
     } else {
       load_all(f0, 0);
-      for (int c = 0; c < n_real; ++c) chunk(c, f0, 1);
+      for (int c = 0; c < n_real; ++c) chunk(c, f0, f0, 1);
     }
   };
   if (n_real > 0) {
@@ -1514,6 +1642,19 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
     } else {
       OF f0, f1;
       run(f0, f1);
+      if constexpr (XCH) {  // the rows of the last kDelay chunks: every load in flight before the first use
+        static_assert(kDelay <= 3, "tail");
+        const int c0 = n_real > kDelay ? n_real - kDelay : 0;
+        float s0[2], s1[2], s2[2];
+        load_sums(c0, s0);  // a chunk past the end reads valid rows and is not used
+        load_sums(c0 + 1, s1);
+        if constexpr (kDelay == 3) load_sums(c0 + 2, s2);
+        finish_rows(c0, s0);
+        if (c0 + 1 < n_real) finish_rows(c0 + 1, s1);
+        if constexpr (kDelay == 3) {
+          if (c0 + 2 < n_real) finish_rows(c0 + 2, s2);
+        }
+      }
     }
   }
 
@@ -1550,8 +1691,9 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
   }
 }
 
-// the gated RMSNorm when a head's columns were split: out = w * o / rms(o) * silu(z)
-// (one thread per 4 columns of one (sequence, token, head) row; rows past len are left alone)
+// the gated RMSNorm when a head's columns were split and the state pass left the rows unnormalised:
+// out = w * o / rms(o) * silu(z), one thread per 4 columns of one (sequence, token, head) row; rows
+// past len are left alone
 template <typename ActT, int D, int NPART>
 __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
   constexpr int Q = D / 4;
@@ -1561,10 +1703,12 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int rr = i / Q, cq = i % Q;
   if (rr >= p.len[b] * p.n_v) return;
+  const int t = rr / p.n_v, h = rr % p.n_v;
   const long row = (long)b * p.Lb * p.n_v + rr;
+  const float* sp = sspart + (((long)b * p.n_v + h) * p.Lb + t) * NPART;
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < NPART; ++k) ss += sspart[row * NPART + k];
+  for (int k = 0; k < NPART; ++k) ss += sp[k];
   const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
   const float4 o = *(const float4*)(oraw + row * D + 4 * cq);
   const float4 z = Act4<ActT>::load((const ActT*)p.z + row * D + 4 * cq);
@@ -1576,12 +1720,27 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
 
 // ---- launch configuration --------------------------------------------------------------------------
 // 16-column tiles per state-pass workgroup. A head's chain of chunks is sequential, so the only way
-// to spread a short batch over the 256 CUs is to split its value columns: NSPLIT = 256 / (B n_v)
-// slices (a power of two, at most 8), the whole head once there are 256 (sequence, head) pairs.
+// to spread a short batch over the 256 CUs is to split its value columns: NSPLIT slices per head, the
+// largest power of two (at most 8) with NSPLIT B n_v <= 256, the whole head from 129 (sequence, head)
+// pairs on. The grid then never exceeds one workgroup per CU: every slice of a head is resident at
+// once, which the slices' exchange of row sums for the gated norm relies on.
 int pass_nt(int B, int n_v, int D) {
   if (D != 128) return D / 16;
   const long pairs = (long)B * n_v;
-  return pairs >= 256 ? 8 : pairs >= 128 ? 4 : pairs >= 64 ? 2 : 1;
+  return pairs > 128 ? 8 : pairs > 64 ? 4 : pairs > 32 ? 2 : 1;
+}
+
+// A split head finishes its gated norm by the slices' exchange of row sums when its slices are 32 or
+// 64 columns wide (2 or 4 per head, which comes with a grid of more than 128 workgroups) and the call
+// runs at least 16 chunks. The state pass then streams its records at full bandwidth and the
+// exchange's uncached round trips hide behind it, while the norm pass it replaces would move 12 bytes
+// per output element. With 16-column slices (8 per head) each chunk is mostly latency and the round
+// trips lengthened the chain by more than the norm pass costs; on a short call the last chunks' round
+// trip, which nothing hides, costs more than the norm pass too. Those split heads save o and their
+// sums for a separate norm pass.
+bool pass_exchange(int B, int n_v, int D, int Lb) {
+  const int nsplit = D / (16 * pass_nt(B, n_v, D));
+  return (nsplit == 2 || nsplit == 4) && Lb >= 16 * kChunk;
 }
 
 // bytes of one value record and of one key record (zero without key records)
@@ -1603,6 +1762,12 @@ void rec_sizes(int D, bool split_all, bool sh, long& vrec, long& krec) {
   }
 }
 
+template <typename ActT, int D, int NT, bool SPLIT, int NM, bool SH>
+void launch_pass(const PrefillArgs& p, hipStream_t st) {
+  constexpr int NSPLIT = D / (16 * NT);
+  hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NM, (NT <= 4), SH>), dim3(NSPLIT * p.n_v * p.B), dim3(512), 0, st, p);
+}
+
 template <typename ActT, int D, int R, bool SPLIT, int NT>
 hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   constexpr int NSPLIT = D / (16 * NT);
@@ -1615,10 +1780,17 @@ hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timing_before("state_pass", st);
-  hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NSPLIT == 1, (NT <= 4), (R > 1)>), dim3(NSPLIT * p.n_v * p.B), dim3(512), 0, st, p);
+  if constexpr (NSPLIT == 1) {
+    launch_pass<ActT, D, NT, SPLIT, kNormFused, (R > 1)>(p, st);
+  } else if constexpr (NSPLIT == 2 || NSPLIT == 4) {
+    if (p.exchange) launch_pass<ActT, D, NT, SPLIT, kNormExchange, (R > 1)>(p, st);
+    else launch_pass<ActT, D, NT, SPLIT, kNormPass, (R > 1)>(p, st);
+  } else {
+    launch_pass<ActT, D, NT, SPLIT, kNormPass, (R > 1)>(p, st);
+  }
   timing_after(st);
   e = hipGetLastError();
-  if (e != hipSuccess || NSPLIT == 1) return e;
+  if (e != hipSuccess || NSPLIT == 1 || p.exchange) return e;
   const long per_seq = (long)p.Lb * p.n_v * (D / 4);  // < 2^31, checked by the caller
   timing_before("norm", st);
   hipLaunchKernelGGL((norm_kernel<ActT, D, NSPLIT>), dim3((unsigned)((per_seq + 255) / 256), p.B), dim3(256), 0, st, p);
@@ -1644,8 +1816,8 @@ size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bo
   rec_sizes(D, split_all, n_v > n_k, vrec, krec);
   size_t bytes = (size_t)B * n_chunks * ((size_t)n_v * vrec + (size_t)n_k * krec);
   if (nsplit > 1) {
-    bytes += (size_t)B * Lb * n_v * D * 4;             // unnormalised o
-    bytes += (size_t)B * Lb * n_v * nsplit * 4;        // partial sums of squares
+    bytes += (size_t)B * Lb * n_v * nsplit * 4;                        // partial sums of squares
+    if (!pass_exchange(B, n_v, D, Lb)) bytes += (size_t)B * Lb * n_v * D * 4;  // unnormalised o
     bytes = (bytes + 255) / 256 * 256;
   }
   return bytes;
@@ -1656,8 +1828,10 @@ void prefill_ws_layout(PrefillArgs& p, int D, bool split_all) {
   rec_sizes(D, split_all, p.n_v > p.n_k, vrec, krec);
   p.key_off = (long)p.B * p.n_v * p.n_chunks * vrec;
   const size_t rec = (size_t)p.key_off + (size_t)p.B * p.n_k * p.n_chunks * krec;
-  p.oraw_off = (long)rec;
-  p.ss_off = (long)(rec + (size_t)p.B * p.Lb * p.n_v * D * 4);
+  p.nsplit = D / (16 * pass_nt(p.B, p.n_v, D));
+  p.exchange = pass_exchange(p.B, p.n_v, D, p.Lb) ? 1 : 0;
+  p.ss_off = (long)rec;
+  p.oraw_off = (long)(rec + (size_t)p.B * p.Lb * p.n_v * p.nsplit * 4);
 }
 
 hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hipStream_t st) {

@@ -99,7 +99,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc* desc, int B, int Lb);
  *   conv_tail [B][Kc][C_ch] in/out (as gdn_conv_chunk); state [B][n_v][d_k][d_v] fp32 in/out
  *   out   [B][Lb][n_v*d_v] gated-RMSNorm output; rows >= len[b] carry no meaning
  *   ws    device workspace of at least gdn_prefill_workspace_bytes(desc, B, Lb) bytes, 256-aligned;
- *         its contents on entry do not matter and are garbage on return
+ *         its contents on entry do not matter and are garbage on return; it serves one call at a
+ *         time (calls that may overlap, e.g. on two streams, need workspaces of their own)
  * Limits: B <= 65535, Lb * n_v * d_v < 2^31 and B * ceil(Lb / 64) * n_k < 2^31 (GDN_EINVAL otherwise).
  * Must not alias: out with any input; state or conv_tail with anything else.
  */
