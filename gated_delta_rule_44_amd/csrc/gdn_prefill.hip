@@ -1816,8 +1816,11 @@ size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bo
   rec_sizes(D, split_all, n_v > n_k, vrec, krec);
   size_t bytes = (size_t)B * n_chunks * ((size_t)n_v * vrec + (size_t)n_k * krec);
   if (nsplit > 1) {
-    bytes += (size_t)B * Lb * n_v * nsplit * 4;                        // partial sums of squares
-    if (!pass_exchange(B, n_v, D, Lb)) bytes += (size_t)B * Lb * n_v * D * 4;  // unnormalised o
+    // partial sums of squares, and the unnormalised o for a norm pass; the o area is counted even
+    // when the slices exchange their sums, so that the size never shrinks as Lb grows (a workspace
+    // sized for the longest call serves every shorter one)
+    bytes += (size_t)B * Lb * n_v * nsplit * 4;
+    bytes += (size_t)B * Lb * n_v * D * 4;
     bytes = (bytes + 255) / 256 * 256;
   }
   return bytes;

@@ -91,6 +91,11 @@ def test_sizes():
     # few (sequence, head) pairs: heads are split over workgroups and o is staged per token
     assert gdn.prefill_workspace_bytes(d, 1, 128) > gdn.prefill_workspace_bytes(d, 1, 100) > 0
     assert gdn.prefill_workspace_bytes(gdn.GdnDesc(n_k=2, n_v=4, d_k=128, d_v=128, act_dtype=gdn.GDN_F32), 1, 64) == 0
+    # for a fixed batch the size never shrinks as Lb grows, also where the split heads of a call of
+    # 1024 tokens or more switch from the norm pass to the exchange of row sums
+    for B in (1, 2, 3, 4, 5):
+        sizes = [gdn.prefill_workspace_bytes(d, B, L) for L in (64, 960, 1000, 1023, 1024, 1025, 2048)]
+        assert sizes == sorted(sizes), (B, sizes)
 
 
 def test_python_layer_rejects_cpu_tensors():
