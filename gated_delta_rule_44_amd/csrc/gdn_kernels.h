@@ -65,8 +65,9 @@ struct PrefillArgs {
   float* state;         // [B][n_v][D][D] in/out
   void* out;            // [B][Lb][n_v*D]
   void* ws;             // workspace: value records, key records (n_v > n_k), then (split heads only)
-                        // the partial sums of squares of every (sequence, head, token) row, one per
-                        // slice, and, when a norm pass finishes the rows, the unnormalised o
+                        // the partial sums of squares of every row, one per slice ([sequence][head]
+                        // [token][slice] for the exchange, [sequence][token][head][slice] for a norm
+                        // pass), and the unnormalised o for a norm pass
   long key_off, ss_off, oraw_off;  // byte offsets inside ws: key records, partial sums, unnormalised o
   int B, Lb, n_k, n_v, C, n_chunks;
   int nsplit;           // column slices per head in the state pass (1: the whole head)

@@ -1313,7 +1313,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
   float* sspart = (float*)((char*)p.ws + p.ss_off);
   float* oraw = (float*)((char*)p.ws + p.oraw_off);
 
-  // split head: the partial sums of squares that every slice posted for the row of token
+  // row-sum exchange: the partial sums of squares that every slice posted for the row of token
   // 16 tt + r16 of chunk cc, [sequence][head][token][slice], read past the caches (agent scope: the
   // slices may sit on different L2s). Lane group g16 loads pair g16 % NP of its row's sums, so a wave
   // reads 16 consecutive rows in one contiguous sweep; finish_rows combines the groups' pairs.
@@ -1608,8 +1608,8 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
         } else {
           if (c >= 2) finish_rows(c - 2, sums);
         }
-      } else if (t < Lb) {  // norm pass: this slice's sum of squares and its unnormalised o
-        if (g16 == 0) ssrow[(long)t * NSPLIT + split] = ss;
+      } else if (t < Lb) {  // norm pass: this slice's sum of squares ([sequence][token][head][slice]) and o
+        if (g16 == 0) sspart[row * NSPLIT + split] = ss;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           *(float4*)(oraw + row * D + cb + 16 * nt + 4 * g16) = make_float4(OT[nt][0], OT[nt][1], OT[nt][2], OT[nt][3]);
@@ -1692,8 +1692,9 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
 }
 
 // the gated RMSNorm when a head's columns were split and the state pass left the rows unnormalised:
-// out = w * o / rms(o) * silu(z), one thread per 4 columns of one (sequence, token, head) row; rows
-// past len are left alone
+// out = w * o / rms(o) * silu(z), one thread per 4 columns of one (sequence, token, head) row; the
+// slices' partial sums of a row are adjacent, [sequence][token][head][slice]; rows past len are left
+// alone
 template <typename ActT, int D, int NPART>
 __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
   constexpr int Q = D / 4;
@@ -1703,9 +1704,8 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int rr = i / Q, cq = i % Q;
   if (rr >= p.len[b] * p.n_v) return;
-  const int t = rr / p.n_v, h = rr % p.n_v;
   const long row = (long)b * p.Lb * p.n_v + rr;
-  const float* sp = sspart + (((long)b * p.n_v + h) * p.Lb + t) * NPART;
+  const float* sp = sspart + row * NPART;
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < NPART; ++k) ss += sp[k];
