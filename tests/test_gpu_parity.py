@@ -515,3 +515,55 @@ def test_continuation_graph_replay_equals_eager():
         for i, c in enumerate(calls):
             assert torch.equal(c[5][0, :c[6]], ref_out[i]), f"replay {rep}: chunk {i} output differs"
         assert torch.equal(state, ref_state) and torch.equal(tail, ref_tail), f"replay {rep}: state differs"
+
+
+def test_split_exchange_graph_replay_equals_eager():
+    """Two continued 1100-token calls on 2 sequences of a 16/32-head layer (64 pairs: 32-column slices
+    that exchange their partial row sums, which chunk_prep marks pending on every call) captured once
+    into a HIP graph: three replays, each after resetting the state, tail and outputs eagerly, give the
+    eager run's outputs and final state bit for bit."""
+    dims, B, L = NEXT, 2, 1100
+    _say("split-head exchange graph replay")
+    w, x, rng = make_layer(64, dims, B, 2 * L)
+    d = desc_of(dims)
+    W = weights(w, dims)
+    lens = i32([L, L - 37])
+    calls = []
+    for i in range(2):
+        sl = slice(i * L, (i + 1) * L)
+        calls.append((act(x.mixed[:, sl], dims), act(x.z[:, sl], dims), act(x.a[:, sl], dims), act(x.b[:, sl], dims),
+                      torch.empty(B, L, dims.value_dim, dtype=torch.bfloat16, device="cuda")))
+    ws = gdn.prefill_workspace(d, B, L)
+    tail = torch.zeros(B, 3, dims.conv_dim, dtype=torch.bfloat16, device="cuda")
+    state = torch.zeros(B, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda")
+
+    def run():
+        for mx, zz, aa, bb, out in calls:
+            gdn.prefill_chunk(d, W, mx, zz, aa, bb, lens, tail, state, out, ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref_out = [torch.cat([c[4][0], c[4][1, :L - 37]]).clone() for c in calls]
+    ref_state, ref_tail = state.clone(), tail.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        state.zero_()
+        tail.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        state.zero_()
+        tail.zero_()
+        for c in calls:
+            c[4].fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, c in enumerate(calls):
+            got = torch.cat([c[4][0], c[4][1, :L - 37]])
+            assert torch.equal(got, ref_out[i]), f"replay {rep}: call {i} output differs"
+        assert torch.equal(state, ref_state) and torch.equal(tail, ref_tail), f"replay {rep}: state differs"
