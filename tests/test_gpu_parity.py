@@ -73,14 +73,15 @@ def test_prefill_column_splits_d128(B):
     _prefill_case(NEXT, 11, B, 150, lens, state_std=0.05, tail_rand=True)
 
 
-@pytest.mark.parametrize("dims,B,L,lens", [(LayerDims(n_k=16, n_v=16, d_k=128, d_v=128), 3, 1030, [1030, 64, 700]),
+@pytest.mark.parametrize("dims,B,L,lens", [(LayerDims(n_k=16, n_v=16, d_k=128, d_v=128), 3, 1030, [1030, 0, 700]),
                                             (LayerDims(n_k=24, n_v=24, d_k=128, d_v=128), 3, 1030, [1030, 1, 900]),
                                             (NEXT, 2, 1030, [1030, 999]),
                                             (NEXT, 3, 1030, [1030, 500, 1])])
 def test_prefill_split_row_sum_exchange(dims, B, L, lens):
     """Calls of at least 1024 tokens with 32- or 64-column state-pass slices: the slices of a head
     exchange their partial row sums for the gated norm. 48 and 72 (sequence, head) pairs with one value
-    head per key head, 64 and 96 with two; ragged lengths, from a non-zero state and tail."""
+    head per key head, 64 and 96 with two; ragged lengths (one sequence empty), from a non-zero state
+    and tail."""
     _prefill_case(dims, 12, B, L, lens, state_std=0.05, tail_rand=True)
 
 
