@@ -4,8 +4,9 @@
 // tail is rows len .. len+2 of xin (the "qev_fast/statecache.py" page, CacheQwen35._gdn: conv on
 // [saved conv inputs | chunk] with SiLU and no bias, then the copy of the last Kc real inputs).
 //
-// HBM-bound elementwise work.  Each thread owns 4 adjacent channels and a span of kSpan tokens, which it
-// walks in groups of kG rows with a rolling 3-row window: the next group's rows are loaded before the
+// HBM-bound elementwise work.  Each thread owns 8 adjacent bf16 channels (one 16-byte access per row;
+// 4 fp32 channels) and a span of kSpan tokens, which it walks in groups of kG rows with a rolling 3-row
+// window: the next group's rows are loaded before the
 // current group is computed, so every input row is read once (plus a 3-row halo per span) and loads
 // stay in flight under the arithmetic.  Workgroup w runs job J = (w % 8) * (N / 8) + w / 8 so that each
 // XCD walks consecutive spans of one channel stripe and finds the halo rows in its own L2.  Only the
@@ -23,39 +24,48 @@ constexpr int kGroups = 8;
 constexpr int kSpan = kG * kGroups;
 constexpr int kThreads = 256;
 
+// the channels one thread owns in one row: 8 bf16 (one 16-byte access) or 4 fp32, widened to fp32
 template <typename ActT>
-struct Vec4;
+struct Row;
 template <>
-struct Vec4<float> {
-  static __device__ __forceinline__ float4 load(const float* p) { return *(const float4*)p; }
-  static __device__ __forceinline__ void store(float* p, float4 v) { *(float4*)p = v; }
+struct Row<float> {
+  static constexpr int kC = 4;
+  typedef float4 raw;
+  static __device__ __forceinline__ raw ld(const float* p) { return *(const float4*)p; }
+  static __device__ __forceinline__ void widen(raw v, float (&f)[kC]) { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
+  static __device__ __forceinline__ void store(float* p, const float (&f)[kC]) { *(float4*)p = make_float4(f[0], f[1], f[2], f[3]); }
 };
 template <>
-struct Vec4<bf16_t> {
-  static __device__ __forceinline__ float4 load(const bf16_t* p) {
-    const uint2 u = *(const uint2*)p;
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+struct Row<bf16_t> {
+  static constexpr int kC = 8;
+  typedef uint4 raw;
+  static __device__ __forceinline__ raw ld(const bf16_t* p) { return *(const uint4*)p; }
+  static __device__ __forceinline__ void widen(raw u, float (&f)[kC]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
   }
-  static __device__ __forceinline__ void store(bf16_t* p, float4 v) {
-    uint2 u;
-    u.x = pack_bf16x2(v.x, v.y);
-    u.y = pack_bf16x2(v.z, v.w);
-    *(uint2*)p = u;
+  static __device__ __forceinline__ void store(bf16_t* p, const float (&f)[kC]) {
+    *(uint4*)p = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
   }
 };
 
 template <typename ActT>
 __global__ __launch_bounds__(kThreads) void conv_kernel(ConvArgs p) {
+  typedef Row<ActT> V;
+  constexpr int K = V::kC;
   const int C = p.C, Lb = p.Lb;
-  const int nx = (C / 4 + kThreads - 1) / kThreads, ny = (Lb + kSpan - 1) / kSpan;
+  const int nx = (C / K + kThreads - 1) / kThreads, ny = (Lb + kSpan - 1) / kSpan;
   const long N = (long)nx * ny * p.B;
   const long wg = blockIdx.x;
   const long J = wg < (N / 8) * 8 ? (wg % 8) * (N / 8) + wg / 8 : wg;
   const int by = (int)(J % ny);
   const int bx = (int)((J / ny) % nx);
   const int b = (int)(J / ((long)ny * nx));
-  const int c0 = (bx * kThreads + threadIdx.x) * 4;
+  const int c0 = (bx * kThreads + threadIdx.x) * K;
   if (c0 >= C) return;
   const int t0 = by * kSpan;
   const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
@@ -63,75 +73,97 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(ConvArgs p) {
   ActT* y = (ActT*)p.y + (long)b * Lb * C;
   const ActT* cw = (const ActT*)p.conv_w;
 
-  float w[4][4];  // [channel][tap]
+  float w[K][4];  // [channel][tap]
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 v = Vec4<ActT>::load(cw + (long)(c0 + i) * 4);
-    w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+  for (int i = 0; i < K; ++i) {
+    float f[4];
+    f[0] = to_f32(cw[(long)(c0 + i) * 4 + 0]); f[1] = to_f32(cw[(long)(c0 + i) * 4 + 1]);
+    f[2] = to_f32(cw[(long)(c0 + i) * 4 + 2]); f[3] = to_f32(cw[(long)(c0 + i) * 4 + 3]);
+    w[i][0] = f[0]; w[i][1] = f[1]; w[i][2] = f[2]; w[i][3] = f[3];
   }
-  float4 h[3];  // the 3 rows before the current group
+  float h[3][K];  // the 3 rows before the current group
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int t = t0 - 3 + i;
     const ActT* src = t < 0 ? tail + (long)(t + 3) * C : mixed + (long)(t < Lb ? t : Lb - 1) * C;
-    const float4 v = Vec4<ActT>::load(src + c0);
-    h[i] = t < Lb ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float4 old0 = h[0], old1 = h[1], old2 = h[2];
-  const int ng = min(kGroups, (Lb - t0 + kG - 1) / kG);
-  float4 cur[kG], nxt[kG];
+    V::widen(V::ld(src + c0), h[i]);
+    if (t >= Lb) {
 #pragma unroll
-  for (int i = 0; i < kG; ++i) cur[i] = Vec4<ActT>::load(mixed + (long)min(t0 + i, Lb - 1) * C + c0);
+      for (int k = 0; k < K; ++k) h[i][k] = 0.f;
+    }
+  }
+  float old[3][K];
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int k = 0; k < K; ++k) old[i][k] = h[i][k];
+  const int ng = min(kGroups, (Lb - t0 + kG - 1) / kG);
+  typename V::raw cur[kG], nxt[kG];
+#pragma unroll
+  for (int i = 0; i < kG; ++i) cur[i] = V::ld(mixed + (long)min(t0 + i, Lb - 1) * C + c0);
 #pragma unroll 1
   for (int g = 0; g < ng; ++g) {
     const int tg = t0 + g * kG;
     if (g + 1 < ng) {
 #pragma unroll
-      for (int i = 0; i < kG; ++i) nxt[i] = Vec4<ActT>::load(mixed + (long)min(tg + kG + i, Lb - 1) * C + c0);
+      for (int i = 0; i < kG; ++i) nxt[i] = V::ld(mixed + (long)min(tg + kG + i, Lb - 1) * C + c0);
     }
     const bool whole = tg + kG <= Lb;
-    if (!whole) {
+    float win[3][K];  // rows tg + tt - 3 .. tg + tt - 1
 #pragma unroll
-      for (int i = 0; i < kG; ++i)
-        if (tg + i >= Lb) cur[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int k = 0; k < K; ++k) win[i][k] = h[i][k];
 #pragma unroll
     for (int tt = 0; tt < kG; ++tt) {
-      const float4 x0 = tt >= 3 ? cur[tt - 3] : h[tt];
-      const float4 x1 = tt >= 2 ? cur[tt - 2] : h[tt + 1];
-      const float4 x2 = tt >= 1 ? cur[tt - 1] : h[2];
-      const float4 x3 = cur[tt];
-      float4 o;
-      o.x = silu(w[0][0] * x0.x + w[0][1] * x1.x + w[0][2] * x2.x + w[0][3] * x3.x);
-      o.y = silu(w[1][0] * x0.y + w[1][1] * x1.y + w[1][2] * x2.y + w[1][3] * x3.y);
-      o.z = silu(w[2][0] * x0.z + w[2][1] * x1.z + w[2][2] * x2.z + w[2][3] * x3.z);
-      o.w = silu(w[3][0] * x0.w + w[3][1] * x1.w + w[3][2] * x2.w + w[3][3] * x3.w);
-      if (whole || tg + tt < Lb) Vec4<ActT>::store(y + (long)(tg + tt) * C + c0, o);
+      float x3[K];
+      V::widen(cur[tt], x3);
+      if (!whole && tg + tt >= Lb) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) x3[k] = 0.f;
+      }
+      float o[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        o[k] = silu(w[k][0] * win[0][k] + w[k][1] * win[1][k] + w[k][2] * win[2][k] + w[k][3] * x3[k]);
+      if (whole || tg + tt < Lb) V::store(y + (long)(tg + tt) * C + c0, o);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        win[0][k] = win[1][k];
+        win[1][k] = win[2][k];
+        win[2][k] = x3[k];
+      }
     }
-    h[0] = cur[kG - 3]; h[1] = cur[kG - 2]; h[2] = cur[kG - 1];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int k = 0; k < K; ++k) h[i][k] = win[i][k];
 #pragma unroll
     for (int i = 0; i < kG; ++i) cur[i] = nxt[i];
   }
   if (by == 0) {
-    // new tail = rows len .. len+2 of [tail | mixed]; old0..2 hold the old tail rows
+    // new tail = rows len .. len+2 of [tail | mixed]; old[] holds the old tail rows
     const int len = p.len[b];
-    float4 nt[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int src = len + i;
-      const float4 v = Vec4<ActT>::load(mixed + (long)(src >= 3 ? src - 3 : 0) * C + c0);
-      nt[i] = src < 3 ? (src == 0 ? old0 : src == 1 ? old1 : old2) : v;
-    }
+      float v[K];
+      V::widen(V::ld(mixed + (long)(src >= 3 ? src - 3 : 0) * C + c0), v);
+      if (src < 3) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) Vec4<ActT>::store(tail + (long)i * C + c0, nt[i]);
+        for (int k = 0; k < K; ++k) v[k] = src == 0 ? old[0][k] : src == 1 ? old[1][k] : old[2][k];
+      }
+      V::store(tail + (long)i * C + c0, v);
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_conv(const ConvArgs& p, int act_dtype, hipStream_t st) {
-  // one workgroup per (batch, 1024-channel stripe, kSpan-token span), flattened into grid.x
-  const long n = (long)((p.C / 4 + kThreads - 1) / kThreads) * ((p.Lb + kSpan - 1) / kSpan) * p.B;
+  // one workgroup per (batch, 256-thread channel stripe, kSpan-token span), flattened into grid.x
+  const int k = act_dtype == kActBf16 ? Row<bf16_t>::kC : Row<float>::kC;
+  const long n = (long)((p.C / k + kThreads - 1) / kThreads) * ((p.Lb + kSpan - 1) / kSpan) * p.B;
   if (n >= (1L << 31)) return hipErrorInvalidValue;
   dim3 grid((unsigned)n), block(kThreads);
   timing_before("conv", st);
