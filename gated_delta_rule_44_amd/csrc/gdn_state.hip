@@ -2,7 +2,7 @@
 //
 // A record is {fp32 state [n_v][d_k][d_v], conv tail [3][C_ch]}: fixed size, O(1) in context length
 // (the "uni_engine.py" page: copy_cache_ copies the conv and recurrent tables in place, its bridge
-// moves only that fixed payload). The copy streams 16-byte vectors, 4 per thread in flight; grid.y
+// moves only that fixed payload). The copy streams 16-byte vectors, 8 per thread in flight; grid.y
 // is the record, grid.x tiles the record's bytes.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
@@ -12,7 +12,7 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // kUnroll 16-byte vectors of one range per thread: every load is issued before the first store, and
