@@ -46,12 +46,19 @@ struct StepShape {
   static constexpr int QD = D / 4;                             // column quads per row
   static constexpr int RG = HT / QD;                           // row groups per head
   static constexpr int RPT = D / RG;                           // rows per thread
+  // at d = 128 with up to two value heads per key head, half of each thread's rows live in LDS (32 KB
+  // per head, only ever touched by their own thread), so that the kernel fits 128 VGPRs and two
+  // workgroups share a CU: one's loads and stores overlap the other's reductions and barriers
+  static constexpr bool LH = D == 128 && R <= 2;
+  static constexpr int RR = LH ? RPT / 2 : RPT;                // rows per thread held in registers
 };
 
 template <typename ActT, int D, int R>
-__global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p) {
+__global__ __launch_bounds__((StepShape<D, R>::NTH))
+__attribute__((amdgpu_waves_per_eu(StepShape<D, R>::LH ? 2 * StepShape<D, R>::NTH / 256 : 1)))
+void step_kernel(StepArgs p) {
   using S = StepShape<D, R>;
-  constexpr int HT = S::HT, NTH = S::NTH, QD = S::QD, RPT = S::RPT, HW = HT / kWave;
+  constexpr int HT = S::HT, NTH = S::NTH, QD = S::QD, RPT = S::RPT, HW = HT / kWave, RR = S::RR, RL = RPT - RR;
   constexpr int NCH = 2 * D + R * D;         // channels owned by an item
   constexpr int CPT = (NCH + NTH - 1) / NTH;
   static_assert(RPT >= 1 && S::RG * RPT == D, "thread layout");
@@ -61,6 +68,7 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
   __shared__ float sY[NCH];                  // conv outputs of the current token: q | k | v(R heads)
   __shared__ float sRed[R][HW][2][D];        // per head, per wave: partial H^T k and H^T q
   __shared__ __attribute__((aligned(16))) float sTot[R][2][D];  // per head: H^T k and H^T q
+  __shared__ f32x4 sHL[RL > 0 ? R * S::RG * RL * QD : 1];   // rows RR.. of each thread's block
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int r = tid / HT;                    // value head of the group owned by this thread
@@ -84,10 +92,14 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
     const int kh = item % n_k;
     return p.state_in + slot_of(item) * SZ + (long)(kh * R + r) * D * D + (long)(rg * RPT) * D + 4 * cq;
   };
-  auto load_H = [&](f32x4 (&H)[RPT], int item) {
+  // row RR + j of this thread's block in LDS
+  auto hl_at = [&](int j) -> f32x4& { return sHL[((r * S::RG + rg) * (RL > 0 ? RL : 1) + j) * QD + cq]; };
+  auto load_H = [&](f32x4 (&H)[RR], int item) {
     const float* src = state_src(item);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) H[i] = __builtin_nontemporal_load((const f32x4*)(src + (long)i * D));
+    for (int i = 0; i < RR; ++i) H[i] = __builtin_nontemporal_load((const f32x4*)(src + (long)i * D));
+#pragma unroll
+    for (int j = 0; j < RL; ++j) hl_at(j) = __builtin_nontemporal_load((const f32x4*)(src + (long)(RR + j) * D));
   };
 
   // per-token activations of one item, loaded ahead of use
@@ -100,7 +112,7 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
 #pragma unroll
   for (int c = 0; c < 4; ++c) nw[c] = p.norm_w[4 * cq + c];
 
-  f32x4 H[RPT];
+  f32x4 H[RR];
   {
     const int item = blockIdx.x;
     const int kh = item % n_k, bp = item / n_k;  // row: sequence bp / P, path bp % P
@@ -202,10 +214,11 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const float qn = sY[rg * RPT + i] * rq, kn = sY[D + rg * RPT + i] * rk;
+        const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          pk[c] = fmaf(H[i][c], kn, pk[c]);
-          pq[c] = fmaf(H[i][c], qn, pq[c]);
+          pk[c] = fmaf(hv[c], kn, pk[c]);
+          pq[c] = fmaf(hv[c], qn, pq[c]);
         }
       }
       // across the row groups inside the wave (lanes with the same column quad)
@@ -249,10 +262,12 @@ __global__ __launch_bounds__((StepShape<D, R>::NTH)) void step_kernel(StepArgs p
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const float kn = sY[D + rg * RPT + i] * rk;
+        const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
         f32x4 nh;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) nh[c] = fmaf(kn, u[c], decay * H[i][c]);
-        H[i] = nh;
+        for (int c = 0; c < 4; ++c) nh[c] = fmaf(kn, u[c], decay * hv[c]);
+        if (i < RR) H[i < RR ? i : 0] = nh;
+        else hl_at(i < RR ? 0 : i - RR) = nh;
         __builtin_nontemporal_store(nh, (f32x4*)(dst + (long)(rg * RPT + i) * D + 4 * cq));
       }
       // gated RMSNorm over the D columns held by the QD lanes of row group 0
