@@ -19,8 +19,9 @@
 // The state is HBM-streamed fp32, read and written exactly once per call. Each value head has its own
 // 256 threads (the workgroup is 256 R threads); a thread holds a 4-column x RPT-row block of its head's
 // H in registers; column partial sums are reduced across the row groups of a wave with lane shuffles
-// and across the head's waves in LDS. The register footprint is kept small (three waves per SIMD at
-// d = 128), so that the waves of different workgroups overlap one's loads with another's arithmetic
+// and across the head's waves in LDS. The register footprint is kept small (at d = 128 with up to two
+// value heads per key head half of a thread's rows wait in LDS, which leaves room for two workgroups
+// per CU), so that the waves of different workgroups overlap one's loads with another's arithmetic
 // and stores. Keeping the q/k
 // channels of a key head in one workgroup is what lets decode update the conv tail in place without a
 // race.
