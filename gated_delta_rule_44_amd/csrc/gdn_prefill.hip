@@ -42,6 +42,7 @@
 // must stay >= 2^-14: operands of unit scale are carried multiplied by 2^8 (exact), and the scales are
 // chosen so that every product lands in a consistent domain: the state pass keeps H as 2^16 H, U as
 // 2^8 U and O^T as 2^16 O^T, with 2^8 Q~, 2^8 P~, 2^8 K~, 2^8 U' and unscaled -W in the record.
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -1743,6 +1744,26 @@ bool pass_exchange(int B, int n_v, int D, int Lb) {
   return (nsplit == 2 || nsplit == 4) && Lb >= 16 * kChunk;
 }
 
+// The exchange's waits end because every slice of a head is resident at once: the grid (at most 256
+// workgroups, one per CU) must fit the device's CUs, which a partitioned or shared device may not
+// offer; then the call takes the norm pass, which never waits. CU counts are read once per device.
+bool exchange_fits(long grid) {
+  static int cus[64];
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return false;
+  }
+  std::call_once(once[dev], [dev] {
+    if (hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      cus[dev] = 0;
+    }
+  });
+  return grid <= cus[dev];
+}
+
 // bytes of one value record and of one key record (zero without key records)
 template <int D, bool SPLIT>
 void rec_sizes_t(bool sh, long& vrec, long& krec) {
@@ -1832,7 +1853,7 @@ void prefill_ws_layout(PrefillArgs& p, int D, bool split_all) {
   p.key_off = (long)p.B * p.n_v * p.n_chunks * vrec;
   const size_t rec = (size_t)p.key_off + (size_t)p.B * p.n_k * p.n_chunks * krec;
   p.nsplit = D / (16 * pass_nt(p.B, p.n_v, D));
-  p.exchange = pass_exchange(p.B, p.n_v, D, p.Lb) ? 1 : 0;
+  p.exchange = pass_exchange(p.B, p.n_v, D, p.Lb) && exchange_fits((long)p.nsplit * p.B * p.n_v) ? 1 : 0;
   p.ss_off = (long)rec;
   p.oraw_off = (long)(rec + (size_t)p.B * p.Lb * p.n_v * p.nsplit * 4);
 }
