@@ -85,10 +85,10 @@ def test_prefill_split_row_sum_exchange(dims, B, L, lens):
     _prefill_case(dims, 12, B, L, lens, state_std=0.05, tail_rand=True)
 
 
-_F32_TAIL = ("fp32 activations carry every MFMA operand as a hi/lo f16 pair (about 22 bits, a quarter of "
-             "fp32's precision); the gated norm amplifies that on output rows whose rms is small against their "
-             "terms: here one row ends 2.28e-3 from the oracle, over the 2e-3 bound (1 of 120 measured seed x "
-             "shape cases of the fp32 path; median worst error 3e-4, states within 2e-5 relative)")
+_F32_TAIL = ("open defect of the fp32-activation kernels: one output element of this case ends 2.28e-3 from "
+             "the oracle, over the 2e-3 bound (1 of 120 measured seed x shape cases of that path; median worst "
+             "error 3e-4, states within 2e-5 relative), while a rounding model of the kernels' documented operand "
+             "precision puts it 1.8e-7 away")
 
 
 @pytest.mark.parametrize("D,R,act_t", [(32, 1, ACT_BF16), (32, 4, ACT_BF16), (64, 4, ACT_BF16),
