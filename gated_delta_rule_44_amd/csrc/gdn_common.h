@@ -90,8 +90,20 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// x as one rounded fp32 value in a register, opaque to the optimiser (an empty asm, no memory access).
+// A hi/lo split converts x to f16 twice, once for the stored high half and once for the residual. Left
+// visible, the product that forms x was fused into the residual's conversion only (v_fma_mixlo_f16
+// rounds the exact product once, the stored half came from the fp32-rounded one): where the exact
+// product lies within half an fp32 ulp of an f16 tie the two high halves then differ, and hi + lo
+// misses x by one f16 ulp of the high half.
+__device__ __forceinline__ float pin_f32(float x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 // hi/lo split of an fp32 value into two f16 values: x ~= hi + lo to about 2^-22 relative
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  x = pin_f32(x);
   hi = (_Float16)x;
   lo = (_Float16)(x - (float)hi);
 }

@@ -89,15 +89,19 @@ __device__ __forceinline__ void frag_row_f(const float* row32, int g, float (&x)
 __device__ __forceinline__ void split8(const float (&x)[8], f16x8& hi, f16x8& lo) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    hi[e] = (_Float16)x[e];
-    lo[e] = (_Float16)(x[e] - (float)hi[e]);
+    _Float16 h, l;
+    split_f16(x[e], h, l);
+    hi[e] = h;
+    lo[e] = l;
   }
 }
 __device__ __forceinline__ void split4(f32x4 x, f16x4& hi, f16x4& lo) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    hi[e] = (_Float16)x[e];
-    lo[e] = (_Float16)(x[e] - (float)hi[e]);
+    _Float16 h, l;
+    split_f16(x[e], h, l);
+    hi[e] = h;
+    lo[e] = l;
   }
 }
 
