@@ -6,9 +6,9 @@
 //
 // HBM-bound elementwise work.  Each thread owns 8 adjacent bf16 channels (one 16-byte access per row;
 // 4 fp32 channels) and a span of kSpan tokens, which it walks in groups of kG rows with a rolling 3-row
-// window: the next group's rows are loaded before the
-// current group is computed, so every input row is read once (plus a 3-row halo per span) and loads
-// stay in flight under the arithmetic.  Workgroup w runs job J = (w % 8) * (N / 8) + w / 8 so that each
+// window: the next group's rows are loaded before the current group is computed, so every input row is
+// read once (plus a 3-row halo per span) and loads stay in flight under the arithmetic.  Rows are
+// streamed, so they are loaded and stored non-temporally.  Workgroup w runs job J = (w % 8) * (N / 8) + w / 8 so that each
 // XCD walks consecutive spans of one channel stripe and finds the halo rows in its own L2.  Only the
 // workgroups of the first span read the old tail, and each rewrites the tail of exactly its own
 // channels after its reads, so no other workgroup can observe a half-updated tail.
@@ -25,21 +25,22 @@ constexpr int kSpan = kG * kGroups;
 constexpr int kThreads = 256;
 
 // the channels one thread owns in one row: 8 bf16 (one 16-byte access) or 4 fp32, widened to fp32
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 template <typename ActT>
 struct Row;
 template <>
 struct Row<float> {
   static constexpr int kC = 4;
   typedef float4 raw;
-  static __device__ __forceinline__ raw ld(const float* p) { return *(const float4*)p; }
+  static __device__ __forceinline__ raw ld(const float* p) { const f32x4 v = __builtin_nontemporal_load((const f32x4*)p); return make_float4(v[0], v[1], v[2], v[3]); }
   static __device__ __forceinline__ void widen(raw v, float (&f)[kC]) { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
-  static __device__ __forceinline__ void store(float* p, const float (&f)[kC]) { *(float4*)p = make_float4(f[0], f[1], f[2], f[3]); }
+  static __device__ __forceinline__ void store(float* p, const float (&f)[kC]) { const f32x4 v = {f[0], f[1], f[2], f[3]}; __builtin_nontemporal_store(v, (f32x4*)p); }
 };
 template <>
 struct Row<bf16_t> {
   static constexpr int kC = 8;
   typedef uint4 raw;
-  static __device__ __forceinline__ raw ld(const bf16_t* p) { return *(const uint4*)p; }
+  static __device__ __forceinline__ raw ld(const bf16_t* p) { const u32x4 v = __builtin_nontemporal_load((const u32x4*)p); return make_uint4(v[0], v[1], v[2], v[3]); }
   static __device__ __forceinline__ void widen(raw u, float (&f)[kC]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -49,7 +50,8 @@ struct Row<bf16_t> {
     }
   }
   static __device__ __forceinline__ void store(bf16_t* p, const float (&f)[kC]) {
-    *(uint4*)p = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    const u32x4 v = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+    __builtin_nontemporal_store(v, (u32x4*)p);
   }
 };
 
