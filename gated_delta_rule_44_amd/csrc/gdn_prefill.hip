@@ -149,8 +149,15 @@ __device__ __forceinline__ char* key_ptr(const PrefillArgs& p, int b, int kh, in
 }
 // (the lane offset is an unsigned 32-bit value added to a wave-uniform base, which the compiler can
 // encode as a scalar base plus vector offset instead of a per-lane 64-bit address)
+// NTS: a non-temporal store, for records too large to stay cached until the state pass reads them
+template <bool NTS, typename V>
+__device__ __forceinline__ void st_rec(V* dst, V v) {
+  if constexpr (NTS) __builtin_nontemporal_store(v, dst);
+  else *dst = v;
+}
+template <bool NTS = false>
 __device__ __forceinline__ void put_frag(char* rec, int blk, int lane, f16x8 v) {
-  *(f16x8*)(rec + blk * 1024 + (uint32_t)(lane * 16)) = v;
+  st_rec<NTS>((f16x8*)(rec + blk * 1024 + (uint32_t)(lane * 16)), v);
 }
 __device__ __forceinline__ f16x8 get_frag(const char* rec, int blk, int lane) {
   return *(const f16x8*)(rec + blk * 1024 + (uint32_t)(lane * 16));
@@ -712,7 +719,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 // from it); the Gram accumulators stay in registers and become P~ (record) and A (LDS) per value head;
 // the W operands of every value head are built while k is staged, and the U' operand of a head waits
 // in registers while its T is formed.
-template <typename ActT, int D, int R>
+template <typename ActT, int D, int R, bool NTS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void chunk_prep2_kernel(PrefillArgs p) {
   constexpr bool SH = R > 1;
   using RC = Rec<D, false, SH>;
@@ -898,8 +905,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       const int row = (16 * mt + r16) * LQ + 32 * kk;
       const f16x8 qh = frag_row_h(sQh + row, g16), ql = frag_row_h(sQl + row, g16);
       if constexpr (SH) {
-        put_frag(krec, KR::Q_HI + mt * KD + kk, lane, qh);
-        put_frag(krec, KR::Q_LO + mt * KD + kk, lane, ql);
+        put_frag<NTS>(krec, KR::Q_HI + mt * KD + kk, lane, qh);
+        put_frag<NTS>(krec, KR::Q_LO + mt * KD + kk, lane, ql);
       } else {
         const float fq = p.scale * sEg[16 * mt + r16];
         float x[8];
@@ -907,8 +914,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qh[e] + (float)ql[e]);
         f16x8 hi, lo;
         split8(x, hi, lo);
-        put_frag(rec0, RC::Q_HI + mt * KD + kk, lane, hi);
-        put_frag(rec0, RC::Q_LO + mt * KD + kk, lane, lo);
+        put_frag<NTS>(rec0, RC::Q_HI + mt * KD + kk, lane, hi);
+        put_frag<NTS>(rec0, RC::Q_LO + mt * KD + kk, lane, lo);
       }
     }
   }
@@ -938,8 +945,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     f16x8 hi, lo;
     split8(x, hi, lo);
     char* rec = rec_ptr<D, false, SH>(p, b, kh * R + r, c);
-    put_frag(rec, RC::P_HI + pmt * 2 + pkk, lane, hi);
-    put_frag(rec, RC::P_LO + pmt * 2 + pkk, lane, lo);
+    put_frag<NTS>(rec, RC::P_HI + pmt * 2 + pkk, lane, hi);
+    put_frag<NTS>(rec, RC::P_LO + pmt * 2 + pkk, lane, lo);
   }
   // K K^T tiles, two for the waves without K Q^T tiles: waves 0-3 tiles 0-3, 4: 4-5, 5: 6-7, 6: 8, 7: 9
   const int kt0 = w < 4 ? w : w == 4 ? 4 : w == 5 ? 6 : w + 2;
@@ -971,15 +978,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     f16x8 hi, lo;
     k_col(hm, kk, hi, lo);
     if constexpr (SH) {
-      put_frag(krec, KR::K_HI + hm * 2 + kk, lane, hi);
-      put_frag(krec, KR::K_LO + hm * 2 + kk, lane, lo);
+      put_frag<NTS>(krec, KR::K_HI + hm * 2 + kk, lane, hi);
+      put_frag<NTS>(krec, KR::K_LO + hm * 2 + kk, lane, lo);
     } else {  // K~^T: 2^8 e^{gamma_C - gamma_s} k_s
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = sEd[32 * kk + kslot(g16, e)] * ((float)hi[e] + (float)lo[e]);
       split8(x, hi, lo);
-      put_frag(rec0, RC::K_HI + hm * 2 + kk, lane, hi);
-      put_frag(rec0, RC::K_LO + hm * 2 + kk, lane, lo);
+      put_frag<NTS>(rec0, RC::K_HI + hm * 2 + kk, lane, hi);
+      put_frag<NTS>(rec0, RC::K_LO + hm * 2 + kk, lane, lo);
     }
   }
   // the W operand of wave w (d tile w) for every value head: 2^8 beta_s e^{gamma_s} k_s as f16
@@ -1102,7 +1109,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         for (int ks = 0; ks < 2; ++ks) acc = mfma16(kb[r][ks], th[ks], acc);
         f16x4 hi, lo;
         split4(acc * -kInvS16, hi, lo);
-        *(f16x4*)(rec + (RC::W_HI + mt * KD + (w >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (w & 1))) = hi;
+        st_rec<NTS>((f16x4*)(rec + (RC::W_HI + mt * KD + (w >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (w & 1))), hi);
         // U' tile (mt, w) = (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
         f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
@@ -1110,7 +1117,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           a0 = mfma16(th[ks], vl[ks], a0);
           a1 = mfma16(th[ks], vh[ks], a1);
         }
-        *(f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)) = (a1 + a0) * kInvS8;
+        st_rec<NTS>((f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)), (a1 + a0) * kInvS8);
       }
     }
     if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gam[C64 - 1]);
@@ -1793,13 +1800,21 @@ void launch_pass(const PrefillArgs& p, hipStream_t st) {
   hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NM, (NT <= 4), SH>), dim3(NSPLIT * p.n_v * p.B), dim3(512), 0, st, p);
 }
 
+constexpr long kNtRecordBytes = 160L << 20;
+
 template <typename ActT, int D, int R, bool SPLIT, int NT>
 hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   constexpr int NSPLIT = D / (16 * NT);
   timing_before("chunk_prep", st);
-  if constexpr (R <= 2 && !SPLIT && (D == 64 || D == 128))
-    hipLaunchKernelGGL((chunk_prep2_kernel<ActT, D, R>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
-  else
+  if constexpr (R <= 2 && !SPLIT && (D == 64 || D == 128)) {
+    // the records end at ss_off. Up to 134 MB they were still cached when the state pass read them
+    // (non-temporal stores cost 160 -> 207 us at 16 value heads x 4096 tokens); from 201 MB on,
+    // non-temporal stores measured 4-6% faster calls (32 value heads x 1-3 sequences x 4096 tokens)
+    if (p.ss_off > kNtRecordBytes)
+      hipLaunchKernelGGL((chunk_prep2_kernel<ActT, D, R, true>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((chunk_prep2_kernel<ActT, D, R, false>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+  } else
     hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
   timing_after(st);
   hipError_t e = hipGetLastError();
