@@ -113,6 +113,13 @@ def test_prefill_4k_single_layer():
     _prefill_case(SMALL, 0, 1, 4096, [4096])
 
 
+def test_prefill_streamed_records_ragged():
+    """Two ragged sequences (4096 and 3000 tokens) at 16/32 heads: about 400 MB of chunk records, which
+    the record builder stores non-temporally, and 64 (sequence, head) pairs, whose 32-column state-pass
+    slices exchange row sums for the gated norm. Both sequences against the oracle."""
+    _prefill_case(NEXT, 13, 2, 4096, [4096, 3000], state_std=0.05, tail_rand=True)
+
+
 def test_prefill_stack_layer_sampled():
     """Stack-layer shape (8 x 8192 tokens, 16/32 heads) on the GPU; sequences 0 and 7 against the oracle."""
     _prefill_case(NEXT, 1, 8, 8192, [8192] * 8, sample=[0, 7])
