@@ -8,10 +8,11 @@
 // 4 fp32 channels) and a span of kSpan tokens, which it walks in groups of kG rows with a rolling 3-row
 // window: the next group's rows are loaded before the current group is computed, so every input row is
 // read once (plus a 3-row halo per span) and loads stay in flight under the arithmetic.  Rows are
-// streamed, so they are loaded and stored non-temporally.  Workgroup w runs job J = (w % 8) * (N / 8) + w / 8 so that each
-// XCD walks consecutive spans of one channel stripe and finds the halo rows in its own L2.  Only the
-// workgroups of the first span read the old tail, and each rewrites the tail of exactly its own
-// channels after its reads, so no other workgroup can observe a half-updated tail.
+// streamed, so they are loaded and stored non-temporally.  Workgroup w runs job
+// J = (w % 8) * (N / 8) + w / 8 so that each XCD walks consecutive spans of one channel stripe and
+// finds the halo rows in its own L2.  Only the workgroups of the first span read the old tail, and
+// each rewrites the tail of exactly its own channels after its reads, so no other workgroup can
+// observe a half-updated tail.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
