@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_BF16 = 0
 GDN_F32 = 1
+GDN_OUT_ACT = 0          # out in the activation dtype
+GDN_STATUS_RANGE = 1     # device status bit: a prefill's final state left the f16 operand range
 _ACT_TORCH = {GDN_BF16: torch.bfloat16, GDN_F32: torch.float32}
 
 _STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_EUNSUPPORTED", -3: "GDN_EHIP"}
@@ -40,7 +42,8 @@ class GdnUnsupported(GdnError):
 class _Desc(ctypes.Structure):
     _fields_ = [("n_k", ctypes.c_int32), ("n_v", ctypes.c_int32), ("d_k", ctypes.c_int32),
                 ("d_v", ctypes.c_int32), ("conv_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("out_dtype", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -53,7 +56,8 @@ EXPORTS = ("gdn_last_error", "gdn_version", "gdn_conv_chunk", "gdn_prefill_works
            "gdn_decode_step", "gdn_verify_with_checkpoints", "gdn_verify_paths", "gdn_accept", "gdn_accept_paths",
            "gdn_state_copy",
            "gdn_state_record_bytes", "gdn_state_zero", "gdn_pcache_create", "gdn_pcache_destroy", "gdn_pcache_row",
-           "gdn_pcache_stats", "gdn_pcache_alive", "gdn_mfma_probe", "gdn_timing_begin", "gdn_timing_end")
+           "gdn_pcache_stats", "gdn_pcache_alive", "gdn_mfma_probe", "gdn_timing_begin", "gdn_timing_end",
+           "gdn_device_status")
 
 
 def load_library(path: str = LIB_PATH):
@@ -91,6 +95,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_pcache_stats.argtypes = [P, ctypes.POINTER(L)]
     lib.gdn_pcache_alive.argtypes = [P, I, ctypes.POINTER(L)]
     lib.gdn_mfma_probe.argtypes = [P, I, I, P]
+    lib.gdn_device_status.argtypes = [I, P]
+    lib.gdn_device_status.restype = I
     lib.gdn_timing_begin.argtypes = [I]
     lib.gdn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), I]
     for name in ("gdn_conv_chunk", "gdn_prefill_chunk", "gdn_decode_step", "gdn_verify_with_checkpoints",
@@ -116,6 +122,7 @@ class GdnDesc:
     scale: float = 0.0      # <= 0: d_k ** -0.5
     l2_eps: float = 1e-6
     rms_eps: float = 1e-6
+    out_dtype: int = GDN_OUT_ACT  # or GDN_F32: fp32 outputs (with bf16 activations, before bf16 rounding)
 
     @property
     def conv_dim(self) -> int:
@@ -129,9 +136,14 @@ class GdnDesc:
     def act(self) -> torch.dtype:
         return _ACT_TORCH[self.act_dtype]
 
+    @property
+    def out(self) -> torch.dtype:
+        """dtype of the layer output"""
+        return torch.float32 if self.out_dtype == GDN_F32 else self.act
+
     def c(self) -> _Desc:
         return _Desc(self.n_k, self.n_v, self.d_k, self.d_v, self.conv_k, self.act_dtype, self.scale, self.l2_eps,
-                     self.rms_eps)
+                     self.rms_eps, self.out_dtype)
 
 
 @dataclass
@@ -221,7 +233,7 @@ def prefill_chunk(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, lens, conv_tail,
     dev = mixed.device
     nvd = desc.n_v * desc.d_v
     if out is None:
-        out = torch.empty(B, Lb, nvd, dtype=desc.act, device=dev)
+        out = torch.empty(B, Lb, nvd, dtype=desc.out, device=dev)
     if ws is None:
         ws = prefill_workspace(desc, B, Lb, dev)
     cw = _weights(desc, w, dev)
@@ -232,7 +244,7 @@ def prefill_chunk(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, lens, conv_tail,
             _dev(lens, "lens", (B,), torch.int32, dev),
             _dev(conv_tail, "conv_tail", (B, desc.kc, desc.conv_dim), desc.act, dev),
             _dev(state, "state", (B, desc.n_v, desc.d_k, desc.d_v), torch.float32, dev),
-            _dev(out, "out", (B, Lb, nvd), desc.act, dev))
+            _dev(out, "out", (B, Lb, nvd), desc.out, dev))
     wsp = _dev(ws, "ws", None, torch.uint8, dev)
     _check("gdn_prefill_chunk", lib.gdn_prefill_chunk(ctypes.byref(desc.c()), ctypes.byref(cw), *args, B, Lb, wsp,
                                                       ws.numel(), _stream()))
@@ -248,7 +260,7 @@ def decode_step(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, slot, conv_tail_po
     nvd = desc.n_v * desc.d_v
     npool = state_pool.shape[0]
     if out is None:
-        out = torch.empty(B, nvd, dtype=desc.act, device=dev)
+        out = torch.empty(B, nvd, dtype=desc.out, device=dev)
     if slot is not None and check_slots:
         _check_index(slot, "slot", npool, True)
     if slot is None and B > npool:
@@ -261,7 +273,7 @@ def decode_step(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, slot, conv_tail_po
             _opt(slot, "slot", (B,), torch.int32, dev),
             _dev(conv_tail_pool, "conv_tail_pool", (npool, desc.kc, desc.conv_dim), desc.act, dev),
             _dev(state_pool, "state_pool", (npool, desc.n_v, desc.d_k, desc.d_v), torch.float32, dev),
-            _dev(out, "out", (B, nvd), desc.act, dev))
+            _dev(out, "out", (B, nvd), desc.out, dev))
     _check("gdn_decode_step", lib.gdn_decode_step(ctypes.byref(desc.c()), ctypes.byref(cw), *args, B, _stream()))
     return out
 
@@ -280,7 +292,7 @@ def verify_with_checkpoints(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, slot, 
     if ckpt_tail is None:
         ckpt_tail = torch.empty(B, T, desc.kc, desc.conv_dim, dtype=desc.act, device=dev)
     if out is None:
-        out = torch.empty(B, T, nvd, dtype=desc.act, device=dev)
+        out = torch.empty(B, T, nvd, dtype=desc.out, device=dev)
     if slot is not None and check_slots:
         _check_index(slot, "slot", npool, False)
     cw = _weights(desc, w, dev)
@@ -293,7 +305,7 @@ def verify_with_checkpoints(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, slot, 
             _dev(state_pool, "state_pool", (npool, desc.n_v, desc.d_k, desc.d_v), torch.float32, dev),
             _dev(ckpt_state, "ckpt_state", (B, T, desc.n_v, desc.d_k, desc.d_v), torch.float32, dev),
             _dev(ckpt_tail, "ckpt_tail", (B, T, desc.kc, desc.conv_dim), desc.act, dev),
-            _dev(out, "out", (B, T, nvd), desc.act, dev))
+            _dev(out, "out", (B, T, nvd), desc.out, dev))
     _check("gdn_verify_with_checkpoints",
            lib.gdn_verify_with_checkpoints(ctypes.byref(desc.c()), ctypes.byref(cw), *args, T, *rest, B, _stream()))
     return ckpt_state, ckpt_tail, out
@@ -314,7 +326,7 @@ def verify_paths(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, slot, conv_tail_p
     if ckpt_tail is None:
         ckpt_tail = torch.empty(B, P, T, desc.kc, desc.conv_dim, dtype=desc.act, device=dev)
     if out is None:
-        out = torch.empty(B, P, T, nvd, dtype=desc.act, device=dev)
+        out = torch.empty(B, P, T, nvd, dtype=desc.out, device=dev)
     if slot is not None and check_slots:
         _check_index(slot, "slot", npool, False)
     cw = _weights(desc, w, dev)
@@ -327,7 +339,7 @@ def verify_paths(desc: GdnDesc, w: GdnWeights, mixed, z, a, b, slot, conv_tail_p
             _dev(state_pool, "state_pool", (npool, desc.n_v, desc.d_k, desc.d_v), torch.float32, dev),
             _dev(ckpt_state, "ckpt_state", (B, P, T, desc.n_v, desc.d_k, desc.d_v), torch.float32, dev),
             _dev(ckpt_tail, "ckpt_tail", (B, P, T, desc.kc, desc.conv_dim), desc.act, dev),
-            _dev(out, "out", (B, P, T, nvd), desc.act, dev))
+            _dev(out, "out", (B, P, T, nvd), desc.out, dev))
     _check("gdn_verify_paths",
            lib.gdn_verify_paths(ctypes.byref(desc.c()), ctypes.byref(cw), *args, T, P, *rest, B, _stream()))
     return ckpt_state, ckpt_tail, out
@@ -412,7 +424,7 @@ def state_zero(desc: GdnDesc, state, tail, idx=None, n: int = None):
 
 
 PCACHE_STATS = ("rows", "hits", "partial", "cold", "plain", "tokens_reused", "tokens_computed", "ckpts_made",
-                "evicted")
+                "evicted", "rows_kept")
 
 
 class PrefixStateCache:

@@ -3,7 +3,10 @@
 // synchronises with the host.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <mutex>
 
 #include <new>
 
@@ -47,7 +50,19 @@ int check_desc(const gdn_desc* d) {
   if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128)
     return fail(GDN_EUNSUPPORTED, "d_k=%d (built: 32, 64, 128)", d->d_k);
   if (!(d->l2_eps >= 0.f) || !(d->rms_eps >= 0.f)) return fail(GDN_EINVAL, "negative or NaN epsilon");
+  if (d->out_dtype != GDN_OUT_ACT && d->out_dtype != GDN_F32) return fail(GDN_EINVAL, "out_dtype=%d", d->out_dtype);
   return GDN_OK;
+}
+
+// fp32 outputs: with fp32 activations always, with bf16 ones when the caller asks for them
+int out_f32(const gdn_desc* d) { return d->act_dtype == GDN_F32 || d->out_dtype == GDN_F32 ? 1 : 0; }
+
+// The fused prefill serves d_k = d_v = 128 with bf16 activations. GDN_PREFILL_PATH=two_phase in the
+// environment selects the two-launch path instead (the one every other shape takes), for comparison.
+bool use_fused(const gdn_desc* d) {
+  if (d->d_k != 128 || d->act_dtype != GDN_BF16) return false;
+  const char* e = getenv("GDN_PREFILL_PATH");
+  return !(e && strcmp(e, "two_phase") == 0);
 }
 
 float q_scale(const gdn_desc* d) { return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->d_k); }
@@ -67,6 +82,33 @@ struct TimedLaunch {
 thread_local TimedLaunch* t_launch = nullptr;  // open session: capacity t_cap, t_used recorded
 thread_local int t_cap = 0, t_used = 0;
 
+}  // namespace
+
+// Device status word: kernels set bits in it (atomic OR) for conditions found on the device, which
+// gdn_device_status reports. Bit 0: a prefill's exit state (final state or segment map) left the range
+// its f16 operands can hold (|H| >= 255, or not finite).
+__device__ int gdn_status_word;
+
+namespace {
+// the word's device address on the current device (each device holds its own copy), looked up once
+int* status_ptr() {
+  static int* ptr[64];
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(gdn_status_word)) != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+    ptr[dev] = (int*)p;
+  });
+  return ptr[dev];
+}
 }  // namespace
 
 namespace gdn {
@@ -137,6 +179,21 @@ int gdn_timing_end(const char** kernels, float* ms, int cap) {
 
 const char* gdn_last_error(void) { return g_err; }
 
+int gdn_device_status(int clear, gdn_stream_t stream) {
+  int* ptr = status_ptr();
+  if (!ptr) return fail(GDN_EHIP, "gdn_device_status: no device status word on this device");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  int v = 0;
+  if (e == hipSuccess) e = hipMemcpy(&v, ptr, sizeof(int), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    const int zero = 0;
+    e = hipMemcpy(ptr, &zero, sizeof(int), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) return hip_status(e, "gdn_device_status");
+  g_err[0] = 0;
+  return v;
+}
+
 const char* gdn_version(void) { return "gdn-mi355x 0.1 (gfx950)"; }
 
 size_t gdn_state_record_bytes(const gdn_desc* d) {
@@ -161,6 +218,7 @@ int gdn_conv_chunk(const gdn_desc* d, const void* conv_w, const void* mixed, con
 
 size_t gdn_prefill_workspace_bytes(const gdn_desc* d, int B, int Lb) {
   if (check_desc(d) || B <= 0 || Lb <= 0) return 0;
+  if (use_fused(d)) return gdn::fused_ws_bytes(B, d->n_v, Lb);
   if (d->act_dtype == GDN_F32 && d->d_k > 64) return 0;
   const int n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
   return gdn::prefill_ws_bytes(B, d->n_k, d->n_v, d->d_k, Lb, n_chunks, d->act_dtype == GDN_F32);
@@ -184,14 +242,27 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
   const size_t need = gdn_prefill_workspace_bytes(d, B, Lb);
   if (ws_bytes < need) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace %zu bytes < %zu needed", ws_bytes, need);
   if (((uintptr_t)ws & 255u) != 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace must be 256-byte aligned");
-  if (!aligned16(state) || !aligned16(mixed) || !aligned16(z) || !aligned16(out) || !aligned16(conv_tail))
+  if (!aligned16(state) || !aligned16(mixed) || !aligned16(z) || !aligned16(out) || !aligned16(conv_tail) ||
+      !aligned16(w->norm_w))
     return fail(GDN_EINVAL, "gdn_prefill_chunk: buffers must be 16-byte aligned");
   if (out == mixed || out == z || (void*)state == out || conv_tail == out)
     return fail(GDN_EINVAL, "gdn_prefill_chunk: out aliases another buffer");
+  if (use_fused(d)) {
+    gdn::FusedArgs f{};
+    f.conv_w = w->conv_w; f.A_log = w->A_log; f.dt_bias = w->dt_bias; f.norm_w = w->norm_w;
+    f.mixed = mixed; f.z = z; f.a = a; f.b = b; f.len = len; f.tail = conv_tail; f.state = state; f.out = out;
+    f.out_f32 = out_f32(d); f.ws = ws; f.status = status_ptr();
+    f.B = B; f.Lb = Lb; f.n_k = d->n_k; f.n_v = d->n_v; f.C = (int)conv_channels(d);
+    gdn::fused_plan(B, d->n_v, Lb, f.nseg, f.seg_chunks);
+    f.scale = q_scale(d); f.l2_eps = d->l2_eps; f.rms_eps = d->rms_eps;
+    if ((long)B * d->n_v * f.nseg >= (1L << 31)) return fail(GDN_EINVAL, "gdn_prefill_chunk: grid too large");
+    return hip_status(gdn::launch_fused(f, (hipStream_t)stream), "gdn_prefill_chunk");
+  }
   gdn::PrefillArgs p{};
   p.conv_w = w->conv_w; p.A_log = w->A_log; p.dt_bias = w->dt_bias; p.norm_w = w->norm_w;
   p.mixed = mixed; p.z = z; p.a = a; p.b = b; p.len = len; p.tail = conv_tail; p.state = state; p.out = out;
   p.ws = ws; p.B = B; p.Lb = Lb; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d);
+  p.out_f32 = out_f32(d);
   p.n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
   p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
   gdn::prefill_ws_layout(p, d->d_k, d->act_dtype == GDN_F32);
@@ -215,6 +286,7 @@ static int step_common(const gdn_desc* d, const gdn_weights* w, const void* mixe
   p.mixed = mixed; p.z = z; p.a = a; p.b = b; p.slot = slot; p.tail_in = tail_in; p.state_in = state_in;
   p.tail_out = tail_out; p.state_out = state_out; p.out = out;
   p.B = B; p.T = T; p.P = P; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d); p.verify = verify;
+  p.out_f32 = out_f32(d);
   p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
   return hip_status(gdn::launch_step(p, d->act_dtype, d->d_k, d->n_v / d->n_k, (hipStream_t)stream), name);
 }

@@ -30,6 +30,7 @@ struct StepArgs {
   void* tail_out;       // decode: the pool; verify: [B*P*T][3][C]
   float* state_out;     // decode: the pool; verify: [B*P*T][n_v][D][D]
   void* out;            // [B*P][T][n_v*D]
+  int out_f32;          // 1: out is fp32 (always with fp32 activations), 0: the activation type
   int B, T, n_k, n_v, C;
   int P;                // rows per sequence: 1, or the paths of a batch-of-paths verify
   int verify;
@@ -64,6 +65,7 @@ struct PrefillArgs {
   void* tail;           // [B][3][C] in/out
   float* state;         // [B][n_v][D][D] in/out
   void* out;            // [B][Lb][n_v*D]
+  int out_f32;          // 1: out is fp32 (always with fp32 activations), 0: the activation type
   void* ws;             // workspace: value records, key records (n_v > n_k), then (split heads only)
                         // the partial sums of squares of every row, one per slice ([sequence][head]
                         // [token][slice] for the exchange, [sequence][token][head][slice] for a norm
@@ -78,6 +80,36 @@ struct PrefillArgs {
 size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool split_all);
 void prefill_ws_layout(PrefillArgs& p, int D, bool split_all);
 hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hipStream_t st);
+
+// ---- fused prefill (d_k = d_v = 128, bf16 activations) ----------------------------------------------
+struct FusedArgs {
+  const void* conv_w;
+  const float* A_log;
+  const float* dt_bias;
+  const float* norm_w;
+  const void* mixed;    // [B][Lb][C]
+  const void* z;        // [B][Lb][n_v*128]
+  const void* a;        // [B][Lb][n_v]
+  const void* b;        // [B][Lb][n_v]
+  const int32_t* len;   // [B]
+  void* tail;           // [B][3][C] in/out (updated by the last launch of the call)
+  float* state;         // [B][n_v][128][128] in/out
+  void* out;            // [B][Lb][n_v*128]
+  int out_f32;          // 1: out is fp32, 0: bf16
+  void* ws;             // segment maps and states (nseg > 1), else unused
+  float* seg_map;       // [B][n_v][nseg-1][2][128][128]: N_s, M_s (set by launch_fused)
+  float* seg_in;        // [B][n_v][nseg][128][128]: entering state of segment s >= 1 (set by launch_fused)
+  int* status;          // device word: bit 0 set when a final state leaves the operand range (or null)
+  int B, Lb, n_k, n_v, C;
+  int nseg, seg_chunks; // segments per (sequence, head) and chunks per segment
+  float scale, l2_eps, rms_eps;
+};
+// compute units of the current device (read once per device; 0 if unknown)
+int device_cus();
+// segment plan of a call (nseg = 1: one workgroup per (sequence, head) walks every chunk)
+void fused_plan(int B, int n_v, int Lb, int& nseg, int& seg_chunks);
+size_t fused_ws_bytes(int B, int n_v, int Lb);
+hipError_t launch_fused(FusedArgs p, hipStream_t st);
 
 // ---- state records and accept ---------------------------------------------------------------------
 struct CopyArgs {

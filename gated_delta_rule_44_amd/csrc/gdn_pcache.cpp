@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <list>
+#include <map>
 #include <new>
 #include <set>
 #include <unordered_map>
@@ -23,7 +24,7 @@
 
 struct gdn_pcache {
   struct Ckpt {
-    int group;
+    int64_t group;
     int pos;
     int slot;
     std::list<int64_t>::iterator lru;  // position in the use order
@@ -31,9 +32,11 @@ struct gdn_pcache {
   struct Group {
     std::vector<int32_t> ids;          // the prefix tokens of the row that made it
     std::vector<int64_t> ckpts;        // its checkpoints, in position order (evicted ones included)
+    int live = 0;                      // of which still cached; the group goes with its last one
   };
   int slots, stride, tail, align, max_chunk, min_prefix;
-  std::vector<Group> groups;                  // creation order
+  std::map<int64_t, Group> groups;            // rows with a live checkpoint, by creation number
+  int64_t groups_made = 0;
   std::unordered_map<int64_t, Ckpt> ckpts;    // live checkpoints by number
   std::list<int64_t> lru;                     // least recently used first
   std::vector<int> free_slots;
@@ -100,14 +103,16 @@ int gdn_pcache_row(gdn_pcache* c, const int32_t* ids, int n, int p_state, int ca
   // the deepest usable checkpoint (the first one found among equals)
   int64_t best = -1;
   int best_pos = -1;
-  for (const gdn_pcache::Group& g : c->groups) {
+  for (const auto& kv : c->groups) {
+    const gdn_pcache::Group& g = kv.second;
     const int m = std::min((int)g.ids.size(), p);
     if (m == 0 || g.ids[0] != ids[0]) continue;
     int lcp = 0;
     while (lcp < m && g.ids[lcp] == ids[lcp]) ++lcp;
     for (int64_t num : g.ckpts) {
       auto it = c->ckpts.find(num);
-      if (it != c->ckpts.end() && it->second.pos <= lcp && it->second.pos > best_pos) {
+      if (it == c->ckpts.end() || it->second.pos > lcp) continue;
+      if (it->second.pos > best_pos || (it->second.pos == best_pos && num < best)) {  // ties: made first
         best = num;
         best_pos = it->second.pos;
       }
@@ -131,15 +136,16 @@ int gdn_pcache_row(gdn_pcache* c, const int32_t* ids, int n, int p_state, int ca
   }
   std::vector<int64_t> fresh;
   if (!bs.empty()) {
-    c->groups.push_back(gdn_pcache::Group());
-    gdn_pcache::Group& g = c->groups.back();
+    const int64_t gid = c->groups_made++;
+    gdn_pcache::Group& g = c->groups[gid];
     g.ids.assign(ids, ids + p);
+    g.live = (int)bs.size();
     for (int b : bs) {
       const int64_t num = c->made++;
       g.ckpts.push_back(num);
       c->lru.push_back(num);
       gdn_pcache::Ckpt k;
-      k.group = (int)c->groups.size() - 1;
+      k.group = gid;
       k.pos = b;
       k.slot = -1;
       k.lru = std::prev(c->lru.end());
@@ -155,9 +161,12 @@ int gdn_pcache_row(gdn_pcache* c, const int32_t* ids, int n, int p_state, int ca
     c->lru.pop_front();
     auto it = c->ckpts.find(num);
     if (it->second.slot >= 0) c->free_slots.push_back(it->second.slot);
+    auto g = c->groups.find(it->second.group);
+    if (--g->second.live == 0) c->groups.erase(g);  // no checkpoint of that row is left
     c->ckpts.erase(it);
     c->stats[GDN_PCACHE_EVICTED]++;
   }
+  c->stats[GDN_PCACHE_ROWS_KEPT] = (int64_t)c->groups.size();
   for (size_t i = 0; i < fresh.size(); ++i) {
     auto it = c->ckpts.find(fresh[i]);
     if (it != c->ckpts.end()) {

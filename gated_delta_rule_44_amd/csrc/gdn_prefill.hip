@@ -202,6 +202,14 @@ struct Act4<bf16_t> {
   }
 };
 
+// four output values at element index i of out: fp32 when the call asked for fp32 outputs, else the
+// activation type
+template <typename ActT>
+__device__ __forceinline__ void store_out4(const PrefillArgs& p, long i, float4 v) {
+  if (std::is_same<ActT, float>::value || p.out_f32) *(float4*)((float*)p.out + i) = v;
+  else Act4<ActT>::store((ActT*)p.out + i, v);
+}
+
 // two adjacent activations (4 bytes of bf16 or 8 of fp32), loaded as stored and widened when used
 template <typename ActT>
 struct Pair {
@@ -1321,7 +1329,6 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
   __shared__ float4 sY[XCH ? kRing * 4 * NT * kWave : 1];
   __shared__ RawZ sZ[XCH ? 2 * 4 * NT * kWave : 1];
 
-  ActT* out = (ActT*)p.out;
   float* sspart = (float*)((char*)p.ws + p.ss_off);
   float* oraw = (float*)((char*)p.ws + p.oraw_off);
 
@@ -1370,7 +1377,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float4 y = sY[(((cc % kRing) * 4 + tt) * NT + nt) * kWave + lane];
-        Act4<ActT>::store(out + row * D + cb + 16 * nt + 4 * g16, make_float4(y.x * inv, y.y * inv, y.z * inv, y.w * inv));
+        store_out4<ActT>(p, row * D + cb + 16 * nt + 4 * g16, make_float4(y.x * inv, y.y * inv, y.z * inv, y.w * inv));
       }
     }
   };
@@ -1602,7 +1609,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
         ld_z(f, cn);
         if (t < Lb) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) Act4<ActT>::store(out + row * D + cb + 16 * nt + 4 * g16, res[nt]);
+          for (int nt = 0; nt < NT; ++nt) store_out4<ActT>(p, row * D + cb + 16 * nt + 4 * g16, res[nt]);
         }
       } else if constexpr (XCH) {
 #pragma unroll
@@ -1727,7 +1734,7 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
   const float4 nw = *(const float4*)(p.norm_w + 4 * cq);
   const float4 v = make_float4(nw.x * (o.x * inv) * silu(z.x), nw.y * (o.y * inv) * silu(z.y),
                                nw.z * (o.z * inv) * silu(z.z), nw.w * (o.w * inv) * silu(z.w));
-  Act4<ActT>::store((ActT*)p.out + row * D + 4 * cq, v);
+  store_out4<ActT>(p, row * D + 4 * cq, v);
 }
 
 // ---- launch configuration --------------------------------------------------------------------------
@@ -1758,22 +1765,7 @@ bool pass_exchange(int B, int n_v, int D, int Lb) {
 // The exchange's waits end because every slice of a head is resident at once: the grid (at most 256
 // workgroups, one per CU) must fit the device's CUs, which a partitioned or shared device may not
 // offer; then the call takes the norm pass, which never waits. CU counts are read once per device.
-bool exchange_fits(long grid) {
-  static int cus[64];
-  static std::once_flag once[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipGetLastError();
-    return false;
-  }
-  std::call_once(once[dev], [dev] {
-    if (hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-      (void)hipGetLastError();
-      cus[dev] = 0;
-    }
-  });
-  return grid <= cus[dev];
-}
+bool exchange_fits(long grid) { return grid <= device_cus(); }
 
 // bytes of one value record and of one key record (zero without key records)
 template <int D, bool SPLIT>
@@ -1849,6 +1841,23 @@ hipError_t launch_r(const PrefillArgs& p, int R, hipStream_t st) {
 }
 
 }  // namespace
+
+int device_cus() {
+  static int cus[64];
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::call_once(once[dev], [dev] {
+    if (hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      cus[dev] = 0;
+    }
+  });
+  return cus[dev];
+}
 
 size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool split_all) {
   const int nsplit = D / (16 * pass_nt(B, n_v, D));

@@ -277,7 +277,11 @@ void step_kernel(StepArgs p) {
         const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
         const long ob = row * (long)n_v * D + (long)h * D;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) out[ob + 4 * cq + c] = from_f32<ActT>(nw[c] * (o[c] * inv) * silu(in.z[c]));
+        for (int c = 0; c < 4; ++c) {
+          const float y = nw[c] * (o[c] * inv) * silu(in.z[c]);
+          if (p.out_f32) ((float*)p.out)[ob + 4 * cq + c] = y;
+          else out[ob + 4 * cq + c] = from_f32<ActT>(y);
+        }
       }
       lds_barrier();  // sY, sRed and sTot reused by the next token or item
     }

@@ -46,6 +46,7 @@ typedef struct ihipStream_t* gdn_stream_t; /* the same handle as hipStream_t */
 
 enum { GDN_OK = 0, GDN_EINVAL = -1, GDN_EUNSUPPORTED = -2, GDN_EHIP = -3 };
 enum { GDN_BF16 = 0, GDN_F32 = 1 };
+enum { GDN_OUT_ACT = 0 };
 
 /* Layer shape and constants (host struct, read during the call only). */
 typedef struct {
@@ -56,6 +57,9 @@ typedef struct {
   float scale;        /* q scale; <= 0 selects d_k^-1/2 */
   float l2_eps;       /* q/k L2 norm: x / sqrt(sum x^2 + l2_eps) */
   float rms_eps;      /* gated RMSNorm epsilon */
+  int32_t out_dtype;  /* dtype of `out` in prefill, decode and verify: GDN_OUT_ACT (0) = the activation
+                         dtype, or GDN_F32 = fp32 (with bf16 activations: the output before its bf16
+                         rounding) */
 } gdn_desc;
 
 /* Layer weights (host struct holding device pointers). */
@@ -71,6 +75,17 @@ const char* gdn_last_error(void);
 
 /* Library version string. */
 const char* gdn_version(void);
+
+/*
+ * Conditions found on the device by earlier calls, as bits (host function; synchronizes `stream`,
+ * then reads the device's status word, and clears it when `clear` is non-zero). Returns the bits
+ * (>= 0) or GDN_EHIP. Bit 0 (GDN_STATUS_RANGE): a prefill's final state left the range its f16
+ * operand pairs carry (|state| >= 255 or not finite); that call's state and outputs are not to be
+ * trusted. Kernels only set bits, so the word collects every call since it was last cleared, on
+ * every stream of the device.
+ */
+enum { GDN_STATUS_RANGE = 1 };
+int gdn_device_status(int clear, gdn_stream_t stream);
 
 /*
  * Causal conv1d + SiLU over [conv_tail | mixed] (statecache.py page, CacheQwen35._gdn: the conv on
@@ -232,6 +247,7 @@ enum {
   GDN_PCACHE_TOKENS_COMPUTED,
   GDN_PCACHE_CKPTS_MADE,
   GDN_PCACHE_EVICTED,
+  GDN_PCACHE_ROWS_KEPT,         /* rows whose token ids are kept: those with a live checkpoint (a gauge) */
   GDN_PCACHE_NSTATS
 };
 int gdn_pcache_create(int slots, int stride, int tail, int align, int max_chunk, int min_prefix, gdn_pcache** out);

@@ -1,102 +1,155 @@
-"""Bookkeeping of the GDN prefix-state cache, written plainly from the "qev_fast/statecache.py" page
-(StateCache: _lookup, _bounds, _row, _done, _touch, _evict). TEST INFRASTRUCTURE ONLY.
+"""Reference model of the GDN prefix-state cache's bookkeeping. TEST INFRASTRUCTURE ONLY: the tests use it
+to check the library's host-side cache (gdn_pcache_*); nothing in the product imports it.
 
-Only the recurrent part is modelled: a checkpoint is the fp32 state and conv tail after its first
-`pos` tokens; the attention K / V the page also keeps is not part of this layer. Capacity is counted
-in checkpoints (every checkpoint has the same size), where the page counts bytes. Checkpoints are
-numbered in the order they are made, so that another implementation can be compared with this one.
+What it models, as the "qev_fast/statecache.py" page's StateCache describes the cache (its lookup, chunk
+ends, row bookkeeping and LRU eviction), restated as rules:
+
+  * a checkpoint is the recurrent state (fp32 state + conv tail) of one sequence after its first `pos`
+    tokens, made while some earlier row ran; the attention K / V that the page also keeps belongs to
+    other layers and is left out;
+  * a row of n tokens whose state should cover p_state tokens can only checkpoint P = min(p_state, n)
+    tokens, rounded down to a multiple of `align` (p); rows with p < min_prefix bypass the cache;
+  * a checkpoint serves a new row when its pos is no longer than the prefix the new row (its first p
+    tokens) has in common with the row that made it; the row starts from the deepest such checkpoint
+    (among equally deep ones, the one made first), or from zero;
+  * the row then stops, and saves a checkpoint, at every multiple of `stride` strictly between the
+    start and p, at P - tail rounded down, and at p itself (each only if it lies past the start),
+    with extra stops so that no stretch is longer than max_chunk;
+  * capacity counts checkpoints (all have the same size; the page counts bytes); using a checkpoint
+    makes it the most recently used one, new checkpoints are the most recent, and the least recently
+    used ones go while there are too many.
+
+Checkpoints are numbered in the order they are made so that another implementation can be compared
+with this one number for number. A row whose checkpoints have all been evicted is forgotten.
 """
 from __future__ import annotations
 
-from collections import OrderedDict
+from dataclasses import dataclass
 
 import numpy as np
+
+
+@dataclass
+class _Checkpoint:
+    num: int      # order of creation
+    pos: int      # tokens the saved state covers
+    owner: int    # key of the row (token ids) that made it
+
+
+def common_prefix(a: np.ndarray, b: np.ndarray) -> int:
+    """Length of the longest common prefix of two id arrays."""
+    m = min(len(a), len(b))
+    same = a[:m] == b[:m]
+    if same.all():
+        return m
+    return int(np.argmin(same))  # first position where they differ
 
 
 class PrefixCacheModel:
     def __init__(self, capacity: int, stride: int = 2048, tail: int = 16, align: int = 64, max_chunk: int = 2048,
                  min_prefix: int = 256):
+        if max_chunk <= 0:
+            raise ValueError("max_chunk must be positive")
         self.capacity, self.stride, self.tail, self.align = capacity, stride, tail, align
         self.max_chunk, self.min_prefix = max_chunk, min_prefix
-        self.groups = []              # [ids, [checkpoint numbers]] in creation order
-        self.ckpts = OrderedDict()    # number -> (group index, pos); least recently used first
-        self.made = 0
+        self.lru: list[_Checkpoint] = []        # live checkpoints, least recently used first
+        self.owners: dict[int, np.ndarray] = {}  # row key -> the token ids it checkpointed
+        self.next_num = 0
+        self.next_owner = 0
         self.stats = dict(rows=0, hits=0, partial=0, cold=0, plain=0, tokens_reused=0, tokens_computed=0,
-                          ckpts_made=0, evicted=0)
+                          ckpts_made=0, evicted=0, rows_kept=0)
 
-    def _down(self, x):
-        return x - x % self.align if self.align else x
+    def round_down(self, x: int) -> int:
+        if not self.align:
+            return x
+        return (x // self.align) * self.align
 
-    def _lookup(self, x):
-        """Checkpoints usable by a row whose checkpointable prefix is x: pos <= the prefix it shares with the
-        row that made them."""
-        out = []
-        for gi, (ids, nums) in enumerate(self.groups):
-            m = min(len(ids), len(x))
-            if m == 0 or ids[0] != x[0]:
-                continue
-            ne = np.flatnonzero(ids[:m] != x[:m])
-            lcp = int(ne[0]) if len(ne) else m
-            out += [c for c in nums if c in self.ckpts and self.ckpts[c][1] <= lcp]
-        return out
+    def deepest(self, prefix: np.ndarray):
+        """The live checkpoint a row with this checkpointable prefix starts from, or None."""
+        shared = {}   # owner -> common prefix length with this row, computed once per owner
+        best = None
+        for ck in sorted(self.lru, key=lambda c: c.num):
+            if ck.owner not in shared:
+                shared[ck.owner] = common_prefix(self.owners[ck.owner], prefix)
+            if ck.pos <= shared[ck.owner] and (best is None or ck.pos > best.pos):
+                best = ck
+        return best
 
-    def _bounds(self, c, p):
-        """Chunk ends from c for a state of p tokens: multiples of stride, p - tail and p (rounded down to
-        align), no chunk longer than max_chunk."""
-        e = self._down(p)
-        b = {k for k in range(self.stride, e, self.stride) if k > c} if self.stride else set()
-        if self.tail and self._down(p - self.tail) > c:
-            b.add(self._down(p - self.tail))
-        if e > c:
-            b.add(e)
-        out, s = [], c
-        for x in sorted(b):
-            while x - s > self.max_chunk:
-                s += self.max_chunk
-                out.append(s)
-            out.append(x)
-            s = x
-        return out
+    def chunk_ends(self, start: int, state_len: int) -> list[int]:
+        """The stops of a row that resumes at `start` and should checkpoint `state_len` tokens."""
+        end = self.round_down(state_len)
+        stops = set()
+        if self.stride:
+            k = (start // self.stride + 1) * self.stride
+            while k < end:
+                stops.add(k)
+                k += self.stride
+        if self.tail:
+            before_tail = self.round_down(state_len - self.tail)
+            if before_tail > start:
+                stops.add(before_tail)
+        if end > start:
+            stops.add(end)
+        ends, prev = [], start
+        for stop in sorted(stops):
+            extra = (stop - prev - 1) // self.max_chunk  # stretches longer than max_chunk are cut
+            ends.extend(prev + self.max_chunk * i for i in range(1, extra + 1))
+            ends.append(stop)
+            prev = stop
+        return ends
+
+    def _evict(self):
+        while len(self.lru) > self.capacity:
+            gone = self.lru.pop(0)
+            self.stats["evicted"] += 1
+            if not any(c.owner == gone.owner for c in self.lru):
+                del self.owners[gone.owner]
 
     def row(self, ids, p_state):
-        """Plan and book one row -> (restored checkpoint number or -1, c0, p, bounds, new checkpoint numbers
-        that survive the row's eviction, or -1 for those evicted at once)."""
+        """Plan and book one row -> (restored checkpoint number or -1, c0, p, chunk ends, the new
+        checkpoints' numbers, with -1 for those evicted at once)."""
         ids = np.asarray(ids, dtype=np.int64)
         n = len(ids)
-        p = self._down(min(p_state, n))
+        state_len = min(p_state, n)
+        p = self.round_down(state_len)
         if p < self.min_prefix:
             self.stats["plain"] += 1
             self.stats["tokens_computed"] += n
             return -1, 0, p, [], []
-        x = ids[:p]
-        cands = self._lookup(x)
-        best = None
-        for c in cands:  # the first of the deepest
-            if best is None or self.ckpts[c][1] > self.ckpts[best][1]:
-                best = c
-        c0 = self.ckpts[best][1] if best is not None else 0
+        prefix = ids[:p]
+        start_ck = self.deepest(prefix)
+        c0 = start_ck.pos if start_ck is not None else 0
         self.stats["rows"] += 1
-        self.stats["hits" if c0 == p else ("partial" if c0 > 0 else "cold")] += 1
-        bounds = self._bounds(c0, min(p_state, n)) if c0 < p else []  # the page passes the unrounded length
+        if c0 == p:
+            self.stats["hits"] += 1
+        elif c0 > 0:
+            self.stats["partial"] += 1
+        else:
+            self.stats["cold"] += 1
         self.stats["tokens_reused"] += c0
         self.stats["tokens_computed"] += n - c0
-        if best is not None:
-            self.ckpts.move_to_end(best)
-        new = []
-        if bounds:
-            self.groups.append([x.copy(), []])
-            gi = len(self.groups) - 1
-            for b in bounds:
-                num = self.made
-                self.made += 1
-                self.groups[gi][1].append(num)
-                self.ckpts[num] = (gi, b)
-                new.append(num)
+        if start_ck is not None:  # a use: most recently used now
+            self.lru.remove(start_ck)
+            self.lru.append(start_ck)
+        ends = self.chunk_ends(c0, state_len) if c0 < p else []
+        made = []
+        if ends:
+            owner = self.next_owner
+            self.next_owner += 1
+            self.owners[owner] = prefix.copy()
+            for pos in ends:
+                ck = _Checkpoint(self.next_num, pos, owner)
+                self.next_num += 1
+                self.lru.append(ck)
+                made.append(ck.num)
                 self.stats["ckpts_made"] += 1
-        while len(self.ckpts) > self.capacity:
-            self.ckpts.popitem(last=False)
-            self.stats["evicted"] += 1
-        return (best if best is not None else -1), c0, p, bounds, [c if c in self.ckpts else -1 for c in new]
+        self._evict()
+        self.stats["rows_kept"] = len(self.owners)
+        live = {c.num for c in self.lru}
+        return (start_ck.num if start_ck is not None else -1), c0, p, ends, [m if m in live else -1 for m in made]
 
     def alive(self):
-        return sorted(self.ckpts)
+        return sorted(c.num for c in self.lru)
+
+    def rows_remembered(self) -> int:
+        return len(self.owners)

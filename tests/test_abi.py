@@ -84,18 +84,44 @@ def test_sizes():
     lib = gdn.load_library()
     d = gdn.GdnDesc(n_k=16, n_v=32, d_k=128, d_v=128)
     assert gdn.state_record_bytes(d) == 32 * 128 * 128 * 4 + 3 * 8192 * 2
-    # 8 x 32 (sequence, head) pairs fill the chip with whole heads: only the chunk records count
+    # the fused prefill (d = 128, bf16): no workspace where the (sequence, head) units fill the chip or
+    # the call is short; segment maps and states where few units run long calls
+    assert gdn.prefill_workspace_bytes(d, 8, 100) == 0
+    assert gdn.prefill_workspace_bytes(d, 8, 8192) == 0
+    assert gdn.prefill_workspace_bytes(d, 1, 256) == 0           # 4 chunks: too short for segments
+    S = 5                                                          # 32 units: min(256 / 64 + 1, 64 / 4)
+    assert gdn.prefill_workspace_bytes(d, 1, 4096) == 32 * (2 * (S - 1) + S) * 128 * 128 * 4
+    assert gdn.prefill_workspace_bytes(gdn.GdnDesc(n_k=2, n_v=4, d_k=128, d_v=128, act_dtype=gdn.GDN_F32), 1, 64) == 0
+    # a workspace sized for the longest call serves every shorter one (sizes never shrink as Lb grows)
+    for dd in (d, gdn.GdnDesc(n_k=16, n_v=16, d_k=128, d_v=128), gdn.GdnDesc(n_k=2, n_v=4, d_k=64, d_v=64)):
+        for B in (1, 2, 3, 4, 5):
+            sizes = [gdn.prefill_workspace_bytes(dd, B, L) for L in (64, 511, 512, 960, 1024, 1025, 2048, 4096, 8192)]
+            assert sizes == sorted(sizes), (dd, B, sizes)
+
+
+def test_sizes_two_phase(monkeypatch):
+    """The two-launch path (every shape but d = 128 bf16, or all with GDN_PREFILL_PATH=two_phase): chunk
+    records, plus the staged o of split heads."""
+    monkeypatch.setenv("GDN_PREFILL_PATH", "two_phase")
+    d = gdn.GdnDesc(n_k=16, n_v=32, d_k=128, d_v=128)
     n = gdn.prefill_workspace_bytes(d, 8, 100)
     assert n > 0 and n % 256 == 0
     assert gdn.prefill_workspace_bytes(d, 8, 128) == n  # 100 and 128 tokens both take two chunks
-    # few (sequence, head) pairs: heads are split over workgroups and o is staged per token
     assert gdn.prefill_workspace_bytes(d, 1, 128) > gdn.prefill_workspace_bytes(d, 1, 100) > 0
-    assert gdn.prefill_workspace_bytes(gdn.GdnDesc(n_k=2, n_v=4, d_k=128, d_v=128, act_dtype=gdn.GDN_F32), 1, 64) == 0
-    # for a fixed batch the size never shrinks as Lb grows, also where the split heads of a call of
-    # 1024 tokens or more switch from the norm pass to the exchange of row sums
     for B in (1, 2, 3, 4, 5):
         sizes = [gdn.prefill_workspace_bytes(d, B, L) for L in (64, 960, 1000, 1023, 1024, 1025, 2048)]
         assert sizes == sorted(sizes), (B, sizes)
+
+
+def test_desc_out_dtype_checked():
+    lib = gdn.load_library()
+    d = _desc()
+    d.out_dtype = 7
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(d), 1, 64) == 0
+    p = ctypes.c_void_p(256)
+    w = gdn._Weights(256, 256, 256, 256)
+    assert lib.gdn_decode_step(ctypes.byref(d), ctypes.byref(w), p, p, p, p, None, p, p, p, 1, None) == -1
+    assert b"out_dtype=7" in lib.gdn_last_error()
 
 
 def test_python_layer_rejects_cpu_tensors():

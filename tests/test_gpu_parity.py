@@ -591,14 +591,38 @@ def test_split_exchange_graph_replay_equals_eager():
 
 
 @pytest.mark.parametrize("dims,B,L,launches", [
+    (SMALL, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),       # 16 units: segment maps, scan, segments
+    (NEXT, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),        # 32 units
+    (NEXT, 2, 1030, ["fused", "tail"]),                                   # 64 units, 17 chunks: too short for segments
+    (NEXT, 8, 512, ["fused", "tail"]),                                    # 256 units fill the chip
+])
+def test_prefill_fused_launches(dims, B, L, launches):
+    """Which launches a d = 128 bf16 prefill call makes: the fused kernel with one workgroup per
+    (sequence, value head), preceded by the segment maps and the scan where few units run long calls,
+    then the conv-tail update."""
+    _say(f"fused launches B={B} L={L} dims={dims}")
+    d = desc_of(dims)
+    w, x, rng = make_layer(7, dims, B, L)
+    tail = act(np.zeros(dims.tail_shape(B), np.float32), dims)
+    st = f32(np.zeros(dims.state_shape(B), np.float32))
+    gdn.timing_begin(16)
+    gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims),
+                      i32(x.lens), tail, st)
+    recs = gdn.timing_end(16)
+    assert [n for n, _ in recs] == launches
+
+
+@pytest.mark.parametrize("dims,B,L,launches", [
     (SMALL, 1, 4096, ["chunk_prep", "state_pass", "norm"]),                # 8 slices of 16 columns: norm pass
     (NEXT, 2, 1030, ["chunk_prep", "state_pass"]),                        # 4 slices, >= 1024 tokens: exchange
     (NEXT, 2, 512, ["chunk_prep", "state_pass", "norm"]),                 # 4 slices, a short call: norm pass
     (NEXT, 5, 256, ["chunk_prep", "state_pass"]),                         # 160 pairs: whole heads
 ])
-def test_prefill_norm_mode_launches(dims, B, L, launches):
-    """Which launches a prefill call makes: the gated norm is finished by the state pass (whole heads, or
-    split heads exchanging row sums on calls of at least 1024 tokens) or by a separate norm pass."""
+def test_prefill_norm_mode_launches(dims, B, L, launches, monkeypatch):
+    """The two-launch path (GDN_PREFILL_PATH=two_phase): the gated norm is finished by the state pass
+    (whole heads, or split heads exchanging row sums on calls of at least 1024 tokens) or by a separate
+    norm pass."""
+    monkeypatch.setenv("GDN_PREFILL_PATH", "two_phase")
     _say(f"norm mode launches B={B} L={L} dims={dims}")
     d = desc_of(dims)
     w, x, rng = make_layer(7, dims, B, L)

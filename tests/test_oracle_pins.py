@@ -396,12 +396,12 @@ def test_prefix_model_bounds_hand_worked():
     from oracle.prefix_cache import PrefixCacheModel
     m = PrefixCacheModel(8, stride=2048, tail=16, align=64)
     # stride multiples below p = 4992, p - tail = 4984 rounded down to 4928, and p
-    assert m._bounds(0, 5000) == [2048, 4096, 4928, 4992]
-    assert m._bounds(4096, 5000) == [4928, 4992]
+    assert m.chunk_ends(0, 5000) == [2048, 4096, 4928, 4992]
+    assert m.chunk_ends(4096, 5000) == [4928, 4992]
     # p - tail rounds down to 0, not past the start: only p
-    assert m._bounds(0, 64) == [64]
+    assert m.chunk_ends(0, 64) == [64]
     # no stride, no tail: p alone, cut into chunks of at most 2048
-    assert PrefixCacheModel(8, stride=0, tail=0, max_chunk=2048)._bounds(0, 5000) == [2048, 4096, 4992]
+    assert PrefixCacheModel(8, stride=0, tail=0, max_chunk=2048).chunk_ends(0, 5000) == [2048, 4096, 4992]
 
 
 def test_prefix_model_lookup_and_lru_hand_worked():
@@ -424,4 +424,16 @@ def test_prefix_model_lookup_and_lru_hand_worked():
     # a row below min_prefix takes the plain path
     assert m.row(A[:200], 200) == (-1, 0, 192, [], [])
     assert m.stats == dict(rows=5, hits=1, partial=0, cold=4, plain=1, tokens_reused=960,
-                           tokens_computed=4 * 1000 + 40 + 200, ckpts_made=4, evicted=2)
+                           tokens_computed=4 * 1000 + 40 + 200, ckpts_made=4, evicted=2, rows_kept=2)
+    # the rows whose checkpoints are all gone are forgotten: A (checkpoint 0) and D (checkpoint 2) stay
+    assert m.rows_remembered() == 2
+
+
+def test_prefix_model_forgets_evicted_rows():
+    """Many distinct rows through a small pool: the model keeps at most one row per live checkpoint."""
+    from oracle.prefix_cache import PrefixCacheModel
+    m = PrefixCacheModel(3, stride=512, tail=0, align=64, min_prefix=64)
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        m.row(rng.integers(0, 1000, size=int(rng.integers(64, 1500))), 1500)
+        assert m.rows_remembered() <= len(m.alive()) <= 3

@@ -58,6 +58,29 @@ def test_cache_matches_model(cfg):
     st = cache.stats()
     assert st == {k: model.stats[k] for k in gdn.PCACHE_STATS}
     assert st["rows"] + st["plain"] == 120 and st["hits"] + st["partial"] > 0
+    # only rows with a live checkpoint keep their token ids
+    assert st["rows_kept"] == model.rows_remembered() <= len(model.alive())
+
+
+def test_cache_forgets_evicted_rows():
+    """Many distinct rows through a 3-slot pool: the cache keeps the ids of at most 3 rows (bounded
+    host memory and lookup time however many rows pass)."""
+    import ctypes
+    lib = gdn.load_library()
+    h = ctypes.c_void_p()
+    assert lib.gdn_pcache_create(3, 512, 0, 64, 2048, 64, ctypes.byref(h)) == 0
+    rng = np.random.default_rng(3)
+    info = (ctypes.c_int32 * 4)()
+    b = (ctypes.c_int32 * 16)()
+    s = (ctypes.c_int32 * 16)()
+    st = (ctypes.c_int64 * len(gdn.PCACHE_STATS))()
+    for _ in range(300):
+        ids = rng.integers(0, 1000, size=int(rng.integers(64, 1500))).astype(np.int32)
+        assert lib.gdn_pcache_row(h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(ids), len(ids), 16, info,
+                                  b, s, None) >= 0
+        lib.gdn_pcache_stats(h, st)
+        assert st[gdn.PCACHE_STATS.index("rows_kept")] <= 3
+    lib.gdn_pcache_destroy(h)
 
 
 def test_cache_rejects_without_booking():
