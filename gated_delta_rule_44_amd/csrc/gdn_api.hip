@@ -57,12 +57,19 @@ int check_desc(const gdn_desc* d) {
 // fp32 outputs: with fp32 activations always, with bf16 ones when the caller asks for them
 int out_f32(const gdn_desc* d) { return d->act_dtype == GDN_F32 || d->out_dtype == GDN_F32 ? 1 : 0; }
 
-// The fused prefill serves d_k = d_v = 128 with bf16 activations. GDN_PREFILL_PATH=two_phase in the
-// environment selects the two-launch path instead (the one every other shape takes), for comparison.
-bool use_fused(const gdn_desc* d) {
+// Prefill path. The fused kernel (one workgroup per (sequence, value head) walking its chunks, nothing
+// staged in HBM) serves d_k = d_v = 128 with bf16 activations once the units fill most of the chip:
+// measured on 16/32 heads, it is level with the two-launch path at 192 units (6 x 4096 tokens) and
+// 12% faster at 256 (8 x 8192); with fewer units the two-launch path, which spreads a head's state
+// pass over several CUs, is faster. GDN_PREFILL_PATH in the environment overrides the choice for
+// tests and comparisons: "fused" (with segment maps and a scan for few units) or "two_phase".
+constexpr long kFusedMinUnits = 192;
+bool use_fused(const gdn_desc* d, int B) {
   if (d->d_k != 128 || d->act_dtype != GDN_BF16) return false;
   const char* e = getenv("GDN_PREFILL_PATH");
-  return !(e && strcmp(e, "two_phase") == 0);
+  if (e && strcmp(e, "fused") == 0) return true;
+  if (e && strcmp(e, "two_phase") == 0) return false;
+  return (long)B * d->n_v >= kFusedMinUnits;
 }
 
 float q_scale(const gdn_desc* d) { return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->d_k); }
@@ -218,7 +225,7 @@ int gdn_conv_chunk(const gdn_desc* d, const void* conv_w, const void* mixed, con
 
 size_t gdn_prefill_workspace_bytes(const gdn_desc* d, int B, int Lb) {
   if (check_desc(d) || B <= 0 || Lb <= 0) return 0;
-  if (use_fused(d)) return gdn::fused_ws_bytes(B, d->n_v, Lb);
+  if (use_fused(d, B)) return gdn::fused_ws_bytes(B, d->n_v, Lb);
   if (d->act_dtype == GDN_F32 && d->d_k > 64) return 0;
   const int n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
   return gdn::prefill_ws_bytes(B, d->n_k, d->n_v, d->d_k, Lb, n_chunks, d->act_dtype == GDN_F32);
@@ -247,7 +254,7 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
     return fail(GDN_EINVAL, "gdn_prefill_chunk: buffers must be 16-byte aligned");
   if (out == mixed || out == z || (void*)state == out || conv_tail == out)
     return fail(GDN_EINVAL, "gdn_prefill_chunk: out aliases another buffer");
-  if (use_fused(d)) {
+  if (use_fused(d, B)) {
     gdn::FusedArgs f{};
     f.conv_w = w->conv_w; f.A_log = w->A_log; f.dt_bias = w->dt_bias; f.norm_w = w->norm_w;
     f.mixed = mixed; f.z = z; f.a = a; f.b = b; f.len = len; f.tail = conv_tail; f.state = state; f.out = out;

@@ -76,7 +76,8 @@ constexpr int L_G = L_TF + 4 * 16 * LDA * 4;  // beta[64], e^gamma[64], gamma[64
 constexpr int L_SS = L_G + 1024;              // row sums of squares of O: [chain wave 4][token 64]
 constexpr int VROWS = FC + 3;                 // staged conv input rows of a chunk (3 halo rows)
 constexpr int L_VS = L_SS + 1024;             // v inputs per chain wave: [wave 4][VROWS][32] bf16
-constexpr int L_END = L_VS + 4 * VROWS * 64;
+constexpr int L_NW = L_VS + 4 * VROWS * 64;  // norm weights [128] fp32
+constexpr int L_END = L_NW + FD * 4;
 static_assert(L_END <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -107,6 +108,12 @@ __device__ __forceinline__ float bf1(uint16_t u) { return __uint_as_float((uint3
 // fragment-slot position of index j (0..31) inside a 32-block: lane group and element
 __device__ __forceinline__ int slot_g(int j) { return (j & 15) >> 2; }
 __device__ __forceinline__ int slot_e(int j) { return (j & 16 ? 4 : 0) + (j & 3); }
+
+// Slot of lane (g, c) inside a 1 KB fragment block of the q / k (block (mt, kk)) and k~ (block (hm, kb))
+// arrays: rotated within each 16-lane group, so that the prep waves' scattered 4- and 8-byte stores
+// spread over the LDS banks while every 16-lane group of a reading wave still covers all 16 positions
+__device__ __forceinline__ int qk_slot(int g, int c, int kk) { return 16 * g + ((c + 4 * g + kk) & 15); }
+__device__ __forceinline__ int kt_slot(int g, int c, int hm) { return 16 * g + ((c + hm) & 15); }
 
 // pair indices of the lower blocks
 __device__ __forceinline__ int pidx(int mt, int kb) { return mt < 2 ? mt : 2 + 2 * (mt - 2) + kb; }   // P: (t tile, s 32-block)
@@ -169,7 +176,9 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
   const float* sEg = sBeta + 64;
   const float* sEc = sBeta + 192;
   float* sSS = (float*)(smem + L_SS);
+  float* sNW = (float*)(smem + L_NW);
   char* stage = smem + L_VS + w * VROWS * 64;
+  if (OUT && threadIdx.x < FD) sNW[threadIdx.x] = p.norm_w[threadIdx.x];  // read after the prologue's barriers
 
   const int cw0 = 32 * w;   // first H column of this wave
   f32x4 Hacc[8][2];         // 2^16 H[16 hm + 4 g + i][cw0 + 16 n + c]
@@ -250,14 +259,15 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const f16x8 kf = sK[((mt * 4 + kk) * 2) * 64 + lane];
+        const f16x8 kf = sK[((mt * 4 + kk) * 2) * 64 + qk_slot(g16, c16, kk)];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           Z[mt][n] = mfma32(kf, hl[n], Z[mt][n]);
           Z[mt][n] = mfma32(kf, hh[n], Z[mt][n]);
         }
         if (OUT) {
-          const f16x8 qh = sQ[((mt * 4 + kk) * 2) * 64 + lane], ql = sQ[((mt * 4 + kk) * 2 + 1) * 64 + lane];
+          const int qs = qk_slot(g16, c16, kk);
+          const f16x8 qh = sQ[((mt * 4 + kk) * 2) * 64 + qs], ql = sQ[((mt * 4 + kk) * 2 + 1) * 64 + qs];
 #pragma unroll
           for (int n = 0; n < 2; ++n) {
             Oacc[n][mt] = mfma32(hl[n], qh, Oacc[n][mt]);
@@ -361,7 +371,8 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
       for (int n = 0; n < 2; ++n) Hacc[hm][n] *= ec;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const f16x8 kh8 = sKT[((hm * 2 + kb) * 2) * 64 + lane], kl8 = sKT[((hm * 2 + kb) * 2 + 1) * 64 + lane];
+        const int ks = kt_slot(g16, c16, hm);
+        const f16x8 kh8 = sKT[((hm * 2 + kb) * 2) * 64 + ks], kl8 = sKT[((hm * 2 + kb) * 2 + 1) * 64 + ks];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const f16x8 uh = cat8(Uh[2 * kb][n], Uh[2 * kb + 1][n]), ul = cat8(Ul[2 * kb][n], Ul[2 * kb + 1][n]);
@@ -386,7 +397,7 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const int col = cw0 + 16 * n + 4 * g16;
-          const float4 nw = *(const float4*)(p.norm_w + col);
+          const float4 nw = *(const float4*)(sNW + col);
           const uint2 zz = zr[n][mt];
           const float y0 = nw.x * (Oacc[n][mt][0] * inv) * silu(bf_lo(zz.x));
           const float y1 = nw.y * (Oacc[n][mt][1] * inv) * silu(bf_hi(zz.x));
@@ -421,13 +432,13 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
     if (c + 1 < u.c1) {
       if (WITH_V) v_load(c + 1);
       lds_barrier();  // Y1
+      if (OUT) norm(c);  // beside the prep's Gram products; z has arrived meanwhile
       lds_barrier();  // Y2
-      if (OUT) norm(c);
       if (WITH_V) v_stage();
     } else {
       lds_barrier();
-      lds_barrier();
       if (OUT) norm(c);
+      lds_barrier();
     }
     lds_barrier();  // X: chunk c + 1's operands are ready
   }
@@ -537,8 +548,11 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
       const bool upper = (lane & m) != 0;
 #pragma unroll
       for (int i = 0; i < half; ++i) {
-        const float keep = upper ? ss[i + half] : ss[i];
-        const float give = upper ? ss[i] : ss[i + half];
+        // (the two values are pinned: left visible, the per-lane choice between them became a per-lane
+        // index into ss, lowered to compare-and-select over the whole array)
+        const float lo = pin_f32(ss[i]), hi = pin_f32(ss[i + half]);
+        const float keep = upper ? hi : lo;
+        const float give = upper ? lo : hi;
         ss[i] = keep + __shfl_xor(give, m, kWave);
       }
     }
@@ -584,48 +598,65 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
     g_ec = __expf(gC);
   };
 
-  // q, k (token rows) and k~ (d rows) fragments of the wave's 16 tokens to LDS, and the gates
+  // hi/lo pairs of the wave's operands, formed before the chain frees the LDS buffers (registers):
+  // q and k of token t, channels 2 lane and 2 lane + 1, as f16 pairs; k~ = 2^8 e^{gamma_C - gamma_s} k_s
+  // for channel 2 lane + j and the four tokens 4 gq .. 4 gq + 3 of lane group gq, as f16x4
+  uint32_t qph[16], qpl[16], kph[16], kpl[16];
+  f16x4 kth[2][4], ktl[2][4];
+  auto pack = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      _Float16 h0, l0, h1, l1;
+      split_f16(kS8 * kn[t][0], h0, l0);
+      split_f16(kS8 * kn[t][1], h1, l1);
+      kph[t] = __builtin_bit_cast(uint32_t, f16x2{h0, h1});
+      kpl[t] = __builtin_bit_cast(uint32_t, f16x2{l0, l1});
+      if (WITH_Q) {
+        split_f16(kS8 * qn[t][0], h0, l0);
+        split_f16(kS8 * qn[t][1], h1, l1);
+        qph[t] = __builtin_bit_cast(uint32_t, f16x2{h0, h1});
+        qpl[t] = __builtin_bit_cast(uint32_t, f16x2{l0, l1});
+      }
+    }
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      float ed[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ed[e] = kS8 * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_ed), 16 * pw + 4 * gq + e));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        split4v(f32x4{ed[0] * kn[4 * gq][j], ed[1] * kn[4 * gq + 1][j], ed[2] * kn[4 * gq + 2][j], ed[3] * kn[4 * gq + 3][j]},
+                kth[j][gq], ktl[j][gq]);
+    }
+  };
+
+  // the packed operands to LDS: q, k as token rows (row t of token tile pw; channel 2 lane (+1) is
+  // index j0 (+1) of 32-block kk: lane group slot_g(j0), elements slot_e(j0), slot_e(j0) + 1), k~ as d
+  // rows (channel d is row d % 16 of tile d / 16; token s = 16 pw + t sits in 32-block pw / 2 at index
+  // 16 (pw & 1) + t: lane group t / 4, elements 4 (pw & 1) + t % 4); and the gates
   auto write = [&]() __attribute__((always_inline)) {
-    // channel d = 2 lane (+1) is index j0 (+1) of 32-block kk: lane group slot_g(j0), elements
-    // slot_e(j0), slot_e(j0) + 1; token 16 pw + t is row t of token tile pw
     const int j0 = (2 * lane) & 31, kk = (2 * lane) >> 5;
     const int sg = slot_g(j0), se = slot_e(j0);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      _Float16 qh0, ql0, qh1, ql1, kh0, kl0, kh1, kl1;
-      split_f16(kS8 * kn[t][0], kh0, kl0);
-      split_f16(kS8 * kn[t][1], kh1, kl1);
-      const int base = ((pw * 4 + kk) * 2) * 64 + 16 * sg + t;
-      *(f16x2*)((_Float16*)&sK[base] + se) = f16x2{kh0, kh1};
-      *(f16x2*)((_Float16*)&sK[base + 64] + se) = f16x2{kl0, kl1};
+      const int base = ((pw * 4 + kk) * 2) * 64 + qk_slot(sg, t, kk);
+      *(uint32_t*)((_Float16*)&sK[base] + se) = kph[t];
+      *(uint32_t*)((_Float16*)&sK[base + 64] + se) = kpl[t];
       if (WITH_Q) {
-        split_f16(kS8 * qn[t][0], qh0, ql0);
-        split_f16(kS8 * qn[t][1], qh1, ql1);
-        *(f16x2*)((_Float16*)&sQ[base] + se) = f16x2{qh0, qh1};
-        *(f16x2*)((_Float16*)&sQ[base + 64] + se) = f16x2{ql0, ql1};
+        *(uint32_t*)((_Float16*)&sQ[base] + se) = qph[t];
+        *(uint32_t*)((_Float16*)&sQ[base + 64] + se) = qpl[t];
       }
-      __builtin_amdgcn_sched_barrier(0);  // token by token (register pressure)
     }
-    // k~ = 2^8 e^{gamma_C - gamma_s} k_s, the A operand of K~^T U (row d, contraction over tokens s):
-    // channel d is row d % 16 of tile d / 16; token s = 16 pw + t sits in 32-block pw / 2 at index
-    // 16 (pw & 1) + t: lane group t / 4, elements 4 (pw & 1) + t % 4
-    float ed[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-      ed[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_ed), 16 * pw + t));
     const int kb = pw >> 1, eo = 4 * (pw & 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int d = 2 * lane + j, hm = d >> 4, cr = d & 15;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        f16x4 hi, lo;
-        split4v(f32x4{ed[4 * gq] * kn[4 * gq][j], ed[4 * gq + 1] * kn[4 * gq + 1][j], ed[4 * gq + 2] * kn[4 * gq + 2][j],
-                      ed[4 * gq + 3] * kn[4 * gq + 3][j]} * kS8, hi, lo);
-        const int base = ((hm * 2 + kb) * 2) * 64 + 16 * gq + cr;
-        *(f16x4*)((_Float16*)&sKT[base] + eo) = hi;
-        *(f16x4*)((_Float16*)&sKT[base + 64] + eo) = lo;
-        __builtin_amdgcn_sched_barrier(0);
+        const int base = ((hm * 2 + kb) * 2) * 64 + kt_slot(gq, cr, hm);
+        *(f16x4*)((_Float16*)&sKT[base] + eo) = kth[j][gq];
+        *(f16x4*)((_Float16*)&sKT[base + 64] + eo) = ktl[j][gq];
       }
     }
     if (pw == 0) {
@@ -636,39 +667,45 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
     }
   };
 
-  // Gram products. Job < 10: K K^T tile (mt, nt), nt <= mt; otherwise K Q^T. Both as D = X_nt Y_mt^T,
-  // so that lane (g, c) holds entry [16 mt + c][16 nt + 4 g + i]: the layout of a 16x16x16 A operand
-  // (row 16 mt + c, contraction indices 4 g .. 4 g + 3) and of half a 16x16x32 A operand (elements
-  // 4 (nt & 1) .. +3 of 32-block nt / 2)
+  // Gram products of tile (mt, nt), nt <= mt: K K^T and (OUT) K Q^T, both as D = K_nt Y_mt^T so that lane
+  // (g, c) holds entry [16 mt + c][16 nt + 4 g + i]: the layout of a 16x16x16 A operand (row 16 mt + c,
+  // contraction indices 4 g .. 4 g + 3) and of half a 16x16x32 A operand (elements 4 (nt & 1) .. +3 of
+  // 32-block nt / 2). The ten tiles go round-robin over the prep waves.
   auto gram = [&]() __attribute__((always_inline)) {
-    for (int job = pw; job < (WITH_Q ? 20 : 10); job += 4) {
-      const bool isP = job >= 10;
-      const int tile = job % 10;
+#pragma unroll 1
+    for (int i = 0; i < 3; ++i) {
+      const int tile = pw + 4 * i;
+      if (tile >= 10) break;
       const int mt = tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0;
       const int nt = tile - mt * (mt + 1) / 2;
-      const f16x8* Y = isP ? sQ : sK;
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+      f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, k2 = k0, q0 = k0, q1 = k0, q2 = k0;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const f16x8 xh = sK[((nt * 4 + kk) * 2) * 64 + lane], xl = sK[((nt * 4 + kk) * 2 + 1) * 64 + lane];
-        const f16x8 yh = Y[((mt * 4 + kk) * 2) * 64 + lane], yl = Y[((mt * 4 + kk) * 2 + 1) * 64 + lane];
-        a0 = mfma32(xl, yh, a0);
-        a1 = mfma32(xh, yl, a1);
-        a2 = mfma32(xh, yh, a2);
+        const int qs = qk_slot(g16, c16, kk);
+        const f16x8 xh = sK[((nt * 4 + kk) * 2) * 64 + qs], xl = sK[((nt * 4 + kk) * 2 + 1) * 64 + qs];
+        const f16x8 yh = sK[((mt * 4 + kk) * 2) * 64 + qs], yl = sK[((mt * 4 + kk) * 2 + 1) * 64 + qs];
+        k0 = mfma32(xl, yh, k0);
+        k1 = mfma32(xh, yl, k1);
+        k2 = mfma32(xh, yh, k2);
+        if (WITH_Q) {
+          const f16x8 zh = sQ[((mt * 4 + kk) * 2) * 64 + qs], zl = sQ[((mt * 4 + kk) * 2 + 1) * 64 + qs];
+          q0 = mfma32(xl, zh, q0);
+          q1 = mfma32(xh, zl, q1);
+          q2 = mfma32(xh, zh, q2);
+        }
       }
-      const f32x4 acc = (a2 + (a0 + a1)) * kIS16;  // k.k or k.q
       const int r = 16 * mt + c16;
-      const float gr = sGam[r];
+      const float gr = sGam[r], br = sBeta[r];
       const float4 gs4 = *(const float4*)(sGam + 16 * nt + 4 * g16);
       const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
-      f32x4 x;
-      if (!isP) {
-        const float br = sBeta[r];
+      float dec[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * nt + 4 * g16 + i;
-          x[i] = s < r ? br * __expf(gr - gs[i]) * acc[i] : 0.f;
-        }
+      for (int e = 0; e < 4; ++e) dec[e] = __expf(gr - gs[e]);  // s <= r here for the entries kept
+      {
+        const f32x4 kk4 = (k2 + (k0 + k1)) * kIS16;  // k_r . k_s
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = 16 * nt + 4 * g16 + e < r ? br * dec[e] * kk4[e] : 0.f;
         if (nt < mt) {
           f16x4 hi, lo;
           split4v(x * -kS8, hi, lo);
@@ -677,12 +714,12 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
         } else {
           *(float4*)&sAD[(mt * 16 + c16) * LDA + 4 * g16] = make_float4(x[0], x[1], x[2], x[3]);
         }
-      } else {
+      }
+      if (WITH_Q) {
+        const f32x4 qk4 = (q2 + (q0 + q1)) * kIS16;  // q_r . k_s
+        f32x4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * nt + 4 * g16 + i;
-          x[i] = s <= r ? (p.scale * kS16) * __expf(gr - gs[i]) * acc[i] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) x[e] = 16 * nt + 4 * g16 + e <= r ? (p.scale * kS16) * dec[e] * qk4[e] : 0.f;
         f16x4 hi, lo;
         split4v(x, hi, lo);
         const int pi = pidx(mt, nt >> 1), eo = 4 * (nt & 1);
@@ -727,6 +764,7 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
   // prologue: chunk c0's operands
   load(u.c0);
   conv(u.c0);
+  pack();
   lds_barrier();
   write();
   if (u.c0 + 1 < u.c1) load(u.c0 + 1);
@@ -737,6 +775,7 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
   lds_barrier();
   for (int c = u.c0; c + 1 < u.c1; ++c) {  // the chain runs chunk c meanwhile
     conv(c + 1);
+    pack();
     lds_barrier();  // Y: the chain is done with chunk c's operands
     write();
     if (c + 2 < u.c1) load(c + 2);

@@ -84,19 +84,31 @@ def test_sizes():
     lib = gdn.load_library()
     d = gdn.GdnDesc(n_k=16, n_v=32, d_k=128, d_v=128)
     assert gdn.state_record_bytes(d) == 32 * 128 * 128 * 4 + 3 * 8192 * 2
-    # the fused prefill (d = 128, bf16): no workspace where the (sequence, head) units fill the chip or
-    # the call is short; segment maps and states where few units run long calls
+    # d = 128, bf16: from 192 (sequence, head) units on, the fused prefill, which needs no workspace
     assert gdn.prefill_workspace_bytes(d, 8, 100) == 0
     assert gdn.prefill_workspace_bytes(d, 8, 8192) == 0
-    assert gdn.prefill_workspace_bytes(d, 1, 256) == 0           # 4 chunks: too short for segments
-    S = 5                                                          # 32 units: min(256 / 64 + 1, 64 / 4)
-    assert gdn.prefill_workspace_bytes(d, 1, 4096) == 32 * (2 * (S - 1) + S) * 128 * 128 * 4
+    assert gdn.prefill_workspace_bytes(d, 6, 4096) == 0
+    # fewer units take the two-launch path and its chunk records
+    assert gdn.prefill_workspace_bytes(d, 5, 4096) > 0
     assert gdn.prefill_workspace_bytes(gdn.GdnDesc(n_k=2, n_v=4, d_k=128, d_v=128, act_dtype=gdn.GDN_F32), 1, 64) == 0
     # a workspace sized for the longest call serves every shorter one (sizes never shrink as Lb grows)
     for dd in (d, gdn.GdnDesc(n_k=16, n_v=16, d_k=128, d_v=128), gdn.GdnDesc(n_k=2, n_v=4, d_k=64, d_v=64)):
-        for B in (1, 2, 3, 4, 5):
+        for B in (1, 2, 3, 4, 5, 8):
             sizes = [gdn.prefill_workspace_bytes(dd, B, L) for L in (64, 511, 512, 960, 1024, 1025, 2048, 4096, 8192)]
             assert sizes == sorted(sizes), (dd, B, sizes)
+
+
+def test_sizes_fused_segments(monkeypatch):
+    """The fused path forced for few units: segment maps and states where few units run long calls."""
+    monkeypatch.setenv("GDN_PREFILL_PATH", "fused")
+    d = gdn.GdnDesc(n_k=16, n_v=32, d_k=128, d_v=128)
+    assert gdn.prefill_workspace_bytes(d, 8, 8192) == 0          # 256 units: no segments
+    assert gdn.prefill_workspace_bytes(d, 1, 256) == 0           # 4 chunks: too short for segments
+    S = 5                                                          # 32 units: min(256 / 64 + 1, 64 / 4)
+    assert gdn.prefill_workspace_bytes(d, 1, 4096) == 32 * (2 * (S - 1) + S) * 128 * 128 * 4
+    for B in (1, 2, 3, 4, 5):
+        sizes = [gdn.prefill_workspace_bytes(d, B, L) for L in (64, 511, 512, 960, 1024, 1025, 2048, 4096, 8192)]
+        assert sizes == sorted(sizes), (B, sizes)
 
 
 def test_sizes_two_phase(monkeypatch):

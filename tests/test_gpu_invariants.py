@@ -1,0 +1,189 @@
+"""The layer's invariants checked through the GPU kernels (the oracle's own pins are in test_oracle_pins.py):
+
+  * exact write: a token with g = 0 and beta = 1 leaves a state S with S k = v for its (unit) key k;
+  * padding: a token with g = 0 and beta = 0 changes nothing, so an all-padding call leaves state and
+    tail bit for bit as they were, and a call padded to a bucket ends in exactly the state (and emits
+    exactly the outputs) of the call of the real length;
+  * nothing is written outside the buffers: every output, state and checkpoint buffer carries canary
+    margins that must come back untouched.
+
+Run on an MI355X: python -u -m pytest tests -m gpu -x -v --timeout 300 --timeout-method thread
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_44_amd as gdn
+from gdn_inputs import NEXT, LayerDims, make_inputs, make_layer, path_inputs, random_state
+from tests.gpu_helpers import BOTH, Guarded, act, assert_state_close, desc_of, f32, host, i32, prefill_path, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    gdn.load_library()
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _write_token(x, t):
+    """Make token t of every sequence an exact write: a = -inf (g = -exp(A_log) softplus(-inf) = 0) and
+    b = +inf (beta = sigmoid(+inf) = 1); both are exact in bf16."""
+    x.a[:, t] = -np.inf
+    x.b[:, t] = np.inf
+
+
+def _unit_keys_and_values(dims: LayerDims, w, mixed, tail0, t):
+    """k^ (L2-normalised) and v of token t of one sequence, from the oracle's conv on the same inputs."""
+    y, _ = oracle.conv(w.conv_w, tail0, mixed, mixed.shape[0])
+    nk, dk = dims.n_k, dims.d_k
+    k = y[t, nk * dk:2 * nk * dk].reshape(nk, dk)
+    k = k / np.sqrt((k * k).sum(-1, keepdims=True) + dims.l2_eps)
+    v = y[t, 2 * nk * dk:].reshape(dims.n_v, dims.d_v)
+    return k, v
+
+
+def _check_exact_write(dims: LayerDims, H, k, v, what):
+    """S k = v with S = H^T for every value head (key head h // r), within 1e-3 of max|v| per head."""
+    r = dims.n_v // dims.n_k
+    for h in range(dims.n_v):
+        got = H[h].T @ k[h // r]
+        err = np.abs(got - v[h]).max() / max(np.abs(v[h]).max(), 1e-30)
+        assert err <= 1e-3, f"{what}: head {h}: |S k - v| / max|v| = {err:.2e}"
+
+
+@pytest.mark.parametrize("path", BOTH)
+@pytest.mark.parametrize("L", [1, 64, 203])
+def test_exact_write_prefill(path, L):
+    """The last token of each sequence writes exactly (g = 0, beta = 1): the final state maps its key to
+    its value, from a non-zero saved state, through both prefill paths."""
+    dims = LayerDims(n_k=2, n_v=4, d_k=128, d_v=128)
+    B = 2
+    _say(f"exact write prefill path={path} L={L}")
+    w, x, rng = make_layer(21, dims, B, L)
+    _write_token(x, L - 1)
+    H0, t0 = random_state(rng, dims, B)
+    d = desc_of(dims)
+    st, tail = f32(H0), act(t0, dims)
+    with prefill_path(path):
+        gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims),
+                          i32(x.lens), tail, st)
+    torch.cuda.synchronize()
+    od = oracle.Dims.of(dims)
+    for s in range(B):
+        k, v = _unit_keys_and_values(dims, w, x.mixed[s], t0[s], L - 1)
+        _check_exact_write(dims, host(st[s]), k, v, f"seq {s}")
+        ref = oracle.layer_forward(od, w, x.mixed[s:s + 1], x.z[s:s + 1], x.a[s:s + 1], x.b[s:s + 1], None,
+                                   t0[s:s + 1], H0[s:s + 1])
+        assert_state_close(host(st[s]), ref["H"][0], f"state seq {s}")
+
+
+def test_exact_write_decode():
+    """A decode token with g = 0 and beta = 1 leaves S k = v."""
+    dims, B = NEXT, 8
+    _say("exact write decode")
+    w, _, rng = make_layer(22, dims, 1, 1)
+    H0, t0 = random_state(rng, dims, B)
+    x = make_inputs(rng, dims, B, 1)
+    _write_token(x, 0)
+    d = desc_of(dims)
+    sp, tp = f32(H0), act(t0, dims)
+    gdn.decode_step(d, weights(w, dims), act(x.mixed[:, 0], dims), act(x.z[:, 0], dims), act(x.a[:, 0], dims),
+                    act(x.b[:, 0], dims), None, tp, sp)
+    torch.cuda.synchronize()
+    for s in range(B):
+        k, v = _unit_keys_and_values(dims, w, x.mixed[s], t0[s], 0)
+        _check_exact_write(dims, host(sp[s]), k, v, f"decode seq {s}")
+
+
+@pytest.mark.parametrize("path", BOTH)
+@pytest.mark.parametrize("dims,B", [(LayerDims(n_k=2, n_v=4, d_k=128, d_v=128), 3), (NEXT, 8)])
+def test_all_padding_call_leaves_state_bitwise(path, dims, B):
+    """Every length 0: state and tail come back bit for bit, and no byte of the output is written."""
+    L = 130
+    _say(f"all padding path={path} B={B}")
+    w, x, rng = make_layer(23, dims, B, L, [0] * B)
+    H0, t0 = random_state(rng, dims, B)
+    d = desc_of(dims)
+    st = Guarded(dims.state_shape(B), torch.float32, f32(H0))
+    tail = Guarded(dims.tail_shape(B), torch.bfloat16, act(t0, dims))
+    out = Guarded((B, L, dims.value_dim), torch.bfloat16)
+    out.t.view(torch.uint8).fill_(0xA5)  # the whole output as canary: nothing may be written
+    with prefill_path(path):
+        gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims),
+                          i32(x.lens), tail.t, st.t, out.t)
+    torch.cuda.synchronize()
+    assert torch.equal(st.t, f32(H0)), "state changed"
+    assert torch.equal(tail.t, act(t0, dims)), "tail changed"
+    assert bool((out.raw == 0xA5).all()), "an all-padding call wrote output"
+    st.check("state")
+    tail.check("tail")
+
+
+@pytest.mark.parametrize("path", BOTH)
+@pytest.mark.parametrize("dims,B,n,bucket", [(LayerDims(n_k=2, n_v=4, d_k=128, d_v=128), 2, 100, 128),
+                                             (LayerDims(n_k=2, n_v=4, d_k=128, d_v=128), 2, 1000, 1024),
+                                             (NEXT, 8, 37, 64), (NEXT, 8, 300, 512)])
+def test_bucket_padding_bitwise(path, dims, B, n, bucket):
+    """A call whose chunk is padded to its bucket (padding rows random, masked by the length) ends in the
+    same state and tail bits, and emits the same output bits on the real rows, as the call of exactly the
+    real length."""
+    _say(f"bucket padding path={path} B={B} n={n} bucket={bucket}")
+    w, x, rng = make_layer(24, dims, B, bucket, [n] * B)
+    H0, t0 = random_state(rng, dims, B)
+    d = desc_of(dims)
+    W = weights(w, dims)
+
+    def run(L):
+        st, tail = f32(H0), act(t0, dims)
+        ins = [act(a[:, :L], dims) for a in (x.mixed, x.z, x.a, x.b)]
+        with prefill_path(path):
+            out = gdn.prefill_chunk(d, W, *ins, i32([n] * B), tail, st)
+        torch.cuda.synchronize()
+        return out[:, :n], st, tail
+
+    o1, s1, t1 = run(n)
+    o2, s2, t2 = run(bucket)
+    assert torch.equal(s1, s2), "state bits differ between the exact and the bucket-padded call"
+    assert torch.equal(t1, t2), "tail bits differ"
+    assert torch.equal(o1, o2), "output bits differ on the real rows"
+
+
+def test_canaries_decode_verify_paths():
+    """Decode, verify and tree verify write nothing outside out, the pools and the checkpoint buffers."""
+    dims, B, K, P = NEXT, 6, 4, 3
+    T = K + 1
+    _say("canaries decode / verify / paths")
+    w, _, rng = make_layer(25, dims, 1, 1)
+    H0, t0 = random_state(rng, dims, B)
+    W = weights(w, dims)
+    for out_f32 in (False, True):
+        d = desc_of(dims, out_f32)
+        x = make_inputs(rng, dims, B, T)
+        sp = Guarded(dims.state_shape(B), torch.float32, f32(H0))
+        tp = Guarded(dims.tail_shape(B), torch.bfloat16, act(t0, dims))
+        out = Guarded((B, dims.value_dim), d.out)
+        gdn.decode_step(d, W, act(x.mixed[:, 0], dims), act(x.z[:, 0], dims), act(x.a[:, 0], dims),
+                        act(x.b[:, 0], dims), None, tp.t, sp.t, out.t)
+        cks = Guarded((B, T, dims.n_v, dims.d_k, dims.d_v), torch.float32)
+        ckt = Guarded((B, T, dims.kc, dims.conv_dim), torch.bfloat16)
+        vout = Guarded((B, T, dims.value_dim), d.out)
+        gdn.verify_with_checkpoints(d, W, act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims), None,
+                                    tp.t, sp.t, cks.t, ckt.t, vout.t)
+        xp = path_inputs(rng, dims, B, P, T)
+        pcks = Guarded((B, P, T, dims.n_v, dims.d_k, dims.d_v), torch.float32)
+        pckt = Guarded((B, P, T, dims.kc, dims.conv_dim), torch.bfloat16)
+        pout = Guarded((B, P, T, dims.value_dim), d.out)
+        gdn.verify_paths(d, W, act(xp.mixed, dims), act(xp.z, dims), act(xp.a, dims), act(xp.b, dims), None, tp.t,
+                         sp.t, pcks.t, pckt.t, pout.t)
+        torch.cuda.synchronize()
+        for g, name in ((sp, "state pool"), (tp, "tail pool"), (out, "decode out"), (cks, "ckpt_state"),
+                        (ckt, "ckpt_tail"), (vout, "verify out"), (pcks, "path ckpt_state"),
+                        (pckt, "path ckpt_tail"), (pout, "paths out")):
+            g.check(f"{name} (out_f32={out_f32})")

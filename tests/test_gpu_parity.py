@@ -10,8 +10,8 @@ import oracle
 import gated_delta_rule_44_amd as gdn
 from gdn_inputs import (ACT_BF16, ACT_F32, NEXT, SMALL, TINY, LayerDims, chunk_lengths, make_layer, path_inputs,
                         random_state, verify_draws, verify_path_draws)
-from tests.gpu_helpers import (act, assert_out_close, assert_state_close, desc_of, f32, host, i32, out_excess,
-                               state_rel_err, weights)
+from tests.gpu_helpers import (BOTH, Guarded, act, assert_out_close, assert_out_flat, assert_state_close, desc_of, f32,
+                               host, i32, out_excess, prefill_path, state_rel_err, weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,27 +30,50 @@ def _say(msg):
 # ---------------------------------------------------------------------------------------------------
 # prefill
 
-def _prefill_case(dims: LayerDims, seed, B, L, lens, state_std=0.0, tail_rand=False, sample=None):
-    _say(f"prefill seed={seed} B={B} L={L} lens={list(lens)[:4]} dims={dims}")
+def _prefill_case(dims: LayerDims, seed, B, L, lens, state_std=0.0, tail_rand=False, sample=None, paths=(None,)):
+    """Inputs and the oracle once; then every requested path, with the output in the activation dtype and
+    (bf16 activations) in fp32. Buffers carry canary margins; the fp32-output call must leave the same
+    state and tail bits as the other."""
+    _say(f"prefill seed={seed} B={B} L={L} lens={list(lens)[:4]} dims={dims} paths={paths}")
     w, x, rng = make_layer(seed, dims, B, L, lens)
     H0 = (rng.standard_normal(dims.state_shape(B)) * state_std).astype(np.float32)
     t0 = random_state(rng, dims, B)[1] if tail_rand else np.zeros(dims.tail_shape(B), np.float32)
-    d = desc_of(dims)
-    tail = act(t0, dims)
-    st = f32(H0)
-    out = gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims),
-                            act(x.b, dims), i32(x.lens), tail, st)
-    torch.cuda.synchronize()
     idx = range(B) if sample is None else sample
     od = oracle.Dims.of(dims)
-    for s in idx:
-        n = int(x.lens[s])
-        ref = oracle.layer_forward(od, w, x.mixed[s:s + 1], x.z[s:s + 1], x.a[s:s + 1], x.b[s:s + 1],
-                                   x.lens[s:s + 1], t0[s:s + 1], H0[s:s + 1])
-        assert_out_close(host(out[s, :n]), ref["out"][0, :n], dims, f"out[seq {s}]")
-        assert_state_close(host(st[s]), ref["H"][0], f"state[seq {s}]")
-        np.testing.assert_array_equal(host(tail[s]), ref["tail"][0].astype(np.float32))
-    return out, st, tail
+    refs = {s: oracle.layer_forward(od, w, x.mixed[s:s + 1], x.z[s:s + 1], x.a[s:s + 1], x.b[s:s + 1],
+                                    x.lens[s:s + 1], t0[s:s + 1], H0[s:s + 1]) for s in idx}
+    inputs = [act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims), i32(x.lens)]
+    W = weights(w, dims)
+    result = None
+    for path in paths:
+        bits = None
+        for out_f32 in ((False, True) if dims.act == ACT_BF16 else (False,)):
+            d = desc_of(dims, out_f32)
+            _say(f"  path={path} out_f32={out_f32}")
+            tail = Guarded(dims.tail_shape(B), d.act, act(t0, dims))
+            st = Guarded(dims.state_shape(B), torch.float32, f32(H0))
+            out = Guarded((B, L, dims.value_dim), d.out)
+            with prefill_path(path):
+                gdn.prefill_chunk(d, W, *inputs, tail.t, st.t, out.t)
+            torch.cuda.synchronize()
+            for g, name in ((tail, "tail"), (st, "state"), (out, "out")):
+                g.check(f"{name} (path {path})")
+            for s in idx:
+                n = int(x.lens[s])
+                ref = refs[s]
+                if out_f32:
+                    assert_out_flat(host(out.t[s, :n]), ref["out"][0, :n], f"fp32 out[seq {s}] (path {path})")
+                else:
+                    assert_out_close(host(out.t[s, :n]), ref["out"][0, :n], dims, f"out[seq {s}] (path {path})")
+                assert_state_close(host(st.t[s]), ref["H"][0], f"state[seq {s}] (path {path})")
+                np.testing.assert_array_equal(host(tail.t[s]), ref["tail"][0].astype(np.float32))
+            if bits is None:
+                bits = (st.t.clone(), tail.t.clone())
+            else:  # the output's dtype changes nothing else
+                assert torch.equal(st.t, bits[0]) and torch.equal(tail.t, bits[1]), f"state bits differ (path {path})"
+            if not out_f32:
+                result = (out.t, st.t, tail.t)
+    return result
 
 
 def test_prefill_tiny_fp32():
@@ -62,7 +85,7 @@ def test_prefill_tiny_fp32():
 def test_prefill_ragged_multichunk(D, R):
     """Several chunks with a ragged tail and a padded sequence, from a non-zero state and tail."""
     dims = LayerDims(n_k=2, n_v=2 * R, d_k=D, d_v=D)
-    _prefill_case(dims, 3, 3, 300, [300, 171, 1], state_std=0.05, tail_rand=True)
+    _prefill_case(dims, 3, 3, 300, [300, 171, 1], state_std=0.05, tail_rand=True, paths=BOTH if D == 128 else (None,))
 
 
 @pytest.mark.parametrize("B", [2, 4, 5, 8])
@@ -70,7 +93,7 @@ def test_prefill_column_splits_d128(B):
     """32 value heads x B sequences: 64, 128, 160 and 256 (sequence, head) pairs give 4, 2, 1 and 1
     state-pass workgroups per head; the split heads exchange their partial row sums for the gated norm."""
     lens = [150, 64, 1, 100, 129, 0, 150, 37][:B]
-    _prefill_case(NEXT, 11, B, 150, lens, state_std=0.05, tail_rand=True)
+    _prefill_case(NEXT, 11, B, 150, lens, state_std=0.05, tail_rand=True, paths=BOTH)
 
 
 @pytest.mark.parametrize("dims,B,L,lens", [(LayerDims(n_k=16, n_v=16, d_k=128, d_v=128), 3, 1030, [1030, 0, 700]),
@@ -82,7 +105,7 @@ def test_prefill_split_row_sum_exchange(dims, B, L, lens):
     exchange their partial row sums for the gated norm. 48 and 72 (sequence, head) pairs with one value
     head per key head, 64 and 96 with two; ragged lengths (one sequence empty), from a non-zero state
     and tail."""
-    _prefill_case(dims, 12, B, L, lens, state_std=0.05, tail_rand=True)
+    _prefill_case(dims, 12, B, L, lens, state_std=0.05, tail_rand=True, paths=BOTH)
 
 
 @pytest.mark.parametrize("D,R,act_t", [(32, 1, ACT_BF16), (32, 4, ACT_BF16), (64, 4, ACT_BF16),
@@ -105,24 +128,24 @@ def test_prefill_fp32_multichunk():
 
 def test_prefill_zero_length_leaves_state():
     dims = LayerDims(n_k=2, n_v=4, d_k=128, d_v=128)
-    _prefill_case(dims, 5, 2, 64, [0, 2], state_std=0.05, tail_rand=True)
+    _prefill_case(dims, 5, 2, 64, [0, 2], state_std=0.05, tail_rand=True, paths=BOTH)
 
 
 def test_prefill_4k_single_layer():
     """One sequence of 4096 tokens, 16 key / 16 value heads, d=128, bf16 activations, fp32 state."""
-    _prefill_case(SMALL, 0, 1, 4096, [4096])
+    _prefill_case(SMALL, 0, 1, 4096, [4096], paths=BOTH)
 
 
 def test_prefill_streamed_records_ragged():
     """Two ragged sequences (4096 and 3000 tokens) at 16/32 heads: about 400 MB of chunk records, which
     the record builder stores non-temporally, and 64 (sequence, head) pairs, whose 32-column state-pass
     slices exchange row sums for the gated norm. Both sequences against the oracle."""
-    _prefill_case(NEXT, 13, 2, 4096, [4096, 3000], state_std=0.05, tail_rand=True)
+    _prefill_case(NEXT, 13, 2, 4096, [4096, 3000], state_std=0.05, tail_rand=True, paths=BOTH)
 
 
 def test_prefill_stack_layer_sampled():
     """Stack-layer shape (8 x 8192 tokens, 16/32 heads) on the GPU; sequences 0 and 7 against the oracle."""
-    _prefill_case(NEXT, 1, 8, 8192, [8192] * 8, sample=[0, 7])
+    _prefill_case(NEXT, 1, 8, 8192, [8192] * 8, sample=[0, 7], paths=BOTH)
 
 
 def test_prefill_scale_one():
@@ -139,26 +162,35 @@ def test_continuation_equals_single_pass():
     w, x, rng = make_layer(2, dims, 1, total)
     parts = chunk_lengths(rng, total)
     _say(f"continuation {len(parts)} chunks")
-    d = desc_of(dims)
     W = weights(w, dims)
-    tail = act(np.zeros(dims.tail_shape(1)), dims)
-    st = f32(np.zeros(dims.state_shape(1)))
-    outs = []
-    t0 = 0
-    for n, bucket in parts:
-        def pad(a):
-            seg = a[:, t0:t0 + n]
-            fill = rng.standard_normal((1, bucket - n, a.shape[2])).astype(np.float32)
-            return act(np.concatenate([seg, fill], 1), dims)
-        o = gdn.prefill_chunk(d, W, pad(x.mixed), pad(x.z), pad(x.a), pad(x.b), i32([n]), tail, st)
-        outs.append(host(o[0, :n]))
-        t0 += n
-    torch.cuda.synchronize()
-    cont = np.concatenate(outs, 0)
+    fills = [{k: rng.standard_normal((1, bucket - n, a.shape[2])).astype(np.float32)
+              for k, a in (("m", x.mixed), ("z", x.z), ("a", x.a), ("b", x.b))} for n, bucket in parts]
     ref = oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b)
+
+    def continued(out_f32):
+        d = desc_of(dims, out_f32)
+        tail = act(np.zeros(dims.tail_shape(1)), dims)
+        st = f32(np.zeros(dims.state_shape(1)))
+        outs = []
+        t0 = 0
+        for (n, bucket), fill in zip(parts, fills):
+            def pad(a, k):
+                return act(np.concatenate([a[:, t0:t0 + n], fill[k]], 1), dims)
+            o = gdn.prefill_chunk(d, W, pad(x.mixed, "m"), pad(x.z, "z"), pad(x.a, "a"), pad(x.b, "b"), i32([n]),
+                                  tail, st)
+            outs.append(host(o[0, :n]))
+            t0 += n
+        torch.cuda.synchronize()
+        return np.concatenate(outs, 0), st, tail
+
+    cont, st, tail = continued(False)
     assert_out_close(cont, ref["out"][0], dims, "continued out vs oracle")
     assert_state_close(host(st[0]), ref["H"][0], "continued state vs oracle")
     np.testing.assert_array_equal(host(tail[0]), ref["tail"][0].astype(np.float32))
+    cont32, st32, tail32 = continued(True)
+    assert_out_flat(cont32, ref["out"][0], "continued fp32 out vs oracle")
+    assert torch.equal(st32, st) and torch.equal(tail32, tail)
+    d = desc_of(dims)
     # the GPU's own single pass
     tail1 = act(np.zeros(dims.tail_shape(1)), dims)
     st1 = f32(np.zeros(dims.state_shape(1)))
@@ -212,12 +244,13 @@ def _decode_inputs(dims, rng, B, T):
 @pytest.mark.parametrize("dims,B", [(NEXT, 8), (SMALL, 4), (LayerDims(n_k=2, n_v=8, d_k=64, d_v=64), 3),
                                     (LayerDims(n_k=2, n_v=8, d_k=128, d_v=128), 5),
                                     (LayerDims(n_k=2, n_v=4, d_k=32, d_v=32, act=ACT_F32), 2)])
-def test_decode_step_vs_oracle(dims, B):
-    _say(f"decode B={B} dims={dims}")
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_decode_step_vs_oracle(dims, B, out_f32):
+    _say(f"decode B={B} dims={dims} out_f32={out_f32}")
     w, _, rng = make_layer(8, dims, 1, 1)
     H0, T0 = _saved_states(dims, w, rng, B)
     x = _decode_inputs(dims, rng, B, 1)
-    d = desc_of(dims)
+    d = desc_of(dims, out_f32)
     # pool with extra rows and a permuted slot map
     npool = B + 3
     slots = rng.permutation(npool)[:B].astype(np.int32)
@@ -229,7 +262,11 @@ def test_decode_step_vs_oracle(dims, B):
                           act(x.b[:, 0], dims), i32(slots), tp, sp, check_slots=True)
     torch.cuda.synchronize()
     ref = oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, None, T0, H0)
-    assert_out_close(host(out), ref["out"][:, 0], dims)
+    if out_f32:
+        assert out.dtype == torch.float32
+        assert_out_flat(host(out), ref["out"][:, 0], "decode fp32 out")
+    else:
+        assert_out_close(host(out), ref["out"][:, 0], dims)
     hp = host(sp)
     assert_state_close(hp[slots], ref["H"])
     np.testing.assert_array_equal(host(tp)[slots], ref["tail"].astype(np.float32))
@@ -247,15 +284,19 @@ def test_decode_full_batch_sampled():
     x = _decode_inputs(dims, rng, B, 1)
     d = desc_of(dims)
     sp, tp = f32(H0), act(T0, dims)
-    out = gdn.decode_step(d, weights(w, dims), act(x.mixed[:, 0], dims), act(x.z[:, 0], dims), act(x.a[:, 0], dims),
-                          act(x.b[:, 0], dims), None, tp, sp)
+    sp32, tp32 = sp.clone(), tp.clone()
+    ins = (act(x.mixed[:, 0], dims), act(x.z[:, 0], dims), act(x.a[:, 0], dims), act(x.b[:, 0], dims))
+    out = gdn.decode_step(d, weights(w, dims), *ins, None, tp, sp)
+    out32 = gdn.decode_step(desc_of(dims, True), weights(w, dims), *ins, None, tp32, sp32)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
+    assert torch.equal(sp32, sp) and torch.equal(tp32, tp)
     od = oracle.Dims.of(dims)
     for s in (0, 77, 255):
         sl = slice(s, s + 1)
         ref = oracle.layer_forward(od, w, x.mixed[sl], x.z[sl], x.a[sl], x.b[sl], None, T0[sl], H0[sl])
         assert_out_close(host(out[s]), ref["out"][0, 0], dims, f"decode seq {s}")
+        assert_out_flat(host(out32[s]), ref["out"][0, 0], f"decode fp32 out seq {s}")
         assert_state_close(host(sp[s]), ref["H"][0], f"decode state {s}")
         np.testing.assert_array_equal(host(tp[s]), ref["tail"][0].astype(np.float32))
 
@@ -271,14 +312,17 @@ def test_verify_paths_full_size_sampled():
     x = path_inputs(rng, dims, B, P, T)
     d = desc_of(dims)
     sp, tp = f32(H0), act(T0, dims)
-    ck_s, ck_t, out = gdn.verify_paths(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims),
-                                       act(x.b, dims), None, tp, sp)
+    ins = (act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims))
+    ck_s, ck_t, out = gdn.verify_paths(d, weights(w, dims), *ins, None, tp, sp)
+    ck_s32, ck_t32, out32 = gdn.verify_paths(desc_of(dims, True), weights(w, dims), *ins, None, tp, sp)
     torch.cuda.synchronize()
+    assert torch.equal(ck_s32, ck_s) and torch.equal(ck_t32, ck_t)
     od = oracle.Dims.of(dims)
     for s in (5, 63):
         sl = slice(s, s + 1)
         ref = oracle.verify_paths(od, w, x.mixed[sl], x.z[sl], x.a[sl], x.b[sl], T0[sl], H0[sl])
         assert_out_close(host(out[s]), ref["out"][0], dims, f"paths out seq {s}")
+        assert_out_flat(host(out32[s]), ref["out"][0], f"paths fp32 out seq {s}")
         cks = host(ck_s[s])
         for p in range(P):
             for i in range(T):
@@ -301,10 +345,13 @@ def test_verify_checkpoints_and_commit():
     sp, tp = f32(H0), act(T0, dims)
     mx, zz, aa, bb = act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims)
     ck_s, ck_t, out = gdn.verify_with_checkpoints(d, W, mx, zz, aa, bb, None, tp, sp)
+    ck_s32, ck_t32, out32 = gdn.verify_with_checkpoints(desc_of(dims, True), W, mx, zz, aa, bb, None, tp, sp)
     torch.cuda.synchronize()
     assert np.array_equal(host(sp), H0), "verify modified the pool"
+    assert torch.equal(ck_s32, ck_s) and torch.equal(ck_t32, ck_t)
     ref = oracle.verify(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, T0, H0)
     assert_out_close(host(out), ref["out"], dims, "verify out")
+    assert_out_flat(host(out32), ref["out"], "verify fp32 out")
     cks = host(ck_s)
     for i in range(T):
         assert_state_close(cks[:, i], ref["ckpt_H"][:, i], f"checkpoint {i}")
@@ -590,24 +637,27 @@ def test_split_exchange_graph_replay_equals_eager():
         assert torch.equal(state, ref_state) and torch.equal(tail, ref_tail), f"replay {rep}: state differs"
 
 
-@pytest.mark.parametrize("dims,B,L,launches", [
-    (SMALL, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),       # 16 units: segment maps, scan, segments
-    (NEXT, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),        # 32 units
-    (NEXT, 2, 1030, ["fused", "tail"]),                                   # 64 units, 17 chunks: too short for segments
-    (NEXT, 8, 512, ["fused", "tail"]),                                    # 256 units fill the chip
+@pytest.mark.parametrize("path,dims,B,L,launches", [
+    ("fused", SMALL, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),  # 16 units: segment maps, scan, segments
+    ("fused", NEXT, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),   # 32 units
+    ("fused", NEXT, 2, 1030, ["fused", "tail"]),                              # 64 units, 17 chunks: too short for segments
+    (None, NEXT, 8, 512, ["fused", "tail"]),                                  # 256 units: the library's own choice
+    (None, NEXT, 6, 300, ["fused", "tail"]),                                  # 192 units
+    (None, NEXT, 5, 300, ["chunk_prep", "state_pass"]),                       # 160 units: the two-launch path
 ])
-def test_prefill_fused_launches(dims, B, L, launches):
+def test_prefill_fused_launches(path, dims, B, L, launches):
     """Which launches a d = 128 bf16 prefill call makes: the fused kernel with one workgroup per
     (sequence, value head), preceded by the segment maps and the scan where few units run long calls,
-    then the conv-tail update."""
-    _say(f"fused launches B={B} L={L} dims={dims}")
+    then the conv-tail update; the library takes it from 192 units on."""
+    _say(f"fused launches path={path} B={B} L={L} dims={dims}")
     d = desc_of(dims)
     w, x, rng = make_layer(7, dims, B, L)
     tail = act(np.zeros(dims.tail_shape(B), np.float32), dims)
     st = f32(np.zeros(dims.state_shape(B), np.float32))
     gdn.timing_begin(16)
-    gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims),
-                      i32(x.lens), tail, st)
+    with prefill_path(path):
+        gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims),
+                          i32(x.lens), tail, st)
     recs = gdn.timing_end(16)
     assert [n for n, _ in recs] == launches
 
