@@ -640,7 +640,8 @@ def test_split_exchange_graph_replay_equals_eager():
 @pytest.mark.parametrize("path,dims,B,L,launches", [
     ("fused", SMALL, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),  # 16 units: segment maps, scan, segments
     ("fused", NEXT, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),   # 32 units
-    ("fused", NEXT, 2, 1030, ["fused", "tail"]),                              # 64 units, 17 chunks: too short for segments
+    ("fused", NEXT, 2, 1030, ["fused_map", "fused_scan", "fused", "tail"]),   # 64 units, 17 chunks: 3 segments
+    ("fused", NEXT, 2, 700, ["fused", "tail"]),                               # 11 chunks: too short for 3 segments
     (None, NEXT, 8, 512, ["fused", "tail"]),                                  # 256 units: the library's own choice
     (None, NEXT, 6, 300, ["fused", "tail"]),                                  # 192 units
     (None, NEXT, 5, 300, ["chunk_prep", "state_pass"]),                       # 160 units: the two-launch path
