@@ -57,7 +57,7 @@ EXPORTS = ("gdn_last_error", "gdn_version", "gdn_conv_chunk", "gdn_prefill_works
            "gdn_state_copy",
            "gdn_state_record_bytes", "gdn_state_zero", "gdn_pcache_create", "gdn_pcache_destroy", "gdn_pcache_row",
            "gdn_pcache_stats", "gdn_pcache_alive", "gdn_mfma_probe", "gdn_timing_begin", "gdn_timing_end",
-           "gdn_device_status")
+           "gdn_device_status", "gdn_prefill_chunk_noalloc")
 
 
 def load_library(path: str = LIB_PATH):
@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_prefill_workspace_bytes.argtypes = [D, I, I]
     lib.gdn_prefill_workspace_bytes.restype = Z
     lib.gdn_prefill_chunk.argtypes = [D, W, P, P, P, P, P, P, P, P, I, I, P, Z, P]
+    lib.gdn_prefill_chunk_noalloc.argtypes = [D, W, P, P, P, P, P, P, P, P, I, I, P]
+    lib.gdn_prefill_chunk_noalloc.restype = I
     lib.gdn_decode_step.argtypes = [D, W, P, P, P, P, P, P, P, P, I, P]
     lib.gdn_verify_with_checkpoints.argtypes = [D, W, P, P, P, P, I, P, P, P, P, P, P, I, P]
     lib.gdn_verify_paths.argtypes = [D, W, P, P, P, P, I, I, P, P, P, P, P, P, I, P]

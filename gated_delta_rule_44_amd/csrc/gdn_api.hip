@@ -64,8 +64,9 @@ int out_f32(const gdn_desc* d) { return d->act_dtype == GDN_F32 || d->out_dtype 
 // pass over several CUs, is faster. GDN_PREFILL_PATH in the environment overrides the choice for
 // tests and comparisons: "fused" (with segment maps and a scan for few units) or "two_phase".
 constexpr long kFusedMinUnits = 192;
+bool fused_built(const gdn_desc* d) { return d->d_k == 128 && d->act_dtype == GDN_BF16; }
 bool use_fused(const gdn_desc* d, int B) {
-  if (d->d_k != 128 || d->act_dtype != GDN_BF16) return false;
+  if (!fused_built(d)) return false;
   const char* e = getenv("GDN_PREFILL_PATH");
   if (e && strcmp(e, "fused") == 0) return true;
   if (e && strcmp(e, "two_phase") == 0) return false;
@@ -96,6 +97,12 @@ thread_local int t_cap = 0, t_used = 0;
 // its f16 operands can hold (|H| >= 255, or not finite).
 __device__ int gdn_status_word;
 
+// Workspace of gdn_prefill_chunk_noalloc: a file-scope device array (each device that loads the library
+// holds its own copy until the process ends). Host code only ever uses its device address, looked up
+// per device with hipGetSymbolAddress: the array's name on the host is a host-side stand-in.
+constexpr size_t kScratchBytes = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 // the word's device address on the current device (each device holds its own copy), looked up once
 int* status_ptr() {
@@ -113,6 +120,28 @@ int* status_ptr() {
       p = nullptr;
     }
     ptr[dev] = (int*)p;
+  });
+  return ptr[dev];
+}
+}  // namespace
+
+namespace {
+// the scratch array's address on the current device, looked up once per device (with that device current)
+void* scratch_ptr() {
+  static void* ptr[64];
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+    ptr[dev] = p;
   });
   return ptr[dev];
 }
@@ -231,9 +260,10 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc* d, int B, int Lb) {
   return gdn::prefill_ws_bytes(B, d->n_k, d->n_v, d->d_k, Lb, n_chunks, d->act_dtype == GDN_F32);
 }
 
-int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
-                      const void* b, const int32_t* len, void* conv_tail, float* state, void* out, int B, int Lb,
-                      void* ws, size_t ws_bytes, gdn_stream_t stream) {
+// the checks and launches of a prefill call; fused: take the fused path whatever the size
+static int prefill_impl(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
+                        const void* b, const int32_t* len, void* conv_tail, float* state, void* out, int B, int Lb,
+                        void* ws, size_t ws_bytes, gdn_stream_t stream, bool fused) {
   if (int rc = check_desc(d)) return rc;
   if (int rc = check_weights(w)) return rc;
   if (!mixed || !z || !a || !b || !len || !conv_tail || !state || !out || !ws)
@@ -246,7 +276,7 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
     return fail(GDN_EINVAL, "gdn_prefill_chunk: B * chunks * n_k must stay below 2^31");
   if (d->act_dtype == GDN_F32 && d->d_k > 64)
     return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunk: fp32 activations are built for d <= 64 (got %d)", d->d_k);
-  const size_t need = gdn_prefill_workspace_bytes(d, B, Lb);
+  const size_t need = fused ? gdn::fused_ws_bytes(B, d->n_v, Lb) : gdn_prefill_workspace_bytes(d, B, Lb);
   if (ws_bytes < need) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace %zu bytes < %zu needed", ws_bytes, need);
   if (((uintptr_t)ws & 255u) != 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace must be 256-byte aligned");
   if (!aligned16(state) || !aligned16(mixed) || !aligned16(z) || !aligned16(out) || !aligned16(conv_tail) ||
@@ -254,7 +284,7 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
     return fail(GDN_EINVAL, "gdn_prefill_chunk: buffers must be 16-byte aligned");
   if (out == mixed || out == z || (void*)state == out || conv_tail == out)
     return fail(GDN_EINVAL, "gdn_prefill_chunk: out aliases another buffer");
-  if (use_fused(d, B)) {
+  if (fused || use_fused(d, B)) {
     gdn::FusedArgs f{};
     f.conv_w = w->conv_w; f.A_log = w->A_log; f.dt_bias = w->dt_bias; f.norm_w = w->norm_w;
     f.mixed = mixed; f.z = z; f.a = a; f.b = b; f.len = len; f.tail = conv_tail; f.state = state; f.out = out;
@@ -275,6 +305,33 @@ int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed
   gdn::prefill_ws_layout(p, d->d_k, d->act_dtype == GDN_F32);
   return hip_status(gdn::launch_prefill(p, d->act_dtype, d->d_k, d->n_v / d->n_k, (hipStream_t)stream),
                     "gdn_prefill_chunk");
+}
+
+int gdn_prefill_chunk(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
+                      const void* b, const int32_t* len, void* conv_tail, float* state, void* out, int B, int Lb,
+                      void* ws, size_t ws_bytes, gdn_stream_t stream) {
+  return prefill_impl(d, w, mixed, z, a, b, len, conv_tail, state, out, B, Lb, ws, ws_bytes, stream, false);
+}
+
+int gdn_prefill_chunk_noalloc(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
+                              const void* b, const int32_t* len, void* conv_tail, float* state, void* out, int B,
+                              int Lb, gdn_stream_t stream) {
+  if (int rc = check_desc(d)) return rc;
+  if (B <= 0 || Lb <= 0) return fail(GDN_EINVAL, "gdn_prefill_chunk_noalloc: B=%d Lb=%d must be positive", B, Lb);
+  // the call's own path if its workspace fits the scratch; else, where it is built, the fused path,
+  // whose segment workspace never exceeds half the scratch
+  const size_t need = gdn_prefill_workspace_bytes(d, B, Lb);
+  bool fused = false;
+  if (need > kScratchBytes) {
+    if (!fused_built(d) || gdn::fused_ws_bytes(B, d->n_v, Lb) > kScratchBytes)
+      return fail(GDN_EINVAL,
+                  "gdn_prefill_chunk_noalloc: the call needs %zu bytes of workspace, more than the %zu-byte static "
+                  "scratch; use gdn_prefill_chunk with a workspace", need, (size_t)kScratchBytes);
+    fused = true;
+  }
+  void* ws = scratch_ptr();
+  if (!ws) return fail(GDN_EHIP, "gdn_prefill_chunk_noalloc: no device address for the static scratch");
+  return prefill_impl(d, w, mixed, z, a, b, len, conv_tail, state, out, B, Lb, ws, kScratchBytes, stream, fused);
 }
 
 static int step_common(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,

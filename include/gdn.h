@@ -124,6 +124,23 @@ int gdn_prefill_chunk(const gdn_desc* desc, const gdn_weights* w, const void* mi
                       void* out, int B, int Lb, void* ws, size_t ws_bytes, gdn_stream_t stream);
 
 /*
+ * gdn_prefill_chunk for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same call without a workspace argument. The
+ * library's own static device scratch of 64 MiB serves as the workspace; nothing is allocated.
+ *   Path: the one gdn_prefill_chunk takes when its workspace fits the scratch; otherwise, for d = 128
+ *   with bf16 activations, the fused path with segment maps (at most 32 MiB); results of either path
+ *   meet the layer's bounds against the oracle.
+ *   Errors: GDN_EINVAL, with nothing launched, when the call needs more workspace than the scratch
+ *   holds (other shapes with very long calls); otherwise as gdn_prefill_chunk.
+ *   Concurrency: every call on one device shares that device's scratch, which keeps the last call's
+ *   contents; calls that may overlap on one device (two streams, two threads) race and must be
+ *   serialised by the caller.
+ */
+int gdn_prefill_chunk_noalloc(const gdn_desc* desc, const gdn_weights* w, const void* mixed, const void* z,
+                              const void* a, const void* b, const int32_t* len, void* conv_tail, float* state,
+                              void* out, int B, int Lb, gdn_stream_t stream);
+
+/*
  * One decode token for each of B sequences (the recurrence with Lb = len = 1).
  *   mixed [B][C_ch], z [B][n_v*d_v], a and b [B][n_v]
  *   slot  [B] rows of the pools that sequence b owns (device), or NULL for slot[b] = b; slots must
