@@ -113,6 +113,16 @@ def version() -> str:
     return load_library().gdn_version().decode()
 
 
+def device_status(clear: bool = True) -> int:
+    """Bits the kernels raised on the current device since the word was last cleared (synchronizes the
+    current stream): GDN_STATUS_RANGE = a prefill's final state left the f16 operand range."""
+    lib = load_library()
+    rc = lib.gdn_device_status(1 if clear else 0, _stream())
+    if rc < 0:
+        _check("gdn_device_status", rc)
+    return rc
+
+
 @dataclass(frozen=True)
 class GdnDesc:
     n_k: int

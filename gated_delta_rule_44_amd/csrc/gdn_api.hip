@@ -300,6 +300,7 @@ static int prefill_impl(const gdn_desc* d, const gdn_weights* w, const void* mix
   p.mixed = mixed; p.z = z; p.a = a; p.b = b; p.len = len; p.tail = conv_tail; p.state = state; p.out = out;
   p.ws = ws; p.B = B; p.Lb = Lb; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d);
   p.out_f32 = out_f32(d);
+  p.status = status_ptr();
   p.n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
   p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
   gdn::prefill_ws_layout(p, d->d_k, d->act_dtype == GDN_F32);

@@ -74,6 +74,7 @@ struct PrefillArgs {
   int B, Lb, n_k, n_v, C, n_chunks;
   int nsplit;           // column slices per head in the state pass (1: the whole head)
   int exchange;         // split heads: 1 = the slices exchange row sums, 0 = a norm pass finishes
+  int* status;          // device word: bit 0 set when a final state leaves the operand range (or null)
   float scale, l2_eps, rms_eps;
 };
 // fp32 activations run every MFMA operand as a hi/lo pair (split_all) and are built for d <= 64

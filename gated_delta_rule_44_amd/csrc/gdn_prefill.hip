@@ -1677,12 +1677,19 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
     }
   }
 
-  // final state, in place
+  // final state, in place; a value outside the range of the 2^8-scaled f16 operand pairs (or not finite)
+  // raises the range bit of the device status word
   if (owner) {
+    bool bad = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[(long)(16 * w + 4 * g16 + i) * D + cb + 16 * nt + r16] = Hacc[nt][i] * kInvS16;
+      for (int i = 0; i < 4; ++i) {
+        const float v = Hacc[nt][i] * kInvS16;
+        bad |= !(fabsf(v) < 255.f);
+        st[(long)(16 * w + 4 * g16 + i) * D + cb + 16 * nt + r16] = v;
+      }
+    if (p.status && __any(bad) && lane == 0) atomicOr(p.status, 1);
   }
 
   // conv tail: rows len .. len+2 of [old tail | mixed]. Split 0 of value head h owns its v channels;

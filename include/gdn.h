@@ -30,7 +30,14 @@
  * workspace too small); GDN_EUNSUPPORTED = -2 (a shape this build has no kernel for: d_k != d_v, d_k
  * not in {32, 64, 128}, conv_k != 4, n_v / n_k not in {1, 2, 4}, or fp32 activations with d_k > 64 in
  * gdn_prefill_chunk; the caller falls back, as the statecache.py page's StateCache falls back to the
- * plain path on _NotCached); GDN_EHIP = -3.
+ * plain path on _NotCached); GDN_EHIP = -3. The layer definition itself only rules out d_k, d_v outside
+ * {32, 64, 128}, conv_k != 4 and n_v % n_k != 0; the other limits are this build's.
+ *
+ * Value range (prefill): the chunked prefill carries the state, the write vectors u and the keys and
+ * queries as pairs of f16 values scaled by 2^8 (about 22 bits), so |state| and |u| must stay below 255.
+ * Activations of unit scale keep them far below (the saved states of the tests are within |S| < 10). A
+ * prefill whose final state leaves that range, or is not finite, sets GDN_STATUS_RANGE in the device
+ * status word (gdn_device_status); decode and verify run fp32 throughout and have no such limit.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -141,7 +148,9 @@ int gdn_prefill_chunk_noalloc(const gdn_desc* desc, const gdn_weights* w, const 
                               void* out, int B, int Lb, gdn_stream_t stream);
 
 /*
- * One decode token for each of B sequences (the recurrence with Lb = len = 1).
+ * One decode token for each of B sequences: the layer with Lb = len = 1 (the "uni_engine.py" page's
+ * decode path, which advances every sequence's conv and recurrent state by one token in place, and the
+ * per-token step of the "mtp/generate.py" page's decode loop), in fp32 throughout.
  *   mixed [B][C_ch], z [B][n_v*d_v], a and b [B][n_v]
  *   slot  [B] rows of the pools that sequence b owns (device), or NULL for slot[b] = b; slots must
  *         be distinct

@@ -187,3 +187,35 @@ def test_canaries_decode_verify_paths():
                         (ckt, "ckpt_tail"), (vout, "verify out"), (pcks, "path ckpt_state"),
                         (pckt, "path ckpt_tail"), (pout, "paths out")):
             g.check(f"{name} (out_f32={out_f32})")
+
+
+@pytest.mark.parametrize("path", BOTH)
+def test_large_saved_state_range(path):
+    """Saved states far above unit scale: std 30 (|S| up to ~140) stays inside the prefill's operand range
+    and matches the oracle (fp32 outputs at 2e-3, state at 1e-3 of its max); std 400 leaves it, and the
+    call reports that through the device status word instead of passing silently."""
+    from tests.gpu_helpers import assert_out_flat
+    dims = LayerDims(n_k=2, n_v=4, d_k=128, d_v=128)
+    B, L = 2, 200
+    w, x, rng = make_layer(26, dims, B, L)
+    t0 = random_state(rng, dims, B)[1]
+    od = oracle.Dims.of(dims)
+    d = desc_of(dims, True)
+    for std, in_range in ((30.0, True), (400.0, False)):
+        _say(f"large saved state path={path} std={std}")
+        H0 = (rng.standard_normal(dims.state_shape(B)) * std).astype(np.float32)
+        gdn.device_status(clear=True)
+        st, tail = f32(H0), act(t0, dims)
+        with prefill_path(path):
+            out = gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims),
+                                    act(x.b, dims), i32(x.lens), tail, st)
+        status = gdn.device_status(clear=True)
+        if in_range:
+            assert status == 0, status
+            for s in range(B):
+                ref = oracle.layer_forward(od, w, x.mixed[s:s + 1], x.z[s:s + 1], x.a[s:s + 1], x.b[s:s + 1], None,
+                                           t0[s:s + 1], H0[s:s + 1])
+                assert_out_flat(host(out[s]), ref["out"][0], f"out seq {s}")
+                assert_state_close(host(st[s]), ref["H"][0], f"state seq {s}")
+        else:
+            assert status & gdn.GDN_STATUS_RANGE, "a state beyond the operand range went unreported"
