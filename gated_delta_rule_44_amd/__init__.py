@@ -24,6 +24,7 @@ GDN_BF16 = 0
 GDN_F32 = 1
 GDN_OUT_ACT = 0          # out in the activation dtype
 GDN_STATUS_RANGE = 1     # device status bit: a prefill's final state left the f16 operand range
+GDN_STATUS_EXCHANGE = 2  # device status bit: a row-sum exchange wait expired (rows written as NaN)
 _ACT_TORCH = {GDN_BF16: torch.bfloat16, GDN_F32: torch.float32}
 
 _STATUS = {0: "GDN_OK", -1: "GDN_EINVAL", -2: "GDN_EUNSUPPORTED", -3: "GDN_EHIP"}

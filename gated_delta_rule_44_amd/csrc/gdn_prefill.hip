@@ -1364,14 +1364,20 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
       return pend == 0 || t >= Lb;
     };
     float tot;
-    if (!__all(combine(tot))) {
+    bool ready = combine(tot);
+    if (!__all(ready)) {
       const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
       do {
         __builtin_amdgcn_s_sleep(2);
         load_sums(cc, sums);
-      } while (!__all(combine(tot)) && __builtin_amdgcn_s_memrealtime() - t_start < kSpinTicks);
+        ready = combine(tot);
+      } while (!__all(ready) && __builtin_amdgcn_s_memrealtime() - t_start < kSpinTicks);
     }
-    const float inv = rsqrt_fast(tot / (float)D + p.rms_eps);
+    // a row whose sums never all arrived (the bound expired: a slice of the head was not running) is
+    // written as NaN and reported through the device status word, never normalised with a missing sum
+    float inv = rsqrt_fast(tot / (float)D + p.rms_eps);
+    if (!ready) inv = __builtin_nanf("");
+    if (p.status && !__all(ready) && lane == 0) atomicOr(p.status, 2);
     const long row = ((long)b * Lb + t) * n_v + h;
     if (t < Lb) {
 #pragma unroll
@@ -1799,6 +1805,28 @@ void launch_pass(const PrefillArgs& p, hipStream_t st) {
   hipLaunchKernelGGL((state_pass_kernel<ActT, D, NT, SPLIT, NM, (NT <= 4), SH>), dim3(NSPLIT * p.n_v * p.B), dim3(512), 0, st, p);
 }
 
+// The exchanging state pass as a cooperative launch: the runtime starts it only if every workgroup can
+// be resident at once (which the slices' waits need), else refuses and nothing runs
+template <typename ActT, int D, int NT, bool SPLIT, bool SH>
+hipError_t launch_pass_coop(const PrefillArgs& p, hipStream_t st) {
+  constexpr int NSPLIT = D / (16 * NT);
+  PrefillArgs q = p;
+  void* args[] = {&q};
+  return hipLaunchCooperativeKernel((const void*)state_pass_kernel<ActT, D, NT, SPLIT, kNormExchange, true, SH>,
+                                    dim3(NSPLIT * p.n_v * p.B), dim3(512), args, 0, st);
+}
+
+// true while `st` is being captured into a graph (a replay may share the device with other work, so the
+// slices' co-residency that the exchange needs is not guaranteed there)
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
 constexpr long kNtRecordBytes = 160L << 20;
 
 template <typename ActT, int D, int R, bool SPLIT, int NT>
@@ -1818,18 +1846,22 @@ hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
   timing_after(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  bool exchanged = false;
   timing_before("state_pass", st);
   if constexpr (NSPLIT == 1) {
     launch_pass<ActT, D, NT, SPLIT, kNormFused, (R > 1)>(p, st);
   } else if constexpr (NSPLIT == 2 || NSPLIT == 4) {
-    if (p.exchange) launch_pass<ActT, D, NT, SPLIT, kNormExchange, (R > 1)>(p, st);
-    else launch_pass<ActT, D, NT, SPLIT, kNormPass, (R > 1)>(p, st);
+    if (p.exchange && !capturing(st)) {
+      exchanged = launch_pass_coop<ActT, D, NT, SPLIT, (R > 1)>(p, st) == hipSuccess;
+      if (!exchanged) (void)hipGetLastError();  // refused: the norm pass below, which never waits
+    }
+    if (!exchanged) launch_pass<ActT, D, NT, SPLIT, kNormPass, (R > 1)>(p, st);
   } else {
     launch_pass<ActT, D, NT, SPLIT, kNormPass, (R > 1)>(p, st);
   }
   timing_after(st);
   e = hipGetLastError();
-  if (e != hipSuccess || NSPLIT == 1 || p.exchange) return e;
+  if (e != hipSuccess || NSPLIT == 1 || exchanged) return e;
   const long per_seq = (long)p.Lb * p.n_v * (D / 4);  // < 2^31, checked by the caller
   timing_before("norm", st);
   hipLaunchKernelGGL((norm_kernel<ActT, D, NSPLIT>), dim3((unsigned)((per_seq + 255) / 256), p.B), dim3(256), 0, st, p);

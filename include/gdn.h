@@ -88,10 +88,15 @@ const char* gdn_version(void);
  * then reads the device's status word, and clears it when `clear` is non-zero). Returns the bits
  * (>= 0) or GDN_EHIP. Bit 0 (GDN_STATUS_RANGE): a prefill's final state left the range its f16
  * operand pairs carry (|state| >= 255 or not finite); that call's state and outputs are not to be
- * trusted. Kernels only set bits, so the word collects every call since it was last cleared, on
- * every stream of the device.
+ * trusted. Bit 1 (GDN_STATUS_EXCHANGE): in a prefill whose head columns were split over workgroups
+ * that exchange row sums for the gated norm, a workgroup waited in vain for another's sums; the rows
+ * concerned were written as NaN. The exchange is only launched cooperatively (the runtime guarantees
+ * that every workgroup is resident, or refuses, and the call then finishes the norm in a separate pass)
+ * and never under graph capture, so this bit marks a fault, not a case the library expects. Kernels
+ * only set bits, so the word collects every call since it was last cleared, on every stream of the
+ * device.
  */
-enum { GDN_STATUS_RANGE = 1 };
+enum { GDN_STATUS_RANGE = 1, GDN_STATUS_EXCHANGE = 2 };
 int gdn_device_status(int clear, gdn_stream_t stream);
 
 /*

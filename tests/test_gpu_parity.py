@@ -586,10 +586,12 @@ def test_continuation_graph_replay_equals_eager():
 
 
 def test_split_exchange_graph_replay_equals_eager():
-    """Two continued 1100-token calls on 2 sequences of a 16/32-head layer (64 pairs: 32-column slices
-    that exchange their partial row sums, which chunk_prep marks pending on every call) captured once
-    into a HIP graph: three replays, each after resetting the state, tail and outputs eagerly, give the
-    eager run's outputs and final state bit for bit."""
+    """Two continued 1100-token calls on 2 sequences of a 16/32-head layer (64 pairs: 32-column slices)
+    captured once into a HIP graph. Eagerly the slices exchange their partial row sums (a cooperative
+    launch); under capture the library finishes the norm in a separate pass, which never waits. Three
+    replays, each after resetting the state, tail and outputs eagerly, give the same bits every time,
+    the eager run's final state and tail bit for bit (the norm does not touch them), and its outputs
+    within the bound."""
     dims, B, L = NEXT, 2, 1100
     _say("split-head exchange graph replay")
     w, x, rng = make_layer(64, dims, B, 2 * L)
@@ -607,12 +609,16 @@ def test_split_exchange_graph_replay_equals_eager():
 
     def run():
         for mx, zz, aa, bb, out in calls:
-            gdn.prefill_chunk(d, W, mx, zz, aa, bb, lens, tail, state, out, ws)
+            with prefill_path("two_phase"):
+                gdn.prefill_chunk(d, W, mx, zz, aa, bb, lens, tail, state, out, ws)
 
+    gdn.timing_begin(16)
     run()
+    assert [n for n, _ in gdn.timing_end(16)] == ["chunk_prep", "state_pass"] * 2  # eagerly: the exchange
     torch.cuda.synchronize()
-    ref_out = [torch.cat([c[4][0], c[4][1, :L - 37]]).clone() for c in calls]
+    eager_out = [torch.cat([c[4][0], c[4][1, :L - 37]]).clone() for c in calls]
     ref_state, ref_tail = state.clone(), tail.clone()
+    ref_out = None
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -631,9 +637,14 @@ def test_split_exchange_graph_replay_equals_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for i, c in enumerate(calls):
-            got = torch.cat([c[4][0], c[4][1, :L - 37]])
-            assert torch.equal(got, ref_out[i]), f"replay {rep}: call {i} output differs"
+        got = [torch.cat([c[4][0], c[4][1, :L - 37]]).clone() for c in calls]
+        if ref_out is None:
+            ref_out = got
+            for i in range(2):  # two roundings to bf16 of fp32 values that differ in the last bits: 1 ulp apart
+                a, e = host(got[i]), host(eager_out[i])
+                assert np.all(np.abs(a - e) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(e)) + 1e-6), f"call {i}"
+        for i in range(2):
+            assert torch.equal(got[i], ref_out[i]), f"replay {rep}: call {i} output differs"
         assert torch.equal(state, ref_state) and torch.equal(tail, ref_tail), f"replay {rep}: state differs"
 
 
