@@ -36,9 +36,10 @@
 //
 // Precision: MFMA operands are f16 with fp32 accumulation; every operand whose rounding reaches the
 // output or state bounds is carried as a hi/lo pair of f16 values (about 22 bits), each product
-// being the three terms hi.hi + hi.lo + lo.hi: q and k in the Gram products, H, U, Q, P, k~, the -A
-// blocks, T_mm and the right-hand sides of the solve. K in K H is the high half alone (its rounding
-// measured negligible). To keep low halves above f16's subnormal range (which MFMA flushes), operands
+// being the three terms hi.hi + hi.lo + lo.hi: q and k in the Gram products, H, U, Q, P, k~, T_mm
+// and the right-hand sides of the solve. K in K H and the off-diagonal -A blocks of the solve are the
+// high half alone: a rounding model of the chunk form puts their cost at a few hundredths of the
+// output bound, where a single-f16 U, right-hand side or P costs about twice the bound. To keep low halves above f16's subnormal range (which MFMA flushes), operands
 // carry exact power-of-two scales: 2^8 for q, k, H, U, A, T, right-hand sides; 2^16 for P, whose
 // entries span many decades. Accumulators: H as 2^16 H, K H and U as 2^16, O^T as 2^24 O^T.
 // The scales bound what the operands can hold: |H| and |U| must stay below 255.
@@ -67,8 +68,8 @@ constexpr int L_Q = 0;                       // q:   [mt 4][kk 4][hl 2][lane] f1
 constexpr int L_K = L_Q + 32768;             // k:   [mt 4][kk 4][hl 2][lane] f16x8, 2^8 k (token rows)
 constexpr int L_KT = L_K + 32768;            // k~:  [hm 8][kb 2][hl 2][lane] f16x8, 2^8 e^{gC-g} k (d rows)
 constexpr int L_P = L_KT + 32768;            // P:   [pair 6][hl 2][lane] f16x8, 2^16 scale e^{gt-gs} q.k
-constexpr int L_AO = L_P + 6 * 2 * 1024;     // -A:  [pair 6][hl 2][lane] f16x4, 2^8 (off-diagonal 16 x 16 blocks)
-constexpr int L_TI = L_AO + 6 * 2 * 512;     // T_mm:[m 4][hl 2][lane] f16x4, 2^8
+constexpr int L_AO = L_P + 6 * 2 * 1024;     // -A:  [pair 6][lane] f16x4, 2^8, hi only (off-diagonal 16 x 16 blocks)
+constexpr int L_TI = L_AO + 6 * 512;     // T_mm:[m 4][hl 2][lane] f16x4, 2^8
 constexpr int LDA = 20;                      // row stride (floats) of the fp32 16 x 16 blocks (16-byte rows)
 constexpr int L_AD = L_TI + 4 * 2 * 512;     // A_mm fp32 [m 4][16][LDA] (strictly lower part)
 constexpr int L_TF = L_AD + 4 * 16 * LDA * 4; // T_mm fp32 [m 4][16][LDA]
@@ -310,10 +311,9 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
       for (int j = 0; j < mt; ++j) {
-        const f16x4 ah = sAO[(aidx(mt, j) * 2) * 64 + lane], al = sAO[(aidx(mt, j) * 2 + 1) * 64 + lane];
+        const f16x4 ah = sAO[aidx(mt, j) * 64 + lane];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          Z[mt][n] = mfma16k(al, Uh[j][n], Z[mt][n]);
           Z[mt][n] = mfma16k(ah, Ul[j][n], Z[mt][n]);
           Z[mt][n] = mfma16k(ah, Uh[j][n], Z[mt][n]);
         }
@@ -707,10 +707,10 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = 16 * nt + 4 * g16 + e < r ? br * dec[e] * kk4[e] : 0.f;
         if (nt < mt) {
-          f16x4 hi, lo;
-          split4v(x * -kS8, hi, lo);
-          sAO[(aidx(mt, nt) * 2) * 64 + lane] = hi;
-          sAO[(aidx(mt, nt) * 2 + 1) * 64 + lane] = lo;
+          f16x4 hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hi[e] = (_Float16)(x[e] * -kS8);
+          sAO[aidx(mt, nt) * 64 + lane] = hi;
         } else {
           *(float4*)&sAD[(mt * 16 + c16) * LDA + 4 * g16] = make_float4(x[0], x[1], x[2], x[3]);
         }

@@ -41,7 +41,10 @@
 // fp32 activations every operand is split. MFMA flushes f16 subnormals, so the lo half of a split value
 // must stay >= 2^-14: operands of unit scale are carried multiplied by 2^8 (exact), and the scales are
 // chosen so that every product lands in a consistent domain: the state pass keeps H as 2^16 H, U as
-// 2^8 U and O^T as 2^16 O^T, with 2^8 Q~, 2^8 P~, 2^8 K~, 2^8 U' and unscaled -W in the record.
+// 2^8 U and O^T as 2^24 O^T, with 2^16 Q~, 2^16 P~, 2^8 K~, 2^16 U' and 2^8 -W in the record. Q~ and
+// P~ hold scale (< 1) and the decays folded in, and -W is small: at 2^8 their lo halves (and the small
+// entries of -W) would fall below 2^-14 and flush, which costs about half of a 2e-3 output bound at a
+// 4096-token prefill; at these scales the rounding costs a fifth of it.
 #include <mutex>
 #include <type_traits>
 
@@ -56,6 +59,7 @@ constexpr int C64 = kChunk;
 constexpr float kS8 = 256.f;              // 2^8 operand scale
 constexpr float kInvS8 = 1.f / 256.f;
 constexpr float kInvS16 = 1.f / 65536.f;
+constexpr float kInvS24 = 1.f / 16777216.f;
 // a split head's partial sum of squares not posted yet (a posted sum is >= 0 or NaN, never -1)
 constexpr float kSsPending = -1.f;
 // bound of a slice's wait for the other slices' sums, in ticks of the 100 MHz constant clock (1 s)
@@ -116,18 +120,18 @@ __device__ __forceinline__ void split4(f32x4 x, f16x4& hi, f16x4& lo) {
 template <int D, bool SPLIT, bool SH>
 struct Rec {
   static constexpr int KD = D / 32, HM = D / 16;
-  static constexpr int W_HI = 0;                               // [mt][kk]: -W[token][d_k]
+  static constexpr int W_HI = 0;                               // [mt][kk]: 2^8 -W[token][d_k]
   static constexpr int W_LO = W_HI + 4 * KD;                   // (fp32 activations only)
-  static constexpr int Q_HI = W_LO + (SPLIT ? 4 * KD : 0);     // [mt][kk]: 2^8 Q~[token][d_k] (SH false)
+  static constexpr int Q_HI = W_LO + (SPLIT ? 4 * KD : 0);     // [mt][kk]: 2^16 Q~[token][d_k] (SH false)
   static constexpr int Q_LO = Q_HI + 4 * KD;
-  static constexpr int P_HI = SH ? Q_HI : Q_LO + 4 * KD;       // [mt][kk]: 2^8 P~[token t][token s]
+  static constexpr int P_HI = SH ? Q_HI : Q_LO + 4 * KD;       // [mt][kk]: 2^16 P~[token t][token s]
   static constexpr int P_LO = P_HI + 8;
   static constexpr int K_HI = P_LO + 8;                        // [hm][kk]: 2^8 K~^T[d_k][token] (SH false)
   static constexpr int K_LO = K_HI + 2 * HM;
-  static constexpr int UP = SH ? K_HI : K_LO + 2 * HM;         // [mt][nt]: 2^8 U' in accumulator order
+  static constexpr int UP = SH ? K_HI : K_LO + 2 * HM;         // [mt][nt]: 2^16 U' in accumulator order
   static constexpr int NBLK = UP + 4 * HM;
   static constexpr long kGc = NBLK * 1024L;                    // e^{gamma_C}
-  static constexpr long kEg = kGc + 256;                       // SH: scale e^{gamma_t}, t = 0..63
+  static constexpr long kEg = kGc + 256;                       // SH: 2^8 scale e^{gamma_t}, t = 0..63
   static constexpr long kEd = kEg + 256;                       // SH: e^{gamma_C - gamma_t}
   static constexpr long kBytes = kGc + (SH ? 768 : 256);
 };
@@ -547,13 +551,13 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
       for (int i = 0; i < 16; ++i) sTf[(16 * blk + i) * LF + 16 * blk + jj] = x[i];
     }
     {
-      // Q~ (token tile q & 3, block q >> 2): 2^8 scale e^{gamma_t} q_t
+      // Q~ (token tile q & 3, block q >> 2): 2^16 scale e^{gamma_t} q_t
 #pragma unroll
       for (int i = 0; i < QPW; ++i) {
         const int q = w + NWV * i;
         if (!SH && q < 4 * KD) {
           const int mt = q & 3, kk = q >> 2;
-          const float fq = p.scale * sEg[16 * mt + r16];
+          const float fq = kS8 * p.scale * sEg[16 * mt + r16];
           float x[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qfh[i][e] + (float)qfl[i][e]);
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
           put_frag(rec, RC::Q_LO + mt * KD + kk, lane, lo);
         }
       }
-      // P~ (token tile w & 3, block w >> 2): 2^8 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
+      // P~ (token tile w & 3, block w >> 2): 2^16 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
       {
         const int mt = w & 3, kk = w >> 2;
         const int t = 16 * mt + r16;
@@ -573,7 +577,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int s = 32 * kk + kslot(g16, e);
-          x[e] = s <= t ? p.scale * __expf(gt - gam[s]) * (kInvS8 * x[e]) : 0.f;
+          x[e] = s <= t ? p.scale * __expf(gt - gam[s]) * x[e] : 0.f;
         }
         f16x8 hi, lo;
         split8(x, hi, lo);
@@ -583,7 +587,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
       // K~^T (row tile idx >> 1, block idx & 1 for idx = w, w + 8, ...): 2^8 e^{gamma_C - gamma_s} k_s;
       // with a key record, the per-token decays instead
       if (SH && tid < C64) {
-        *(float*)(rec + RC::kEg + 4 * tid) = p.scale * sEg[tid];
+        *(float*)(rec + RC::kEg + 4 * tid) = kS8 * p.scale * sEg[tid];
         *(float*)(rec + RC::kEd + 4 * tid) = sEd[tid];
       }
       for (int idx = SH ? 2 * HM : w; idx < 2 * HM; idx += NWV) {
@@ -651,7 +655,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
         }
       }
       for (int j = w; j < HM; j += NWV) {
-        // W^T tile (j, mt) = (2^8 beta e^gamma K)^T (2^8 T)^T = 2^16 W^T; lane (g, c) holds
+        // W^T tile (j, mt) = (2^8 beta e^gamma K)^T (2^8 T)^T = 2^16 W^T, stored as 2^8 -W; lane (g, c) holds
         // W[16 mt + c][16 j + 4 g + i], half (j & 1) of the fragment of block j >> 1
         f16x8 kbh[2], kbl[2];
 #pragma unroll
@@ -679,14 +683,14 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f16x4 hi, lo;
-          split4(acc[mt] * -kInvS16, hi, lo);
+          split4(acc[mt] * -kInvS8, hi, lo);
           char* dst = rec + (RC::W_HI + mt * KD + (j >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (j & 1));
           *(f16x4*)dst = hi;
           if (SPLIT) *(f16x4*)(dst + 4 * KD * 1024) = lo;
         }
       }
       for (int nt = w; nt < HM; nt += NWV) {
-        // U' tile (mt, nt) = (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
+        // U' tile (mt, nt) = (2^8 T)(2^8 beta V) = 2^16 U', stored as is
         f16x8 vh[2], vl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -712,7 +716,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
         }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          *(f32x4*)(rec + (RC::UP + mt * HM + nt) * 1024 + (uint32_t)(lane * 16)) = (a1[mt] + a0[mt]) * kInvS8;
+          *(f32x4*)(rec + (RC::UP + mt * HM + nt) * 1024 + (uint32_t)(lane * 16)) = a1[mt] + a0[mt];
       }
     }
     if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gC);
@@ -900,7 +904,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // lower 16x16 tiles (mt, nt), nt <= mt, in row order
   auto tile_mt = [](int tile) { return tile >= 6 ? 3 : tile >= 3 ? 2 : tile >= 1 ? 1 : 0; };
 
-  // q: with one value head, Q~ = 2^8 scale e^{gamma_t} q_t into the value record; with several, 2^8 q
+  // q: with one value head, Q~ = 2^16 scale e^{gamma_t} q_t into the value record; with several, 2^8 q
   // into the key record (fragment (token tile q & 3, 32-block q >> 2) for q = w, w + 8, ...)
   constexpr int QPW = (4 * KD + NWV - 1) / NWV;
   char* krec = SH ? key_ptr<D>(p, b, kh, c) : nullptr;
@@ -916,7 +920,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         put_frag<NTS>(krec, KR::Q_HI + mt * KD + kk, lane, qh);
         put_frag<NTS>(krec, KR::Q_LO + mt * KD + kk, lane, ql);
       } else {
-        const float fq = p.scale * sEg[16 * mt + r16];
+        const float fq = kS8 * p.scale * sEg[16 * mt + r16];
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = fq * ((float)qh[e] + (float)ql[e]);
@@ -933,7 +937,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pb = pa;
   if (2 * pkk <= pmt) pa = gram(sKh, sKl, 32 * pkk, sQh, sQl, 16 * pmt);
   if (2 * pkk + 1 <= pmt) pb = gram(sKh, sKl, 32 * pkk + 16, sQh, sQl, 16 * pmt);
-  // P~ of every value head: 2^8 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
+  // P~ of every value head: 2^16 scale e^{gamma_t - gamma_s} q_t.k_s for s <= t, else 0
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float* gam = sGam + r * C64;
@@ -948,7 +952,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int s = 32 * pkk + kslot(g16, e);
-      x[e] = s <= t ? p.scale * __expf(gt - gam[s]) * (kInvS8 * x[e]) : 0.f;
+      x[e] = s <= t ? p.scale * __expf(gt - gam[s]) * x[e] : 0.f;
     }
     f16x8 hi, lo;
     split8(x, hi, lo);
@@ -1035,7 +1039,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (two) put_A(kt0 + 1, kkb);
     // with a key record: the per-token decays the state pass applies
     if (SH && tid < C64) {
-      *(float*)(rec + RC::kEg + 4 * tid) = p.scale * sEg[r * C64 + tid];
+      *(float*)(rec + RC::kEg + 4 * tid) = kS8 * p.scale * sEg[r * C64 + tid];
       *(float*)(rec + RC::kEd + 4 * tid) = sEd[r * C64 + tid];
     }
     // v of this head channel-major, into the k region
@@ -1110,22 +1114,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         f16x8 th[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) th[ks] = frag_row_h(sT + (16 * mt + r16) * LDT + 32 * ks, g16);
-        // W^T tile (w, mt) = 2^16 W^T; lane (g, c) holds W[16 mt + c][16 w + 4 g + i], half (w & 1)
+        // W^T tile (w, mt) = 2^16 W^T (stored as 2^8 -W); lane (g, c) holds W[16 mt + c][16 w + 4 g + i], half (w & 1)
         // of the fragment of block w >> 1
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) acc = mfma16(kb[r][ks], th[ks], acc);
         f16x4 hi, lo;
-        split4(acc * -kInvS16, hi, lo);
+        split4(acc * -kInvS8, hi, lo);
         st_rec<NTS>((f16x4*)(rec + (RC::W_HI + mt * KD + (w >> 1)) * 1024 + (uint32_t)(lane * 16 + 8 * (w & 1))), hi);
-        // U' tile (mt, w) = (2^8 T)(2^8 beta V) = 2^16 U', stored as 2^8 U'
+        // U' tile (mt, w) = (2^8 T)(2^8 beta V) = 2^16 U', stored as is
         f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           a0 = mfma16(th[ks], vl[ks], a0);
           a1 = mfma16(th[ks], vh[ks], a1);
         }
-        st_rec<NTS>((f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)), (a1 + a0) * kInvS8);
+        st_rec<NTS>((f32x4*)(rec + (RC::UP + mt * HM + w) * 1024 + (uint32_t)(lane * 16)), a1 + a0);
       }
     }
     if (tid == 0) *(float*)(rec + RC::kGc) = __expf(gam[C64 - 1]);
@@ -1402,7 +1406,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
     }
     lds_barrier();  // H of this chunk is in sH
     if constexpr (kChain) {
-      // ---- U = U' - W H (token tile tt); the hi*lo and hi*hi terms accumulate separately ----
+      // ---- 2^8 U = 2^-8 (2^16 U' + (2^8 -W)(2^8 H)) (token tile tt); hi*lo and hi*hi terms apart ----
       f32x4 U[NT];
 #pragma unroll
       for (int n0 = 0; n0 < NT; n0 += NG) {
@@ -1434,7 +1438,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
           if (n0 + NG >= NT) ld_w(f, cn, kk);  // last use of this block's W in the chunk
         }
 #pragma unroll
-        for (int g = 0; g < NG; ++g) U[n0 + g] = ua[g] + ub[g];
+        for (int g = 0; g < NG; ++g) U[n0 + g] = (ua[g] + ub[g]) * kInvS8;
       }
       // U hi/lo into its fragment slots: token tile tt is half (tt & 1) of 32-block tt >> 1 (and, with a
       // key record, the decayed U the state update takes)
@@ -1594,7 +1598,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
       float ss = 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        OT[nt] = OT[nt] * kInvS16;
+        OT[nt] = OT[nt] * kInvS24;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ss += OT[nt][i] * OT[nt][i];
       }
