@@ -9,9 +9,10 @@ write-back). Input sets rotate so that the 256 MB last-level cache does not hold
 `ms_per_step` is the median of per-call HIP-event times on the launch stream.
 
 `roofline` is that of the dominant launch of the call, timed live through the library's per-launch
-event session (gdn_timing_begin/end) on the launch stream: the state pass, priced against the dense
-f16 MFMA peak with the algorithmic FLOP of the inter-chunk step (6 d_k d_v per token and value head),
-or chunk_prep with the intra-chunk contractions (Gram, W, U', P). `call` prices the whole call: its
+event session (gdn_timing_begin/end) on the launch stream, priced against the dense f16 MFMA peak with
+its algorithmic FLOP: the state pass with the inter-chunk step (6 d_k d_v per token and value head),
+chunk_prep with the intra-chunk contractions (Gram, W, U', P), the fused launch (the path of shapes
+with many (sequence, value head) units, such as the stack layer) with both. `call` prices the whole call: its
 algorithmic bytes against HBM (the call's bound: 141 FLOP/B is below the ~312 FLOP/B ridge) and its
 algorithmic FLOP against MFMA. `traffic` is the counter-measured HBM bytes of that launch when the
 committed counter summary was taken on the current sources, else null.
@@ -27,7 +28,9 @@ The same run also measures, each as a sub-object of the one JSON line:
   conv    - the standalone causal conv + SiLU over 8 x 8192 tokens of the stack layer's channels
   copy    - the O(1) state bridge: 256 records {fp32 state, conv tail} of one layer
   measured_peaks - the MFMA probe's dense f16 TFLOP/s and the copy leg's GB/s beside the published peaks
-  cpu_baseline - the fp64 oracle on the host cores on the prefill workload
+  cpu_baseline - the fp64 oracle on the host cores on the prefill workload; the stack, decode, verify,
+                 verify_paths and continuation legs carry their own, on bounded samples of their
+                 workloads scaled to the leg's unit (the sample is stated in each)
 """
 from __future__ import annotations
 
@@ -45,6 +48,44 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0
+
+
+# ---- device tensors from the seeded numpy inputs --------------------------------------------------------
+def _desc(gdn, d):
+    from gdn_inputs import ACT_BF16
+    return gdn.GdnDesc(n_k=d.n_k, n_v=d.n_v, d_k=d.d_k, d_v=d.d_v, conv_k=d.conv_k,
+                       act_dtype=gdn.GDN_BF16 if d.act == ACT_BF16 else gdn.GDN_F32,
+                       scale=0.0 if d.scale is None else d.scale, l2_eps=d.l2_eps, rms_eps=d.rms_eps)
+
+
+def _act(torch, x, d):
+    from gdn_inputs import ACT_BF16
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32))).to("cuda")
+    return t.to(torch.bfloat16 if d.act == ACT_BF16 else torch.float32).contiguous()
+
+
+def _f32(torch, x):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32))).to("cuda")
+
+
+def _i32(torch, x):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.int32))).to("cuda")
+
+
+def _weights(torch, gdn, w, d):
+    return gdn.GdnWeights(_act(torch, w.conv_w, d), _f32(torch, w.A_log), _f32(torch, w.dt_bias),
+                          _f32(torch, w.norm_w))
+
+
+class _dev:
+    """The helpers above bound to torch and the binding."""
+
+    def __init__(self, torch, gdn):
+        self.desc_of = lambda d: _desc(gdn, d)
+        self.act = lambda x, d: _act(torch, x, d)
+        self.f32 = lambda x: _f32(torch, x)
+        self.i32 = lambda x: _i32(torch, x)
+        self.weights = lambda w, d: _weights(torch, gdn, w, d)
 
 
 def prefill_work(dims, T: int, C: int = 64):
@@ -66,6 +107,10 @@ KERNEL_SOURCES = {
     "chunk_prep": ("gdn_prefill.hip", "gdn_common.h", "gdn_kernels.h"),
     "state_pass": ("gdn_prefill.hip", "gdn_common.h", "gdn_kernels.h"),
     "norm": ("gdn_prefill.hip", "gdn_common.h", "gdn_kernels.h"),
+    "fused": ("gdn_fused.hip", "gdn_common.h", "gdn_kernels.h"),
+    "fused_map": ("gdn_fused.hip", "gdn_common.h", "gdn_kernels.h"),
+    "fused_scan": ("gdn_fused.hip", "gdn_common.h", "gdn_kernels.h"),
+    "tail": ("gdn_fused.hip", "gdn_common.h", "gdn_kernels.h"),
     "step_decode": ("gdn_step.hip", "gdn_common.h", "gdn_kernels.h"),
     "step_verify": ("gdn_step.hip", "gdn_common.h", "gdn_kernels.h"),
     "copy": ("gdn_state.hip", "gdn_common.h", "gdn_kernels.h"),
@@ -137,11 +182,14 @@ class Timer:
 
 
 def prefill_kernel_flop(dims, T: int, C: int = 64):
-    """Algorithmic FLOP of one prefill call split by the launch that does it: the intra-chunk WY/UT
-    contractions (Gram, W, U', P) in chunk_prep, the inter-chunk state pass (U, O, H) in state_pass."""
+    """Algorithmic FLOP of one prefill call split by the launch that does it. Two-phase path: the
+    intra-chunk WY/UT contractions (Gram, W, U', P) in chunk_prep, the inter-chunk state pass (U, O, H)
+    in state_pass. Fused path: all of it in the fused launch (its segment maps and scan are extra work,
+    not counted)."""
     nk, nv, dk, dv = dims.n_k, dims.n_v, dims.d_k, dims.d_v
-    return {"chunk_prep": T * (nv * 2 * C * (dk + 2 * dv) + nk * 4 * C * dk),
-            "state_pass": T * nv * 6 * dk * dv}
+    intra = T * (nv * 2 * C * (dk + 2 * dv) + nk * 4 * C * dk)
+    inter = T * nv * 6 * dk * dv
+    return {"chunk_prep": intra, "state_pass": inter, "fused": intra + inter}
 
 
 def kernel_roofline(workload, kernel, ms, flop=None, nbytes=None):
@@ -161,7 +209,8 @@ def kernel_roofline(workload, kernel, ms, flop=None, nbytes=None):
 
 def _prefill_sets(torch, gdn, dims, B, T, nsets, seed0):
     from gdn_inputs import make_layer, random_state
-    from tests.gpu_helpers import act, desc_of, f32, i32, weights
+    H = _dev(torch, gdn)
+    act, desc_of, f32, i32, weights = H.act, H.desc_of, H.f32, H.i32, H.weights
     d = desc_of(dims)
     sets = []
     for k in range(nsets):
@@ -220,7 +269,8 @@ def bench_prefill_stack(torch, gdn, args):
 
 def bench_decode(torch, gdn, args):
     from gdn_inputs import NEXT, make_layer
-    from tests.gpu_helpers import act, desc_of, weights
+    H = _dev(torch, gdn)
+    act, desc_of, weights = H.act, H.desc_of, H.weights
     dims = NEXT
     L, B = 36, 256
     d = desc_of(dims)
@@ -252,7 +302,8 @@ def bench_decode(torch, gdn, args):
 
 def bench_verify(torch, gdn, args):
     from gdn_inputs import NEXT, make_layer, random_state, verify_draws
-    from tests.gpu_helpers import act, desc_of, f32, i32, weights
+    H = _dev(torch, gdn)
+    act, desc_of, f32, i32, weights = H.act, H.desc_of, H.f32, H.i32, H.weights
     dims = NEXT
     B, K = 64, 4
     T = K + 1
@@ -284,14 +335,15 @@ def bench_verify(torch, gdn, args):
     nbytes = verify_bytes + B * 2 * (rec + tail_b)
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"workload": "64 sequences x (1+4) tokens, 16/32 heads, d=128: verify + accept + commit",
-            "ms_per_step": ms, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+            "ms_per_step": ms, "tokens_per_s": B * T / (ms / 1e3), "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
             "roofline": kernel_roofline("verify_b64_k4", "step_verify", kern["step_verify"][1], nbytes=verify_bytes),
             "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()}}
 
 
 def bench_verify_paths(torch, gdn, args):
     from gdn_inputs import NEXT, make_layer, path_inputs, random_state, verify_path_draws
-    from tests.gpu_helpers import act, desc_of, f32, i32, weights
+    H = _dev(torch, gdn)
+    act, desc_of, f32, i32, weights = H.act, H.desc_of, H.f32, H.i32, H.weights
     dims = NEXT
     B, P, K = 64, 4, 4
     T = K + 1
@@ -324,7 +376,7 @@ def bench_verify_paths(torch, gdn, args):
     nbytes = verify_bytes + B * 2 * (rec + tail_b)
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"workload": "64 sequences x 4 paths x (1+4) tokens, 16/32 heads, d=128: verify + accept + commit",
-            "ms_per_step": ms, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+            "ms_per_step": ms, "tokens_per_s": B * P * T / (ms / 1e3), "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
             "roofline": kernel_roofline("verify_paths_b64_p4_k4", "step_verify", kern["step_verify"][1],
                                         nbytes=verify_bytes),
             "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()}}
@@ -335,7 +387,8 @@ def bench_continuation(torch, gdn, args):
     padded to its bucket, continuing from the previous call's fp32 state and conv tail. Throughput counts
     real tokens only."""
     from gdn_inputs import NEXT, chunk_lengths, make_layer
-    from tests.gpu_helpers import act, desc_of, i32, weights
+    H = _dev(torch, gdn)
+    act, desc_of, i32, weights = H.act, H.desc_of, H.i32, H.weights
     dims, total = NEXT, 32768
     d = desc_of(dims)
     w, x, rng = make_layer(304, dims, 1, total)
@@ -372,10 +425,44 @@ def bench_continuation(torch, gdn, args):
     torch.cuda.current_stream().wait_stream(cs)
     ms_g, _ = Timer(torch, reps).run(lambda i: g.replay(), reps, 1)
     padded = sum(b for _, b in parts)
+    # each call's time on its own, by bucket, and a straight-line fit ms = fixed + per_token * bucket
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+    for (e0, e1), (mx, zz, aa, bb, ln, out) in zip(ev, calls):
+        e0.record()
+        gdn.prefill_chunk(d, W, mx, zz, aa, bb, ln, tail, state, out, ws)
+        e1.record()
+    torch.cuda.synchronize()
+    call_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    by = {}
+    for (_, bucket), t in zip(parts, call_ms):
+        by.setdefault(bucket, []).append(t)
+    per_tok, fixed = np.polyfit([b for _, b in parts], call_ms, 1)
+    # roofline of the dominant launch over the prompt: its algorithmic work on the real tokens per launch
+    kern = launch_breakdown(torch, gdn, step, 1)
+    kflop, nbytes = {}, 0
+    for n, _ in parts:
+        for k, v in prefill_kernel_flop(dims, n).items():
+            kflop[k] = kflop.get(k, 0) + v
+        nbytes += prefill_work(dims, n)[1]
+    dominant = max(kern, key=lambda k: kern[k][0] * kern[k][1])
+    launches = kern[dominant][0]
+    roof = kernel_roofline("continuation_32k", dominant, kern[dominant][1],
+                           flop=kflop[dominant] / launches if dominant in kflop else None,
+                           nbytes=None if dominant in kflop else nbytes / launches)
+    flop = sum(kflop[k] for k in ("chunk_prep", "state_pass"))
+    sec = ms / 1e3
     return {"workload": "1 x 32768 tokens in %d bucketed chunks, 16/32 heads, d=128" % len(parts),
-            "ms_per_prompt": ms, "tokens_per_s": total / (ms / 1e3), "chunks": len(parts),
+            "ms_per_prompt": ms, "tokens_per_s": total / sec, "chunks": len(parts),
             "padded_tokens": padded, "ms_per_chunk": ms / len(parts),
-            "graph": {"ms_per_prompt": ms_g, "tokens_per_s": total / (ms_g / 1e3)}}
+            "graph": {"ms_per_prompt": ms_g, "tokens_per_s": total / (ms_g / 1e3)},
+            "roofline": roof,
+            "call": {"hbm_achieved_GBs": nbytes / sec / 1e9, "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                     "mfma_achieved_TFLOPs": flop / sec / 1e12, "mfma_frac": flop / sec / 1e12 / MFMA_PEAK_TFLOPS,
+                     "algorithmic_bytes": nbytes, "algorithmic_flop": flop},
+            "ms_per_call_by_bucket": {str(k): round(float(np.mean(v)), 4) for k, v in sorted(by.items())},
+            "calls_by_bucket": {str(k): len(v) for k, v in sorted(by.items())},
+            "fit_ms_per_call": {"fixed": float(fixed), "per_bucket_token": float(per_tok)},
+            "kernels_ms": {k: round(v[1], 4) for k, v in kern.items()}}
 
 
 def bench_prefix_cache(torch, gdn, args):
@@ -383,7 +470,8 @@ def bench_prefix_cache(torch, gdn, args):
     through the prefix-state cache (restore, 2048-token chunks, snapshots) and through the plain path
     (every row from zero). Throughput counts every row token, computed or reused."""
     from gdn_inputs import NEXT, make_layer
-    from tests.gpu_helpers import act, desc_of, weights
+    H = _dev(torch, gdn)
+    act, desc_of, weights = H.act, H.desc_of, H.weights
     dims = NEXT
     rows_n, n, shared, vocab = 8, 8192, 6144, 512
     d = desc_of(dims)
@@ -421,7 +509,8 @@ def bench_spec_loop(torch, gdn, args):
     committing verify checkpoints directly and, for comparison, replaying the accepted prefix."""
     from gated_delta_rule_44_amd import spec
     from gdn_inputs import NEXT, SpecStream, make_layer, random_state
-    from tests.gpu_helpers import act, desc_of, f32, weights
+    H = _dev(torch, gdn)
+    act, desc_of, f32, weights = H.act, H.desc_of, H.f32, H.weights
     dims, B, K, vocab, steps = NEXT, 64, 4, 1024, 24
     d = desc_of(dims)
     w, table, rng = make_layer(303, dims, 1, vocab)
@@ -453,7 +542,8 @@ def bench_conv(torch, gdn, args):
     of 8192 bf16 channels, with the conv tail rolled forward. Algorithmic bytes: mixed read once, y
     written once, tails read and written."""
     from gdn_inputs import NEXT
-    from tests.gpu_helpers import desc_of
+    H = _dev(torch, gdn)
+    desc_of = H.desc_of
     dims, B, L = NEXT, 8, 8192
     d = desc_of(dims)
     g = torch.Generator(device="cuda")
@@ -478,7 +568,8 @@ def bench_conv(torch, gdn, args):
 
 def bench_copy(torch, gdn, args):
     from gdn_inputs import NEXT
-    from tests.gpu_helpers import desc_of
+    H = _dev(torch, gdn)
+    desc_of = H.desc_of
     dims = NEXT
     n = 256
     d = desc_of(dims)
@@ -498,6 +589,124 @@ def bench_copy(torch, gdn, args):
     return {"workload": "256 state records (fp32 state + bf16 conv tail) of one 16/32-head layer",
             "ms_per_call": ms, "mib": nbytes / 2 / 2 ** 20, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
             "roofline": kernel_roofline("state_copy_256", "copy", ms, nbytes=nbytes)}
+
+
+def _best_time(fn, reps):
+    best = None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    return best
+
+
+def _cpu(value, unit, threads, sample, seconds, **extra):
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "sample": sample,
+            "seconds": seconds, **extra}
+
+
+def cpu_prefill_stack():
+    """The oracle on one of the stack layer's 8 sequences (8192 tokens, 16/32 heads, saved state): the
+    leg's rate is tokens/s of one layer, and the sequences are independent, so the sample's rate is it."""
+    import oracle
+    from gdn_inputs import NEXT, make_layer, random_state
+    dims, T = NEXT, 8192
+    w, x, rng = make_layer(400, dims, 1, T)
+    S0, tail0 = random_state(rng, dims, 1)
+    th = oracle.default_threads()
+    sec = _best_time(lambda: oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, tail=tail0,
+                                                  H=S0, threads=th), 1)
+    return _cpu(T / sec, "tokens/s", th, "1 of the 8 sequences of one layer (8192 tokens), tokens/s of the sample",
+                sec)
+
+
+def cpu_decode():
+    """The oracle's decode step (one token from a saved state and conv tail) for the 256 sequences in 1 of
+    the 36 layers, scaled to the whole step (x 36)."""
+    import oracle
+    from gdn_inputs import NEXT, make_layer, random_state
+    dims, B, L, nb = NEXT, 256, 36, 256
+    w, x, rng = make_layer(200, dims, nb, 1)
+    S0, tail0 = random_state(rng, dims, nb)
+    th = oracle.default_threads()
+    sec = _best_time(lambda: oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, tail=tail0,
+                                                  H=S0, threads=th), 2)
+    step = sec * (B / nb) * L
+    return _cpu(B / step, "tokens/s", th, "256 sequences x 1 of 36 layers, scaled x36", sec,
+                ms_per_step=step * 1e3, GB_per_s=L * B * decode_bytes(dims) / step / 1e9)
+
+
+def cpu_verify():
+    """The oracle's verify (1+4 tokens per sequence, token by token, every checkpoint kept), accept, and
+    the commit of the accepted checkpoint, for the 64 sequences."""
+    import oracle
+    from gdn_inputs import NEXT, make_layer, random_state, verify_draws
+    dims, B, nb, K = NEXT, 64, 64, 4
+    w, x, rng = make_layer(300, dims, nb, K + 1)
+    S0, tail0 = random_state(rng, dims, nb)
+    drafts, preds, _ = verify_draws(rng, nb, K)
+    th = oracle.default_threads()
+
+    def run():
+        r = oracle.verify(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, tail0, S0, threads=th)
+        m = oracle.accept(drafts, preds)[0]
+        return r["ckpt_H"][np.arange(nb), m].copy(), r["ckpt_tail"][np.arange(nb), m].copy()
+
+    sec = _best_time(run, 2)
+    step = sec * B / nb
+    return _cpu(B * (K + 1) / step, "tokens/s", th, "64 sequences x (1+4) tokens", sec,
+                ms_per_step=step * 1e3)
+
+
+def cpu_verify_paths():
+    """The oracle's tree verify (4 paths x (1+4) tokens from each sequence's state), accept over paths
+    and the commit, for 16 of the 64 sequences, scaled x4."""
+    import oracle
+    from gdn_inputs import NEXT, make_layer, path_inputs, random_state, verify_path_draws
+    dims, B, nb, P, K = NEXT, 64, 16, 4, 4
+    w, _, rng = make_layer(301, dims, 1, 1)
+    x = path_inputs(rng, dims, nb, P, K + 1)
+    S0, tail0 = random_state(rng, dims, nb)
+    drafts, preds, _ = verify_path_draws(rng, nb, P, K)
+    th = oracle.default_threads()
+
+    def run():
+        r = oracle.verify_paths(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, tail0, S0, threads=th)
+        m, path = oracle.accept_paths(drafts, preds)[:2]
+        return r["ckpt_H"][np.arange(nb), path, m].copy()
+
+    sec = _best_time(run, 2)
+    step = sec * B / nb
+    return _cpu(B * P * (K + 1) / step, "tokens/s", th, "16 of 64 sequences x 4 paths x (1+4) tokens, scaled x4",
+                sec, ms_per_step=step * 1e3)
+
+
+def cpu_continuation():
+    """The oracle over an 8192-token prompt of the same recipe (chunk lengths drawn from the same buckets),
+    each call continuing from the previous call's state and conv tail, real tokens only."""
+    import oracle
+    from gdn_inputs import NEXT, chunk_lengths, make_layer
+    dims, total = NEXT, 8192
+    w, x, rng = make_layer(304, dims, 1, total)
+    parts = chunk_lengths(rng, total)
+    th = oracle.default_threads()
+    od = oracle.Dims.of(dims)
+
+    def run():
+        t0, tail, H = 0, None, None
+        for n, _ in parts:
+            sl = slice(t0, t0 + n)
+            r = oracle.layer_forward(od, w, x.mixed[:, sl], x.z[:, sl], x.a[:, sl], x.b[:, sl], tail=tail, H=H,
+                                     threads=th)
+            tail, H, t0 = r["tail"], r["H"], t0 + n
+        return t0
+
+    t0 = time.perf_counter()
+    ntok = run()
+    sec = time.perf_counter() - t0
+    return _cpu(ntok / sec, "tokens/s", th, "an %d-token prompt in %d bucketed chunks (the 32768-token recipe, cut)"
+                % (ntok, len(parts)), sec)
 
 
 def cpu_baseline():
@@ -577,8 +786,14 @@ def main():
         line["measured_peaks"] = {"mfma_f16_TFLOPs": tf, "mfma_frac_of_published": tf / MFMA_PEAK_TFLOPS,
                                   "hbm_copy_GBs": line.get("copy", {}).get("GB_per_s"),
                                   "published": {"mfma_bf16_f16_TFLOPs": MFMA_PEAK_TFLOPS, "hbm_GBs": HBM_PEAK_GBS}}
-    if not args.no_cpu and only in ("all", "prefill"):
-        line["cpu_baseline"] = cpu_baseline()
+    if not args.no_cpu:
+        # the oracle on the host cores beside each leg that has one (bounded samples, scaled as stated)
+        if only in ("all", "prefill"):
+            line["cpu_baseline"] = cpu_baseline()
+        for leg, fn in (("prefill_stack", cpu_prefill_stack), ("decode", cpu_decode), ("verify", cpu_verify),
+                        ("verify_paths", cpu_verify_paths), ("continuation", cpu_continuation)):
+            if leg in line:
+                line[leg]["cpu_baseline"] = fn()
     line["kernel_hash"] = kernel_hash()
     print(json.dumps(line))
 
