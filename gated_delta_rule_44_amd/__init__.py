@@ -18,7 +18,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# GDN_LIBRARY names another build of the same library (the host-sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_HERE, "libgdn.so")
 
 GDN_BF16 = 0
 GDN_F32 = 1

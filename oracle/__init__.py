@@ -22,7 +22,10 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (-O2, IEEE semantics, OpenMP)."""
+    """Compile the oracle with gcc (-O2, IEEE semantics, OpenMP). GDN_ORACLE_LIBRARY names another build
+    of the same source to load instead (the sanitizer build of the CPU tests)."""
+    if os.environ.get("GDN_ORACLE_LIBRARY"):
+        return os.environ["GDN_ORACLE_LIBRARY"]
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared",
