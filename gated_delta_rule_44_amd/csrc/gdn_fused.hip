@@ -236,10 +236,12 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
   };
 
   // the products of chunk c
-  auto chunk = [&]() __attribute__((always_inline)) {
-    // K H (K high half alone) and, for OUT, H^T Q^T; H fragments one 32-row block at a time: rows
-    // 32 kk + {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3} are accumulator rows of tiles 2 kk and 2 kk + 1
-    f32x4 Z[4][2];
+  // K H (K high half alone) and, for OUT, H^T Q^T of a chunk: they need only its q and k and the state
+  // it enters with, so they run while the prep forms the chunk's Gram products. H fragments one 32-row
+  // block at a time: rows 32 kk + {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3} are accumulator rows of
+  // tiles 2 kk and 2 kk + 1.
+  f32x4 Z[4][2];            // 2^16 K H, then the right-hand sides of the solve
+  auto products_kh = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -278,6 +280,10 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
         }
       }
     }
+  };
+
+  // the rest of a chunk's products, once its Gram products and T_mm are in LDS
+  auto chunk = [&]() __attribute__((always_inline)) {
     // right-hand sides 2^16 Y = beta (2^16 V - e^gamma 2^16 K H); V = conv + SiLU of this wave's value
     // channels at token 16 mt + 4 g + i, column cw0 + 16 n + c, from the staged inputs
     {
@@ -416,31 +422,32 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
     }
   };
 
-  // prologue: stage chunk c0's v inputs; the prep builds chunk c0's operands meanwhile
+  // prologue: stage chunk c0's v inputs while the prep builds chunk c0's operands, and form K H and
+  // H^T Q^T of chunk c0 beside its Gram products
   if (WITH_V) v_load(u.c0);
   lds_barrier();
   if (WITH_V) v_stage();
   lds_barrier();
+  products_kh();
   lds_barrier();
   lds_barrier();
-  // (loads are issued after the products so that nothing in flight holds registers through them; the
-  // prep's Gram phase covers their latency)
+  // Per chunk c: the rest of its products (beside the prep's conv of chunk c + 1); Y; its gated norm and
+  // stores (beside the prep's operand writes; z is loaded at the start, the v inputs of chunk c + 1 are
+  // loaded before and staged after the norm); Y1; K H and H^T Q^T of chunk c + 1 (beside its Gram
+  // products); Y2; X. (Loads are issued after the products so that nothing in flight holds registers
+  // through them.)
   for (int c = u.c0; c < u.c1; ++c) {
     chunk();
     lds_barrier();  // Y: chunk c's operands are free
     if (OUT) z_load(c);
-    if (c + 1 < u.c1) {
-      if (WITH_V) v_load(c + 1);
-      lds_barrier();  // Y1
-      if (OUT) norm(c);  // beside the prep's Gram products; z has arrived meanwhile
-      lds_barrier();  // Y2
-      if (WITH_V) v_stage();
-    } else {
-      lds_barrier();
-      if (OUT) norm(c);
-      lds_barrier();
-    }
-    lds_barrier();  // X: chunk c + 1's operands are ready
+    const bool next = c + 1 < u.c1;
+    if (WITH_V && next) v_load(c + 1);
+    if (OUT) norm(c);
+    if (WITH_V && next) v_stage();
+    lds_barrier();  // Y1: chunk c + 1's q, k and k~ are in LDS
+    if (next) products_kh();
+    lds_barrier();  // Y2
+    lds_barrier();  // X: chunk c + 1's Gram products and T_mm are ready
   }
 
   // the exit state
@@ -496,13 +503,18 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
   const uint2* ktap = (const uint2*)((const uint16_t*)p.conv_w + (long)(n_k * FD + kh * FD + 2 * lane) * 4);
   auto load = [&](int c) __attribute__((always_inline)) {
     const int T0 = c * FC + 16 * pw - 3;
+    // rows T0 .. T0 + 18: T < 0 the saved tail, T >= Lb zero (never read); the row pointer steps by one
+    // row and moves from the tail to the call's first row at T = 0 (the first chunk only)
+    const uint16_t* row = T0 >= 0 ? mixed + (long)T0 * C : tail + (long)(T0 + 3) * C;
+    const int o = kh * FD + 2 * lane;
 #pragma unroll
     for (int r = 0; r < 19; ++r) {
-      const int T = T0 + r;  // < 0: the saved tail; >= Lb: zero, never read
+      const int T = T0 + r;
+      if (T == 0) row = mixed;
       const bool ok = T < Lb;
-      const uint16_t* row = ok ? (T < 0 ? tail + (long)(T + 3) * C : mixed + (long)T * C) : tail;
-      xq[r] = ok ? *(const uint32_t*)(row + kh * FD + 2 * lane) : 0u;
-      xk[r] = ok ? *(const uint32_t*)(row + n_k * FD + kh * FD + 2 * lane) : 0u;
+      xq[r] = ok ? *(const uint32_t*)(row + o) : 0u;
+      xk[r] = ok ? *(const uint32_t*)(row + o + n_k * FD) : 0u;
+      row += C;
     }
     const int t = c * FC + lane;
     const long gi = ((long)b * Lb + (t < Lb ? t : Lb - 1)) * n_v + h;
@@ -510,6 +522,9 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
     b_raw = ((const uint16_t*)p.b)[gi];
   };
 
+  // gate parameters of the head, read once (the loop's barriers would make the compiler read them again
+  // every chunk, a memory round trip each)
+  const float negA = -__expf(p.A_log[h]), dtb = p.dt_bias[h];
   float qn[16][2], kn[16][2];
   float g_gam = 0.f, g_beta = 0.f, g_eg = 0.f, g_ed = 0.f, g_ec = 0.f;
   // conv + SiLU of the lane's q and k channel pairs over the wave's 16 tokens, L2 norms, and the
@@ -583,7 +598,7 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
     }
     const int t = c * FC + lane;
     const bool real = t < len;
-    const float g0 = -__expf(p.A_log[h]) * softplus(bf1(a_raw) + p.dt_bias[h]);
+    const float g0 = negA * softplus(bf1(a_raw) + dtb);
     float gm = real ? g0 : 0.f;
     g_beta = real ? sigmoid(bf1(b_raw)) : 0.f;
 #pragma unroll
