@@ -108,4 +108,17 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
+// The same split of two values, with the high halves rounded once, into one register
+// (v_cvt_pk_f16_f32), and that register made opaque (an empty asm, no instruction) so that the residuals
+// are formed from the stored halves: hipcc then forms each residual x - hi with one v_fma_mix_f32 from the
+// f16 half, folding a multiply that produced x into it exactly, and rounds both low halves with one more
+// v_cvt_pk_f16_f32 (six instructions for two values where split_f16 takes ten with the multiplies).
+__device__ __forceinline__ void split2_f16(float x0, float x1, f16x2& hi, f16x2& lo) {
+  uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x0, x1}, f16x2));
+  asm("" : "+v"(hb));
+  hi = __builtin_bit_cast(f16x2, hb);
+  const f32x2_t back = __builtin_convertvector(hi, f32x2_t);
+  lo = __builtin_convertvector(f32x2_t{x0 - back[0], x1 - back[1]}, f16x2);
+}
+
 }  // namespace gdn

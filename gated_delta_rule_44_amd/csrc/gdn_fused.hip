@@ -621,16 +621,14 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
   auto pack = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      _Float16 h0, l0, h1, l1;
-      split_f16(kS8 * kn[t][0], h0, l0);
-      split_f16(kS8 * kn[t][1], h1, l1);
-      kph[t] = __builtin_bit_cast(uint32_t, f16x2{h0, h1});
-      kpl[t] = __builtin_bit_cast(uint32_t, f16x2{l0, l1});
+      f16x2 hp, lp;
+      split2_f16(kS8 * kn[t][0], kS8 * kn[t][1], hp, lp);
+      kph[t] = __builtin_bit_cast(uint32_t, hp);
+      kpl[t] = __builtin_bit_cast(uint32_t, lp);
       if (WITH_Q) {
-        split_f16(kS8 * qn[t][0], h0, l0);
-        split_f16(kS8 * qn[t][1], h1, l1);
-        qph[t] = __builtin_bit_cast(uint32_t, f16x2{h0, h1});
-        qpl[t] = __builtin_bit_cast(uint32_t, f16x2{l0, l1});
+        split2_f16(kS8 * qn[t][0], kS8 * qn[t][1], hp, lp);
+        qph[t] = __builtin_bit_cast(uint32_t, hp);
+        qpl[t] = __builtin_bit_cast(uint32_t, lp);
       }
     }
 #pragma unroll

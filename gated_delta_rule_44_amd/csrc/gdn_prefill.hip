@@ -92,20 +92,24 @@ __device__ __forceinline__ void frag_row_f(const float* row32, int g, float (&x)
 
 __device__ __forceinline__ void split8(const float (&x)[8], f16x8& hi, f16x8& lo) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    _Float16 h, l;
-    split_f16(x[e], h, l);
-    hi[e] = h;
-    lo[e] = l;
+  for (int e = 0; e < 8; e += 2) {
+    f16x2 h, l;
+    split2_f16(x[e], x[e + 1], h, l);
+    hi[e] = h[0];
+    hi[e + 1] = h[1];
+    lo[e] = l[0];
+    lo[e + 1] = l[1];
   }
 }
 __device__ __forceinline__ void split4(f32x4 x, f16x4& hi, f16x4& lo) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    _Float16 h, l;
-    split_f16(x[e], h, l);
-    hi[e] = h;
-    lo[e] = l;
+  for (int e = 0; e < 4; e += 2) {
+    f16x2 h, l;
+    split2_f16(x[e], x[e + 1], h, l);
+    hi[e] = h[0];
+    hi[e + 1] = h[1];
+    lo[e] = l[0];
+    lo[e + 1] = l[1];
   }
 }
 
@@ -402,10 +406,17 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     for (int tt = 0; tt < TPW; ++tt) {
       const int o = (TPW * w + tt) * LQ + CPL * lane;
       _Float16 qh[CPL], ql[CPL], kh_[CPL], kl[CPL];
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        split_f16(kS8 * qn[tt][j], qh[j], ql[j]);
-        split_f16(kS8 * kn[tt][j], kh_[j], kl[j]);
+      if constexpr (CPL == 2) {
+        f16x2 h2, l2;
+        split2_f16(kS8 * qn[tt][0], kS8 * qn[tt][1], h2, l2);
+        qh[0] = h2[0]; qh[1] = h2[1]; ql[0] = l2[0]; ql[1] = l2[1];
+        split2_f16(kS8 * kn[tt][0], kS8 * kn[tt][1], h2, l2);
+        kh_[0] = h2[0]; kh_[1] = h2[1]; kl[0] = l2[0]; kl[1] = l2[1];
+      } else {
+        for (int j = 0; j < CPL; ++j) {
+          split_f16(kS8 * qn[tt][j], qh[j], ql[j]);
+          split_f16(kS8 * kn[tt][j], kh_[j], kl[j]);
+        }
       }
       if (CPL == 2) {
         *(f16x2*)&sQh[o] = f16x2{qh[0], qh[CPL - 1]};
@@ -870,10 +881,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   for (int tt = 0; tt < TPW; ++tt) {
     const int o = (TPW * w + tt) * LQ + CPL * lane;
     _Float16 qh[CPL], ql[CPL], kh_[CPL], kl[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      split_f16(kS8 * qn[tt][j], qh[j], ql[j]);
-      split_f16(kS8 * kn[tt][j], kh_[j], kl[j]);
+    if constexpr (CPL == 2) {
+      f16x2 h2, l2;
+      split2_f16(kS8 * qn[tt][0], kS8 * qn[tt][1], h2, l2);
+      qh[0] = h2[0]; qh[1] = h2[1]; ql[0] = l2[0]; ql[1] = l2[1];
+      split2_f16(kS8 * kn[tt][0], kS8 * kn[tt][1], h2, l2);
+      kh_[0] = h2[0]; kh_[1] = h2[1]; kl[0] = l2[0]; kl[1] = l2[1];
+    } else {
+      for (int j = 0; j < CPL; ++j) {
+        split_f16(kS8 * qn[tt][j], qh[j], ql[j]);
+        split_f16(kS8 * kn[tt][j], kh_[j], kl[j]);
+      }
     }
     if constexpr (CPL == 2) {
       *(f16x2*)&sQh[o] = f16x2{qh[0], qh[CPL - 1]};
