@@ -44,8 +44,6 @@ int check_desc(const gdn_desc* d) {
   if (d->act_dtype != GDN_BF16 && d->act_dtype != GDN_F32) return fail(GDN_EINVAL, "act_dtype=%d", d->act_dtype);
   if (d->conv_k != 4) return fail(GDN_EUNSUPPORTED, "conv_k=%d (only 4 is built)", d->conv_k);
   if (d->n_v % d->n_k) return fail(GDN_EUNSUPPORTED, "n_v=%d is not a multiple of n_k=%d", d->n_v, d->n_k);
-  const int R = d->n_v / d->n_k;
-  if (R != 1 && R != 2 && R != 4) return fail(GDN_EUNSUPPORTED, "GQA ratio n_v/n_k=%d (built: 1, 2, 4)", R);
   if (d->d_k != d->d_v) return fail(GDN_EUNSUPPORTED, "d_k=%d != d_v=%d", d->d_k, d->d_v);
   if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128)
     return fail(GDN_EUNSUPPORTED, "d_k=%d (built: 32, 64, 128)", d->d_k);
@@ -272,8 +270,8 @@ static int prefill_impl(const gdn_desc* d, const gdn_weights* w, const void* mix
   if (B > 65535) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d exceeds 65535", B);
   if ((long)Lb * d->n_v * d->d_v >= (1L << 31))
     return fail(GDN_EINVAL, "gdn_prefill_chunk: Lb * n_v * d_v = %ld must stay below 2^31", (long)Lb * d->n_v * d->d_v);
-  if ((long)B * ((Lb + gdn::kChunk - 1) / gdn::kChunk) * d->n_k >= (1L << 31))
-    return fail(GDN_EINVAL, "gdn_prefill_chunk: B * chunks * n_k must stay below 2^31");
+  if ((long)B * ((Lb + gdn::kChunk - 1) / gdn::kChunk) * d->n_v >= (1L << 31))
+    return fail(GDN_EINVAL, "gdn_prefill_chunk: B * chunks * n_v must stay below 2^31");
   if (d->act_dtype == GDN_F32 && d->d_k > 64)
     return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunk: fp32 activations are built for d <= 64 (got %d)", d->d_k);
   const size_t need = fused ? gdn::fused_ws_bytes(B, d->n_v, Lb) : gdn_prefill_workspace_bytes(d, B, Lb);
@@ -304,7 +302,7 @@ static int prefill_impl(const gdn_desc* d, const gdn_weights* w, const void* mix
   p.n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
   p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
   gdn::prefill_ws_layout(p, d->d_k, d->act_dtype == GDN_F32);
-  return hip_status(gdn::launch_prefill(p, d->act_dtype, d->d_k, d->n_v / d->n_k, (hipStream_t)stream),
+  return hip_status(gdn::launch_prefill(p, d->act_dtype, d->d_k, p.grp, (hipStream_t)stream),
                     "gdn_prefill_chunk");
 }
 

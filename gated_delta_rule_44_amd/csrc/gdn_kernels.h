@@ -72,12 +72,16 @@ struct PrefillArgs {
                         // pass), and the unnormalised o for a norm pass
   long key_off, ss_off, oraw_off;  // byte offsets inside ws: key records, partial sums, unnormalised o
   int B, Lb, n_k, n_v, C, n_chunks;
+  int grp;              // value heads per chunk_prep workgroup (a divisor of n_v / n_k: 1, 2 or 4)
   int nsplit;           // column slices per head in the state pass (1: the whole head)
   int exchange;         // split heads: 1 = the slices exchange row sums, 0 = a norm pass finishes
   int* status;          // device word: bit 0 set when a final state leaves the operand range (or null)
   float scale, l2_eps, rms_eps;
 };
 // fp32 activations run every MFMA operand as a hi/lo pair (split_all) and are built for d <= 64
+// value heads per chunk_prep workgroup: the GQA ratio n_v / n_k where a kernel is built for it (1, 2,
+// 4), else its largest divisor among 4, 2, 1 (each group then forms the shared q and k again)
+int prefill_group(int n_k, int n_v);
 size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool split_all);
 void prefill_ws_layout(PrefillArgs& p, int D, bool split_all);
 hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hipStream_t st);

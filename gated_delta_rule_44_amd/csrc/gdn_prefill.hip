@@ -152,8 +152,8 @@ __device__ __forceinline__ char* rec_ptr(const PrefillArgs& p, int b, int h, int
   return (char*)p.ws + (((long)b * p.n_v + h) * p.n_chunks + c) * Rec<D, SPLIT, SH>::kBytes;
 }
 template <int D>
-__device__ __forceinline__ char* key_ptr(const PrefillArgs& p, int b, int kh, int c) {
-  return (char*)p.ws + p.key_off + (((long)b * p.n_k + kh) * p.n_chunks + c) * KeyRec<D>::kBytes;
+__device__ __forceinline__ char* key_ptr(const PrefillArgs& p, int b, int vk, int c) {
+  return (char*)p.ws + p.key_off + (((long)b * (p.n_v / p.grp) + vk) * p.n_chunks + c) * KeyRec<D>::kBytes;
 }
 // (the lane offset is an unsigned 32-bit value added to a wave-uniform base, which the compiler can
 // encode as a scalar base plus vector offset instead of a per-lane 64-bit address)
@@ -240,13 +240,13 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // With a head's columns split over state-pass slices: mark the partial sums of squares of this chunk's
 // rows (every value head of key head kh) pending; each slice overwrites its own when it posts it.
 // Layout [sequence][value head][token][slice].
-__device__ __forceinline__ void mark_sums_pending(const PrefillArgs& p, int b, int kh, int R, int t0, int tid) {
+__device__ __forceinline__ void mark_sums_pending(const PrefillArgs& p, int b, int vk, int R, int t0, int tid) {
   const int ns = p.nsplit;
   if (ns <= 1 || !p.exchange) return;
   float* ss = (float*)((char*)p.ws + p.ss_off);
   for (int i = tid; i < R * C64 * ns; i += 512) {
     const int hr = i / (C64 * ns), t = t0 + (i / ns) % C64;
-    if (t < p.Lb) ss[(((long)b * p.n_v + kh * R + hr) * p.Lb + t) * ns + i % ns] = kSsPending;
+    if (t < p.Lb) ss[(((long)b * p.n_v + vk * R + hr) * p.Lb + t) * ns + i % ns] = kSsPending;
   }
 }
 
@@ -299,13 +299,15 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   float* sEg = (float*)(smem + OFF_E);
   float* sEd = sEg + C64;
 
-  const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  // group vk: value heads vk R .. vk R + R - 1 of key head kh
+  const int c = blockIdx.x, vk = blockIdx.y, b = blockIdx.z;
+  const int kh = vk * R / (p.n_v / p.n_k);
   const int t0 = c * C64;
   const int len = p.len[b];
   if (t0 >= len) return;  // all padding: the state pass stops before this chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so addresses built on it stay scalar
-  mark_sums_pending(p, b, kh, R, t0, tid);
+  mark_sums_pending(p, b, vk, R, t0, tid);
   const int g16 = lane >> 4, r16 = lane & 15;
   const int Lb = p.Lb, C = p.C, n_k = p.n_k;
   const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   constexpr int NCV = 2 + R;  // convolutions: q, k, then the value heads
   typedef typename std::conditional<CPL == 2, typename Pair<ActT>::type, ActT>::type XRaw;
   typedef typename Raw4<ActT>::type WRaw;
-  const int hg = kh * R + (w < R ? w : 0);
+  const int hg = vk * R + (w < R ? w : 0);
   const int tg = t0 + lane;
   const long gi = ((long)b * Lb + (tg < len ? tg : len - 1)) * p.n_v + hg;  // len >= 1 here
   const ActT a_raw = ((const ActT*)p.a)[gi], b_raw = ((const ActT*)p.b)[gi];
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
   WRaw wr[NCV][CPL];
 #pragma unroll
   for (int j = 0; j < NCV; ++j) {
-    const int base = j == 0 ? kh * D : j == 1 ? (n_k + kh) * D : (2 * n_k + kh * R + j - 2) * D;
+    const int base = j == 0 ? kh * D : j == 1 ? (n_k + kh) * D : (2 * n_k + vk * R + j - 2) * D;
     const int gc = base + (CPL == 2 ? 2 * lane : (lane < D ? lane : 0));
 #pragma unroll
     for (int i = 0; i < CPL; ++i) wr[j][i] = Raw4<ActT>::load(cw + (gc + i) * 4);
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
     // the key record: 2^8 q (token tile q & 3, block q >> 2) and 2^8 k^T (row tile idx >> 1, block
     // idx & 1), once for all value heads of the group
     using KR = KeyRec<D>;
-    char* krec = key_ptr<D>(p, b, kh, c);
+    char* krec = key_ptr<D>(p, b, vk, c);
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       const int q = w + NWV * i;
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 
   // ---- 5. per value head of the group ------------------------------------------------------------
   for (int r = 0; r < R; ++r) {
-    const int h = kh * R + r;
+    const int h = vk * R + r;
     const float* gam = sGam + r * C64;
     const float* bet = sBet + r * C64;
     char* rec = rec_ptr<D, SPLIT, SH>(p, b, h, c);
@@ -776,14 +778,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   float* sEg = sBet + R * C64;
   float* sEd = sEg + R * C64;
 
-  const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  // group vk: value heads vk R .. vk R + R - 1 of key head kh
+  const int c = blockIdx.x, vk = blockIdx.y, b = blockIdx.z;
+  const int kh = vk * R / (p.n_v / p.n_k);
   const int t0 = c * C64;
   const int len = p.len[b];
   if (t0 >= len) return;  // all padding: the state pass stops before this chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g16 = lane >> 4, r16 = lane & 15;
-  mark_sums_pending(p, b, kh, R, t0, tid);
+  mark_sums_pending(p, b, vk, R, t0, tid);
   const int Lb = p.Lb, C = p.C, n_k = p.n_k;
   const ActT* mixed = (const ActT*)p.mixed + (long)b * Lb * C;
   const ActT* tail = (const ActT*)p.tail + (long)b * 3 * C;
@@ -794,7 +798,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   constexpr int NCV = 2 + R;
   typedef typename std::conditional<CPL == 2, typename Pair<ActT>::type, ActT>::type XRaw;
   typedef typename Raw4<ActT>::type WRaw;
-  const int hg = kh * R + (w < R ? w : 0);
+  const int hg = vk * R + (w < R ? w : 0);
   const int tg = t0 + lane;
   const long gi = ((long)b * Lb + (tg < len ? tg : len - 1)) * p.n_v + hg;
   const ActT a_raw = ((const ActT*)p.a)[gi], b_raw = ((const ActT*)p.b)[gi];
@@ -802,7 +806,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   WRaw wr[NCV][CPL];
 #pragma unroll
   for (int j = 0; j < NCV; ++j) {
-    const int gc = (j == 0 ? kh : j == 1 ? n_k + kh : 2 * n_k + kh * R + j - 2) * D + CPL * lane;
+    const int gc = (j == 0 ? kh : j == 1 ? n_k + kh : 2 * n_k + vk * R + j - 2) * D + CPL * lane;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) wr[j][i] = Raw4<ActT>::load(cw + (gc + i) * 4);
 #pragma unroll
@@ -925,8 +929,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // q: with one value head, Q~ = 2^16 scale e^{gamma_t} q_t into the value record; with several, 2^8 q
   // into the key record (fragment (token tile q & 3, 32-block q >> 2) for q = w, w + 8, ...)
   constexpr int QPW = (4 * KD + NWV - 1) / NWV;
-  char* krec = SH ? key_ptr<D>(p, b, kh, c) : nullptr;
-  char* rec0 = rec_ptr<D, false, SH>(p, b, kh * R, c);
+  char* krec = SH ? key_ptr<D>(p, b, vk, c) : nullptr;
+  char* rec0 = rec_ptr<D, false, SH>(p, b, vk * R, c);
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
     const int q = w + NWV * i;
@@ -974,7 +978,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     f16x8 hi, lo;
     split8(x, hi, lo);
-    char* rec = rec_ptr<D, false, SH>(p, b, kh * R + r, c);
+    char* rec = rec_ptr<D, false, SH>(p, b, vk * R + r, c);
     put_frag<NTS>(rec, RC::P_HI + pmt * 2 + pkk, lane, hi);
     put_frag<NTS>(rec, RC::P_LO + pmt * 2 + pkk, lane, lo);
   }
@@ -1042,7 +1046,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   for (int r = 0; r < R; ++r) {
     const float* gam = sGam + r * C64;
     const float* bet = sBet + r * C64;
-    char* rec = rec_ptr<D, false, SH>(p, b, kh * R + r, c);
+    char* rec = rec_ptr<D, false, SH>(p, b, vk * R + r, c);
     // A (strictly lower, fp32) from the K K^T accumulators, into the q region
     auto put_A = [&](int tile, f32x4 acc) __attribute__((always_inline)) {
       const int mt = tile_mt(tile), nt = tile - mt * (mt + 1) / 2;
@@ -1237,7 +1241,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
 
   // single fragments of chunk c (past the end: the last chunk, loaded and unused, branch-free)
   auto rec_of = [&](int c) { return (const char*)rec_ptr<D, SPLIT, SH>(p, b, h, c < n_real ? c : n_real - 1); };
-  auto key_of = [&](int c) { return (const char*)key_ptr<D>(p, b, h / (n_v / p.n_k), c < n_real ? c : n_real - 1); };
+  auto key_of = [&](int c) { return (const char*)key_ptr<D>(p, b, h / p.grp, c < n_real ? c : n_real - 1); };
   auto ld_w = [&](CF& f, int c, int kk) __attribute__((always_inline)) {
     const char* rec = rec_of(c);
     f.w[kk] = get_frag(rec, RC::W_HI + tt * KD + kk, lane);
@@ -1860,11 +1864,11 @@ hipError_t launch_t(const PrefillArgs& p, hipStream_t st) {
     // (non-temporal stores cost 160 -> 207 us at 16 value heads x 4096 tokens); from 201 MB on,
     // non-temporal stores measured 4-6% faster calls (32 value heads x 1-3 sequences x 4096 tokens)
     if (p.ss_off > kNtRecordBytes)
-      hipLaunchKernelGGL((chunk_prep2_kernel<ActT, D, R, true>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+      hipLaunchKernelGGL((chunk_prep2_kernel<ActT, D, R, true>), dim3(p.n_chunks, p.n_v / R, p.B), dim3(512), 0, st, p);
     else
-      hipLaunchKernelGGL((chunk_prep2_kernel<ActT, D, R, false>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+      hipLaunchKernelGGL((chunk_prep2_kernel<ActT, D, R, false>), dim3(p.n_chunks, p.n_v / R, p.B), dim3(512), 0, st, p);
   } else
-    hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_k, p.B), dim3(512), 0, st, p);
+    hipLaunchKernelGGL((chunk_prep_kernel<ActT, D, R, SPLIT>), dim3(p.n_chunks, p.n_v / R, p.B), dim3(512), 0, st, p);
   timing_after(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1920,11 +1924,18 @@ int device_cus() {
   return cus[dev];
 }
 
+int prefill_group(int n_k, int n_v) {
+  const int R = n_v / n_k;
+  if (R == 1 || R == 2 || R == 4) return R;
+  return R % 4 == 0 ? 4 : R % 2 == 0 ? 2 : 1;
+}
+
 size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool split_all) {
   const int nsplit = D / (16 * pass_nt(B, n_v, D));
   long vrec, krec;
-  rec_sizes(D, split_all, n_v > n_k, vrec, krec);
-  size_t bytes = (size_t)B * n_chunks * ((size_t)n_v * vrec + (size_t)n_k * krec);
+  const int grp = prefill_group(n_k, n_v);
+  rec_sizes(D, split_all, grp > 1, vrec, krec);
+  size_t bytes = (size_t)B * n_chunks * ((size_t)n_v * vrec + (size_t)(n_v / grp) * krec);
   if (nsplit > 1) {
     // partial sums of squares, and the unnormalised o for a norm pass; the o area is counted even
     // when the slices exchange their sums, so that the size never shrinks as Lb grows (a workspace
@@ -1938,9 +1949,10 @@ size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bo
 
 void prefill_ws_layout(PrefillArgs& p, int D, bool split_all) {
   long vrec, krec;
-  rec_sizes(D, split_all, p.n_v > p.n_k, vrec, krec);
+  p.grp = prefill_group(p.n_k, p.n_v);
+  rec_sizes(D, split_all, p.grp > 1, vrec, krec);
   p.key_off = (long)p.B * p.n_v * p.n_chunks * vrec;
-  const size_t rec = (size_t)p.key_off + (size_t)p.B * p.n_k * p.n_chunks * krec;
+  const size_t rec = (size_t)p.key_off + (size_t)p.B * (p.n_v / p.grp) * p.n_chunks * krec;
   p.nsplit = D / (16 * pass_nt(p.B, p.n_v, D));
   p.exchange = pass_exchange(p.B, p.n_v, D, p.Lb) && exchange_fits((long)p.nsplit * p.B * p.n_v) ? 1 : 0;
   p.ss_off = (long)rec;

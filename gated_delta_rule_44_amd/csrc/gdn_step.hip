@@ -1,7 +1,7 @@
 // Single-token recurrence for decode and for verify-with-checkpoints (gfx950).
 //
 // Work item = (key head kh, row bp = b P + p): T tokens one after the other through the conv on the
-// channels of key head kh (its q and k channels and the v channels of its R value heads), the q/k L2
+// channels of key head kh (its q and k channels and the v channels of its value heads, R at a time), the q/k L2
 // norm, the gates, one delta-rule step per value head, the gated RMSNorm, and the state/tail stores.
 // Decode is T = 1 writing back to the pool row; verify writes each token's state and tail to its
 // checkpoint row and leaves the pool untouched. Both run this one kernel, so checkpoint i is bitwise
@@ -54,7 +54,7 @@ struct StepShape {
   static constexpr int RR = LH ? RPT / 2 : RPT;                // rows per thread held in registers
 };
 
-template <typename ActT, int D, int R>
+template <typename ActT, int D, int R, bool GROUPED>
 __global__ __launch_bounds__((StepShape<D, R>::NTH))
 __attribute__((amdgpu_waves_per_eu(StepShape<D, R>::LH ? 2 * StepShape<D, R>::NTH / 256 : 1)))
 void step_kernel(StepArgs p) {
@@ -88,15 +88,14 @@ void step_kernel(StepArgs p) {
   ActT* out = (ActT*)p.out;
 
   auto slot_of = [&](int item) { const int b = item / n_k / p.P; return p.slot ? (long)p.slot[b] : (long)b; };
-  // this thread's block of its head's state: rows rg*RPT + i, columns 4 cq .. 4 cq + 3
-  auto state_src = [&](int item) {
-    const int kh = item % n_k;
-    return p.state_in + slot_of(item) * SZ + (long)(kh * R + r) * D * D + (long)(rg * RPT) * D + 4 * cq;
+  // this thread's block of value head h's state: rows rg*RPT + i, columns 4 cq .. 4 cq + 3
+  auto state_src = [&](int item, int h) {
+    return p.state_in + slot_of(item) * SZ + (long)h * D * D + (long)(rg * RPT) * D + 4 * cq;
   };
   // row RR + j of this thread's block in LDS
   auto hl_at = [&](int j) -> f32x4& { return sHL[((r * S::RG + rg) * (RL > 0 ? RL : 1) + j) * QD + cq]; };
-  auto load_H = [&](f32x4 (&H)[RR], int item) {
-    const float* src = state_src(item);
+  auto load_H = [&](f32x4 (&H)[RR], int item, int h) {
+    const float* src = state_src(item, h);
 #pragma unroll
     for (int i = 0; i < RR; ++i) H[i] = __builtin_nontemporal_load((const f32x4*)(src + (long)i * D));
 #pragma unroll
@@ -117,9 +116,16 @@ void step_kernel(StepArgs p) {
   {
     const int item = blockIdx.x;
     const int kh = item % n_k, bp = item / n_k;  // row: sequence bp / P, path bp % P
-    const int h = kh * R + r;
     const long s = slot_of(item);
     const ActT* tail_in = (const ActT*)p.tail_in + s * TZ;
+    // With more value heads per key head than one workgroup holds (R of the n_v / n_k), the workgroup
+    // takes them R at a time, forming q and k again for each group. The q and k channels of the conv
+    // tail are written by the last group only: decode updates the tail in place, and every group reads
+    // the old rows.
+    const int RQ = GROUPED ? n_v / n_k : R, ngroups = GROUPED ? RQ / R : 1;
+    for (int grp = 0; grp < ngroups; ++grp) {
+    const int h = kh * RQ + grp * R + r;
+    const bool qk_tail = grp + 1 == ngroups;
 
     // The item's small inputs are loaded before the next item's state: loads complete in issue
     // order, so anything issued after that prefetch would wait for all of it.
@@ -131,7 +137,7 @@ void step_kernel(StepArgs p) {
       int gc = -1;
       if (lc < D) gc = kh * D + lc;
       else if (lc < 2 * D) gc = n_k * D + kh * D + (lc - D);
-      else if (lc < NCH) gc = 2 * n_k * D + kh * R * D + (lc - 2 * D);
+      else if (lc < NCH) gc = 2 * n_k * D + (kh * RQ + grp * R) * D + (lc - 2 * D);
       gch[j] = gc;
       const int gl = gc >= 0 ? gc : 0;  // unconditional loads (a clamped channel for unowned slots)
       w0[j] = to_f32(conv_w[gl * 4 + 0]);
@@ -155,7 +161,7 @@ void step_kernel(StepArgs p) {
     };
     TokIn cur;
     load_tok(cur, 0);
-    load_H(H, item);
+    load_H(H, item, h);
 
     for (int t = 0; t < p.T; ++t) {
       const long row = (long)bp * p.T + t;
@@ -183,7 +189,7 @@ void step_kernel(StepArgs p) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
           const int gc = gch[j];
-          if (gc >= 0) {
+          if (gc >= 0 && (qk_tail || tid + j * NTH >= 2 * D)) {
             to[0L * C + gc] = from_f32<ActT>(t0[j]);
             to[1L * C + gc] = from_f32<ActT>(t1[j]);
             to[2L * C + gc] = from_f32<ActT>(t2[j]);
@@ -283,43 +289,49 @@ void step_kernel(StepArgs p) {
           else out[ob + 4 * cq + c] = from_f32<ActT>(y);
         }
       }
-      lds_barrier();  // sY, sRed and sTot reused by the next token or item
+      lds_barrier();  // sY, sRed and sTot reused by the next token or group
+    }
     }
   }
 }
 
 // one workgroup per (key head, sequence): many small independent workgroups keep every CU's memory
 // pipe busy, one finishing its stores while the next loads
-template <typename ActT, int D, int R>
+template <typename ActT, int D, int R, bool GROUPED>
 hipError_t launch_step_r(const StepArgs& p, hipStream_t st) {
   using S = StepShape<D, R>;
   timing_before(p.verify ? "step_verify" : "step_decode", st);
-  hipLaunchKernelGGL((step_kernel<ActT, D, R>), dim3(p.n_k * p.B * p.P), dim3(S::NTH), 0, st, p);
+  hipLaunchKernelGGL((step_kernel<ActT, D, R, GROUPED>), dim3(p.n_k * p.B * p.P), dim3(S::NTH), 0, st, p);
   timing_after(st);
   return hipGetLastError();
 }
 
+// value heads per workgroup pass: the GQA ratio itself where a shape is built for it (1, 2, 4), else its
+// largest divisor among 4, 2, 1, the workgroup looping over the groups
 template <typename ActT, int D>
-hipError_t launch_step_d(const StepArgs& p, int R, hipStream_t st) {
-  switch (R) {
-    case 1: return launch_step_r<ActT, D, 1>(p, st);
-    case 2: return launch_step_r<ActT, D, 2>(p, st);
-    case 4: return launch_step_r<ActT, D, 4>(p, st);
-    default: return hipErrorInvalidValue;
+hipError_t launch_step_d(const StepArgs& p, int ratio, hipStream_t st) {
+  switch (ratio) {
+    case 1: return launch_step_r<ActT, D, 1, false>(p, st);
+    case 2: return launch_step_r<ActT, D, 2, false>(p, st);
+    case 4: return launch_step_r<ActT, D, 4, false>(p, st);
+    default:
+      if (ratio % 4 == 0) return launch_step_r<ActT, D, 4, true>(p, st);
+      if (ratio % 2 == 0) return launch_step_r<ActT, D, 2, true>(p, st);
+      return launch_step_r<ActT, D, 1, true>(p, st);
   }
 }
 
 }  // namespace
 
-hipError_t launch_step(const StepArgs& p, int act_dtype, int D, int R, hipStream_t st) {
+hipError_t launch_step(const StepArgs& p, int act_dtype, int D, int ratio, hipStream_t st) {
   if (act_dtype == kActBf16) {
-    if (D == 32) return launch_step_d<bf16_t, 32>(p, R, st);
-    if (D == 64) return launch_step_d<bf16_t, 64>(p, R, st);
-    if (D == 128) return launch_step_d<bf16_t, 128>(p, R, st);
+    if (D == 32) return launch_step_d<bf16_t, 32>(p, ratio, st);
+    if (D == 64) return launch_step_d<bf16_t, 64>(p, ratio, st);
+    if (D == 128) return launch_step_d<bf16_t, 128>(p, ratio, st);
   } else {
-    if (D == 32) return launch_step_d<float, 32>(p, R, st);
-    if (D == 64) return launch_step_d<float, 64>(p, R, st);
-    if (D == 128) return launch_step_d<float, 128>(p, R, st);
+    if (D == 32) return launch_step_d<float, 32>(p, ratio, st);
+    if (D == 64) return launch_step_d<float, 64>(p, ratio, st);
+    if (D == 128) return launch_step_d<float, 128>(p, ratio, st);
   }
   return hipErrorInvalidValue;
 }

@@ -39,11 +39,15 @@ def _desc(**kw):
 
 def test_unsupported_shapes_are_reported():
     lib = gdn.load_library()
-    for kw in (dict(d_k=48, d_v=48), dict(conv_k=3), dict(n_v=6, n_k=4), dict(n_k=1, n_v=8), dict(d_k=64, d_v=32)):
+    for kw in (dict(d_k=48, d_v=48), dict(conv_k=3), dict(n_v=6, n_k=4), dict(d_k=64, d_v=32)):
         d = _desc(**kw)
         rc = lib.gdn_conv_chunk(ctypes.byref(d), None, None, None, None, None, 1, 1, None)
         assert rc == -2, (kw, rc)
         assert lib.gdn_last_error()
+    # every GQA ratio is built (those other than 1, 2, 4 run in groups): the shape passes, the NULL fails
+    for kw in (dict(n_k=1, n_v=8), dict(n_k=2, n_v=6), dict(n_k=1, n_v=3)):
+        d = _desc(**kw)
+        assert lib.gdn_conv_chunk(ctypes.byref(d), None, None, None, None, None, 1, 1, None) == -1, kw
 
 
 def test_null_and_size_errors():

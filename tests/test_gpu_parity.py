@@ -110,7 +110,8 @@ def test_prefill_split_row_sum_exchange(dims, B, L, lens):
 
 @pytest.mark.parametrize("D,R,act_t", [(32, 1, ACT_BF16), (32, 4, ACT_BF16), (64, 4, ACT_BF16),
                                        (32, 1, ACT_F32), (32, 4, ACT_F32), (64, 1, ACT_F32),
-                                       (64, 4, ACT_F32)])
+                                       (64, 4, ACT_F32), (64, 3, ACT_BF16), (32, 6, ACT_F32),
+                                       (128, 8, ACT_BF16), (128, 3, ACT_BF16)])
 def test_prefill_every_head_shape(D, R, act_t):
     """The remaining compiled (d, value heads per key head, activation type) combinations: ragged
     multi-chunk sequences from a non-zero state and tail. At d = 64 with four value heads per key head
@@ -118,7 +119,8 @@ def test_prefill_every_head_shape(D, R, act_t):
     fails by one f16 ulp of a U' element (2.3e-3 at the output) when a hi/lo split's two halves are
     rounded from different values."""
     dims = LayerDims(n_k=2, n_v=2 * R, d_k=D, d_v=D, act=act_t)
-    _prefill_case(dims, 8, 2, 150, [150, 67], state_std=0.05, tail_rand=True)
+    paths = BOTH if D == 128 and act_t == ACT_BF16 else (None,)
+    _prefill_case(dims, 8, 2, 150, [150, 67], state_std=0.05, tail_rand=True, paths=paths)
 
 
 def test_prefill_fp32_multichunk():
@@ -243,7 +245,10 @@ def _decode_inputs(dims, rng, B, T):
 
 @pytest.mark.parametrize("dims,B", [(NEXT, 8), (SMALL, 4), (LayerDims(n_k=2, n_v=8, d_k=64, d_v=64), 3),
                                     (LayerDims(n_k=2, n_v=8, d_k=128, d_v=128), 5),
-                                    (LayerDims(n_k=2, n_v=4, d_k=32, d_v=32, act=ACT_F32), 2)])
+                                    (LayerDims(n_k=2, n_v=4, d_k=32, d_v=32, act=ACT_F32), 2),
+                                    (LayerDims(n_k=2, n_v=6, d_k=64, d_v=64), 3),
+                                    (LayerDims(n_k=1, n_v=8, d_k=128, d_v=128), 4),
+                                    (LayerDims(n_k=2, n_v=12, d_k=32, d_v=32, act=ACT_F32), 2)])
 @pytest.mark.parametrize("out_f32", [False, True])
 def test_decode_step_vs_oracle(dims, B, out_f32):
     _say(f"decode B={B} dims={dims} out_f32={out_f32}")
@@ -381,6 +386,39 @@ def test_verify_checkpoints_and_commit():
         assert torch.equal(sp[s], ck_s[s, m_ref[s]])
         assert torch.equal(tp[s], ck_t[s, m_ref[s]])
     assert_state_close(host(sp), ref["ckpt_H"][np.arange(B), m_ref])
+
+
+@pytest.mark.parametrize("dims", [LayerDims(n_k=2, n_v=16, d_k=128, d_v=128), LayerDims(n_k=2, n_v=6, d_k=64, d_v=64)])
+def test_verify_grouped_gqa_ratio(dims):
+    """GQA ratios the kernels run in groups (8: four value heads at a time, 3: one): verify against the
+    oracle, and every checkpoint bitwise equal to repeated in-place decode, which only holds if every
+    group reads the conv tail's q and k rows before the last group writes them."""
+    B, K = 5, 4
+    T = K + 1
+    _say(f"verify grouped ratio dims={dims}")
+    w, _, rng = make_layer(19, dims, 1, 1)
+    H0, T0 = _saved_states(dims, w, rng, B)
+    x = _decode_inputs(dims, rng, B, T)
+    d = desc_of(dims)
+    W = weights(w, dims)
+    sp, tp = f32(H0), act(T0, dims)
+    mx, zz, aa, bb = act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims)
+    ck_s, ck_t, out = gdn.verify_with_checkpoints(d, W, mx, zz, aa, bb, None, tp, sp)
+    torch.cuda.synchronize()
+    ref = oracle.verify(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, T0, H0)
+    assert_out_close(host(out), ref["out"], dims, "verify out")
+    cks = host(ck_s)
+    for i in range(T):
+        assert_state_close(cks[:, i], ref["ckpt_H"][:, i], f"checkpoint {i}")
+    np.testing.assert_array_equal(host(ck_t), ref["ckpt_tail"].astype(np.float32))
+    sp2, tp2 = sp.clone(), tp.clone()
+    for i in range(T):
+        o = gdn.decode_step(d, W, mx[:, i].contiguous(), zz[:, i].contiguous(), aa[:, i].contiguous(),
+                            bb[:, i].contiguous(), None, tp2, sp2)
+        torch.cuda.synchronize()
+        assert torch.equal(sp2, ck_s[:, i]), f"checkpoint {i} differs bitwise from {i + 1} decode calls"
+        assert torch.equal(tp2, ck_t[:, i])
+        assert torch.equal(o, out[:, i])
 
 
 def test_verify_paths_and_commit():
