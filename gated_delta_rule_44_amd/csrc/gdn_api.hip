@@ -253,7 +253,6 @@ int gdn_conv_chunk(const gdn_desc* d, const void* conv_w, const void* mixed, con
 size_t gdn_prefill_workspace_bytes(const gdn_desc* d, int B, int Lb) {
   if (check_desc(d) || B <= 0 || Lb <= 0) return 0;
   if (use_fused(d, B)) return gdn::fused_ws_bytes(B, d->n_v, Lb);
-  if (d->act_dtype == GDN_F32 && d->d_k > 64) return 0;
   const int n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
   return gdn::prefill_ws_bytes(B, d->n_k, d->n_v, d->d_k, Lb, n_chunks, d->act_dtype == GDN_F32);
 }
@@ -272,8 +271,6 @@ static int prefill_impl(const gdn_desc* d, const gdn_weights* w, const void* mix
     return fail(GDN_EINVAL, "gdn_prefill_chunk: Lb * n_v * d_v = %ld must stay below 2^31", (long)Lb * d->n_v * d->d_v);
   if ((long)B * ((Lb + gdn::kChunk - 1) / gdn::kChunk) * d->n_v >= (1L << 31))
     return fail(GDN_EINVAL, "gdn_prefill_chunk: B * chunks * n_v must stay below 2^31");
-  if (d->act_dtype == GDN_F32 && d->d_k > 64)
-    return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunk: fp32 activations are built for d <= 64 (got %d)", d->d_k);
   const size_t need = fused ? gdn::fused_ws_bytes(B, d->n_v, Lb) : gdn_prefill_workspace_bytes(d, B, Lb);
   if (ws_bytes < need) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace %zu bytes < %zu needed", ws_bytes, need);
   if (((uintptr_t)ws & 255u) != 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: workspace must be 256-byte aligned");

@@ -1905,6 +1905,16 @@ hipError_t launch_r(const PrefillArgs& p, int R, hipStream_t st) {
   }
 }
 
+// fp32 activations at d = 128: groups of one or two value heads (chunk_prep2), the bf16 operands
+template <typename ActT, int D, int NT>
+hipError_t launch_r12(const PrefillArgs& p, int R, hipStream_t st) {
+  switch (R) {
+    case 1: return launch_t<ActT, D, 1, false, NT>(p, st);
+    case 2: return launch_t<ActT, D, 2, false, NT>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 int device_cus() {
@@ -1924,16 +1934,22 @@ int device_cus() {
   return cus[dev];
 }
 
-int prefill_group(int n_k, int n_v) {
+int prefill_group(int n_k, int n_v, int D, bool act_f32) {
   const int R = n_v / n_k;
+  if (act_f32 && D == 128) return R % 2 == 0 ? 2 : 1;  // chunk_prep2 only (R <= 2) at this shape
   if (R == 1 || R == 2 || R == 4) return R;
   return R % 4 == 0 ? 4 : R % 2 == 0 ? 2 : 1;
 }
 
-size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool split_all) {
+// hi/lo operands throughout (fp32-equivalent) for fp32 activations up to d = 64; from d = 128 the
+// records would not fit chunk_prep's LDS, and fp32 activations take the bf16 activations' operands
+bool prefill_split_all(int D, bool act_f32) { return act_f32 && D <= 64; }
+
+size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool act_f32) {
+  const bool split_all = prefill_split_all(D, act_f32);
   const int nsplit = D / (16 * pass_nt(B, n_v, D));
   long vrec, krec;
-  const int grp = prefill_group(n_k, n_v);
+  const int grp = prefill_group(n_k, n_v, D, act_f32);
   rec_sizes(D, split_all, grp > 1, vrec, krec);
   size_t bytes = (size_t)B * n_chunks * ((size_t)n_v * vrec + (size_t)(n_v / grp) * krec);
   if (nsplit > 1) {
@@ -1947,9 +1963,10 @@ size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bo
   return bytes;
 }
 
-void prefill_ws_layout(PrefillArgs& p, int D, bool split_all) {
+void prefill_ws_layout(PrefillArgs& p, int D, bool act_f32) {
+  const bool split_all = prefill_split_all(D, act_f32);
   long vrec, krec;
-  p.grp = prefill_group(p.n_k, p.n_v);
+  p.grp = prefill_group(p.n_k, p.n_v, D, act_f32);
   rec_sizes(D, split_all, p.grp > 1, vrec, krec);
   p.key_off = (long)p.B * p.n_v * p.n_chunks * vrec;
   const size_t rec = (size_t)p.key_off + (size_t)p.B * (p.n_v / p.grp) * p.n_chunks * krec;
@@ -1973,6 +1990,12 @@ hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hip
   } else {
     if (D == 32) return launch_r<float, 32, true, 2>(p, R, st);
     if (D == 64) return launch_r<float, 64, true, 4>(p, R, st);
+    if (D == 128) {
+      if (nt == 8) return launch_r12<float, 128, 8>(p, R, st);
+      if (nt == 4) return launch_r12<float, 128, 4>(p, R, st);
+      if (nt == 2) return launch_r12<float, 128, 2>(p, R, st);
+      return launch_r12<float, 128, 1>(p, R, st);
+    }
   }
   return hipErrorInvalidValue;
 }

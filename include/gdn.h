@@ -28,12 +28,13 @@
  *
  * Status codes: GDN_OK = 0; GDN_EINVAL = -1 (null pointer, non-positive size, inconsistent sizes,
  * workspace too small); GDN_EUNSUPPORTED = -2 (a shape this build has no kernel for: d_k != d_v, d_k
- * not in {32, 64, 128}, conv_k != 4, n_v not a multiple of n_k, or fp32 activations with d_k > 64 in
- * gdn_prefill_chunk; the caller falls back, as the statecache.py page's StateCache falls back to the
- * plain path on _NotCached); GDN_EHIP = -3. The layer definition itself only rules out d_k, d_v outside
- * {32, 64, 128}, conv_k != 4 and n_v % n_k != 0; the other limits are this build's. Every GQA ratio
- * n_v / n_k is built; ratios other than 1, 2 and 4 run their value heads 4, 2 or 1 at a time (the
- * largest that divides the ratio), forming the shared q and k once per group.
+ * not in {32, 64, 128}, conv_k != 4 or n_v not a multiple of n_k; the caller falls back, as the
+ * statecache.py page's StateCache falls back to the plain path on _NotCached); GDN_EHIP = -3. The layer
+ * definition itself only rules out d_k, d_v outside {32, 64, 128}, conv_k != 4 and n_v % n_k != 0; d_k
+ * != d_v is this build's limit. Every GQA ratio n_v / n_k is built; ratios other than 1, 2 and 4 run
+ * their value heads 4, 2 or 1 at a time (the largest that divides the ratio), forming the shared q and
+ * k once per group. Prefill with fp32 activations carries every MFMA operand as a hi/lo pair up to d =
+ * 64; at d = 128 it uses the operand precisions of bf16 activations (same output and state bounds).
  *
  * Value range (prefill): the chunked prefill carries the state, the write vectors u and the keys and
  * queries as pairs of f16 values scaled by 2^8 (about 22 bits), so |state| and |u| must stay below 255.

@@ -94,7 +94,8 @@ def test_sizes():
     assert gdn.prefill_workspace_bytes(d, 6, 4096) == 0
     # fewer units take the two-launch path and its chunk records
     assert gdn.prefill_workspace_bytes(d, 5, 4096) > 0
-    assert gdn.prefill_workspace_bytes(gdn.GdnDesc(n_k=2, n_v=4, d_k=128, d_v=128, act_dtype=gdn.GDN_F32), 1, 64) == 0
+    # fp32 activations at d = 128 take the two-launch path (records of the bf16 operand layout)
+    assert gdn.prefill_workspace_bytes(gdn.GdnDesc(n_k=2, n_v=4, d_k=128, d_v=128, act_dtype=gdn.GDN_F32), 1, 64) > 0
     # a workspace sized for the longest call serves every shorter one (sizes never shrink as Lb grows)
     for dd in (d, gdn.GdnDesc(n_k=16, n_v=16, d_k=128, d_v=128), gdn.GdnDesc(n_k=2, n_v=4, d_k=64, d_v=64)):
         for B in (1, 2, 3, 4, 5, 8):

@@ -111,7 +111,8 @@ def test_prefill_split_row_sum_exchange(dims, B, L, lens):
 @pytest.mark.parametrize("D,R,act_t", [(32, 1, ACT_BF16), (32, 4, ACT_BF16), (64, 4, ACT_BF16),
                                        (32, 1, ACT_F32), (32, 4, ACT_F32), (64, 1, ACT_F32),
                                        (64, 4, ACT_F32), (64, 3, ACT_BF16), (32, 6, ACT_F32),
-                                       (128, 8, ACT_BF16), (128, 3, ACT_BF16)])
+                                       (128, 8, ACT_BF16), (128, 3, ACT_BF16), (128, 1, ACT_F32),
+                                       (128, 2, ACT_F32), (128, 4, ACT_F32)])
 def test_prefill_every_head_shape(D, R, act_t):
     """The remaining compiled (d, value heads per key head, activation type) combinations: ragged
     multi-chunk sequences from a non-zero state and tail. At d = 64 with four value heads per key head
