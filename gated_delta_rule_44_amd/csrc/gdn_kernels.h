@@ -80,8 +80,9 @@ struct PrefillArgs {
 };
 // fp32 activations run every MFMA operand as a hi/lo pair (split_all) and are built for d <= 64
 // value heads per chunk_prep workgroup: the GQA ratio n_v / n_k where a kernel is built for it (1, 2,
-// 4), else its largest divisor among 4, 2, 1 (each group then forms the shared q and k again)
-int prefill_group(int n_k, int n_v, int D, bool act_f32);
+// 4), else its largest divisor among 4, 2, 1 (each group then forms the shared q and k again); one
+// where the grid would be too small to fill the device
+int prefill_group(int n_k, int n_v, int D, bool act_f32, int B, int n_chunks);
 size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool act_f32);
 void prefill_ws_layout(PrefillArgs& p, int D, bool act_f32);
 hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hipStream_t st);

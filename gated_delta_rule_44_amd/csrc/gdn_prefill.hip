@@ -45,6 +45,7 @@
 // P~ hold scale (< 1) and the decays folded in, and -W is small: at 2^8 their lo halves (and the small
 // entries of -W) would fall below 2^-14 and flush, which costs about half of a 2e-3 output bound at a
 // 4096-token prefill; at these scales the rounding costs a fifth of it.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -1934,24 +1935,47 @@ int device_cus() {
   return cus[dev];
 }
 
-int prefill_group(int n_k, int n_v, int D, bool act_f32) {
+// value heads per chunk_prep workgroup where its grid fills the device
+static int natural_group(int n_k, int n_v, int D, bool act_f32) {
   const int R = n_v / n_k;
   if (act_f32 && D == 128) return R % 2 == 0 ? 2 : 1;  // chunk_prep2 only (R <= 2) at this shape
   if (R == 1 || R == 2 || R == 4) return R;
   return R % 4 == 0 ? 4 : R % 2 == 0 ? 2 : 1;
 }
 
+// Below this many chunk_prep workgroups the grid leaves CUs idle and one workgroup's latency sets
+// chunk_prep's time; a call then runs one value head per workgroup (at 16/32 heads a single chunk
+// takes 23 us with two value heads per workgroup and 18 us with one), forming q and k once per head.
+constexpr long kSmallPrepGrid = 256;
+
+int prefill_group(int n_k, int n_v, int D, bool act_f32, int B, int n_chunks) {
+  const int g = natural_group(n_k, n_v, D, act_f32);
+  if (g > 1 && (long)B * n_chunks * (n_v / g) < kSmallPrepGrid) return 1;
+  return g;
+}
+
 // hi/lo operands throughout (fp32-equivalent) for fp32 activations up to d = 64; from d = 128 the
 // records would not fit chunk_prep's LDS, and fp32 activations take the bf16 activations' operands
 bool prefill_split_all(int D, bool act_f32) { return act_f32 && D <= 64; }
 
+static size_t records_bytes(int B, int n_v, int D, int n_chunks, bool split_all, int grp) {
+  long vrec, krec;
+  rec_sizes(D, split_all, grp > 1, vrec, krec);
+  return (size_t)B * n_chunks * ((size_t)n_v * vrec + (size_t)(n_v / grp) * krec);
+}
+
 size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool act_f32) {
   const bool split_all = prefill_split_all(D, act_f32);
   const int nsplit = D / (16 * pass_nt(B, n_v, D));
-  long vrec, krec;
-  const int grp = prefill_group(n_k, n_v, D, act_f32);
-  rec_sizes(D, split_all, grp > 1, vrec, krec);
-  size_t bytes = (size_t)B * n_chunks * ((size_t)n_v * vrec + (size_t)(n_v / grp) * krec);
+  const int g = natural_group(n_k, n_v, D, act_f32);
+  const int grp = prefill_group(n_k, n_v, D, act_f32, B, n_chunks);
+  size_t bytes = records_bytes(B, n_v, D, n_chunks, split_all, grp);
+  if (grp == g && g > 1) {
+    // the longest call that still takes one value head per workgroup has larger records than a
+    // slightly longer call with groups: the size covers both, so that it never shrinks as Lb grows
+    const long nc_small = (kSmallPrepGrid - 1) / ((long)B * (n_v / g));
+    if (nc_small >= 1) bytes = std::max(bytes, records_bytes(B, n_v, D, (int)nc_small, split_all, 1));
+  }
   if (nsplit > 1) {
     // partial sums of squares, and the unnormalised o for a norm pass; the o area is counted even
     // when the slices exchange their sums, so that the size never shrinks as Lb grows (a workspace
@@ -1966,7 +1990,7 @@ size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bo
 void prefill_ws_layout(PrefillArgs& p, int D, bool act_f32) {
   const bool split_all = prefill_split_all(D, act_f32);
   long vrec, krec;
-  p.grp = prefill_group(p.n_k, p.n_v, D, act_f32);
+  p.grp = prefill_group(p.n_k, p.n_v, D, act_f32, p.B, p.n_chunks);
   rec_sizes(D, split_all, p.grp > 1, vrec, krec);
   p.key_off = (long)p.B * p.n_v * p.n_chunks * vrec;
   const size_t rec = (size_t)p.key_off + (size_t)p.B * (p.n_v / p.grp) * p.n_chunks * krec;
