@@ -547,16 +547,17 @@ def test_state_copy_gather_scatter():
 
 
 def test_timing_session_names_every_launch():
-    """The per-launch timing session sees each kernel a call launches, in order, with its time."""
+    """The per-launch timing session sees each kernel a call launches, in order, with its time (256
+    tokens: calls of up to 128 take whole heads and no norm pass)."""
     dims = LayerDims(n_k=2, n_v=4, d_k=128, d_v=128)
     _say("timing session: prefill (split heads) then decode")
-    w, x, rng = make_layer(5, dims, 1, 128)
+    w, x, rng = make_layer(5, dims, 1, 256)
     d = desc_of(dims)
     W = weights(w, dims)
     tail = act(np.zeros(dims.tail_shape(1), np.float32), dims)
     st = f32(np.zeros(dims.state_shape(1), np.float32))
-    out = torch.empty(1, 128, dims.value_dim, dtype=torch.bfloat16, device="cuda")
-    ws = gdn.prefill_workspace(d, 1, 128)
+    out = torch.empty(1, 256, dims.value_dim, dtype=torch.bfloat16, device="cuda")
+    ws = gdn.prefill_workspace(d, 1, 256)
     gdn.timing_begin(16)
     gdn.prefill_chunk(d, W, act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims), i32(x.lens),
                       tail, st, out, ws)
