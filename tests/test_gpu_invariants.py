@@ -219,3 +219,73 @@ def test_large_saved_state_range(path):
                 assert_state_close(host(st[s]), ref["H"][0], f"state seq {s}")
         else:
             assert status & gdn.GDN_STATUS_RANGE, "a state beyond the operand range went unreported"
+
+
+def test_two_runs_bitwise():
+    """Every launch is deterministic: the same inputs give the same bits twice (prefill on both paths,
+    decode, verify with checkpoints, tree verify, accept and the state copy)."""
+    dims, B, K, P = NEXT, 4, 4, 3
+    T = K + 1
+    _say("two runs bitwise")
+    w, x, rng = make_layer(41, dims, 8, 300, [300, 1, 64, 250, 300, 200, 129, 300])
+    H0, t0 = random_state(rng, dims, 8)
+    W = weights(w, dims)
+    d = desc_of(dims)
+    ins = [act(a, dims) for a in (x.mixed, x.z, x.a, x.b)] + [i32(x.lens)]
+
+    def prefill(path):
+        st, tail = f32(H0), act(t0, dims)
+        with prefill_path(path):
+            out = gdn.prefill_chunk(d, W, *ins, tail, st)
+        torch.cuda.synchronize()
+        return out, st, tail
+
+    for path in BOTH:
+        a, b = prefill(path), prefill(path)
+        for s, n in enumerate(x.lens):  # rows past a sequence's length are not outputs (left unwritten)
+            assert torch.equal(a[0][s, :n], b[0][s, :n]), f"prefill ({path}) out of sequence {s} differs"
+        for u, v, name in zip(a[1:], b[1:], ("state", "tail")):
+            assert torch.equal(u, v), f"prefill ({path}) {name} differs between two runs"
+
+    xs = make_inputs(rng, dims, B, T)
+    sp, tp = f32(H0[:B]), act(t0[:B], dims)
+    step_in = [act(a, dims) for a in (xs.mixed, xs.z, xs.a, xs.b)]
+
+    def decode():
+        s2, t2 = sp.clone(), tp.clone()
+        o = gdn.decode_step(d, W, *[a[:, 0].contiguous() for a in step_in], None, t2, s2)
+        torch.cuda.synchronize()
+        return o, s2, t2
+
+    assert all(torch.equal(u, v) for u, v in zip(decode(), decode())), "decode differs between two runs"
+
+    def verify():
+        r = gdn.verify_with_checkpoints(d, W, *step_in, None, tp, sp)
+        torch.cuda.synchronize()
+        return r
+
+    assert all(torch.equal(u, v) for u, v in zip(verify(), verify())), "verify differs between two runs"
+
+    xp = path_inputs(rng, dims, B, P, T)
+    path_in = [act(a, dims) for a in (xp.mixed, xp.z, xp.a, xp.b)]
+
+    def paths():
+        r = gdn.verify_paths(d, W, *path_in, None, tp, sp)
+        torch.cuda.synchronize()
+        return r
+
+    assert all(torch.equal(u, v) for u, v in zip(paths(), paths())), "tree verify differs between two runs"
+
+    drafts = i32(rng.integers(0, 3, size=(B, K)))
+    preds = i32(rng.integers(0, 3, size=(B, K + 1)))
+    a1, a2 = gdn.accept(drafts, preds), gdn.accept(drafts, preds)
+    assert all(torch.equal(u, v) for u, v in zip(a1, a2)), "accept differs between two runs"
+    ck_s, ck_t, _ = verify()
+
+    def commit():
+        s2, t2 = sp.clone(), tp.clone()
+        gdn.state_copy(d, s2, t2, i32(np.arange(B)), ck_s, ck_t, a1[3], B)
+        torch.cuda.synchronize()
+        return s2, t2
+
+    assert all(torch.equal(u, v) for u, v in zip(commit(), commit())), "state copy differs between two runs"
