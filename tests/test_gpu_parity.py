@@ -688,6 +688,57 @@ def test_split_exchange_graph_replay_equals_eager():
         assert torch.equal(state, ref_state) and torch.equal(tail, ref_tail), f"replay {rep}: state differs"
 
 
+@pytest.mark.parametrize("B,L", [(6, 300), (2, 1030)])
+def test_fused_graph_replay_equals_eager(B, L):
+    """The fused prefill captured into a HIP graph (two continued calls): whole heads at 192 units, and
+    segment maps, scan and segments at 64 units. Three replays, each after resetting the state, tail and
+    outputs eagerly, give the eager run's bits every time (the fused path takes the same launches
+    either way and clears nothing with memsets)."""
+    dims = NEXT
+    _say(f"fused graph replay B={B} L={L}")
+    w, x, rng = make_layer(65, dims, B, 2 * L)
+    d = desc_of(dims)
+    W = weights(w, dims)
+    lens = i32([L] + [L - 37] * (B - 1))
+    calls = []
+    for i in range(2):
+        sl = slice(i * L, (i + 1) * L)
+        calls.append((act(x.mixed[:, sl], dims), act(x.z[:, sl], dims), act(x.a[:, sl], dims), act(x.b[:, sl], dims),
+                      torch.zeros(B, L, dims.value_dim, dtype=torch.bfloat16, device="cuda")))
+    with prefill_path("fused"):
+        ws = gdn.prefill_workspace(d, B, L)
+    tail = torch.zeros(B, 3, dims.conv_dim, dtype=torch.bfloat16, device="cuda")
+    state = torch.zeros(B, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda")
+
+    def run():
+        for mx, zz, aa, bb, out in calls:
+            with prefill_path("fused"):
+                gdn.prefill_chunk(d, W, mx, zz, aa, bb, lens, tail, state, out, ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [c[4].clone() for c in calls], state.clone(), tail.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        state.zero_()
+        tail.zero_()
+        for c in calls:
+            c[4].fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, c in enumerate(calls):
+            assert torch.equal(c[4], ref[0][i]), f"replay {rep}: call {i} output differs from eager"
+        assert torch.equal(state, ref[1]) and torch.equal(tail, ref[2]), f"replay {rep}: state or tail differs"
+
+
 @pytest.mark.parametrize("path,dims,B,L,launches", [
     ("fused", SMALL, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),  # 16 units: segment maps, scan, segments
     ("fused", NEXT, 1, 4096, ["fused_map", "fused_scan", "fused", "tail"]),   # 32 units
