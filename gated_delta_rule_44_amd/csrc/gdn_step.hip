@@ -66,9 +66,13 @@ void step_kernel(StepArgs p) {
   static_assert(QD <= kWave && kWave % QD == 0, "a wave holds whole row groups");
   static_assert(HT >= 2 * D, "one thread per column sum");
 
-  __shared__ float sY[NCH];                  // conv outputs of the current token: q | k | v(R heads)
-  __shared__ float sRed[R][HW][2][D];        // per head, per wave: partial H^T k and H^T q
-  __shared__ __attribute__((aligned(16))) float sTot[R][2][D];  // per head: H^T k and H^T q
+  // Two LDS barriers per token. The conv outputs are double-buffered by token parity: token t + 1
+  // writes the other buffer before its first barrier, while slower waves may still read token t's;
+  // the buffer of token t is written again only after the second barrier of token t + 1, which every
+  // wave reaches after its last read of token t. The wave partials are written after the first
+  // barrier of their token, which every wave reaches only after it has summed the previous token's.
+  __shared__ float sY[2][NCH];               // conv outputs of a token: q | k | v(R heads)
+  __shared__ __attribute__((aligned(16))) float sRed[R][HW][2][D];  // per head, per wave: partial H^T k, H^T q
   __shared__ f32x4 sHL[RL > 0 ? R * S::RG * RL * QD : 1];   // rows RR.. of each thread's block
 
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -123,12 +127,13 @@ void step_kernel(StepArgs p) {
     // tail are written by the last group only: decode updates the tail in place, and every group reads
     // the old rows.
     const int RQ = GROUPED ? n_v / n_k : R, ngroups = GROUPED ? RQ / R : 1;
+    int par = 0;  // parity of the token over all groups: selects the conv output buffer
     for (int grp = 0; grp < ngroups; ++grp) {
     const int h = kh * RQ + grp * R + r;
     const bool qk_tail = grp + 1 == ngroups;
 
-    // The item's small inputs are loaded before the next item's state: loads complete in issue
-    // order, so anything issued after that prefetch would wait for all of it.
+    // The group's small inputs are loaded before its state: loads complete in issue order, so
+    // anything issued after the state would wait for all of it.
     int gch[CPT];
     float w0[CPT], w1[CPT], w2[CPT], w3[CPT], t0[CPT], t1[CPT], t2[CPT];
 #pragma unroll
@@ -167,6 +172,7 @@ void step_kernel(StepArgs p) {
       const long row = (long)bp * p.T + t;
       TokIn in = cur;
       if (t + 1 < p.T) load_tok(cur, t + 1);  // verify only
+      float* const y = sY[par];
       // ---- conv + SiLU on the owned channels, tail shift
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
@@ -177,7 +183,7 @@ void step_kernel(StepArgs p) {
           pre = fmaf(w1[j], t1[j], pre);
           pre = fmaf(w2[j], t2[j], pre);
           pre = fmaf(w3[j], x, pre);
-          sY[tid + j * NTH] = silu(pre);
+          y[tid + j * NTH] = silu(pre);
           t0[j] = t1[j];
           t1[j] = t2[j];
           t2[j] = x;
@@ -203,7 +209,7 @@ void step_kernel(StepArgs p) {
       // ---- q/k L2 norm and k.q (every wave computes them, no broadcast needed)
       float sq = 0.f, sk = 0.f, skq = 0.f;
       for (int i = lane; i < D; i += kWave) {
-        const float qv = sY[i], kv = sY[D + i];
+        const float qv = y[i], kv = y[D + i];
         sq = fmaf(qv, qv, sq);
         sk = fmaf(kv, kv, sk);
         skq = fmaf(kv, qv, skq);
@@ -220,7 +226,7 @@ void step_kernel(StepArgs p) {
       float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float qn = sY[rg * RPT + i] * rq, kn = sY[D + rg * RPT + i] * rk;
+        const float qn = y[rg * RPT + i] * rq, kn = y[D + rg * RPT + i] * rk;
         const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -245,21 +251,22 @@ void step_kernel(StepArgs p) {
         }
       }
       lds_barrier();
-      // the head's wave partials summed by 2 D of its threads (one column of H^T k or H^T q each)
-      if (th < 2 * D) {
-        const int which = th / D, col = th % D;
-        float acc = sRed[r][0][which][col];
+      // H^T k and H^T q on this thread's four columns: the head's wave partials, summed in wave order
+      f32x4 hk4 = *(const f32x4*)&sRed[r][0][0][4 * cq], hq4 = *(const f32x4*)&sRed[r][0][1][4 * cq];
 #pragma unroll
-        for (int ww = 1; ww < HW; ++ww) acc = acc + sRed[r][ww][which][col];
-        sTot[r][which][col] = acc;
+      for (int ww = 1; ww < HW; ++ww) {
+        const f32x4 pk4 = *(const f32x4*)&sRed[r][ww][0][4 * cq], pq4 = *(const f32x4*)&sRed[r][ww][1][4 * cq];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          hk4[c] = hk4[c] + pk4[c];
+          hq4[c] = hq4[c] + pq4[c];
+        }
       }
-      lds_barrier();
-      const f32x4 hk4 = *(const f32x4*)&sTot[r][0][4 * cq], hq4 = *(const f32x4*)&sTot[r][1][4 * cq];
       float u[4], o[4];
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float v = sY[2 * D + r * D + 4 * cq + c];
+        const float v = y[2 * D + r * D + 4 * cq + c];
         u[c] = beta * (v - decay * hk4[c]);
         o[c] = p.scale * fmaf(kq, u[c], decay * hq4[c]);
         ss = fmaf(o[c], o[c], ss);
@@ -268,7 +275,7 @@ void step_kernel(StepArgs p) {
       float* dst = p.state_out + (p.verify ? row * SZ : s * SZ) + (long)h * D * D;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float kn = sY[D + rg * RPT + i] * rk;
+        const float kn = y[D + rg * RPT + i] * rk;
         const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
         f32x4 nh;
 #pragma unroll
@@ -289,7 +296,7 @@ void step_kernel(StepArgs p) {
           else out[ob + 4 * cq + c] = from_f32<ActT>(y);
         }
       }
-      lds_barrier();  // sY, sRed and sTot reused by the next token or group
+      par ^= 1;
     }
     }
   }
