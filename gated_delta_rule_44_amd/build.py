@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_api.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_fused.hip", "gdn_state.hip", "gdn_step.hip", "gdn_probe.hip", "gdn_pcache.cpp"]
+SOURCES = ["gdn_api.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_fused.hip", "gdn_state.hip", "gdn_step.hip", "gdn_pad.hip", "gdn_probe.hip", "gdn_pcache.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

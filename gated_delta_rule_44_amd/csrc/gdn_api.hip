@@ -44,9 +44,10 @@ int check_desc(const gdn_desc* d) {
   if (d->act_dtype != GDN_BF16 && d->act_dtype != GDN_F32) return fail(GDN_EINVAL, "act_dtype=%d", d->act_dtype);
   if (d->conv_k != 4) return fail(GDN_EUNSUPPORTED, "conv_k=%d (only 4 is built)", d->conv_k);
   if (d->n_v % d->n_k) return fail(GDN_EUNSUPPORTED, "n_v=%d is not a multiple of n_k=%d", d->n_v, d->n_k);
-  if (d->d_k != d->d_v) return fail(GDN_EUNSUPPORTED, "d_k=%d != d_v=%d", d->d_k, d->d_v);
   if (d->d_k != 32 && d->d_k != 64 && d->d_k != 128)
     return fail(GDN_EUNSUPPORTED, "d_k=%d (built: 32, 64, 128)", d->d_k);
+  if (d->d_v != 32 && d->d_v != 64 && d->d_v != 128)
+    return fail(GDN_EUNSUPPORTED, "d_v=%d (built: 32, 64, 128)", d->d_v);
   if (!(d->l2_eps >= 0.f) || !(d->rms_eps >= 0.f)) return fail(GDN_EINVAL, "negative or NaN epsilon");
   if (d->out_dtype != GDN_OUT_ACT && d->out_dtype != GDN_F32) return fail(GDN_EINVAL, "out_dtype=%d", d->out_dtype);
   return GDN_OK;
@@ -62,7 +63,7 @@ int out_f32(const gdn_desc* d) { return d->act_dtype == GDN_F32 || d->out_dtype 
 // pass over several CUs, is faster. GDN_PREFILL_PATH in the environment overrides the choice for
 // tests and comparisons: "fused" (with segment maps and a scan for few units) or "two_phase".
 constexpr long kFusedMinUnits = 192;
-bool fused_built(const gdn_desc* d) { return d->d_k == 128 && d->act_dtype == GDN_BF16; }
+bool fused_built(const gdn_desc* d) { return d->d_k == 128 && d->d_v == 128 && d->act_dtype == GDN_BF16; }
 bool use_fused(const gdn_desc* d, int B) {
   if (!fused_built(d)) return false;
   const char* e = getenv("GDN_PREFILL_PATH");
@@ -142,6 +143,92 @@ void* scratch_ptr() {
     ptr[dev] = p;
   });
   return ptr[dev];
+}
+}  // namespace
+
+namespace {
+
+// ---- prefill with d_k != d_v: the square kernels at D = max(d_k, d_v) on zero-padded copies ----
+// Workspace: the padded inputs, weights, conv tail, state and output, then the square call's own.
+struct PadLayout {
+  int D;
+  long Cp;
+  size_t mixed, z, out, tail, state, conv_w, norm_w, inner, total;
+};
+
+PadLayout pad_layout(const gdn_desc* d, int B, int Lb) {
+  PadLayout L{};
+  L.D = d->d_k > d->d_v ? d->d_k : d->d_v;
+  L.Cp = (2L * d->n_k + d->n_v) * L.D;
+  const size_t act = d->act_dtype == GDN_BF16 ? 2 : 4, oel = out_f32(d) ? 4 : act;
+  const size_t rows = (size_t)B * Lb;
+  size_t off = 0;
+  auto take = [&off](size_t n) {
+    const size_t o = off;
+    off += (n + 255) / 256 * 256;
+    return o;
+  };
+  L.mixed = take(rows * L.Cp * act);
+  L.z = take(rows * d->n_v * L.D * act);
+  L.out = take(rows * d->n_v * L.D * oel);
+  L.tail = take((size_t)B * (d->conv_k - 1) * L.Cp * act);
+  L.state = take((size_t)B * d->n_v * L.D * L.D * 4);
+  L.conv_w = take((size_t)L.Cp * d->conv_k * act);
+  L.norm_w = take((size_t)L.D * 4);
+  L.inner = off;
+  const int n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
+  L.total = off + gdn::prefill_ws_bytes(B, d->n_k, d->n_v, L.D, Lb, n_chunks, d->act_dtype == GDN_F32);
+  return L;
+}
+
+// Copies in, the square two-launch prefill, copies out, all on `stream`. The RMSNorm averages over
+// the d_v real columns (the padded columns of o are exactly zero). Output rows past a sequence's length
+// are left unwritten, as in the square call.
+int prefill_padded(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,
+                   const void* b, const int32_t* len, void* conv_tail, float* state, void* out, int B, int Lb,
+                   void* ws, gdn_stream_t stream) {
+  const hipStream_t st = (hipStream_t)stream;
+  const PadLayout L = pad_layout(d, B, Lb);
+  char* base = (char*)ws;
+  const int act = d->act_dtype == GDN_BF16 ? 2 : 4, oel = out_f32(d) ? 4 : act, Kc = d->conv_k - 1;
+  const int ga = 16 / act;              // activation channels per 16-byte unit
+  const int gw = 16 / (act * d->conv_k);  // conv_w channels per unit (all conv_k taps of a channel)
+  const int go = 16 / oel;              // output channels per unit
+  const gdn::ChanMap chan{d->n_k, d->n_v, d->d_k / ga, d->d_v / ga, L.D / ga};
+  const gdn::ChanMap vchan{0, d->n_v, 0, d->d_v / ga, L.D / ga};
+  const gdn::ChanMap wchan{d->n_k, d->n_v, d->d_k / gw, d->d_v / gw, L.D / gw};
+  const gdn::ChanMap nchan{0, 1, 0, d->d_v / 4, L.D / 4};
+  const gdn::ChanMap ochan{0, d->n_v, 0, d->d_v / go, L.D / go};
+  const int C = (int)conv_channels(d), Cp = (int)L.Cp;
+  const long rows = (long)B * Lb, mats = (long)B * d->n_v;
+  hipError_t e = hipSuccess;
+  auto ok = [&e](hipError_t r) {
+    if (e == hipSuccess) e = r;
+    return e == hipSuccess;
+  };
+  if (ok(gdn::launch_pad_units(mixed, base + L.mixed, rows, C / ga, Cp / ga, chan, st)) &&
+      ok(gdn::launch_pad_units(z, base + L.z, rows, d->n_v * d->d_v / ga, d->n_v * L.D / ga, vchan, st)) &&
+      ok(gdn::launch_pad_units(conv_tail, base + L.tail, (long)B * Kc, C / ga, Cp / ga, chan, st)) &&
+      ok(gdn::launch_pad_state(state, (float*)(base + L.state), mats, d->d_k, d->d_v, L.D, st)) &&
+      ok(gdn::launch_pad_units(w->conv_w, base + L.conv_w, 1, C / gw, Cp / gw, wchan, st)) &&
+      ok(gdn::launch_pad_units(w->norm_w, base + L.norm_w, 1, d->d_v / 4, L.D / 4, nchan, st))) {
+    gdn::PrefillArgs p{};
+    p.conv_w = base + L.conv_w; p.A_log = w->A_log; p.dt_bias = w->dt_bias; p.norm_w = (const float*)(base + L.norm_w);
+    p.mixed = base + L.mixed; p.z = base + L.z; p.a = a; p.b = b; p.len = len; p.tail = base + L.tail;
+    p.state = (float*)(base + L.state); p.out = base + L.out;
+    p.ws = base + L.inner; p.B = B; p.Lb = Lb; p.n_k = d->n_k; p.n_v = d->n_v; p.C = Cp;
+    p.out_f32 = out_f32(d);
+    p.status = status_ptr();
+    p.n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
+    p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps; p.rms_n = (float)d->d_v;
+    gdn::prefill_ws_layout(p, L.D, d->act_dtype == GDN_F32);
+    if (ok(gdn::launch_prefill(p, d->act_dtype, L.D, p.grp, st)) &&
+        ok(gdn::launch_unpad_state((const float*)(base + L.state), state, mats, d->d_k, d->d_v, L.D, st)) &&
+        ok(gdn::launch_unpad_units(base + L.tail, conv_tail, (long)B * Kc, Cp / ga, C / ga, chan, nullptr, 0, st)))
+      ok(gdn::launch_unpad_units(base + L.out, out, rows, d->n_v * L.D / go, d->n_v * d->d_v / go, ochan, len, Lb,
+                                 st));
+  }
+  return hip_status(e, "gdn_prefill_chunk");
 }
 }  // namespace
 
@@ -252,6 +339,7 @@ int gdn_conv_chunk(const gdn_desc* d, const void* conv_w, const void* mixed, con
 
 size_t gdn_prefill_workspace_bytes(const gdn_desc* d, int B, int Lb) {
   if (check_desc(d) || B <= 0 || Lb <= 0) return 0;
+  if (d->d_k != d->d_v) return pad_layout(d, B, Lb).total;
   if (use_fused(d, B)) return gdn::fused_ws_bytes(B, d->n_v, Lb);
   const int n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
   return gdn::prefill_ws_bytes(B, d->n_k, d->n_v, d->d_k, Lb, n_chunks, d->act_dtype == GDN_F32);
@@ -267,8 +355,11 @@ static int prefill_impl(const gdn_desc* d, const gdn_weights* w, const void* mix
     return fail(GDN_EINVAL, "gdn_prefill_chunk: NULL pointer");
   if (B <= 0 || Lb <= 0) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d Lb=%d must be positive", B, Lb);
   if (B > 65535) return fail(GDN_EINVAL, "gdn_prefill_chunk: B=%d exceeds 65535", B);
-  if ((long)Lb * d->n_v * d->d_v >= (1L << 31))
-    return fail(GDN_EINVAL, "gdn_prefill_chunk: Lb * n_v * d_v = %ld must stay below 2^31", (long)Lb * d->n_v * d->d_v);
+  // (heads of different key and value dims run padded to the larger: D = max(d_k, d_v))
+  const long dmax = d->d_k > d->d_v ? d->d_k : d->d_v;
+  if ((long)Lb * d->n_v * dmax >= (1L << 31))
+    return fail(GDN_EINVAL, "gdn_prefill_chunk: Lb * n_v * max(d_k, d_v) = %ld must stay below 2^31",
+                (long)Lb * d->n_v * dmax);
   if ((long)B * ((Lb + gdn::kChunk - 1) / gdn::kChunk) * d->n_v >= (1L << 31))
     return fail(GDN_EINVAL, "gdn_prefill_chunk: B * chunks * n_v must stay below 2^31");
   const size_t need = fused ? gdn::fused_ws_bytes(B, d->n_v, Lb) : gdn_prefill_workspace_bytes(d, B, Lb);
@@ -279,6 +370,7 @@ static int prefill_impl(const gdn_desc* d, const gdn_weights* w, const void* mix
     return fail(GDN_EINVAL, "gdn_prefill_chunk: buffers must be 16-byte aligned");
   if (out == mixed || out == z || (void*)state == out || conv_tail == out)
     return fail(GDN_EINVAL, "gdn_prefill_chunk: out aliases another buffer");
+  if (d->d_k != d->d_v) return prefill_padded(d, w, mixed, z, a, b, len, conv_tail, state, out, B, Lb, ws, stream);
   if (fused || use_fused(d, B)) {
     gdn::FusedArgs f{};
     f.conv_w = w->conv_w; f.A_log = w->A_log; f.dt_bias = w->dt_bias; f.norm_w = w->norm_w;
@@ -297,7 +389,7 @@ static int prefill_impl(const gdn_desc* d, const gdn_weights* w, const void* mix
   p.out_f32 = out_f32(d);
   p.status = status_ptr();
   p.n_chunks = (Lb + gdn::kChunk - 1) / gdn::kChunk;
-  p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
+  p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps; p.rms_n = (float)d->d_v;
   gdn::prefill_ws_layout(p, d->d_k, d->act_dtype == GDN_F32);
   return hip_status(gdn::launch_prefill(p, d->act_dtype, d->d_k, p.grp, (hipStream_t)stream),
                     "gdn_prefill_chunk");
@@ -348,7 +440,7 @@ static int step_common(const gdn_desc* d, const gdn_weights* w, const void* mixe
   p.B = B; p.T = T; p.P = P; p.n_k = d->n_k; p.n_v = d->n_v; p.C = (int)conv_channels(d); p.verify = verify;
   p.out_f32 = out_f32(d);
   p.scale = q_scale(d); p.l2_eps = d->l2_eps; p.rms_eps = d->rms_eps;
-  return hip_status(gdn::launch_step(p, d->act_dtype, d->d_k, d->n_v / d->n_k, (hipStream_t)stream), name);
+  return hip_status(gdn::launch_step(p, d->act_dtype, d->d_k, d->d_v, d->n_v / d->n_k, (hipStream_t)stream), name);
 }
 
 int gdn_decode_step(const gdn_desc* d, const gdn_weights* w, const void* mixed, const void* z, const void* a,

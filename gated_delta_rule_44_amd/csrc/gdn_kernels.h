@@ -21,22 +21,23 @@ struct StepArgs {
   const float* dt_bias;
   const float* norm_w;
   const void* mixed;    // [B*P][T][C]
-  const void* z;        // [B*P][T][n_v*D]
+  const void* z;        // [B*P][T][n_v*d_v]
   const void* a;        // [B*P][T][n_v]
   const void* b;        // [B*P][T][n_v]
   const int32_t* slot;  // [B] or null
   const void* tail_in;  // pool [*][3][C]
-  const float* state_in;  // pool [*][n_v][D][D]
+  const float* state_in;  // pool [*][n_v][d_k][d_v]
   void* tail_out;       // decode: the pool; verify: [B*P*T][3][C]
-  float* state_out;     // decode: the pool; verify: [B*P*T][n_v][D][D]
-  void* out;            // [B*P][T][n_v*D]
+  float* state_out;     // decode: the pool; verify: [B*P*T][n_v][d_k][d_v]
+  void* out;            // [B*P][T][n_v*d_v]
   int out_f32;          // 1: out is fp32 (always with fp32 activations), 0: the activation type
   int B, T, n_k, n_v, C;
   int P;                // rows per sequence: 1, or the paths of a batch-of-paths verify
   int verify;
   float scale, l2_eps, rms_eps;
 };
-hipError_t launch_step(const StepArgs& p, int act_dtype, int D, int R, hipStream_t st);
+// head dims DK, DV each in {32, 64, 128}; ratio = n_v / n_k
+hipError_t launch_step(const StepArgs& p, int act_dtype, int DK, int DV, int ratio, hipStream_t st);
 
 // ---- standalone conv ------------------------------------------------------------------------------
 struct ConvArgs {
@@ -77,8 +78,11 @@ struct PrefillArgs {
   int exchange;         // split heads: 1 = the slices exchange row sums, 0 = a norm pass finishes
   int* status;          // device word: bit 0 set when a final state leaves the operand range (or null)
   float scale, l2_eps, rms_eps;
+  float rms_n;          // columns the gated RMSNorm averages over: d_v (below D in a call run on
+                        // zero-padded heads, whose extra columns of o are exactly zero)
 };
-// fp32 activations run every MFMA operand as a hi/lo pair (split_all) and are built for d <= 64
+// fp32 activations run every MFMA operand as a hi/lo pair (split_all) up to d = 64; at d = 128 they
+// take the bf16 operand precisions
 // value heads per chunk_prep workgroup: the GQA ratio n_v / n_k where a kernel is built for it (1, 2,
 // 4), else its largest divisor among 4, 2, 1 (each group then forms the shared q and k again); one
 // where the grid would be too small to fill the device
@@ -86,6 +90,22 @@ int prefill_group(int n_k, int n_v, int D, bool act_f32, int B, int n_chunks);
 size_t prefill_ws_bytes(int B, int n_k, int n_v, int D, int Lb, int n_chunks, bool act_f32);
 void prefill_ws_layout(PrefillArgs& p, int D, bool act_f32);
 hipError_t launch_prefill(const PrefillArgs& p, int act_dtype, int D, int R, hipStream_t st);
+
+// ---- zero-padded heads (prefill with d_k != d_v) --------------------------------------------------
+// A row of channels [q: n_k heads of dk | k: n_k heads of dk | v: n_v heads of dv], counted in 16-byte
+// units, and its padded form with every head widened to D units (n_k = 0 describes a row of value
+// heads only: z, out, norm_w).
+struct ChanMap {
+  int n_k, n_v, dk, dv, D;
+};
+// dst [rows][Ud] padded (zero units where the original has none) from src [rows][Us]
+hipError_t launch_pad_units(const void* src, void* dst, long rows, int Us, int Ud, const ChanMap& m, hipStream_t st);
+// dst [rows][Ud] original from src [rows][Us] padded; with len (rows = [B][Lb]) only rows t < len[b]
+hipError_t launch_unpad_units(const void* src, void* dst, long rows, int Us, int Ud, const ChanMap& m,
+                              const int32_t* len, int Lb, hipStream_t st);
+// fp32 states: [mats][D][D] (zero outside dk x dv) from [mats][dk][dv], and back
+hipError_t launch_pad_state(const float* src, float* dst, long mats, int dk, int dv, int D, hipStream_t st);
+hipError_t launch_unpad_state(const float* src, float* dst, long mats, int dk, int dv, int D, hipStream_t st);
 
 // ---- fused prefill (d_k = d_v = 128, bf16 activations) ----------------------------------------------
 struct FusedArgs {

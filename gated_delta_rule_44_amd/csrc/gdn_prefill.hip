@@ -1402,7 +1402,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
     }
     // a row whose sums never all arrived (the bound expired: a slice of the head was not running) is
     // written as NaN and reported through the device status word, never normalised with a missing sum
-    float inv = rsqrt_fast(tot / (float)D + p.rms_eps);
+    float inv = rsqrt_fast(tot / p.rms_n + p.rms_eps);
     if (!ready) inv = __builtin_nanf("");
     if (p.status && !__all(ready) && lane == 0) atomicOr(p.status, 2);
     const long row = ((long)b * Lb + t) * n_v + h;
@@ -1630,7 +1630,7 @@ __global__ __launch_bounds__(512) void state_pass_kernel(PrefillArgs p) {
       const int t = c * C64 + 16 * tt + r16;
       const long row = ((long)b * Lb + t) * n_v + h;
       if constexpr (FUSED) {
-        const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
+        const float inv = rsqrt_fast(ss / p.rms_n + p.rms_eps);
         float4 res[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -1768,7 +1768,7 @@ __global__ __launch_bounds__(256) void norm_kernel(PrefillArgs p) {
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < NPART; ++k) ss += sp[k];
-  const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
+  const float inv = rsqrt_fast(ss / p.rms_n + p.rms_eps);
   const float4 o = *(const float4*)(oraw + row * D + 4 * cq);
   const float4 z = Act4<ActT>::load((const ActT*)p.z + row * D + 4 * cq);
   const float4 nw = *(const float4*)(p.norm_w + 4 * cq);

@@ -18,7 +18,7 @@
 //
 // The state is HBM-streamed fp32, read and written exactly once per call. Each value head has its own
 // 256 threads (the workgroup is 256 R threads); a thread holds a 4-column x RPT-row block of its head's
-// H in registers; column partial sums are reduced across the row groups of a wave with lane shuffles
+// H (d_k rows of d_v columns, each head dim 32, 64 or 128) in registers; column partial sums are reduced across the row groups of a wave with lane shuffles
 // and across the head's waves in LDS. The register footprint is kept small (at d = 128 with up to two
 // value heads per key head half of a thread's rows wait in LDS, which leaves room for two workgroups
 // per CU), so that the waves of different workgroups overlap one's loads with another's arithmetic
@@ -40,31 +40,30 @@ namespace {
 // Barrier for LDS only: __syncthreads() would also wait for the next item's state loads (vmcnt).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D, int R>
+template <int DK, int DV, int R>
 struct StepShape {
   static constexpr int HT = 256;                               // threads per value head
   static constexpr int NTH = HT * R;
-  static constexpr int QD = D / 4;                             // column quads per row
+  static constexpr int QD = DV / 4;                            // column quads per row
   static constexpr int RG = HT / QD;                           // row groups per head
-  static constexpr int RPT = D / RG;                           // rows per thread
+  static constexpr int RPT = DK / RG;                          // rows per thread
   // at d = 128 with up to two value heads per key head, half of each thread's rows live in LDS (32 KB
   // per head, only ever touched by their own thread), so that the kernel fits 128 VGPRs and two
   // workgroups share a CU: one's loads and stores overlap the other's reductions and barriers
-  static constexpr bool LH = D == 128 && R <= 2;
+  static constexpr bool LH = DK == 128 && DV == 128 && R <= 2;
   static constexpr int RR = LH ? RPT / 2 : RPT;                // rows per thread held in registers
 };
 
-template <typename ActT, int D, int R, bool GROUPED>
-__global__ __launch_bounds__((StepShape<D, R>::NTH))
-__attribute__((amdgpu_waves_per_eu(StepShape<D, R>::LH ? 2 * StepShape<D, R>::NTH / 256 : 1)))
+template <typename ActT, int DK, int DV, int R, bool GROUPED>
+__global__ __launch_bounds__((StepShape<DK, DV, R>::NTH))
+__attribute__((amdgpu_waves_per_eu(StepShape<DK, DV, R>::LH ? 2 * StepShape<DK, DV, R>::NTH / 256 : 1)))
 void step_kernel(StepArgs p) {
-  using S = StepShape<D, R>;
+  using S = StepShape<DK, DV, R>;
   constexpr int HT = S::HT, NTH = S::NTH, QD = S::QD, RPT = S::RPT, HW = HT / kWave, RR = S::RR, RL = RPT - RR;
-  constexpr int NCH = 2 * D + R * D;         // channels owned by an item
+  constexpr int NCH = 2 * DK + R * DV;       // channels owned by an item
   constexpr int CPT = (NCH + NTH - 1) / NTH;
-  static_assert(RPT >= 1 && S::RG * RPT == D, "thread layout");
+  static_assert(RPT >= 1 && S::RG * RPT == DK, "thread layout");
   static_assert(QD <= kWave && kWave % QD == 0, "a wave holds whole row groups");
-  static_assert(HT >= 2 * D, "one thread per column sum");
 
   // Two LDS barriers per token. The conv outputs are double-buffered by token parity: token t + 1
   // writes the other buffer before its first barrier, while slower waves may still read token t's;
@@ -72,7 +71,7 @@ void step_kernel(StepArgs p) {
   // wave reaches after its last read of token t. The wave partials are written after the first
   // barrier of their token, which every wave reaches only after it has summed the previous token's.
   __shared__ float sY[2][NCH];               // conv outputs of a token: q | k | v(R heads)
-  __shared__ __attribute__((aligned(16))) float sRed[R][HW][2][D];  // per head, per wave: partial H^T k, H^T q
+  __shared__ __attribute__((aligned(16))) float sRed[R][HW][2][DV];  // per head, per wave: partial H^T k, H^T q
   __shared__ f32x4 sHL[RL > 0 ? R * S::RG * RL * QD : 1];   // rows RR.. of each thread's block
 
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -81,7 +80,7 @@ void step_kernel(StepArgs p) {
   const int hw = th / kWave;                 // wave inside the head's threads
   const int cq = th % QD, rg = th / QD;
   const int n_k = p.n_k, n_v = p.n_v, C = p.C;
-  const long SZ = (long)n_v * D * D;         // state floats per record
+  const long SZ = (long)n_v * DK * DV;       // state floats per record
   const long TZ = 3L * C;                    // tail elements per record
 
   const ActT* conv_w = (const ActT*)p.conv_w;
@@ -94,16 +93,16 @@ void step_kernel(StepArgs p) {
   auto slot_of = [&](int item) { const int b = item / n_k / p.P; return p.slot ? (long)p.slot[b] : (long)b; };
   // this thread's block of value head h's state: rows rg*RPT + i, columns 4 cq .. 4 cq + 3
   auto state_src = [&](int item, int h) {
-    return p.state_in + slot_of(item) * SZ + (long)h * D * D + (long)(rg * RPT) * D + 4 * cq;
+    return p.state_in + slot_of(item) * SZ + (long)h * DK * DV + (long)(rg * RPT) * DV + 4 * cq;
   };
   // row RR + j of this thread's block in LDS
   auto hl_at = [&](int j) -> f32x4& { return sHL[((r * S::RG + rg) * (RL > 0 ? RL : 1) + j) * QD + cq]; };
   auto load_H = [&](f32x4 (&H)[RR], int item, int h) {
     const float* src = state_src(item, h);
 #pragma unroll
-    for (int i = 0; i < RR; ++i) H[i] = __builtin_nontemporal_load((const f32x4*)(src + (long)i * D));
+    for (int i = 0; i < RR; ++i) H[i] = __builtin_nontemporal_load((const f32x4*)(src + (long)i * DV));
 #pragma unroll
-    for (int j = 0; j < RL; ++j) hl_at(j) = __builtin_nontemporal_load((const f32x4*)(src + (long)(RR + j) * D));
+    for (int j = 0; j < RL; ++j) hl_at(j) = __builtin_nontemporal_load((const f32x4*)(src + (long)(RR + j) * DV));
   };
 
   // per-token activations of one item, loaded ahead of use
@@ -140,9 +139,9 @@ void step_kernel(StepArgs p) {
     for (int j = 0; j < CPT; ++j) {
       const int lc = tid + j * NTH;
       int gc = -1;
-      if (lc < D) gc = kh * D + lc;
-      else if (lc < 2 * D) gc = n_k * D + kh * D + (lc - D);
-      else if (lc < NCH) gc = 2 * n_k * D + (kh * RQ + grp * R) * D + (lc - 2 * D);
+      if (lc < DK) gc = kh * DK + lc;
+      else if (lc < 2 * DK) gc = n_k * DK + kh * DK + (lc - DK);
+      else if (lc < NCH) gc = 2 * n_k * DK + (kh * RQ + grp * R) * DV + (lc - 2 * DK);
       gch[j] = gc;
       const int gl = gc >= 0 ? gc : 0;  // unconditional loads (a clamped channel for unowned slots)
       w0[j] = to_f32(conv_w[gl * 4 + 0]);
@@ -160,7 +159,7 @@ void step_kernel(StepArgs p) {
       for (int j = 0; j < CPT; ++j) in.x[j] = to_f32(mixed[row * C + (gch[j] >= 0 ? gch[j] : 0)]);
       in.av = to_f32(ain[row * n_v + h]);
       in.bv = to_f32(bin[row * n_v + h]);
-      const long ob = row * (long)n_v * D + (long)h * D;
+      const long ob = row * (long)n_v * DV + (long)h * DV;
 #pragma unroll
       for (int c = 0; c < 4; ++c) in.z[c] = to_f32(zin[ob + 4 * cq + c]);
     };
@@ -195,7 +194,7 @@ void step_kernel(StepArgs p) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
           const int gc = gch[j];
-          if (gc >= 0 && (qk_tail || tid + j * NTH >= 2 * D)) {
+          if (gc >= 0 && (qk_tail || tid + j * NTH >= 2 * DK)) {
             to[0L * C + gc] = from_f32<ActT>(t0[j]);
             to[1L * C + gc] = from_f32<ActT>(t1[j]);
             to[2L * C + gc] = from_f32<ActT>(t2[j]);
@@ -208,8 +207,8 @@ void step_kernel(StepArgs p) {
 
       // ---- q/k L2 norm and k.q (every wave computes them, no broadcast needed)
       float sq = 0.f, sk = 0.f, skq = 0.f;
-      for (int i = lane; i < D; i += kWave) {
-        const float qv = y[i], kv = y[D + i];
+      for (int i = lane; i < DK; i += kWave) {
+        const float qv = y[i], kv = y[DK + i];
         sq = fmaf(qv, qv, sq);
         sk = fmaf(kv, kv, sk);
         skq = fmaf(kv, qv, skq);
@@ -226,7 +225,7 @@ void step_kernel(StepArgs p) {
       float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float qn = y[rg * RPT + i] * rq, kn = y[D + rg * RPT + i] * rk;
+        const float qn = y[rg * RPT + i] * rq, kn = y[DK + rg * RPT + i] * rk;
         const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -266,29 +265,29 @@ void step_kernel(StepArgs p) {
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float v = y[2 * D + r * D + 4 * cq + c];
+        const float v = y[2 * DK + r * DV + 4 * cq + c];
         u[c] = beta * (v - decay * hk4[c]);
         o[c] = p.scale * fmaf(kq, u[c], decay * hq4[c]);
         ss = fmaf(o[c], o[c], ss);
       }
       // new state
-      float* dst = p.state_out + (p.verify ? row * SZ : s * SZ) + (long)h * D * D;
+      float* dst = p.state_out + (p.verify ? row * SZ : s * SZ) + (long)h * DK * DV;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float kn = y[D + rg * RPT + i] * rk;
+        const float kn = y[DK + rg * RPT + i] * rk;
         const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
         f32x4 nh;
 #pragma unroll
         for (int c = 0; c < 4; ++c) nh[c] = fmaf(kn, u[c], decay * hv[c]);
         if (i < RR) H[i < RR ? i : 0] = nh;
         else hl_at(i < RR ? 0 : i - RR) = nh;
-        __builtin_nontemporal_store(nh, (f32x4*)(dst + (long)(rg * RPT + i) * D + 4 * cq));
+        __builtin_nontemporal_store(nh, (f32x4*)(dst + (long)(rg * RPT + i) * DV + 4 * cq));
       }
-      // gated RMSNorm over the D columns held by the QD lanes of row group 0
+      // gated RMSNorm over the DV columns held by the QD lanes of row group 0
       ss = wave_sum<QD>(ss);
       if (th < QD) {
-        const float inv = rsqrt_fast(ss / (float)D + p.rms_eps);
-        const long ob = row * (long)n_v * D + (long)h * D;
+        const float inv = rsqrt_fast(ss / (float)DV + p.rms_eps);
+        const long ob = row * (long)n_v * DV + (long)h * DV;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float y = nw[c] * (o[c] * inv) * silu(in.z[c]);
@@ -304,43 +303,50 @@ void step_kernel(StepArgs p) {
 
 // one workgroup per (key head, sequence): many small independent workgroups keep every CU's memory
 // pipe busy, one finishing its stores while the next loads
-template <typename ActT, int D, int R, bool GROUPED>
+template <typename ActT, int DK, int DV, int R, bool GROUPED>
 hipError_t launch_step_r(const StepArgs& p, hipStream_t st) {
-  using S = StepShape<D, R>;
+  using S = StepShape<DK, DV, R>;
   timing_before(p.verify ? "step_verify" : "step_decode", st);
-  hipLaunchKernelGGL((step_kernel<ActT, D, R, GROUPED>), dim3(p.n_k * p.B * p.P), dim3(S::NTH), 0, st, p);
+  hipLaunchKernelGGL((step_kernel<ActT, DK, DV, R, GROUPED>), dim3(p.n_k * p.B * p.P), dim3(S::NTH), 0, st, p);
   timing_after(st);
   return hipGetLastError();
 }
 
 // value heads per workgroup pass: the GQA ratio itself where a shape is built for it (1, 2, 4), else its
 // largest divisor among 4, 2, 1, the workgroup looping over the groups
-template <typename ActT, int D>
+template <typename ActT, int DK, int DV>
 hipError_t launch_step_d(const StepArgs& p, int ratio, hipStream_t st) {
   switch (ratio) {
-    case 1: return launch_step_r<ActT, D, 1, false>(p, st);
-    case 2: return launch_step_r<ActT, D, 2, false>(p, st);
-    case 4: return launch_step_r<ActT, D, 4, false>(p, st);
+    case 1: return launch_step_r<ActT, DK, DV, 1, false>(p, st);
+    case 2: return launch_step_r<ActT, DK, DV, 2, false>(p, st);
+    case 4: return launch_step_r<ActT, DK, DV, 4, false>(p, st);
     default:
-      if (ratio % 4 == 0) return launch_step_r<ActT, D, 4, true>(p, st);
-      if (ratio % 2 == 0) return launch_step_r<ActT, D, 2, true>(p, st);
-      return launch_step_r<ActT, D, 1, true>(p, st);
+      if (ratio % 4 == 0) return launch_step_r<ActT, DK, DV, 4, true>(p, st);
+      if (ratio % 2 == 0) return launch_step_r<ActT, DK, DV, 2, true>(p, st);
+      return launch_step_r<ActT, DK, DV, 1, true>(p, st);
   }
+}
+
+template <typename ActT, int DK>
+hipError_t launch_step_k(const StepArgs& p, int DV, int ratio, hipStream_t st) {
+  if (DV == 32) return launch_step_d<ActT, DK, 32>(p, ratio, st);
+  if (DV == 64) return launch_step_d<ActT, DK, 64>(p, ratio, st);
+  if (DV == 128) return launch_step_d<ActT, DK, 128>(p, ratio, st);
+  return hipErrorInvalidValue;
+}
+
+template <typename ActT>
+hipError_t launch_step_a(const StepArgs& p, int DK, int DV, int ratio, hipStream_t st) {
+  if (DK == 32) return launch_step_k<ActT, 32>(p, DV, ratio, st);
+  if (DK == 64) return launch_step_k<ActT, 64>(p, DV, ratio, st);
+  if (DK == 128) return launch_step_k<ActT, 128>(p, DV, ratio, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_step(const StepArgs& p, int act_dtype, int D, int ratio, hipStream_t st) {
-  if (act_dtype == kActBf16) {
-    if (D == 32) return launch_step_d<bf16_t, 32>(p, ratio, st);
-    if (D == 64) return launch_step_d<bf16_t, 64>(p, ratio, st);
-    if (D == 128) return launch_step_d<bf16_t, 128>(p, ratio, st);
-  } else {
-    if (D == 32) return launch_step_d<float, 32>(p, ratio, st);
-    if (D == 64) return launch_step_d<float, 64>(p, ratio, st);
-    if (D == 128) return launch_step_d<float, 128>(p, ratio, st);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_step(const StepArgs& p, int act_dtype, int DK, int DV, int ratio, hipStream_t st) {
+  return act_dtype == kActBf16 ? launch_step_a<bf16_t>(p, DK, DV, ratio, st) : launch_step_a<float>(p, DK, DV, ratio, st);
 }
 
 }  // namespace gdn

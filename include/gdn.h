@@ -27,13 +27,13 @@
  *    C_ch = 2*n_k*d_k + n_v*d_v with channels ordered [q heads | k heads | v heads], head-major.
  *
  * Status codes: GDN_OK = 0; GDN_EINVAL = -1 (null pointer, non-positive size, inconsistent sizes,
- * workspace too small); GDN_EUNSUPPORTED = -2 (a shape this build has no kernel for: d_k != d_v, d_k
- * not in {32, 64, 128}, conv_k != 4 or n_v not a multiple of n_k; the caller falls back, as the
- * statecache.py page's StateCache falls back to the plain path on _NotCached); GDN_EHIP = -3. The layer
- * definition itself only rules out d_k, d_v outside {32, 64, 128}, conv_k != 4 and n_v % n_k != 0; d_k
- * != d_v is this build's limit. Every GQA ratio n_v / n_k is built; ratios other than 1, 2 and 4 run
- * their value heads 4, 2 or 1 at a time (the largest that divides the ratio), forming the shared q and
- * k once per group. Prefill with fp32 activations carries every MFMA operand as a hi/lo pair up to d =
+ * workspace too small); GDN_EUNSUPPORTED = -2 (a shape outside the layer's definition: d_k or d_v not
+ * in {32, 64, 128}, conv_k != 4 or n_v not a multiple of n_k; the caller falls back, as the
+ * statecache.py page's StateCache falls back to the plain path on _NotCached); GDN_EHIP = -3. Every
+ * pair of head dims is built, d_k != d_v included (prefill then runs the square kernels at max(d_k,
+ * d_v) on zero-padded copies in its workspace, which is exact). Every GQA ratio n_v / n_k is built;
+ * ratios other than 1, 2 and 4 run their value heads 4, 2 or 1 at a time (the largest that divides
+ * the ratio), forming the shared q and k once per group. Prefill with fp32 activations carries every MFMA operand as a hi/lo pair up to d =
  * 64; at d = 128 it uses the operand precisions of bf16 activations (same output and state bounds).
  *
  * Value range (prefill): the chunked prefill carries the state, the write vectors u and the keys and
@@ -61,7 +61,7 @@ enum { GDN_OUT_ACT = 0 };
 /* Layer shape and constants (host struct, read during the call only). */
 typedef struct {
   int32_t n_k, n_v;   /* key heads, value heads; n_v % n_k == 0 */
-  int32_t d_k, d_v;   /* head dims: d_k == d_v, in {32, 64, 128} */
+  int32_t d_k, d_v;   /* head dims, each in {32, 64, 128} */
   int32_t conv_k;     /* conv kernel width; must be 4 */
   int32_t act_dtype;  /* GDN_BF16 or GDN_F32 */
   float scale;        /* q scale; <= 0 selects d_k^-1/2 */
@@ -131,7 +131,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_desc* desc, int B, int Lb);
  *   ws    device workspace of at least gdn_prefill_workspace_bytes(desc, B, Lb) bytes, 256-aligned;
  *         its contents on entry do not matter and are garbage on return; it serves one call at a
  *         time (calls that may overlap, e.g. on two streams, need workspaces of their own)
- * Limits: B <= 65535, Lb * n_v * d_v < 2^31 and B * ceil(Lb / 64) * n_k < 2^31 (GDN_EINVAL otherwise).
+ * Limits: B <= 65535, Lb * n_v * max(d_k, d_v) < 2^31 and B * ceil(Lb / 64) * n_v < 2^31 (GDN_EINVAL
+ * otherwise).
  * Must not alias: out with any input; state or conv_tail with anything else.
  */
 int gdn_prefill_chunk(const gdn_desc* desc, const gdn_weights* w, const void* mixed, const void* z,

@@ -39,13 +39,15 @@ def _desc(**kw):
 
 def test_unsupported_shapes_are_reported():
     lib = gdn.load_library()
-    for kw in (dict(d_k=48, d_v=48), dict(conv_k=3), dict(n_v=6, n_k=4), dict(d_k=64, d_v=32)):
+    for kw in (dict(d_k=48, d_v=48), dict(conv_k=3), dict(n_v=6, n_k=4), dict(d_k=64, d_v=48), dict(d_k=16, d_v=32)):
         d = _desc(**kw)
         rc = lib.gdn_conv_chunk(ctypes.byref(d), None, None, None, None, None, 1, 1, None)
         assert rc == -2, (kw, rc)
         assert lib.gdn_last_error()
-    # every GQA ratio is built (those other than 1, 2, 4 run in groups): the shape passes, the NULL fails
-    for kw in (dict(n_k=1, n_v=8), dict(n_k=2, n_v=6), dict(n_k=1, n_v=3)):
+    # every GQA ratio is built (those other than 1, 2, 4 run in groups), and so is every pair of head dims
+    # in {32, 64, 128}: the shape passes, the NULL fails
+    for kw in (dict(n_k=1, n_v=8), dict(n_k=2, n_v=6), dict(n_k=1, n_v=3), dict(d_k=64, d_v=32),
+               dict(d_k=32, d_v=128), dict(d_k=128, d_v=64)):
         d = _desc(**kw)
         assert lib.gdn_conv_chunk(ctypes.byref(d), None, None, None, None, None, 1, 1, None) == -1, kw
 
@@ -101,6 +103,22 @@ def test_sizes():
         for B in (1, 2, 3, 4, 5, 8):
             sizes = [gdn.prefill_workspace_bytes(dd, B, L) for L in (64, 511, 512, 960, 1024, 1025, 2048, 4096, 8192)]
             assert sizes == sorted(sizes), (dd, B, sizes)
+
+
+def test_sizes_unequal_head_dims():
+    """d_k != d_v: the zero-padded copies at D = max(d_k, d_v) plus the square call's own workspace, which
+    never shrinks as Lb grows, and more than the square layer of the smaller dim needs."""
+    for dk, dv, act_t in ((64, 128, gdn.GDN_BF16), (128, 32, gdn.GDN_BF16), (32, 64, gdn.GDN_F32)):
+        d = gdn.GdnDesc(n_k=2, n_v=4, d_k=dk, d_v=dv, act_dtype=act_t)
+        dm = gdn.GdnDesc(n_k=2, n_v=4, d_k=max(dk, dv), d_v=max(dk, dv), act_dtype=act_t)
+        for B in (1, 3):
+            sizes = [gdn.prefill_workspace_bytes(d, B, L) for L in (1, 64, 65, 300, 1024, 2048)]
+            assert sizes == sorted(sizes) and sizes[0] > 0, (dk, dv, B, sizes)
+            assert all(s % 256 == 0 for s in sizes)
+            # the padded inputs alone: B * L * (2 n_k + n_v) * D activation values
+            esz = 2 if act_t == gdn.GDN_BF16 else 4
+            assert sizes[-1] >= B * 2048 * (2 * 2 + 4) * max(dk, dv) * esz
+            assert sizes[-1] >= gdn.prefill_workspace_bytes(dm, B, 2048)
 
 
 def test_sizes_fused_segments(monkeypatch):

@@ -155,6 +155,42 @@ def test_bucket_padding_bitwise(path, dims, B, n, bucket):
     assert torch.equal(o1, o2), "output bits differ on the real rows"
 
 
+@pytest.mark.parametrize("dims", [LayerDims(n_k=2, n_v=4, d_k=64, d_v=128), LayerDims(n_k=2, n_v=6, d_k=128, d_v=32)])
+def test_unequal_head_dims_padding_bitwise(dims):
+    """Key and value heads of different dims (prefill on zero-padded copies): an all-padding call leaves
+    state and tail bit for bit and writes no output byte; a bucket-padded call ends in the state, tail
+    and real-row output bits of the call of exactly the real length."""
+    B, n, bucket = 2, 100, 128
+    _say(f"unequal head dims padding dims={dims}")
+    w, x, rng = make_layer(25, dims, B, bucket, [n] * B)
+    H0, t0 = random_state(rng, dims, B)
+    d = desc_of(dims)
+    W = weights(w, dims)
+    st = Guarded(dims.state_shape(B), torch.float32, f32(H0))
+    tail = Guarded(dims.tail_shape(B), torch.bfloat16, act(t0, dims))
+    out = Guarded((B, bucket, dims.value_dim), torch.bfloat16)
+    out.t.view(torch.uint8).fill_(0xA5)
+    ins = [act(a, dims) for a in (x.mixed, x.z, x.a, x.b)]
+    gdn.prefill_chunk(d, W, *ins, i32([0] * B), tail.t, st.t, out.t)
+    torch.cuda.synchronize()
+    assert torch.equal(st.t, f32(H0)), "state changed"
+    assert torch.equal(tail.t, act(t0, dims)), "tail changed"
+    assert bool((out.raw == 0xA5).all()), "an all-padding call wrote output"
+    st.check("state")
+    tail.check("tail")
+
+    def run(L):
+        s_, t_ = f32(H0), act(t0, dims)
+        o_ = gdn.prefill_chunk(d, W, *[a[:, :L].contiguous() for a in ins], i32([n] * B), t_, s_)
+        torch.cuda.synchronize()
+        return o_[:, :n], s_, t_
+
+    o1, s1, t1 = run(n)
+    o2, s2, t2 = run(bucket)
+    assert torch.equal(s1, s2) and torch.equal(t1, t2), "state or tail bits differ between exact and bucket call"
+    assert torch.equal(o1, o2), "output bits differ on the real rows"
+
+
 def test_canaries_decode_verify_paths():
     """Decode, verify and tree verify write nothing outside out, the pools and the checkpoint buffers."""
     dims, B, K, P = NEXT, 6, 4, 3

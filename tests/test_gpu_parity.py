@@ -124,6 +124,16 @@ def test_prefill_every_head_shape(D, R, act_t):
     _prefill_case(dims, 8, 2, 150, [150, 67], state_std=0.05, tail_rand=True, paths=paths)
 
 
+@pytest.mark.parametrize("dk,dv,R,act_t", [(64, 128, 2, ACT_BF16), (128, 64, 1, ACT_BF16), (128, 32, 4, ACT_BF16),
+                                           (32, 64, 3, ACT_BF16), (32, 128, 2, ACT_F32), (64, 32, 1, ACT_F32)])
+def test_prefill_unequal_head_dims(dk, dv, R, act_t):
+    """Key and value heads of different dims (the square kernels at max(d_k, d_v) on zero-padded copies):
+    ragged multi-chunk sequences from a non-zero state and tail, outputs in the activation dtype and in
+    fp32, state and tail against the oracle, canaries around every output."""
+    dims = LayerDims(n_k=2, n_v=2 * R, d_k=dk, d_v=dv, act=act_t)
+    _prefill_case(dims, 21, 2, 150, [150, 67], state_std=0.05, tail_rand=True)
+
+
 def test_prefill_fp32_multichunk():
     dims = LayerDims(n_k=2, n_v=4, d_k=64, d_v=64, act=ACT_F32)
     _prefill_case(dims, 4, 2, 200, [200, 129], state_std=0.05, tail_rand=True)
@@ -212,7 +222,8 @@ def test_continuation_equals_single_pass():
 
 # the kernel walks 64-token spans in 8-token groups: 203 and 131 tokens end mid-group in a later span
 @pytest.mark.parametrize("dims,B,L,lens", [(TINY, 1, 64, [64]), (NEXT, 3, 70, [70, 2, 0]), (SMALL, 2, 33, [33, 17]),
-                                           (SMALL, 2, 203, [203, 130]), (NEXT, 3, 131, [131, 1, 64])])
+                                           (SMALL, 2, 203, [203, 130]), (NEXT, 3, 131, [131, 1, 64]),
+                                           (LayerDims(n_k=2, n_v=4, d_k=32, d_v=128), 2, 100, [100, 37])])
 def test_conv_chunk(dims, B, L, lens):
     _say(f"conv B={B} L={L}")
     w, x, rng = make_layer(7, dims, B, L, lens)
@@ -249,7 +260,10 @@ def _decode_inputs(dims, rng, B, T):
                                     (LayerDims(n_k=2, n_v=4, d_k=32, d_v=32, act=ACT_F32), 2),
                                     (LayerDims(n_k=2, n_v=6, d_k=64, d_v=64), 3),
                                     (LayerDims(n_k=1, n_v=8, d_k=128, d_v=128), 4),
-                                    (LayerDims(n_k=2, n_v=12, d_k=32, d_v=32, act=ACT_F32), 2)])
+                                    (LayerDims(n_k=2, n_v=12, d_k=32, d_v=32, act=ACT_F32), 2),
+                                    (LayerDims(n_k=2, n_v=4, d_k=64, d_v=128), 3),
+                                    (LayerDims(n_k=2, n_v=8, d_k=128, d_v=32, act=ACT_F32), 2),
+                                    (LayerDims(n_k=1, n_v=3, d_k=32, d_v=64), 2)])
 @pytest.mark.parametrize("out_f32", [False, True])
 def test_decode_step_vs_oracle(dims, B, out_f32):
     _say(f"decode B={B} dims={dims} out_f32={out_f32}")
@@ -389,11 +403,13 @@ def test_verify_checkpoints_and_commit():
     assert_state_close(host(sp), ref["ckpt_H"][np.arange(B), m_ref])
 
 
-@pytest.mark.parametrize("dims", [LayerDims(n_k=2, n_v=16, d_k=128, d_v=128), LayerDims(n_k=2, n_v=6, d_k=64, d_v=64)])
+@pytest.mark.parametrize("dims", [LayerDims(n_k=2, n_v=16, d_k=128, d_v=128), LayerDims(n_k=2, n_v=6, d_k=64, d_v=64),
+                                  LayerDims(n_k=2, n_v=4, d_k=128, d_v=64), LayerDims(n_k=2, n_v=6, d_k=32, d_v=128)])
 def test_verify_grouped_gqa_ratio(dims):
-    """GQA ratios the kernels run in groups (8: four value heads at a time, 3: one): verify against the
-    oracle, and every checkpoint bitwise equal to repeated in-place decode, which only holds if every
-    group reads the conv tail's q and k rows before the last group writes them."""
+    """GQA ratios the kernels run in groups (8: four value heads at a time, 3: one), and key and value
+    heads of different dims: verify against the oracle, and every checkpoint bitwise equal to repeated
+    in-place decode, which only holds if every group reads the conv tail's q and k rows before the last
+    group writes them."""
     B, K = 5, 4
     T = K + 1
     _say(f"verify grouped ratio dims={dims}")
@@ -521,8 +537,9 @@ def test_accept_exhaustive():
     np.testing.assert_array_equal(ne.cpu().numpy(), ne_ref)
 
 
-def test_state_copy_gather_scatter():
-    dims = NEXT
+@pytest.mark.parametrize("dims", [NEXT, LayerDims(n_k=2, n_v=6, d_k=64, d_v=32)])
+def test_state_copy_gather_scatter(dims):
+    _say(f"state copy dims={dims}")
     d = desc_of(dims)
     rng = np.random.default_rng(10)
     n_src, n_dst, n = 7, 9, 5
