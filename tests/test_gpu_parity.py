@@ -642,6 +642,91 @@ def test_continuation_graph_replay_equals_eager():
         assert torch.equal(state, ref_state) and torch.equal(tail, ref_tail), f"replay {rep}: state differs"
 
 
+def test_speculative_step_graph_replay_equals_eager():
+    """One serving step captured once into a HIP graph: verify 1+K tokens from the pool rows, accept on the
+    device, commit the accepted checkpoints into the pool by the device-side checkpoint index, then one
+    decode step from the committed rows. Before each of three replays the static inputs get new tokens,
+    drafts and predictions (eager copies) and the pools their starting rows; every replay matches an eager
+    run of the same calls on the same inputs bit for bit (pools, checkpoints, outputs, accepted lengths)."""
+    dims, B, K = NEXT, 8, 4
+    T = K + 1
+    _say("speculative step graph replay")
+    w, _, rng = make_layer(64, dims, 1, 1)
+    d = desc_of(dims)
+    W = weights(w, dims)
+    npool = B + 4
+    slots = i32(rng.permutation(npool)[:B])
+    H0, T0 = random_state(rng, dims, npool)
+    pool0_s, pool0_t = f32(H0), act(T0, dims)
+    pool_s, pool_t = pool0_s.clone(), pool0_t.clone()
+
+    def draw(seed):
+        r = np.random.default_rng(seed)
+        x = _decode_inputs(dims, r, B, T + 1)   # the verify tokens, then the token decoded after the commit
+        dr = r.integers(0, 3, size=(B, K)).astype(np.int32)
+        pr = r.integers(0, 3, size=(B, K + 1)).astype(np.int32)
+        return [act(a, dims) for a in (x.mixed, x.z, x.a, x.b)], i32(dr), i32(pr)
+
+    ins0, dr0, pr0 = draw(100)
+    mx, zz, aa, bb = [t.clone() for t in ins0]
+    drafts, preds = dr0.clone(), pr0.clone()
+    ck_s = torch.empty(B, T, dims.n_v, dims.d_k, dims.d_v, dtype=torch.float32, device="cuda")
+    ck_t = torch.empty(B, T, 3, dims.conv_dim, dtype=torch.bfloat16, device="cuda")
+    out_v = torch.empty(B, T, dims.value_dim, dtype=torch.bfloat16, device="cuda")
+    out_d = torch.empty(B, dims.value_dim, dtype=torch.bfloat16, device="cuda")
+    vin = [t[:, :T] for t in (mx, zz, aa, bb)]          # views into the static inputs
+    din = [t[:, T] for t in (mx, zz, aa, bb)]
+    res = {}
+
+    def step():
+        gdn.verify_with_checkpoints(d, W, *[v.contiguous() for v in vin], slots, pool_t, pool_s, ck_s, ck_t, out_v)
+        m, em, ne, ci = gdn.accept(drafts, preds)
+        gdn.state_copy(d, pool_s, pool_t, slots, ck_s, ck_t, ci, B)
+        gdn.decode_step(d, W, *[v.contiguous() for v in din], slots, pool_t, pool_s, out_d)
+        res.update(m=m, ci=ci)
+
+    def snapshot():
+        return [t.clone() for t in (pool_s, pool_t, ck_s, ck_t, out_v, out_d, res["m"], res["ci"])]
+
+    names = ("state pool", "tail pool", "checkpoint states", "checkpoint tails", "verify out", "decode out", "m",
+             "checkpoint index")
+    refs = []
+    for rep in range(3):
+        ins, dr, pr = draw(200 + rep)
+        for dst, src in zip((mx, zz, aa, bb, drafts, preds), (*ins, dr, pr)):
+            dst.copy_(src)
+        pool_s.copy_(pool0_s)
+        pool_t.copy_(pool0_t)
+        step()
+        torch.cuda.synchronize()
+        refs.append(snapshot())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ins, dr, pr = draw(200 + rep)
+        for dst, src in zip((mx, zz, aa, bb, drafts, preds), (*ins, dr, pr)):
+            dst.copy_(src)
+        pool_s.copy_(pool0_s)
+        pool_t.copy_(pool0_t)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip(snapshot(), refs[rep], names):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager step"
+    # the eager steps themselves: accepted lengths as the oracle's accept rule gives them
+    for rep in range(3):
+        _, dr, pr = draw(200 + rep)
+        m_ref = oracle.accept(dr.cpu().numpy(), pr.cpu().numpy())[0]
+        assert np.array_equal(refs[rep][6].cpu().numpy(), m_ref), f"step {rep}: m"
+
+
 def test_split_exchange_graph_replay_equals_eager():
     """Two continued 1100-token calls on 2 sequences of a 16/32-head layer (64 pairs: 32-column slices)
     captured once into a HIP graph. Eagerly the slices exchange their partial row sums (a cooperative
