@@ -68,6 +68,8 @@ def test_noalloc_prefill_two_calls():
     _case(lib, SMALL, 31, 1, 4096, [4096])
     # then a smaller call on the same scratch: three ragged sequences, 2/4 heads, the two-launch path
     _case(lib, LayerDims(n_k=2, n_v=4, d_k=128, d_v=128), 32, 3, 300, [300, 171, 0])
+    # and a smaller one again with key and value heads of different dims (zero-padded copies in the scratch)
+    _case(lib, LayerDims(n_k=2, n_v=4, d_k=64, d_v=128), 33, 2, 150, [150, 67])
     # a call whose workspace exceeds the scratch and has no fused path is refused before any launch
     d = desc_of(LayerDims(n_k=16, n_v=64, d_k=64, d_v=64))
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(d.c()), 4, 8192) > (64 << 20)
