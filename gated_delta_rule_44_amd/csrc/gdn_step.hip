@@ -90,213 +90,226 @@ void step_kernel(StepArgs p) {
   const ActT* bin = (const ActT*)p.b;
   ActT* out = (ActT*)p.out;
 
-  auto slot_of = [&](int item) { const int b = item / n_k / p.P; return p.slot ? (long)p.slot[b] : (long)b; };
-  // this thread's block of value head h's state: rows rg*RPT + i, columns 4 cq .. 4 cq + 3
-  auto state_src = [&](int item, int h) {
-    return p.state_in + slot_of(item) * SZ + (long)h * DK * DV + (long)(rg * RPT) * DV + 4 * cq;
+  // pool row of an item: slot[b], read through the constant address space (the slot map is not written
+  // during the call), so that it is a scalar load, which no vector-memory wait has to drain
+  auto slot_of = [&](int item) {
+    const int b = item / n_k / p.P;
+    typedef const __attribute__((address_space(4))) int32_t* const_i32;
+    return p.slot ? (long)((const_i32)p.slot)[b] : (long)b;
   };
   // row RR + j of this thread's block in LDS
   auto hl_at = [&](int j) -> f32x4& { return sHL[((r * S::RG + rg) * (RL > 0 ? RL : 1) + j) * QD + cq]; };
-  auto load_H = [&](f32x4 (&H)[RR], int item, int h) {
-    const float* src = state_src(item, h);
+  // this thread's block of value head h's state in pool row s: rows rg*RPT + i, columns 4 cq .. 4 cq + 3
+  auto load_H = [&](f32x4 (&H)[RR], long s, int h) __attribute__((always_inline)) {
+    const float* src = p.state_in + s * SZ + (long)h * DK * DV + (long)(rg * RPT) * DV + 4 * cq;
 #pragma unroll
     for (int i = 0; i < RR; ++i) H[i] = __builtin_nontemporal_load((const f32x4*)(src + (long)i * DV));
 #pragma unroll
     for (int j = 0; j < RL; ++j) hl_at(j) = __builtin_nontemporal_load((const f32x4*)(src + (long)(RR + j) * DV));
   };
 
+  // the conv state of the channels a thread owns in one group of an item: q and k channels of key
+  // head kh, v channels of value heads vb .. vb + R - 1 (gc = -1 for an unowned slot), their taps and
+  // the three tail rows
+  struct Conv {
+    int gch[CPT];
+    float w0[CPT], w1[CPT], w2[CPT], w3[CPT], t0[CPT], t1[CPT], t2[CPT];
+  };
   // per-token activations of one item, loaded ahead of use
   struct TokIn {
     float x[CPT];   // pre-conv inputs of the owned channels
     float av, bv;   // gate inputs of this thread's head
     float z[4];     // z of this thread's output columns (row group 0 only)
   };
-  float nw[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) nw[c] = p.norm_w[4 * cq + c];
-
-  f32x4 H[RR];
-  {
-    const int item = blockIdx.x;
-    const int kh = item % n_k, bp = item / n_k;  // row: sequence bp / P, path bp % P
-    const long s = slot_of(item);
-    const ActT* tail_in = (const ActT*)p.tail_in + s * TZ;
-    // With more value heads per key head than one workgroup holds (R of the n_v / n_k), the workgroup
-    // takes them R at a time, forming q and k again for each group. The q and k channels of the conv
-    // tail are written by the last group only: decode updates the tail in place, and every group reads
-    // the old rows.
-    const int RQ = GROUPED ? n_v / n_k : R, ngroups = GROUPED ? RQ / R : 1;
-    int par = 0;  // parity of the token over all groups: selects the conv output buffer
-    for (int grp = 0; grp < ngroups; ++grp) {
-    const int h = kh * RQ + grp * R + r;
-    const bool qk_tail = grp + 1 == ngroups;
-
-    // The group's small inputs are loaded before its state: loads complete in issue order, so
-    // anything issued after the state would wait for all of it.
-    int gch[CPT];
-    float w0[CPT], w1[CPT], w2[CPT], w3[CPT], t0[CPT], t1[CPT], t2[CPT];
+  auto load_conv = [&](Conv& cv, int kh, int vb, const ActT* tail_in) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int lc = tid + j * NTH;
       int gc = -1;
       if (lc < DK) gc = kh * DK + lc;
       else if (lc < 2 * DK) gc = n_k * DK + kh * DK + (lc - DK);
-      else if (lc < NCH) gc = 2 * n_k * DK + (kh * RQ + grp * R) * DV + (lc - 2 * DK);
-      gch[j] = gc;
+      else if (lc < NCH) gc = 2 * n_k * DK + vb * DV + (lc - 2 * DK);
+      cv.gch[j] = gc;
       const int gl = gc >= 0 ? gc : 0;  // unconditional loads (a clamped channel for unowned slots)
-      w0[j] = to_f32(conv_w[gl * 4 + 0]);
-      w1[j] = to_f32(conv_w[gl * 4 + 1]);
-      w2[j] = to_f32(conv_w[gl * 4 + 2]);
-      w3[j] = to_f32(conv_w[gl * 4 + 3]);
-      t0[j] = to_f32(tail_in[0L * C + gl]);
-      t1[j] = to_f32(tail_in[1L * C + gl]);
-      t2[j] = to_f32(tail_in[2L * C + gl]);
+      cv.w0[j] = to_f32(conv_w[gl * 4 + 0]);
+      cv.w1[j] = to_f32(conv_w[gl * 4 + 1]);
+      cv.w2[j] = to_f32(conv_w[gl * 4 + 2]);
+      cv.w3[j] = to_f32(conv_w[gl * 4 + 3]);
+      cv.t0[j] = to_f32(tail_in[0L * C + gl]);
+      cv.t1[j] = to_f32(tail_in[1L * C + gl]);
+      cv.t2[j] = to_f32(tail_in[2L * C + gl]);
     }
-    const float A = -__expf(p.A_log[h]), dtb = p.dt_bias[h];
-    auto load_tok = [&](TokIn& in, int t) {
-      const long row = (long)bp * p.T + t;
+  };
+  auto load_tok = [&](TokIn& in, const Conv& cv, long row, int h) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) in.x[j] = to_f32(mixed[row * C + (gch[j] >= 0 ? gch[j] : 0)]);
-      in.av = to_f32(ain[row * n_v + h]);
-      in.bv = to_f32(bin[row * n_v + h]);
+    for (int j = 0; j < CPT; ++j) in.x[j] = to_f32(mixed[row * C + (cv.gch[j] >= 0 ? cv.gch[j] : 0)]);
+    in.av = to_f32(ain[row * n_v + h]);
+    in.bv = to_f32(bin[row * n_v + h]);
+    const long ob = row * (long)n_v * DV + (long)h * DV;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) in.z[c] = to_f32(zin[ob + 4 * cq + c]);
+  };
+  float nw[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) nw[c] = p.norm_w[4 * cq + c];
+
+  // One token of value head h (this thread's): conv + SiLU of the owned channels and their tail rows
+  // (to tail_to), the q/k norms and gates, the step on H, the new state (to dst, this head's block of
+  // a record) and the output row `row`. Decode and verify run this same code, so a verify checkpoint
+  // is bitwise what the decode calls produce.
+  auto token = [&](f32x4 (&H)[RR], Conv& cv, const TokIn& in, float A, float dtb, int h, long row, ActT* tail_to,
+                   float* dst, bool qk_tail, int& par) __attribute__((always_inline)) {
+    float* const y = sY[par];
+    // ---- conv + SiLU on the owned channels, tail shift
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int gc = cv.gch[j];
+      const float x = in.x[j];
+      if (gc >= 0) {
+        float pre = cv.w0[j] * cv.t0[j];
+        pre = fmaf(cv.w1[j], cv.t1[j], pre);
+        pre = fmaf(cv.w2[j], cv.t2[j], pre);
+        pre = fmaf(cv.w3[j], x, pre);
+        y[tid + j * NTH] = silu(pre);
+        cv.t0[j] = cv.t1[j];
+        cv.t1[j] = cv.t2[j];
+        cv.t2[j] = x;
+      }
+    }
+    // tail after this token: decode writes the pool row, verify the checkpoint row
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int gc = cv.gch[j];
+      if (gc >= 0 && (qk_tail || tid + j * NTH >= 2 * DK)) {
+        tail_to[0L * C + gc] = from_f32<ActT>(cv.t0[j]);
+        tail_to[1L * C + gc] = from_f32<ActT>(cv.t1[j]);
+        tail_to[2L * C + gc] = from_f32<ActT>(cv.t2[j]);
+      }
+    }
+    const float decay = __expf(A * softplus(in.av + dtb));
+    const float beta = sigmoid(in.bv);
+    lds_barrier();
+
+    // ---- q/k L2 norm and k.q (every wave computes them, no broadcast needed)
+    float sq = 0.f, sk = 0.f, skq = 0.f;
+    for (int i = lane; i < DK; i += kWave) {
+      const float qv = y[i], kv = y[DK + i];
+      sq = fmaf(qv, qv, sq);
+      sk = fmaf(kv, kv, sk);
+      skq = fmaf(kv, qv, skq);
+    }
+    sq = wave_sum<kWave>(sq);
+    sk = wave_sum<kWave>(sk);
+    skq = wave_sum<kWave>(skq);
+    const float rq = rsqrt_fast(sq + p.l2_eps);
+    const float rk = rsqrt_fast(sk + p.l2_eps);
+    const float kq = (skq * rk) * rq;  // k^ . q^
+
+    // column partial sums of H^T k and H^T q over this thread's rows (q and k re-read from LDS
+    // where used, which keeps the register footprint to the state blocks)
+    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float qn = y[rg * RPT + i] * rq, kn = y[DK + rg * RPT + i] * rk;
+      const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pk[c] = fmaf(hv[c], kn, pk[c]);
+        pq[c] = fmaf(hv[c], qn, pq[c]);
+      }
+    }
+    // across the row groups inside the wave (lanes with the same column quad)
+#pragma unroll
+    for (int off = QD; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pk[c] = pk[c] + __shfl_xor(pk[c], off, kWave);
+        pq[c] = pq[c] + __shfl_xor(pq[c], off, kWave);
+      }
+    }
+    if (lane < QD) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sRed[r][hw][0][4 * cq + c] = pk[c];
+        sRed[r][hw][1][4 * cq + c] = pq[c];
+      }
+    }
+    lds_barrier();
+    // H^T k and H^T q on this thread's four columns: the head's wave partials, summed in wave order
+    f32x4 hk4 = *(const f32x4*)&sRed[r][0][0][4 * cq], hq4 = *(const f32x4*)&sRed[r][0][1][4 * cq];
+#pragma unroll
+    for (int ww = 1; ww < HW; ++ww) {
+      const f32x4 pk4 = *(const f32x4*)&sRed[r][ww][0][4 * cq], pq4 = *(const f32x4*)&sRed[r][ww][1][4 * cq];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        hk4[c] = hk4[c] + pk4[c];
+        hq4[c] = hq4[c] + pq4[c];
+      }
+    }
+    float u[4], o[4];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float v = y[2 * DK + r * DV + 4 * cq + c];
+      u[c] = beta * (v - decay * hk4[c]);
+      o[c] = p.scale * fmaf(kq, u[c], decay * hq4[c]);
+      ss = fmaf(o[c], o[c], ss);
+    }
+    // new state
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float kn = y[DK + rg * RPT + i] * rk;
+      const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
+      f32x4 nh;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) nh[c] = fmaf(kn, u[c], decay * hv[c]);
+      if (i < RR) H[i < RR ? i : 0] = nh;
+      else hl_at(i < RR ? 0 : i - RR) = nh;
+      __builtin_nontemporal_store(nh, (f32x4*)(dst + (long)(rg * RPT + i) * DV + 4 * cq));
+    }
+    // gated RMSNorm over the DV columns held by the QD lanes of row group 0
+    ss = wave_sum<QD>(ss);
+    if (th < QD) {
+      const float inv = rsqrt_fast(ss / (float)DV + p.rms_eps);
       const long ob = row * (long)n_v * DV + (long)h * DV;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) in.z[c] = to_f32(zin[ob + 4 * cq + c]);
-    };
-    TokIn cur;
-    load_tok(cur, 0);
-    load_H(H, item, h);
+      for (int c = 0; c < 4; ++c) {
+        const float yv = nw[c] * (o[c] * inv) * silu(in.z[c]);
+        if (p.out_f32) ((float*)p.out)[ob + 4 * cq + c] = yv;
+        else out[ob + 4 * cq + c] = from_f32<ActT>(yv);
+      }
+    }
+    par ^= 1;
+  };
 
+  int par = 0;  // parity of the token over every token the workgroup runs: selects the conv output buffer
+  f32x4 H[RR];
+  const int item = blockIdx.x;
+  const int kh = item % n_k, bp = item / n_k;  // row: sequence bp / P, path bp % P
+  const long s = slot_of(item);
+  const ActT* tail_in = (const ActT*)p.tail_in + s * TZ;
+  // With more value heads per key head than one workgroup holds (R of the n_v / n_k), the workgroup
+  // takes them R at a time, forming q and k again for each group. The q and k channels of the conv
+  // tail are written by the last group only: decode updates the tail in place, and every group reads
+  // the old rows.
+  const int RQ = GROUPED ? n_v / n_k : R, ngroups = GROUPED ? RQ / R : 1;
+  for (int grp = 0; grp < ngroups; ++grp) {
+    const int h = kh * RQ + grp * R + r;
+    const bool qk_tail = grp + 1 == ngroups;
+    // The group's small inputs are loaded before its state: loads complete in issue order, so
+    // anything issued after the state would wait for all of it.
+    Conv cv;
+    load_conv(cv, kh, kh * RQ + grp * R, tail_in);
+    const float A = -__expf(p.A_log[h]), dtb = p.dt_bias[h];
+    TokIn cur;
+    load_tok(cur, cv, (long)bp * p.T, h);
+    load_H(H, s, h);
     for (int t = 0; t < p.T; ++t) {
       const long row = (long)bp * p.T + t;
       TokIn in = cur;
-      if (t + 1 < p.T) load_tok(cur, t + 1);  // verify only
-      float* const y = sY[par];
-      // ---- conv + SiLU on the owned channels, tail shift
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int gc = gch[j];
-        const float x = in.x[j];
-        if (gc >= 0) {
-          float pre = w0[j] * t0[j];
-          pre = fmaf(w1[j], t1[j], pre);
-          pre = fmaf(w2[j], t2[j], pre);
-          pre = fmaf(w3[j], x, pre);
-          y[tid + j * NTH] = silu(pre);
-          t0[j] = t1[j];
-          t1[j] = t2[j];
-          t2[j] = x;
-        }
-      }
-      // tail after this token: decode writes the pool row, verify the checkpoint row
-      {
-        ActT* to = (ActT*)p.tail_out + (p.verify ? row * TZ : s * TZ);
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-          const int gc = gch[j];
-          if (gc >= 0 && (qk_tail || tid + j * NTH >= 2 * DK)) {
-            to[0L * C + gc] = from_f32<ActT>(t0[j]);
-            to[1L * C + gc] = from_f32<ActT>(t1[j]);
-            to[2L * C + gc] = from_f32<ActT>(t2[j]);
-          }
-        }
-      }
-      const float decay = __expf(A * softplus(in.av + dtb));
-      const float beta = sigmoid(in.bv);
-      lds_barrier();
-
-      // ---- q/k L2 norm and k.q (every wave computes them, no broadcast needed)
-      float sq = 0.f, sk = 0.f, skq = 0.f;
-      for (int i = lane; i < DK; i += kWave) {
-        const float qv = y[i], kv = y[DK + i];
-        sq = fmaf(qv, qv, sq);
-        sk = fmaf(kv, kv, sk);
-        skq = fmaf(kv, qv, skq);
-      }
-      sq = wave_sum<kWave>(sq);
-      sk = wave_sum<kWave>(sk);
-      skq = wave_sum<kWave>(skq);
-      const float rq = rsqrt_fast(sq + p.l2_eps);
-      const float rk = rsqrt_fast(sk + p.l2_eps);
-      const float kq = (skq * rk) * rq;  // k^ . q^
-
-      // column partial sums of H^T k and H^T q over this thread's rows (q and k re-read from LDS
-      // where used, which keeps the register footprint to the state blocks)
-      float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const float qn = y[rg * RPT + i] * rq, kn = y[DK + rg * RPT + i] * rk;
-        const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          pk[c] = fmaf(hv[c], kn, pk[c]);
-          pq[c] = fmaf(hv[c], qn, pq[c]);
-        }
-      }
-      // across the row groups inside the wave (lanes with the same column quad)
-#pragma unroll
-      for (int off = QD; off < kWave; off <<= 1) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          pk[c] = pk[c] + __shfl_xor(pk[c], off, kWave);
-          pq[c] = pq[c] + __shfl_xor(pq[c], off, kWave);
-        }
-      }
-      if (lane < QD) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          sRed[r][hw][0][4 * cq + c] = pk[c];
-          sRed[r][hw][1][4 * cq + c] = pq[c];
-        }
-      }
-      lds_barrier();
-      // H^T k and H^T q on this thread's four columns: the head's wave partials, summed in wave order
-      f32x4 hk4 = *(const f32x4*)&sRed[r][0][0][4 * cq], hq4 = *(const f32x4*)&sRed[r][0][1][4 * cq];
-#pragma unroll
-      for (int ww = 1; ww < HW; ++ww) {
-        const f32x4 pk4 = *(const f32x4*)&sRed[r][ww][0][4 * cq], pq4 = *(const f32x4*)&sRed[r][ww][1][4 * cq];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          hk4[c] = hk4[c] + pk4[c];
-          hq4[c] = hq4[c] + pq4[c];
-        }
-      }
-      float u[4], o[4];
-      float ss = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float v = y[2 * DK + r * DV + 4 * cq + c];
-        u[c] = beta * (v - decay * hk4[c]);
-        o[c] = p.scale * fmaf(kq, u[c], decay * hq4[c]);
-        ss = fmaf(o[c], o[c], ss);
-      }
-      // new state
-      float* dst = p.state_out + (p.verify ? row * SZ : s * SZ) + (long)h * DK * DV;
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const float kn = y[DK + rg * RPT + i] * rk;
-        const f32x4 hv = i < RR ? H[i < RR ? i : 0] : hl_at(i < RR ? 0 : i - RR);
-        f32x4 nh;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) nh[c] = fmaf(kn, u[c], decay * hv[c]);
-        if (i < RR) H[i < RR ? i : 0] = nh;
-        else hl_at(i < RR ? 0 : i - RR) = nh;
-        __builtin_nontemporal_store(nh, (f32x4*)(dst + (long)(rg * RPT + i) * DV + 4 * cq));
-      }
-      // gated RMSNorm over the DV columns held by the QD lanes of row group 0
-      ss = wave_sum<QD>(ss);
-      if (th < QD) {
-        const float inv = rsqrt_fast(ss / (float)DV + p.rms_eps);
-        const long ob = row * (long)n_v * DV + (long)h * DV;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float y = nw[c] * (o[c] * inv) * silu(in.z[c]);
-          if (p.out_f32) ((float*)p.out)[ob + 4 * cq + c] = y;
-          else out[ob + 4 * cq + c] = from_f32<ActT>(y);
-        }
-      }
-      par ^= 1;
-    }
+      if (t + 1 < p.T) load_tok(cur, cv, row + 1, h);  // verify only
+      token(H, cv, in, A, dtb, h, row, (ActT*)p.tail_out + (p.verify ? row * TZ : s * TZ),
+            p.state_out + (p.verify ? row * SZ : s * SZ) + (long)h * DK * DV, qk_tail, par);
     }
   }
 }
