@@ -43,6 +43,7 @@
 // carry exact power-of-two scales: 2^8 for q, k, H, U, A, T, right-hand sides; 2^16 for P, whose
 // entries span many decades. Accumulators: H as 2^16 H, K H and U as 2^16, O^T as 2^24 O^T.
 // The scales bound what the operands can hold: |H| and |U| must stay below 255.
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -946,14 +947,18 @@ size_t fused_ws_bytes(int B, int n_v, int Lb) {
 }
 
 hipError_t launch_fused(FusedArgs p, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the dynamic LDS limit of the three instantiations, raised once per device (thread-safe)
+  static std::once_flag once[64];
+  static hipError_t attr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
     hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<MODE_OUT>, hipFuncAttributeMaxDynamicSharedMemorySize, L_END);
     if (e == hipSuccess) e = hipFuncSetAttribute((const void*)fused_kernel<MODE_MAP_N>, hipFuncAttributeMaxDynamicSharedMemorySize, L_END);
     if (e == hipSuccess) e = hipFuncSetAttribute((const void*)fused_kernel<MODE_MAP_M>, hipFuncAttributeMaxDynamicSharedMemorySize, L_END);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    attr[dev] = e;
+  });
+  if (attr[dev] != hipSuccess) return attr[dev];
   const int units = p.B * p.n_v;
   if (p.nseg > 1) {
     p.seg_map = (float*)p.ws;
