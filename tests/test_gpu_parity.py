@@ -134,6 +134,49 @@ def test_prefill_unequal_head_dims(dk, dv, R, act_t):
     _prefill_case(dims, 21, 2, 150, [150, 67], state_std=0.05, tail_rand=True)
 
 
+def _random_shape(seed):
+    """A seeded layer shape and call: head dims from {32, 64, 128} (equal or drawn apart), GQA ratio
+    1-4, one or two key heads, bf16 or fp32 activations, 1-3 sequences of ragged lengths (some empty)."""
+    r = np.random.default_rng(1000 + seed)
+    n_k, d_k = int(r.integers(1, 3)), int(r.choice([32, 64, 128]))
+    d_v = d_k if r.random() < 0.4 else int(r.choice([32, 64, 128]))
+    dims = LayerDims(n_k=n_k, n_v=n_k * int(r.integers(1, 5)), d_k=d_k, d_v=d_v,
+                     act=ACT_F32 if r.random() < 0.3 else ACT_BF16)
+    B = int(r.integers(1, 4))
+    L = int(r.integers(1, 300))
+    lens = [int(v) for v in r.integers(0, L + 1, size=B)]
+    lens[int(r.integers(0, B))] = L
+    return dims, B, L, lens
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_random_shapes(seed):
+    """Seeded random shapes and ragged calls through prefill (both paths where the fused one is built),
+    from a non-zero state and tail, against the oracle."""
+    dims, B, L, lens = _random_shape(seed)
+    paths = BOTH if dims.d_k == dims.d_v == 128 and dims.act == ACT_BF16 else (None,)
+    _prefill_case(dims, 50 + seed, B, L, lens, state_std=0.05, tail_rand=True, paths=paths)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_random_shapes(seed):
+    """The same random shapes through decode, from saved states, against the oracle."""
+    dims, B, _, _ = _random_shape(seed)
+    _say(f"decode random seed={seed} B={B} dims={dims}")
+    w, _, rng = make_layer(60 + seed, dims, 1, 1)
+    H0, T0 = _saved_states(dims, w, rng, B)
+    x = _decode_inputs(dims, rng, B, 1)
+    d = desc_of(dims, True)
+    sp, tp = f32(H0), act(T0, dims)
+    out = gdn.decode_step(d, weights(w, dims), act(x.mixed[:, 0], dims), act(x.z[:, 0], dims),
+                          act(x.a[:, 0], dims), act(x.b[:, 0], dims), None, tp, sp)
+    torch.cuda.synchronize()
+    ref = oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, None, T0, H0)
+    assert_out_flat(host(out), ref["out"][:, 0], "decode fp32 out")
+    assert_state_close(host(sp), ref["H"])
+    np.testing.assert_array_equal(host(tp), ref["tail"].astype(np.float32))
+
+
 def test_prefill_fp32_multichunk():
     dims = LayerDims(n_k=2, n_v=4, d_k=64, d_v=64, act=ACT_F32)
     _prefill_case(dims, 4, 2, 200, [200, 129], state_std=0.05, tail_rand=True)
