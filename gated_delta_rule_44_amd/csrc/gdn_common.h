@@ -121,4 +121,15 @@ __device__ __forceinline__ void split2_f16(float x0, float x1, f16x2& hi, f16x2&
   lo = __builtin_convertvector(f32x2_t{x0 - back[0], x1 - back[1]}, f16x2);
 }
 
+// Streamed 16-byte store through a buffer descriptor over [base, base + range) bytes (offsets past the
+// range are dropped by the hardware, never written), with the non-temporal and system-scope cache bits.
+// For the write-heavy state streams (decode's in-place state, verify's checkpoints) this measured 4-9%
+// faster than a non-temporal global store, and a plain global store slower than both.
+constexpr int kCpolStream = 2 | 16;  // nt | sc1
+__device__ __forceinline__ void store_stream16(void* base, uint32_t range, uint32_t byte_off, f32x4 v) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)range, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, byte_off, 0, kCpolStream);
+}
+
 }  // namespace gdn

@@ -265,7 +265,7 @@ void step_kernel(StepArgs p) {
       for (int c = 0; c < 4; ++c) nh[c] = fmaf(kn, u[c], decay * hv[c]);
       if (i < RR) H[i < RR ? i : 0] = nh;
       else hl_at(i < RR ? 0 : i - RR) = nh;
-      __builtin_nontemporal_store(nh, (f32x4*)(dst + (long)(rg * RPT + i) * DV + 4 * cq));
+      store_stream16(dst, DK * DV * 4, ((rg * RPT + i) * DV + 4 * cq) * 4, nh);
     }
     // gated RMSNorm over the DV columns held by the QD lanes of row group 0
     ss = wave_sum<QD>(ss);
