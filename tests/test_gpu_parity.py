@@ -177,6 +177,41 @@ def test_decode_random_shapes(seed):
     np.testing.assert_array_equal(host(tp), ref["tail"].astype(np.float32))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_verify_paths_random_shapes(seed):
+    """The random shapes through tree verify: 1-3 paths of 1+K tokens (K from 1 to 4) per sequence from
+    permuted pool rows, fp32 outputs at the flat bound and every checkpoint against the oracle, the pool
+    untouched, and the paths' shared first token leaving every path in the same bits."""
+    dims, B, _, _ = _random_shape(seed)
+    r = np.random.default_rng(2000 + seed)
+    P, K = int(r.integers(1, 4)), int(r.integers(1, 5))
+    T = K + 1
+    _say(f"verify paths random seed={seed} B={B} P={P} K={K} dims={dims}")
+    w, _, rng = make_layer(70 + seed, dims, 1, 1)
+    H0, T0 = _saved_states(dims, w, rng, B)
+    x = path_inputs(rng, dims, B, P, T)
+    d = desc_of(dims, True)
+    npool = B + 2
+    slots = rng.permutation(npool)[:B].astype(np.int32)
+    poolH = np.zeros(dims.state_shape(npool), np.float32)
+    poolT = np.zeros(dims.tail_shape(npool), np.float32)
+    poolH[slots], poolT[slots] = H0, T0
+    sp, tp = f32(poolH), act(poolT, dims)
+    ck_s, ck_t, out = gdn.verify_paths(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims),
+                                       act(x.b, dims), i32(slots), tp, sp, check_slots=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sp), poolH), "verify modified the pool"
+    ref = oracle.verify_paths(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, T0, H0)
+    assert_out_flat(host(out), ref["out"], "verify_paths fp32 out")
+    cks = host(ck_s)
+    for p in range(P):
+        for i in range(T):
+            assert_state_close(cks[:, p, i], ref["ckpt_H"][:, p, i], f"path {p} checkpoint {i}")
+    np.testing.assert_array_equal(host(ck_t), ref["ckpt_tail"].astype(np.float32))
+    for p in range(1, P):
+        assert torch.equal(ck_s[:, p, 0], ck_s[:, 0, 0]) and torch.equal(out[:, p, 0], out[:, 0, 0])
+
+
 def test_prefill_fp32_multichunk():
     dims = LayerDims(n_k=2, n_v=4, d_k=64, d_v=64, act=ACT_F32)
     _prefill_case(dims, 4, 2, 200, [200, 129], state_std=0.05, tail_rand=True)
