@@ -117,7 +117,10 @@ int gdn_device_status(int clear, gdn_stream_t stream);
 int gdn_conv_chunk(const gdn_desc* desc, const void* conv_w, const void* mixed, const int32_t* len,
                    void* conv_tail, void* y, int B, int Lb, gdn_stream_t stream);
 
-/* Bytes of device workspace gdn_prefill_chunk needs for B sequences of Lb padded tokens. */
+/* Bytes of device workspace gdn_prefill_chunk needs for B sequences of Lb padded tokens (0 when the
+ * shape is not built). With d_k != d_v it includes zero-padded copies of the call's inputs, conv weights,
+ * tail, state and output at max(d_k, d_v). The size never shrinks as Lb grows, so a workspace sized for
+ * the longest call serves every shorter one. */
 size_t gdn_prefill_workspace_bytes(const gdn_desc* desc, int B, int Lb);
 
 /*
