@@ -121,6 +121,21 @@ def test_sizes_unequal_head_dims():
             assert sizes[-1] >= gdn.prefill_workspace_bytes(dm, B, 2048)
 
 
+def test_unequal_dims_workspace_checked():
+    """A prefill with key and value heads of different dims checks its (larger) workspace before any
+    launch: the square layer's size is too small."""
+    lib = gdn.load_library()
+    d = gdn.GdnDesc(n_k=2, n_v=4, d_k=64, d_v=128).c()
+    dsq = gdn.GdnDesc(n_k=2, n_v=4, d_k=64, d_v=64).c()
+    need = lib.gdn_prefill_workspace_bytes(ctypes.byref(d), 1, 300)
+    small = lib.gdn_prefill_workspace_bytes(ctypes.byref(dsq), 1, 300)
+    assert need > small > 0
+    p = ctypes.c_void_p(1 << 20)
+    w = gdn._Weights(1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    rc = lib.gdn_prefill_chunk(ctypes.byref(d), ctypes.byref(w), p, p, p, p, p, p, p, p, 1, 300, p, small, None)
+    assert rc == -1 and b"workspace" in lib.gdn_last_error()
+
+
 def test_sizes_fused_segments(monkeypatch):
     """The fused path forced for few units: segment maps and states where few units run long calls."""
     monkeypatch.setenv("GDN_PREFILL_PATH", "fused")

@@ -258,8 +258,8 @@ def test_large_saved_state_range(path):
 
 
 def test_two_runs_bitwise():
-    """Every launch is deterministic: the same inputs give the same bits twice (prefill on both paths,
-    decode, verify with checkpoints, tree verify, accept and the state copy)."""
+    """Every launch is deterministic: the same inputs give the same bits twice (prefill on both paths and
+    on zero-padded heads, decode, verify with checkpoints, tree verify, accept and the state copy)."""
     dims, B, K, P = NEXT, 4, 4, 3
     T = K + 1
     _say("two runs bitwise")
@@ -282,6 +282,24 @@ def test_two_runs_bitwise():
             assert torch.equal(a[0][s, :n], b[0][s, :n]), f"prefill ({path}) out of sequence {s} differs"
         for u, v, name in zip(a[1:], b[1:], ("state", "tail")):
             assert torch.equal(u, v), f"prefill ({path}) {name} differs between two runs"
+
+    # prefill with key and value heads of different dims (zero-padded copies in the workspace)
+    du = LayerDims(n_k=2, n_v=4, d_k=64, d_v=128)
+    wu, xu, ru = make_layer(42, du, 2, 200, [200, 77])
+    Hu, tu = random_state(ru, du, 2)
+    Wu, dd = weights(wu, du), desc_of(du)
+    insu = [act(a, du) for a in (xu.mixed, xu.z, xu.a, xu.b)] + [i32(xu.lens)]
+
+    def prefill_unequal():
+        st, tail = f32(Hu), act(tu, du)
+        out = gdn.prefill_chunk(dd, Wu, *insu, tail, st)
+        torch.cuda.synchronize()
+        return out, st, tail
+
+    a, b = prefill_unequal(), prefill_unequal()
+    for s, n in enumerate(xu.lens):
+        assert torch.equal(a[0][s, :n], b[0][s, :n]), f"unequal-dims prefill out of sequence {s} differs"
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), "unequal-dims prefill state or tail differs"
 
     xs = make_inputs(rng, dims, B, T)
     sp, tp = f32(H0[:B]), act(t0[:B], dims)
