@@ -22,10 +22,11 @@
 // fragments, then the Gram products K K^T and K Q^T, the off-diagonal blocks of -A, the decayed P,
 // and the four diagonal inverses T_mm by substitution.
 // Four workgroup barriers per chunk order the two roles:
-//   X..Y   chain: products of chunk c             prep: conv, norms, gates of chunk c+1 (registers)
-//   Y..Y1  chain: gated norm + store of chunk c   prep: q, k, k~ fragments and gates of c+1 to LDS
-//   Y1..Y2 chain: -                               prep: Gram products, A blocks, P of c+1
-//   Y2..X  chain: -                               prep (one wave): T_mm of c+1
+//   X..Y   chain: right-hand sides, solve, P U and  prep: conv, norms, gates, operand pairs of c+1
+//          state update of c
+//   Y..Y1  chain: gated norm + stores of c; v of c+1 prep: q, k, k~ and gates of c+1 to LDS; loads of c+2
+//   Y1..Y2 chain: K H and H^T Q^T of c+1             prep: Gram products, A blocks, P of c+1
+//   Y2..X  chain: -                                  prep (one wave): T_mm of c+1
 //
 // Modes: OUT runs a segment of chunks from its entering state and writes the outputs (and, for the
 // segment that holds the sequence's last chunk, the final state). MAP_N and MAP_M run a segment
