@@ -80,7 +80,8 @@ constexpr int L_SS = L_G + 1024;              // row sums of squares of O: [chai
 constexpr int VROWS = FC + 3;                 // staged conv input rows of a chunk (3 halo rows)
 constexpr int L_VS = L_SS + 1024;             // v inputs per chain wave: [wave 4][VROWS][32] bf16
 constexpr int L_NW = L_VS + 4 * VROWS * 64;  // norm weights [128] fp32
-constexpr int L_END = L_NW + FD * 4;
+constexpr int L_VT = L_NW + FD * 4;           // conv taps of the head's value channels [128] (4 bf16 each)
+constexpr int L_END = L_VT + FD * 8;
 static_assert(L_END <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -182,13 +183,17 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
   float* sNW = (float*)(smem + L_NW);
   char* stage = smem + L_VS + w * VROWS * 64;
   if (OUT && threadIdx.x < FD) sNW[threadIdx.x] = p.norm_w[threadIdx.x];  // read after the prologue's barriers
+  // the value channels' conv taps, staged once (the chunk loop's barriers would otherwise make every chunk
+  // wait on a global load of them); read after the prologue's barriers
+  uint2* sVT = (uint2*)(smem + L_VT);
+  if (threadIdx.x < FD)
+    sVT[threadIdx.x] = *(const uint2*)((const uint16_t*)p.conv_w + (long)(2 * n_k * FD + h * FD + threadIdx.x) * 4);
 
   const int cw0 = 32 * w;   // first H column of this wave
   f32x4 Hacc[8][2];         // 2^16 H[16 hm + 4 g + i][cw0 + 16 n + c]
   f32x4 Oacc[2][4];         // 2^24 O^T[cw0 + 16 n + 4 g + i][token 16 mt + c]
   uint2 zr[2][4];           // z of the output rows (4 bf16)
   u32x4 vpre[5];            // staged v inputs of the next chunk, in flight
-  const uint2* vtap = (const uint2*)((const uint16_t*)p.conv_w + (long)(2 * n_k * FD + h * FD + cw0 + c16) * 4);
   // the entering state: OUT from the saved state (segment 0) or the scan's segment state; MAP_N from
   // zero; MAP_M from the identity
   {
@@ -299,7 +304,7 @@ __device__ __forceinline__ void chain_role(const FusedArgs& p, const Unit& u, ch
         for (int n = 0; n < 2; ++n) {
           float x[7] = {}, vw[4] = {};
           if (WITH_V) {
-            const uint2 tp = vtap[16 * n];  // taps of channel cw0 + 16 n + c (read again each chunk, cached)
+            const uint2 tp = sVT[cw0 + 16 * n + c16];  // taps of channel cw0 + 16 n + c
             vw[0] = bf_lo(tp.x); vw[1] = bf_hi(tp.x); vw[2] = bf_lo(tp.y); vw[3] = bf_hi(tp.y);
 #pragma unroll
             for (int r = 0; r < 7; ++r) x[r] = bf1(st[(t0 + r) * 32 + 16 * n + c16]);
