@@ -81,7 +81,8 @@ constexpr int VROWS = FC + 3;                 // staged conv input rows of a chu
 constexpr int L_VS = L_SS + 1024;             // v inputs per chain wave: [wave 4][VROWS][32] bf16
 constexpr int L_NW = L_VS + 4 * VROWS * 64;  // norm weights [128] fp32
 constexpr int L_VT = L_NW + FD * 4;           // conv taps of the head's value channels [128] (4 bf16 each)
-constexpr int L_END = L_VT + FD * 8;
+constexpr int L_QKT = L_VT + FD * 8;          // per prep lane: taps of its q and k channel pairs [wave 4][lane][4]
+constexpr int L_END = L_QKT + 4 * 64 * 4 * 8;
 static_assert(L_END <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -505,9 +506,18 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
 
   uint32_t xq[19], xk[19];     // q / k inputs of the next chunk: rows 16 pw - 3 .. 16 pw + 15, channel pairs
   uint16_t a_raw = 0, b_raw = 0;  // gate inputs of the next chunk (lane = token)
-  // conv taps of the lane's q and k channels 2 lane, 2 lane + 1 (read again each chunk, cached)
-  const uint2* qtap = (const uint2*)((const uint16_t*)p.conv_w + (long)(kh * FD + 2 * lane) * 4);
-  const uint2* ktap = (const uint2*)((const uint16_t*)p.conv_w + (long)(n_k * FD + kh * FD + 2 * lane) * 4);
+  // conv taps of the lane's q and k channels 2 lane, 2 lane + 1, staged once in the lane's own LDS slot
+  // (the chunk loop's barriers would otherwise make every chunk wait on a global load of them)
+  uint2* qtap = (uint2*)(smem + L_QKT) + (pw * 64 + lane) * 4;
+  uint2* ktap = qtap + 2;
+  {
+    const uint2* gq = (const uint2*)((const uint16_t*)p.conv_w + (long)(kh * FD + 2 * lane) * 4);
+    const uint2* gk = (const uint2*)((const uint16_t*)p.conv_w + (long)(n_k * FD + kh * FD + 2 * lane) * 4);
+    qtap[0] = gq[0];
+    qtap[1] = gq[1];
+    ktap[0] = gk[0];
+    ktap[1] = gk[1];
+  }
   auto load = [&](int c) __attribute__((always_inline)) {
     const int T0 = c * FC + 16 * pw - 3;
     // rows T0 .. T0 + 18: T < 0 the saved tail, T >= Lb zero (never read); the row pointer steps by one
