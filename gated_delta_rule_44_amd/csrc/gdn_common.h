@@ -47,6 +47,14 @@ __device__ __forceinline__ float sigmoid(float x) { return fast_rcp(1.0f + __exp
 // softplus(x) = log(1 + e^x), written as max(x, 0) + log1p(e^-|x|) so it never overflows
 __device__ __forceinline__ float softplus(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
 
+// One token's log-decay g for the chunk form, floored at -30. The chunk form takes every decay factor as
+// e^{gamma_r - gamma_s} of in-chunk sums gamma of g, whose rounding error grows with |gamma|, and a full
+// forget (g = -inf) would give -inf - (-inf). With the floor |gamma| stays below 64 * 30, and a factor
+// e^g below e^-30 (about 9.4e-14) becomes 9.4e-14: the state keeps at most that fraction of what it held
+// before the token instead of less. NaN passes through.
+constexpr float kLogDecayFloor = -30.0f;
+__device__ __forceinline__ float chunk_log_decay(float g) { return g < kLogDecayFloor ? kLogDecayFloor : g; }
+
 // ---- wave reductions -----------------------------------------------------------------------------
 // DPP moves inside 16-lane rows (no LDS round trip): quad_perm [1,0,3,2] and [2,3,0,1], then
 // row_half_mirror (lane i <-> 7-i) and row_mirror (lane i <-> 15-i) pair each partial sum with a

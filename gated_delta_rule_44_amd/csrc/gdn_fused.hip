@@ -615,7 +615,7 @@ __device__ __forceinline__ void prep_role(const FusedArgs& p, const Unit& u, cha
     }
     const int t = c * FC + lane;
     const bool real = t < len;
-    const float g0 = negA * softplus(bf1(a_raw) + dtb);
+    const float g0 = chunk_log_decay(negA * softplus(bf1(a_raw) + dtb));
     float gm = real ? g0 : 0.f;
     g_beta = real ? sigmoid(bf1(b_raw)) : 0.f;
 #pragma unroll

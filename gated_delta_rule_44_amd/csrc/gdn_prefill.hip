@@ -345,7 +345,7 @@ __global__ __launch_bounds__(512) void chunk_prep_kernel(PrefillArgs p) {
 
   // ---- 2. gates of the R value heads: wave r, lane = token; inclusive scan of g over the chunk -----
   if (w < R) {
-    const float g0 = -__expf(p.A_log[hg]) * softplus(to_f32(a_raw) + p.dt_bias[hg]);
+    const float g0 = chunk_log_decay(-__expf(p.A_log[hg]) * softplus(to_f32(a_raw) + p.dt_bias[hg]));
     const float b0 = sigmoid(to_f32(b_raw));
     float g = tg < len ? g0 : 0.f;
     const float be = tg < len ? b0 : 0.f;
@@ -821,7 +821,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
   // ---- 2. gates of value head r (wave r, lane = token): inclusive scan of g, the per-token decays ---
   if (w < R) {
-    const float g0 = -__expf(p.A_log[hg]) * softplus(to_f32(a_raw) + p.dt_bias[hg]);
+    const float g0 = chunk_log_decay(-__expf(p.A_log[hg]) * softplus(to_f32(a_raw) + p.dt_bias[hg]));
     const float b0 = sigmoid(to_f32(b_raw));
     float g = tg < len ? g0 : 0.f;
     const float be = tg < len ? b0 : 0.f;

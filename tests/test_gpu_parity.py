@@ -244,6 +244,40 @@ def test_prefill_scale_one():
     _prefill_case(dims, 6, 1, 130, [130], state_std=0.05)
 
 
+@pytest.mark.parametrize("path", BOTH)
+def test_prefill_strong_decays(path):
+    """Gates at the strong end inside chunks of ordinary tokens, from a saved state: runs of tokens with
+    a = 40 or 12 (log-decays of -640 and -192 per token at A = 16) and single full forgets (a = +inf,
+    g = -inf). The in-chunk sums of g then reach 10^4 in magnitude while the decays between the
+    ordinary tokens after them stay near 1; both paths must still match the oracle."""
+    dims = LayerDims(n_k=2, n_v=4, d_k=128, d_v=128)
+    B, L, lens = 2, 300, [300, 171]
+    _say(f"strong decays path={path}")
+    w, x, rng = make_layer(31, dims, B, L, lens)
+    w.A_log[:] = np.float32(np.log(16.0))
+    w.A_log[0] = 0.0  # one slow head beside three fast ones
+    x.a[:, 70:80] = 40.0
+    x.a[:, 130] = np.inf
+    x.a[0, 200:240] = 12.0
+    x.a[0, 290] = np.inf
+    H0, t0 = random_state(rng, dims, B)
+    od = oracle.Dims.of(dims)
+    d = desc_of(dims, out_f32=True)
+    st, tail = f32(H0), act(t0, dims)
+    out = torch.zeros(B, L, dims.value_dim, dtype=torch.float32, device="cuda")
+    with prefill_path(path):
+        gdn.prefill_chunk(d, weights(w, dims), act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims),
+                          i32(x.lens), tail, st, out)
+    torch.cuda.synchronize()
+    for s in range(B):
+        n = lens[s]
+        ref = oracle.layer_forward(od, w, x.mixed[s:s + 1], x.z[s:s + 1], x.a[s:s + 1], x.b[s:s + 1],
+                                   x.lens[s:s + 1], t0[s:s + 1], H0[s:s + 1])
+        assert_out_flat(host(out[s, :n]), ref["out"][0, :n], f"fp32 out[seq {s}] (path {path})")
+        assert_state_close(host(st[s]), ref["H"][0], f"state[seq {s}] (path {path})")
+        np.testing.assert_array_equal(host(tail[s]), ref["tail"][0].astype(np.float32))
+
+
 def test_continuation_equals_single_pass():
     """A 32768-token prompt in bucketed chunks (real lengths drawn inside each bucket, padded with
     g = beta = 0), each continuing from the saved fp32 state and conv tail, against the oracle's single
