@@ -1,4 +1,4 @@
-"""GPU: every entry point at element offsets past 2^31 (byte offsets past 2^32).
+"""GPU: every entry point at element offsets past 2^31 (byte offsets past 2^32), and at its largest batch.
 
 A few seeded base sequences are tiled over enough batch rows (or pool rows, or checkpoint rows) that the
 last rows start beyond 2^31 elements of their buffer. Sequences are independent and every one does the
@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import gated_delta_rule_44_amd as gdn
-from gdn_inputs import NEXT, LayerDims, make_inputs, make_layer, random_state, verify_draws
+from gdn_inputs import NEXT, LayerDims, make_inputs, make_layer, path_inputs, random_state, verify_draws
 from tests.gpu_helpers import (act, assert_out_close, assert_out_flat, assert_state_close, desc_of, f32, host, i32,
                                prefill_path, weights)
 
@@ -55,16 +55,11 @@ def _copies_equal_base(t: torch.Tensor, K: int) -> bool:
     return bool((raw.view(n // K, K, *t.shape[1:]) == raw[:K]).all())
 
 
-def test_prefill_past_2g_elements():
-    """Prefill on both paths over 2112 sequences of 2048 tokens with 1 key / 2 value heads of 128
-    (512 conv channels): the activations of the last sequences start 2.2e9 elements in (4.4 GB)."""
-    dims = LayerDims(n_k=1, n_v=2, d_k=128, d_v=128)
-    K, L, reps = 4, 2048, 528
+def _prefill_tiled(dims, seed, L, lens, reps):
+    """len(lens) seeded base sequences tiled reps times, through both prefill paths (fp32 outputs)"""
+    K = len(lens)
     B = K * reps
-    assert B * L * dims.conv_dim > I32_LIMIT and (B - 1) * L * dims.conv_dim * 2 > 2 * I32_LIMIT
-    lens = np.array([2048, 1500, 2047, 65], np.int32)
-    _say(f"prefill large offsets B={B} L={L} dims={dims}")
-    w, x, rng = make_layer(71, dims, K, L, lens)
+    w, x, rng = make_layer(seed, dims, K, L, lens)
     H0, t0 = random_state(rng, dims, K)
     od = oracle.Dims.of(dims)
     refs = [oracle.layer_forward(od, w, x.mixed[s:s + 1], x.z[s:s + 1], x.a[s:s + 1], x.b[s:s + 1], x.lens[s:s + 1],
@@ -91,6 +86,29 @@ def test_prefill_past_2g_elements():
         for t, name in ((out, "out"), (st, "state"), (tail, "tail")):
             assert _copies_equal_base(t, K), f"{name}: a far copy differs from its base (path {path})"
         del tail, st, out
+
+
+def test_prefill_past_2g_elements():
+    """Prefill on both paths over 2112 sequences of 2048 tokens with 1 key / 2 value heads of 128
+    (512 conv channels): the activations of the last sequences start 2.2e9 elements in (4.4 GB)."""
+    dims = LayerDims(n_k=1, n_v=2, d_k=128, d_v=128)
+    L, reps = 2048, 528
+    lens = np.array([2048, 1500, 2047, 65], np.int32)
+    B = len(lens) * reps
+    assert (B - 1) * L * dims.conv_dim > I32_LIMIT
+    _say(f"prefill large offsets B={B} L={L} dims={dims}")
+    _prefill_tiled(dims, 71, L, lens, reps)
+
+
+def test_prefill_max_batch():
+    """Prefill at its largest batch, 65535 sequences (1 key / 1 value head of 128, 70 tokens: two chunks,
+    ragged, one sequence empty), on both paths."""
+    dims = LayerDims(n_k=1, n_v=1, d_k=128, d_v=128)
+    lens = np.array([70, 64, 1, 0, 33], np.int32)
+    reps = 13107
+    assert len(lens) * reps == 65535
+    _say(f"prefill max batch B=65535 L=70 dims={dims}")
+    _prefill_tiled(dims, 75, 70, lens, reps)
 
 
 def test_conv_past_2g_elements():
@@ -195,3 +213,76 @@ def test_verify_checkpoints_past_2g_elements():
     src = ci.long()
     assert torch.equal(dst_s, ck_s.view(B * T, *dims.state_shape(1)[1:])[src])
     assert torch.equal(dst_t, ck_t.view(B * T, *dims.tail_shape(1)[1:])[src])
+
+
+def test_decode_max_batch():
+    """Decode at its largest batch, 65535 sequences (1/1 heads of 128), sequence b owning pool row
+    65534 - b."""
+    dims = LayerDims(n_k=1, n_v=1, d_k=128, d_v=128)
+    K, reps = 5, 13107
+    B = K * reps
+    _say(f"decode max batch B={B}")
+    w, _, rng = make_layer(76, dims, 1, 1)
+    H0, T0 = _saved(dims, w, rng, K)
+    x = make_inputs(rng, dims, K, 1)
+    d = desc_of(dims, out_f32=True)
+    step_in = [_tile(act(v[:, 0], dims), reps) for v in (x.mixed, x.z, x.a, x.b)]
+    slots = np.arange(B - 1, -1, -1, dtype=np.int32)
+    sp = _tile(f32(H0), reps).flip(0).contiguous()  # row B-1-b holds base b % K
+    tp = _tile(act(T0, dims), reps).flip(0).contiguous()
+    out = gdn.decode_step(d, weights(w, dims), *step_in, i32(slots), tp, sp)
+    torch.cuda.synchronize()
+    ref = oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, None, T0, H0)
+    assert_out_flat(host(out[:K]), ref["out"][:, 0], "decode fp32 out")
+    sq, tq = sp.flip(0).contiguous(), tp.flip(0).contiguous()  # back to row b = sequence b
+    assert_state_close(host(sq[:K]), ref["H"])
+    np.testing.assert_array_equal(host(tq[:K]), ref["tail"].astype(np.float32))
+    for t, name in ((out, "out"), (sq, "state"), (tq, "tail")):
+        assert _copies_equal_base(t, K), f"{name}: a far copy differs from its base"
+
+
+def test_verify_paths_max_batch():
+    """Tree verify at its largest B * P = 65535: 13107 sequences x 5 paths x 2 tokens (1/1 heads of 128),
+    three base sequences tiled."""
+    dims = LayerDims(n_k=1, n_v=1, d_k=128, d_v=128)
+    K, reps, P, T = 3, 4369, 5, 2
+    B = K * reps
+    assert B * P == 65535
+    _say(f"verify paths max batch B={B} P={P} T={T}")
+    w, _, rng = make_layer(77, dims, 1, 1)
+    H0, T0 = _saved(dims, w, rng, K)
+    x = path_inputs(rng, dims, K, P, T)
+    d = desc_of(dims, out_f32=True)
+    ins = [_tile(act(v, dims), reps) for v in (x.mixed, x.z, x.a, x.b)]
+    sp, tp = _tile(f32(H0), reps), _tile(act(T0, dims), reps)
+    ck_s, ck_t, out = gdn.verify_paths(d, weights(w, dims), *ins, None, tp, sp)
+    torch.cuda.synchronize()
+    ref = oracle.verify_paths(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, T0, H0)
+    assert_out_flat(host(out[:K]), ref["out"], "paths fp32 out")
+    cks = host(ck_s[:K])
+    for p in range(P):
+        for i in range(T):
+            assert_state_close(cks[:, p, i], ref["ckpt_H"][:, p, i], f"path {p} checkpoint {i}")
+    np.testing.assert_array_equal(host(ck_t[:K]), ref["ckpt_tail"].astype(np.float32))
+    for t, name in ((out, "out"), (ck_s, "ckpt_state"), (ck_t, "ckpt_tail")):
+        assert _copies_equal_base(t, K), f"{name}: a far copy differs from its base"
+
+
+def test_state_copy_and_zero_max_rows():
+    """The state copy and the state zero at their largest count, 65535 records (1/1 heads of 128): a
+    scatter by a seeded permutation, then zeroing every row through the same index list."""
+    dims = LayerDims(n_k=1, n_v=1, d_k=128, d_v=128)
+    n = 65535
+    _say(f"state copy / zero n={n}")
+    d = desc_of(dims)
+    gen = torch.Generator(device="cuda").manual_seed(78)
+    src_s = torch.randn(dims.state_shape(n), generator=gen, device="cuda")
+    src_t = torch.randn(dims.tail_shape(n), generator=gen, device="cuda").to(torch.bfloat16)
+    perm = torch.from_numpy(np.random.default_rng(78).permutation(n).astype(np.int32)).cuda()
+    dst_s, dst_t = torch.zeros_like(src_s), torch.zeros_like(src_t)
+    gdn.state_copy(d, dst_s, dst_t, perm, src_s, src_t, None, n)  # dst row perm[i] <- src row i
+    torch.cuda.synchronize()
+    assert torch.equal(dst_s[perm.long()], src_s) and torch.equal(dst_t[perm.long()], src_t)
+    gdn.state_zero(d, dst_s, dst_t, perm, n)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dst_s)) == 0 and int(torch.count_nonzero(dst_t)) == 0
