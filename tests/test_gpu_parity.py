@@ -515,6 +515,39 @@ def test_verify_checkpoints_and_commit():
     assert_state_close(host(sp), ref["ckpt_H"][np.arange(B), m_ref])
 
 
+def test_verify_strong_decays():
+    """The step kernel on the prefill test's gate extremes: 8 sequences x 5 tokens from saved states, with
+    a = 40 at token 1, a full forget (a = +inf) at token 2 of every other sequence and a = 12 at token 3
+    of the rest; checkpoints and outputs against the oracle, and bitwise equal to repeated decode."""
+    dims, B, T = LayerDims(n_k=2, n_v=4, d_k=128, d_v=128), 8, 5
+    _say("verify strong decays")
+    w, _, rng = make_layer(32, dims, 1, 1)
+    w.A_log[:] = np.float32(np.log(16.0))
+    w.A_log[0] = 0.0
+    H0, T0 = _saved_states(dims, w, rng, B)
+    x = _decode_inputs(dims, rng, B, T)
+    x.a[:, 1] = 40.0
+    x.a[::2, 2] = np.inf
+    x.a[1::2, 3] = 12.0
+    d = desc_of(dims, True)
+    W = weights(w, dims)
+    sp, tp = f32(H0), act(T0, dims)
+    mx, zz, aa, bb = act(x.mixed, dims), act(x.z, dims), act(x.a, dims), act(x.b, dims)
+    ck_s, ck_t, out = gdn.verify_with_checkpoints(d, W, mx, zz, aa, bb, None, tp, sp)
+    torch.cuda.synchronize()
+    ref = oracle.verify(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, T0, H0)
+    assert_out_flat(host(out), ref["out"], "verify fp32 out")
+    cks = host(ck_s)
+    for i in range(T):
+        assert_state_close(cks[:, i], ref["ckpt_H"][:, i], f"checkpoint {i}")
+    np.testing.assert_array_equal(host(ck_t), ref["ckpt_tail"].astype(np.float32))
+    for i in range(T):
+        o = gdn.decode_step(d, W, mx[:, i].contiguous(), zz[:, i].contiguous(), aa[:, i].contiguous(),
+                            bb[:, i].contiguous(), None, tp, sp)
+        torch.cuda.synchronize()
+        assert torch.equal(sp, ck_s[:, i]) and torch.equal(tp, ck_t[:, i]) and torch.equal(o, out[:, i])
+
+
 @pytest.mark.parametrize("dims", [LayerDims(n_k=2, n_v=16, d_k=128, d_v=128), LayerDims(n_k=2, n_v=6, d_k=64, d_v=64),
                                   LayerDims(n_k=2, n_v=4, d_k=128, d_v=64), LayerDims(n_k=2, n_v=6, d_k=32, d_v=128)])
 def test_verify_grouped_gqa_ratio(dims):
