@@ -41,6 +41,11 @@
  * Activations of unit scale keep them far below (the saved states of the tests are within |S| < 10). A
  * prefill whose final state leaves that range, or is not finite, sets GDN_STATUS_RANGE in the device
  * status word (gdn_device_status); decode and verify run fp32 throughout and have no such limit.
+ *
+ * Strong decays (prefill): the chunked form floors each token's log-decay g at -30, so a decay factor
+ * below e^-30 (about 9.4e-14) counts as e^-30 and a full forget (a = +inf, g = -inf) keeps that fraction
+ * of the state instead of none. Without the floor the in-chunk sums of g would lose accuracy, and a
+ * full forget would give NaN. Decode and verify take e^g as it is.
  */
 #ifndef GDN_H
 #define GDN_H
