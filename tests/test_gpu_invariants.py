@@ -343,3 +343,56 @@ def test_two_runs_bitwise():
         return s2, t2
 
     assert all(torch.equal(u, v) for u, v in zip(commit(), commit())), "state copy differs between two runs"
+
+
+# ---- overlapping calls: two prefill calls on two streams, each with a workspace of its own -----------
+
+_OVERLAP_SHAPES = {
+    # (dims, B, L, lens): which kernels each takes is pinned in test_prefill_fused_launches and
+    # test_prefill_norm_mode_launches
+    "fused": (NEXT, 6, 300, [300, 1, 64, 250, 300, 200]),                                  # 192 units
+    "two_phase": (LayerDims(n_k=16, n_v=16, d_k=128, d_v=128), 2, 300, [300, 129]),         # 32 units
+    "exchange": (LayerDims(n_k=16, n_v=16, d_k=128, d_v=128), 3, 1030, [1030, 0, 700]),     # slices exchange row sums
+}
+
+
+@pytest.mark.parametrize("pair", [("fused", "fused"), ("two_phase", "two_phase"), ("exchange", "exchange"),
+                                  ("fused", "exchange")])
+def test_prefill_overlapping_calls_on_two_streams(pair):
+    """Calls that may overlap need only workspaces of their own: two prefill calls issued back to back on
+    two streams give, each, the bits of the same call run alone."""
+    _say(f"overlapping prefill calls {pair}")
+    calls = []
+    for i, kind in enumerate(pair):
+        dims, B, L, lens = _OVERLAP_SHAPES[kind]
+        w, x, rng = make_layer(60 + i, dims, B, L, lens)
+        H0, t0 = random_state(rng, dims, B)
+        calls.append(dict(d=desc_of(dims), W=weights(w, dims), lens=lens, out_shape=(B, L, dims.value_dim),
+                          ins=[act(a, dims) for a in (x.mixed, x.z, x.a, x.b)] + [i32(x.lens)],
+                          H0=f32(H0), t0=act(t0, dims), ws_args=(B, L)))
+
+    def buffers(c):
+        return (c["H0"].clone(), c["t0"].clone(), torch.zeros(c["out_shape"], dtype=torch.bfloat16, device="cuda"),
+                gdn.prefill_workspace(c["d"], *c["ws_args"]))
+
+    def launch(c, buf):
+        st, tail, out, ws = buf
+        gdn.prefill_chunk(c["d"], c["W"], *c["ins"], tail, st, out, ws)
+
+    alone = []
+    for c in calls:
+        buf = buffers(c)
+        launch(c, buf)
+        torch.cuda.synchronize()
+        alone.append(buf)
+    together = [buffers(c) for c in calls]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for c, buf, s in zip(calls, together, streams):
+        with torch.cuda.stream(s):
+            launch(c, buf)
+    torch.cuda.synchronize()
+    for k, (c, a, t) in enumerate(zip(calls, alone, together)):
+        assert torch.equal(a[0], t[0]) and torch.equal(a[1], t[1]), f"call {k} ({pair[k]}): state or tail differs"
+        for s, n in enumerate(c["lens"]):
+            assert torch.equal(a[2][s, :n], t[2][s, :n]), f"call {k} ({pair[k]}): out of sequence {s} differs"
