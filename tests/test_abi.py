@@ -213,3 +213,23 @@ def test_timing_session_errors():
     assert lib.gdn_timing_begin(0) == -1 and b"capacity" in lib.gdn_last_error()
     assert lib.gdn_timing_end(None, None, 0) == -1 and b"no open session" in lib.gdn_last_error()
 
+
+
+def test_missing_library_fails_loudly():
+    """Without libgdn.so every call raises (in a fresh process, the loader pointed at a missing file): no
+    entry point has a CPU fallback."""
+    import subprocess
+    import sys
+    code = ("import gated_delta_rule_44_amd as g\n"
+            "g.load_library.__defaults__ = ('/nonexistent/libgdn.so',)\n"
+            "calls = {'prefill_workspace_bytes': lambda: g.prefill_workspace_bytes(g.GdnDesc(2, 4, 128, 128), 1, 64),\n"
+            "         'version': g.version, 'accept': lambda: g.accept(None, None)}\n"
+            "for name, f in calls.items():\n"
+            "    try:\n"
+            "        f()\n"
+            "        print(name, 'returned')\n"
+            "    except RuntimeError as e:\n"
+            "        print(name, 'raised', 'is not built' in str(e))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    lines = sorted(r.stdout.split("\n")[:-1])
+    assert lines == ["accept raised True", "prefill_workspace_bytes raised True", "version raised True"], r.stdout + r.stderr
