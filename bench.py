@@ -28,9 +28,9 @@ The same run also measures, each as a sub-object of the one JSON line:
   conv    - the standalone causal conv + SiLU over 8 x 8192 tokens of the stack layer's channels
   copy    - the O(1) state bridge: 256 records {fp32 state, conv tail} of one layer
   measured_peaks - the MFMA probe's dense f16 TFLOP/s and the copy leg's GB/s beside the published peaks
-  cpu_baseline - the fp64 oracle on the host cores on the prefill workload; the stack, decode, verify,
-                 verify_paths and continuation legs carry their own, on bounded samples of their
-                 workloads scaled to the leg's unit (the sample is stated in each)
+  cpu_baseline - the fp64 oracle on the host cores on the prefill workload; every other leg carries its
+                 own, on a bounded sample of its workload scaled to the leg's unit (the sample is
+                 stated in each)
 """
 from __future__ import annotations
 
@@ -709,6 +709,98 @@ def cpu_continuation():
                 % (ntok, len(parts)), sec)
 
 
+def cpu_conv():
+    """The oracle's conv + SiLU (one thread) on one of the leg's 8 sequences (8192 tokens x 8192
+    channels): the sequences are independent, so the sample's GB/s is the leg's rate."""
+    import oracle
+    from gdn_inputs import bf16_round
+    T, Cs, C, B = 8192, 8192, 8192, 8
+    rng = np.random.default_rng(5)
+    x = bf16_round(rng.standard_normal((T, Cs), dtype=np.float32))
+    w = bf16_round(rng.normal(0.0, 0.5, size=(Cs, 4)).astype(np.float32))
+    tail = np.zeros((3, Cs), np.float32)
+    sec = _best_time(lambda: oracle.conv(w, tail, x, T), 1)
+    nbytes = 2 * T * Cs * 2 + 2 * 3 * Cs * 2 + Cs * 4 * 2
+    full = 2 * B * T * C * 2 + 2 * B * 3 * C * 2 + C * 4 * 2
+    return _cpu(nbytes / sec / 1e9, "GB/s", 1, "1 of the 8 sequences (8192 tokens x 8192 channels)", sec,
+                ms_per_call=sec * full / nbytes * 1e3)
+
+
+def cpu_copy():
+    """The oracle's state record copy (numpy, one thread) of the leg's 256 records of one layer."""
+    import oracle
+    from gdn_inputs import NEXT
+    dims, n = NEXT, 256
+    rng = np.random.default_rng(6)
+    src_s = rng.standard_normal(dims.state_shape(n), dtype=np.float32)
+    src_t = rng.integers(0, 1 << 16, size=dims.tail_shape(n), dtype=np.uint16)  # bf16 bit patterns
+    dst_s, dst_t = np.empty_like(src_s), np.empty_like(src_t)
+    sec = _best_time(lambda: oracle.state_copy(dst_s, dst_t, None, src_s, src_t, None, n), 2)
+    nbytes = 2 * (src_s.nbytes + src_t.nbytes)
+    return _cpu(nbytes / sec / 1e9, "GB/s", 1, "the whole leg (256 records)", sec, ms_per_call=sec * 1e3)
+
+
+def cpu_prefix_cache():
+    """The oracle over what the oracle's prefix-cache model plans for the leg's 8 rows (restores, chunk
+    ends, snapshots): the whole leg, cached; tokens/s counts every row token, computed or reused."""
+    import oracle
+    from gdn_inputs import NEXT, make_layer
+    from oracle.prefix_cache import PrefixCacheModel
+    dims = NEXT
+    rows_n, n, shared, vocab = 8, 8192, 6144, 512
+    w, table, rng = make_layer(302, dims, 1, vocab)
+    stem = rng.integers(0, vocab, size=shared)
+    rows = [np.concatenate([stem, rng.integers(0, vocab, size=n - shared)]).astype(np.int32) for _ in range(rows_n)]
+    th = oracle.default_threads()
+    od = oracle.Dims.of(dims)
+
+    def run():
+        model = PrefixCacheModel(16, min_prefix=256)
+        snaps = {}
+        for ids in rows:
+            x = [f[0][ids][None] for f in (table.mixed, table.z, table.a, table.b)]
+            ck, c0, _, ends, made = model.row(ids, shared)
+            tail, H = snaps[ck] if ck >= 0 else (None, None)
+            for e, num in zip(list(ends) + [n], list(made) + [-1]):
+                sl = slice(c0, e)
+                r = oracle.layer_forward(od, w, *[a[:, sl] for a in x], tail=tail, H=H, threads=th)
+                tail, H, c0 = r["tail"], r["H"], e
+                if num >= 0:
+                    snaps[num] = (tail, H)
+            snaps = {k: v for k, v in snaps.items() if k in set(model.alive())}
+
+    t0 = time.perf_counter()
+    run()
+    sec = time.perf_counter() - t0
+    return _cpu(rows_n * n / sec, "tokens/s", th, "the whole leg, cached (8 rows x 8192 tokens sharing 6144)", sec)
+
+
+def cpu_spec_loop():
+    """The oracle driving the leg's loop in direct-commit mode (verify 1+4 tokens of 64 sequences from the
+    token table, accept, keep the accepted checkpoint) for 4 steps of the same seeded draft stream."""
+    import oracle
+    from gdn_inputs import NEXT, SpecStream, make_layer, random_state
+    dims, B, K, vocab, steps = NEXT, 64, 4, 1024, 4
+    w, table, rng = make_layer(303, dims, 1, vocab)
+    H, tail = random_state(rng, dims, B)
+    stream = SpecStream(np.random.default_rng(9), B, 8 * steps * (K + 1), vocab, 0.7)
+    th = oracle.default_threads()
+    od = oracle.Dims.of(dims)
+    emitted = 0
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        x, drafts, preds = stream.draw(K)
+        ids = np.concatenate([x[:, None], drafts], 1)
+        r = oracle.verify(od, w, *[f[0][ids] for f in (table.mixed, table.z, table.a, table.b)], tail, H, threads=th)
+        m = oracle.accept(drafts, preds)[0]
+        H, tail = r["ckpt_H"][np.arange(B), m], r["ckpt_tail"][np.arange(B), m]
+        stream.advance(m)
+        emitted += int((m + 1).sum())
+    sec = time.perf_counter() - t0
+    return _cpu(emitted / sec, "tokens/s", th, "4 direct-commit steps of the leg's loop (64 sequences, K=4)", sec,
+                ms_per_step=sec / steps * 1e3)
+
+
 def cpu_baseline():
     """The oracle (fp64, OpenMP over value heads) on the prefill workload, on the host cores."""
     import oracle
@@ -791,7 +883,9 @@ def main():
         if only in ("all", "prefill"):
             line["cpu_baseline"] = cpu_baseline()
         for leg, fn in (("prefill_stack", cpu_prefill_stack), ("decode", cpu_decode), ("verify", cpu_verify),
-                        ("verify_paths", cpu_verify_paths), ("continuation", cpu_continuation)):
+                        ("verify_paths", cpu_verify_paths), ("continuation", cpu_continuation),
+                        ("prefix_cache", cpu_prefix_cache), ("spec_loop", cpu_spec_loop), ("conv", cpu_conv),
+                        ("copy", cpu_copy)):
             if leg in line:
                 line[leg]["cpu_baseline"] = fn()
     line["kernel_hash"] = kernel_hash()

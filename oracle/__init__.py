@@ -231,3 +231,18 @@ def accept_paths(drafts, preds):
     ne = np.empty(B, np.int32)
     _load().oracle_accept_paths(B, P, K, _p(drafts), _p(preds), _p(m), _p(path), _p(em), _p(ne))
     return m, path, em, ne
+
+
+def state_copy(dst_state, dst_tail, dst_idx, src_state, src_tail, src_idx, n):
+    """The fixed-size state record copy (uni_engine.py page, copy_cache_: the records of a sequence's
+    recurrent state move between pools with the pools' addresses kept): for i < n, record src_idx[i]
+    (or i) of each source pool is written to record dst_idx[i] (or i) of the matching destination pool,
+    as it is, bit for bit. Either pair of pools may be None; pools are arrays [rows, ...] updated in
+    place. Destination rows must be distinct."""
+    si = np.arange(n) if src_idx is None else np.asarray(src_idx, np.int64)[:n]
+    di = np.arange(n) if dst_idx is None else np.asarray(dst_idx, np.int64)[:n]
+    if len(np.unique(di)) != len(di):
+        raise ValueError("state_copy: destination rows must be distinct")
+    for dst, src in ((dst_state, src_state), (dst_tail, src_tail)):
+        if dst is not None and src is not None:
+            dst[di] = src[si]

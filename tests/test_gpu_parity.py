@@ -694,13 +694,12 @@ def test_state_copy_gather_scatter(dims):
     dst_t = act(np.zeros(dims.tail_shape(n_dst)), dims)
     si = rng.permutation(n_src)[:n].astype(np.int32)
     di = rng.permutation(n_dst)[:n].astype(np.int32)
+    exp_s, exp_t = dst_s.cpu().numpy(), dst_t.view(torch.int16).cpu().numpy()
+    oracle.state_copy(exp_s, exp_t, di, src_s.cpu().numpy(), src_t.view(torch.int16).cpu().numpy(), si, n)
     gdn.state_copy(d, dst_s, dst_t, i32(di), src_s, src_t, i32(si), n)
     torch.cuda.synchronize()
-    for k in range(n):
-        assert torch.equal(dst_s[di[k]], src_s[si[k]])
-        assert torch.equal(dst_t[di[k]], src_t[si[k]])
-    untouched = np.setdiff1d(np.arange(n_dst), di)
-    assert float(dst_s[untouched].abs().max()) == 0.0
+    assert dst_s.cpu().numpy().tobytes() == exp_s.tobytes()
+    assert dst_t.view(torch.int16).cpu().numpy().tobytes() == exp_t.tobytes()
     # states only, identity indices
     dst2 = f32(np.zeros(dims.state_shape(n_src)))
     gdn.state_copy(d, dst2, None, None, src_s, None, None, n_src)

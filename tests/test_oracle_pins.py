@@ -437,3 +437,36 @@ def test_prefix_model_forgets_evicted_rows():
     for _ in range(200):
         m.row(rng.integers(0, 1000, size=int(rng.integers(64, 1500))), 1500)
         assert m.rows_remembered() <= len(m.alive()) <= 3
+
+
+# ---- the state record copy (uni_engine.py page, copy_cache_) -------------------------------------
+
+def test_state_copy_hand_worked():
+    """Rows of constant value: records 2 and 0 of the source go to rows 3 and 1 of the destination, only
+    the first n = 2 index pairs count, and the other rows keep their values."""
+    src = np.array([10.0, 11.0, 12.0, 13.0])[:, None] * np.ones((4, 3))
+    tail = np.array([20, 21, 22, 23], np.uint16)[:, None] * np.ones((4, 2), np.uint16)
+    dst, dtail = -np.ones((5, 3)), np.zeros((5, 2), np.uint16)
+    oracle.state_copy(dst, dtail, [3, 1, 0], src, tail, [2, 0, 1], 2)
+    np.testing.assert_array_equal(dst[:, 0], [-1.0, 10.0, -1.0, 12.0, -1.0])
+    np.testing.assert_array_equal(dtail[:, 0], [0, 20, 0, 22, 0])
+
+
+def test_state_copy_is_bitwise_and_round_trips():
+    """NaN payloads and -0.0 survive as bits; a permutation and then its inverse give the source back;
+    None indices copy rows 0..n-1; a repeated destination row is rejected."""
+    rng = np.random.default_rng(3)
+    src = rng.standard_normal((6, 4, 4)).astype(np.float32)
+    src[1, 0, 0] = -0.0
+    src[2].view(np.uint32)[0, 0] = 0x7FC01234  # a NaN with a payload
+    perm = rng.permutation(6)
+    mid = np.zeros_like(src)
+    oracle.state_copy(mid, None, perm, src, None, None, 6)
+    back = np.zeros_like(src)
+    oracle.state_copy(back, None, None, mid, None, perm, 6)
+    assert back.tobytes() == src.tobytes()
+    ident = np.zeros_like(src)
+    oracle.state_copy(ident, None, None, src, None, None, 4)
+    assert ident[:4].tobytes() == src[:4].tobytes() and not ident[4:].any()
+    with pytest.raises(ValueError):
+        oracle.state_copy(np.zeros_like(src), None, [1, 1], src, None, [0, 2], 2)
