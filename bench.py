@@ -767,7 +767,8 @@ def cpu_prefix_cache():
                 tail, H, c0 = r["tail"], r["H"], e
                 if num >= 0:
                     snaps[num] = (tail, H)
-            snaps = {k: v for k, v in snaps.items() if k in set(model.alive())}
+            alive = set(model.alive())
+            snaps = {k: v for k, v in snaps.items() if k in alive}
 
     t0 = time.perf_counter()
     run()
