@@ -396,3 +396,30 @@ def test_prefill_overlapping_calls_on_two_streams(pair):
         assert torch.equal(a[0], t[0]) and torch.equal(a[1], t[1]), f"call {k} ({pair[k]}): state or tail differs"
         for s, n in enumerate(c["lens"]):
             assert torch.equal(a[2][s, :n], t[2][s, :n]), f"call {k} ({pair[k]}): out of sequence {s} differs"
+
+
+def test_step_batch_row_equals_batch_one():
+    """A batch row equals batch = 1: decode and verify of 8 sequences give, for sequences 0, 3 and 7 run
+    alone, the same output, state, checkpoint and tail bits (each sequence's steps do the same
+    arithmetic whatever the batch)."""
+    dims, B, T = NEXT, 8, 5
+    _say("batch row = batch one (decode, verify)")
+    w, _, rng = make_layer(43, dims, 1, 1)
+    H0, t0 = random_state(rng, dims, B)
+    x = make_inputs(rng, dims, B, T)
+    d, W = desc_of(dims), weights(w, dims)
+    ins = [act(a, dims) for a in (x.mixed, x.z, x.a, x.b)]
+    sp, tp = f32(H0), act(t0, dims)
+    out_b = gdn.decode_step(d, W, *[a[:, 0].contiguous() for a in ins], None, tp, sp)
+    ck_s, ck_t, vout = gdn.verify_with_checkpoints(d, W, *ins, None, act(t0, dims), f32(H0))
+    torch.cuda.synchronize()
+    for s in (0, 3, 7):
+        one = [a[s:s + 1].contiguous() for a in ins]
+        sp1, tp1 = f32(H0[s:s + 1]), act(t0[s:s + 1], dims)
+        o1 = gdn.decode_step(d, W, *[a[:, 0].contiguous() for a in one], None, tp1, sp1)
+        c1s, c1t, v1 = gdn.verify_with_checkpoints(d, W, *one, None, act(t0[s:s + 1], dims), f32(H0[s:s + 1]))
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], out_b[s]) and torch.equal(sp1[0], sp[s]) and torch.equal(tp1[0], tp[s]), \
+            f"decode of sequence {s} alone differs from its batch row"
+        assert torch.equal(c1s[0], ck_s[s]) and torch.equal(c1t[0], ck_t[s]) and torch.equal(v1[0], vout[s]), \
+            f"verify of sequence {s} alone differs from its batch row"
