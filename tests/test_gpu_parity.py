@@ -707,6 +707,30 @@ def test_state_copy_gather_scatter(dims):
     assert torch.equal(dst2, src_s)
 
 
+def test_state_zero_rows_and_pools():
+    """The state zero: rows idx[i] of both pools, of the state pool alone and of the tail pool alone, and
+    every row when idx is NULL; rows not named keep their bits."""
+    dims = NEXT
+    _say("state zero")
+    d = desc_of(dims)
+    rng = np.random.default_rng(11)
+    S, T = random_state(rng, dims, 9)
+    idx = np.array([7, 2, 4], np.int32)
+    others = np.setdiff1d(np.arange(9), idx)
+    for which in ("both", "state", "tail"):
+        sp, tp = f32(S), act(T, dims)
+        gdn.state_zero(d, sp if which != "tail" else None, tp if which != "state" else None, i32(idx), 3)
+        torch.cuda.synchronize()
+        zs, zt = which != "tail", which != "state"
+        assert int(torch.count_nonzero(sp[idx.tolist()])) == 0 if zs else torch.equal(sp, f32(S))
+        assert int(torch.count_nonzero(tp[idx.tolist()])) == 0 if zt else torch.equal(tp, act(T, dims))
+        assert torch.equal(sp[others.tolist()], f32(S)[others.tolist()]) and torch.equal(tp[others.tolist()], act(T, dims)[others.tolist()])
+    sp, tp = f32(S), act(T, dims)
+    gdn.state_zero(d, sp, tp)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(sp)) == 0 and int(torch.count_nonzero(tp)) == 0
+
+
 def test_timing_session_names_every_launch():
     """The per-launch timing session sees each kernel a call launches, in order, with its time (256
     tokens: calls of up to 128 take whole heads and no norm pass)."""
