@@ -149,7 +149,7 @@ def _random_shape(seed):
     return dims, B, L, lens
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(40))
 def test_prefill_random_shapes(seed):
     """Seeded random shapes and ragged calls through prefill (both paths where the fused one is built),
     from a non-zero state and tail, against the oracle."""
@@ -158,7 +158,7 @@ def test_prefill_random_shapes(seed):
     _prefill_case(dims, 50 + seed, B, L, lens, state_std=0.05, tail_rand=True, paths=paths)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(24))
 def test_decode_random_shapes(seed):
     """The same random shapes through decode, from saved states, against the oracle."""
     dims, B, _, _ = _random_shape(seed)
@@ -177,7 +177,7 @@ def test_decode_random_shapes(seed):
     np.testing.assert_array_equal(host(tp), ref["tail"].astype(np.float32))
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(24))
 def test_verify_paths_random_shapes(seed):
     """The random shapes through tree verify: 1-3 paths of 1+K tokens (K from 1 to 4) per sequence from
     permuted pool rows, fp32 outputs at the flat bound and every checkpoint against the oracle, the pool
