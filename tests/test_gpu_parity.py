@@ -158,6 +158,31 @@ def test_prefill_random_shapes(seed):
     _prefill_case(dims, 50 + seed, B, L, lens, state_std=0.05, tail_rand=True, paths=paths)
 
 
+def _random_long_shape(seed):
+    """A seeded longer call: 1-16 key heads, GQA ratio 1-4, head dims from {32, 64, 128}, bf16 or fp32,
+    1-6 sequences of 300-4096 tokens (ragged, some empty), bounded so the oracle stays in seconds."""
+    r = np.random.default_rng(5000 + seed)
+    n_k, d_k = int(r.choice([1, 2, 4, 8, 16])), int(r.choice([32, 64, 128]))
+    d_v = d_k if r.random() < 0.6 else int(r.choice([32, 64, 128]))
+    dims = LayerDims(n_k=n_k, n_v=n_k * int(r.integers(1, 5)), d_k=d_k, d_v=d_v,
+                     act=ACT_F32 if r.random() < 0.2 else ACT_BF16)
+    B, L = int(r.integers(1, 7)), int(r.integers(300, 4097))
+    lens = [int(v) for v in r.integers(0, L + 1, size=B)]
+    lens[int(r.integers(0, B))] = L
+    return dims, B, L, lens
+
+
+@pytest.mark.parametrize("seed", range(14))
+def test_prefill_random_long_shapes(seed):
+    """Seeded longer calls (many chunks, column splits, row-sum exchanges, the fused path at its own unit
+    counts) through prefill on both paths where the fused one is built, against the oracle."""
+    dims, B, L, lens = _random_long_shape(seed)
+    if sum(lens) * dims.n_v * dims.d_k * dims.d_v > 4e9:
+        pytest.skip("beyond the oracle's time bound")
+    paths = BOTH if dims.d_k == dims.d_v == 128 and dims.act == ACT_BF16 else (None,)
+    _prefill_case(dims, 7000 + seed, B, L, lens, state_std=0.05, tail_rand=True, paths=paths)
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_decode_random_shapes(seed):
     """The same random shapes through decode, from saved states, against the oracle."""
