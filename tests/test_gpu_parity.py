@@ -303,6 +303,37 @@ def test_prefill_strong_decays(path):
         np.testing.assert_array_equal(host(tail[s]), ref["tail"][0].astype(np.float32))
 
 
+@pytest.mark.parametrize("dims", [LayerDims(n_k=2, n_v=4, d_k=128, d_v=128), LayerDims(n_k=2, n_v=6, d_k=64, d_v=64, act=ACT_F32),
+                                  LayerDims(n_k=1, n_v=2, d_k=32, d_v=128)])
+@pytest.mark.parametrize("parts", [[0, 0, 1, 1, 1], [0, 144, 22, 16, 8], [42, 129, 1], [2, 81, 89, 119]])
+def test_continuation_tiny_calls(dims, parts):
+    """One sequence cut into calls of 0, 1 or 2 real tokens among longer ones (a call of 0 still passes one
+    padded row), each continuing from the last: the outputs, the final state and the conv tail match the
+    oracle's single pass (calls shorter than the conv tail keep its older rows)."""
+    total = sum(parts)
+    _say(f"continuation tiny calls parts={parts} dims={dims}")
+    w, x, rng = make_layer(90, dims, 1, total)
+    H0, t0 = random_state(rng, dims, 1)
+    ref = oracle.layer_forward(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, None, t0, H0)
+    d, W = desc_of(dims, out_f32=True), weights(w, dims)
+    for path in (BOTH if dims.d_k == dims.d_v == 128 and dims.act == ACT_BF16 else (None,)):
+        st, tail = f32(H0), act(t0, dims)
+        outs, pos = [], 0
+        for n in parts:
+            Lb = max(n, 1)
+            seg = [np.concatenate([a[:, pos:pos + n], np.zeros((1, Lb - n, a.shape[2]), np.float32)], 1)
+                   for a in (x.mixed, x.z, x.a, x.b)]
+            out = torch.zeros(1, Lb, dims.value_dim, dtype=torch.float32, device="cuda")
+            with prefill_path(path):
+                gdn.prefill_chunk(d, W, *[act(a, dims) for a in seg], i32([n]), tail, st, out)
+            torch.cuda.synchronize()
+            outs.append(host(out[0, :n]))
+            pos += n
+        assert_out_flat(np.concatenate(outs, 0), ref["out"][0], f"continued out (path {path})")
+        assert_state_close(host(st[0]), ref["H"][0], f"continued state (path {path})")
+        np.testing.assert_array_equal(host(tail[0]), ref["tail"][0].astype(np.float32))
+
+
 def test_continuation_equals_single_pass():
     """A 32768-token prompt in bucketed chunks (real lengths drawn inside each bucket, padded with
     g = beta = 0), each continuing from the saved fp32 state and conv tail, against the oracle's single
