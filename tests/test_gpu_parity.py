@@ -518,6 +518,43 @@ def test_verify_paths_full_size_sampled():
         np.testing.assert_array_equal(host(ck_t[s]), ref["ckpt_tail"][0].astype(np.float32))
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_verify_random_shapes_any_length(seed):
+    """Seeded shapes through verify with 1 to 9 tokens per sequence (1-64 sequences, permuted pool rows):
+    outputs and every checkpoint against the oracle, and bitwise equal to that many decode steps."""
+    r = np.random.default_rng(11000 + seed)
+    n_k, d_k = int(r.choice([1, 2, 4, 16])), int(r.choice([32, 64, 128]))
+    d_v = d_k if r.random() < 0.6 else int(r.choice([32, 64, 128]))
+    dims = LayerDims(n_k=n_k, n_v=n_k * int(r.integers(1, 5)), d_k=d_k, d_v=d_v,
+                     act=ACT_F32 if r.random() < 0.25 else ACT_BF16)
+    B, T = int(r.integers(1, 65)), int(r.integers(1, 10))
+    _say(f"verify random seed={seed} B={B} T={T} dims={dims}")
+    w, _, rng = make_layer(11500 + seed, dims, 1, 1)
+    H0, T0 = random_state(rng, dims, B)
+    x = _decode_inputs(dims, rng, B, T)
+    npool = B + int(r.integers(0, 5))
+    slots = rng.permutation(npool)[:B].astype(np.int32)
+    poolH = np.zeros(dims.state_shape(npool), np.float32)
+    poolT = np.zeros(dims.tail_shape(npool), np.float32)
+    poolH[slots], poolT[slots] = H0, T0
+    sp, tp = f32(poolH), act(poolT, dims)
+    d, W = desc_of(dims, True), weights(w, dims)
+    ins = [act(a, dims) for a in (x.mixed, x.z, x.a, x.b)]
+    ck_s, ck_t, out = gdn.verify_with_checkpoints(d, W, *ins, i32(slots), tp, sp)
+    torch.cuda.synchronize()
+    ref = oracle.verify(oracle.Dims.of(dims), w, x.mixed, x.z, x.a, x.b, T0, H0)
+    assert_out_flat(host(out), ref["out"], "verify fp32 out")
+    cks = host(ck_s)
+    for i in range(T):
+        assert_state_close(cks[:, i], ref["ckpt_H"][:, i], f"checkpoint {i}")
+    np.testing.assert_array_equal(host(ck_t), ref["ckpt_tail"].astype(np.float32))
+    sl = torch.as_tensor(slots, device="cuda").long()
+    for i in range(T):
+        o = gdn.decode_step(d, W, *[a[:, i].contiguous() for a in ins], i32(slots), tp, sp)
+        torch.cuda.synchronize()
+        assert torch.equal(sp[sl], ck_s[:, i]) and torch.equal(tp[sl], ck_t[:, i]) and torch.equal(o, out[:, i])
+
+
 def test_verify_checkpoints_and_commit():
     """Verify batch: 64 sequences x (1+4) tokens with per-token checkpoints; accept with m ~ U{0..4};
     restore the checkpoint; compare with the oracle and, bitwise, with repeated GPU decode."""
