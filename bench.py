@@ -506,7 +506,8 @@ def bench_prefix_cache(torch, gdn, args):
 def bench_spec_loop(torch, gdn, args):
     """The speculative-decoding loop (verify + accept + commit per step, the host reading m back each
     step) over 64 sequences with K = 4 and drafts that match the synthetic verifier with probability 0.7,
-    committing verify checkpoints directly and, for comparison, replaying the accepted prefix."""
+    committing verify checkpoints directly, committing them by row index (one copy back into the pool at
+    the end, timed), and, for comparison, replaying the accepted prefix."""
     from gated_delta_rule_44_amd import spec
     from gdn_inputs import NEXT, SpecStream, make_layer, random_state
     H = _dev(torch, gdn)
@@ -518,7 +519,7 @@ def bench_spec_loop(torch, gdn, args):
     tab = [act(f, dims)[0] for f in (table.mixed, table.z, table.a, table.b)]
     S0, tail0 = random_state(rng, dims, B)
     res = {}
-    for mode in ("direct", "replay"):
+    for mode in ("direct", "remap", "replay"):
         sp, tp = f32(S0), act(tail0, dims)
         loop = spec.SpecDecodeLoop(d, W, tab, K, np.arange(B), sp, tp, mode=mode)
         stream = SpecStream(np.random.default_rng(9), B, 8 * steps * (K + 1), vocab, 0.7)
@@ -529,6 +530,7 @@ def bench_spec_loop(torch, gdn, args):
         t0 = time.perf_counter()
         for _ in range(steps):
             stream.advance(loop.step(*stream.draw(K))[0])
+        loop.finish()
         torch.cuda.synchronize()
         sec = time.perf_counter() - t0
         res[mode] = {"tokens_per_s": loop.stats.tokens / sec, "ms_per_step": sec / steps * 1e3,

@@ -5,7 +5,10 @@ K drafts through gdn_verify_with_checkpoints (the pool is only read), measures t
 with gdn_accept, and commits directly: the checkpoint after token m is copied into the pool
 (gdn_state_copy). The fallback the page keeps for a cache without checkpoints replays the accepted
 prefix instead, one gdn_decode_step per token; verify checkpoints are bitwise repeated decode steps,
-so both end in the same pool bits. Drafts and the verifier's greedy predictions come from the caller
+so both end in the same pool bits. A third mode commits without a copy: the checkpoints of a step go
+to rows of their own (two sets of rows, used in turn, so that a step reads the rows the previous one
+wrote and writes the others), the commit only moves each sequence's row index to its accepted
+checkpoint, and finish() copies the current states back into the caller's pool rows. Drafts and the verifier's greedy predictions come from the caller
 (the layer has no LM head); token ids pick rows of the caller's table of projected inputs. The bridge
 (the "uni_engine.py" page's _bridge) copies the fixed-size recurrent state records from one pool to
 another. Every GPU step is a libgdn call; this module only orders them and keeps the counts.
@@ -81,10 +84,11 @@ class LoopStats:
 class SpecDecodeLoop:
     """B sequences in pool rows `slots`, K drafts per step. table: (mixed, z, a, b) projected inputs per
     token id ([V, C_ch], [V, n_v*d_v], [V, n_v], [V, n_v] on the GPU). mode "direct" commits verify
-    checkpoints; "replay" decodes the accepted prefix again."""
+    checkpoints; "replay" decodes the accepted prefix again; "remap" commits by row index (call finish()
+    before reading the caller's pool)."""
 
     def __init__(self, desc: GdnDesc, w: GdnWeights, table, K: int, slots, state_pool, tail_pool, mode="direct"):
-        if mode not in ("direct", "replay"):
+        if mode not in ("direct", "replay", "remap"):
             raise ValueError(f"mode {mode!r}")
         self.desc, self.w, self.table, self.K, self.mode = desc, w, table, int(K), mode
         self.state_pool, self.tail_pool = state_pool, tail_pool
@@ -92,10 +96,20 @@ class SpecDecodeLoop:
         self.B = self.slots.numel()
         T = self.K + 1
         dev = state_pool.device
-        self.ck_s = torch.empty(self.B, T, desc.n_v, desc.d_k, desc.d_v, dtype=torch.float32, device=dev)
-        self.ck_t = torch.empty(self.B, T, desc.kc, desc.conv_dim, dtype=desc.act, device=dev)
+        self.ck_shape = ((self.B, T, desc.n_v, desc.d_k, desc.d_v), (self.B, T, desc.kc, desc.conv_dim))
+        if mode != "remap":
+            self.ck_s = torch.empty(self.ck_shape[0], dtype=torch.float32, device=dev)
+            self.ck_t = torch.empty(self.ck_shape[1], dtype=desc.act, device=dev)
         self.out = torch.empty(self.B, T, desc.n_v * desc.d_v, dtype=desc.act, device=dev)
         self.stats = LoopStats(self.K, self.B)
+        # remap: the rows the sequences' states are in (None: the caller's pool at `slots`), and the two
+        # sets of checkpoint rows
+        self.cur = None
+        self.region = 0
+        if mode == "remap":
+            self.rows = [(torch.empty(self.B * T, desc.n_v, desc.d_k, desc.d_v, dtype=torch.float32, device=dev),
+                          torch.empty(self.B * T, desc.kc, desc.conv_dim, dtype=desc.act, device=dev))
+                         for _ in range(2)]
 
     def _inputs(self, ids: torch.Tensor):
         return [t[ids.long()].contiguous() for t in self.table]
@@ -109,8 +123,14 @@ class SpecDecodeLoop:
         ids = torch.as_tensor(np.concatenate([np.asarray(x, np.int32)[:, None], np.asarray(drafts, np.int32)], 1),
                               device=dev)
         mx, zz, aa, bb = self._inputs(ids)
-        verify_with_checkpoints(d, self.w, mx, zz, aa, bb, self.slots, self.tail_pool, self.state_pool, self.ck_s,
-                                self.ck_t, self.out)
+        if self.mode == "remap":
+            src_s, src_t, src_idx = self.cur if self.cur is not None else (self.state_pool, self.tail_pool, self.slots)
+            dst_s, dst_t = self.rows[self.region]
+            verify_with_checkpoints(d, self.w, mx, zz, aa, bb, src_idx, src_t, src_s, dst_s.view(self.ck_shape[0]),
+                                    dst_t.view(self.ck_shape[1]), self.out)
+        else:
+            verify_with_checkpoints(d, self.w, mx, zz, aa, bb, self.slots, self.tail_pool, self.state_pool, self.ck_s,
+                                    self.ck_t, self.out)
         dr = torch.as_tensor(np.asarray(drafts, np.int32), device=dev)
         pr = torch.as_tensor(np.asarray(preds, np.int32), device=dev)
         m, em, _, ci = accept(dr, pr)
@@ -118,6 +138,11 @@ class SpecDecodeLoop:
         st = self.stats
         if self.mode == "direct":
             state_copy(d, self.state_pool, self.tail_pool, self.slots, self.ck_s, self.ck_t, ci, B)
+            st.direct_commits += 1
+        elif self.mode == "remap":
+            # sequence b's state is now checkpoint row b (1+K) + m_b of this step's rows
+            self.cur = (dst_s, dst_t, ci)
+            self.region ^= 1
             st.direct_commits += 1
         else:
             # tokens 0 .. m_b of each sequence again, one decode step per position for the sequences that
@@ -140,3 +165,11 @@ class SpecDecodeLoop:
         for v in m_h:
             st.accept_hist[int(v)] += 1
         return m_h, em_h, self.out
+
+    def finish(self):
+        """remap: copy every sequence's current state into its row of the caller's pool (a no-op otherwise,
+        and after the copy the loop reads the caller's pool again)"""
+        if self.cur is not None:
+            src_s, src_t, src_idx = self.cur
+            state_copy(self.desc, self.state_pool, self.tail_pool, self.slots, src_s, src_t, src_idx, self.B)
+            self.cur = None

@@ -1,5 +1,6 @@
 """The speculative-decoding control loop (gated_delta_rule_44_amd.spec) on the GPU: direct commit from
-verify checkpoints and the replay fallback end in the same pool bits and emit the same tokens; the pool
+verify checkpoints, the replay fallback and the commit by row index (then finish()) end in the same pool
+bits and emit the same tokens; the pool
 after the loop equals the oracle's recurrence over the tokens the loop consumed; the bridge copies pools."""
 import numpy as np
 import pytest
@@ -29,12 +30,12 @@ def test_spec_loop_direct_equals_replay_and_oracle():
     d = desc_of(dims)
     W = weights(w, dims)
     tab = [act(f, dims)[0] for f in (table.mixed, table.z, table.a, table.b)]
-    pools = {mode: (f32(H0), act(T0, dims)) for mode in ("direct", "replay")}
+    pools = {mode: (f32(H0), act(T0, dims)) for mode in ("direct", "replay", "remap")}
     loops = {mode: spec.SpecDecodeLoop(d, W, tab, K, np.arange(B), *pools[mode], mode=mode) for mode in pools}
     streams = {mode: SpecStream(np.random.default_rng(7), B, 400, vocab, 0.6) for mode in pools}
     for _ in range(steps):
         res = {}
-        for mode in ("direct", "replay"):
+        for mode in ("direct", "replay", "remap"):
             x, dr, pr = streams[mode].draw(K)
             res[mode] = loops[mode].step(x, dr, pr)
             m, em, _ = res[mode]
@@ -42,10 +43,15 @@ def test_spec_loop_direct_equals_replay_and_oracle():
                 p0 = streams[mode].pos[b]
                 np.testing.assert_array_equal(em[b, :m[b] + 1], streams[mode].truth[b, p0 + 1:p0 + m[b] + 2])
             streams[mode].advance(m)
-        np.testing.assert_array_equal(res["direct"][0], res["replay"][0])
-        assert torch.equal(res["direct"][2], res["replay"][2])
+        for mode in ("replay", "remap"):
+            np.testing.assert_array_equal(res["direct"][0], res[mode][0])
+            assert torch.equal(res["direct"][2], res[mode][2])
     torch.cuda.synchronize()
-    assert torch.equal(pools["direct"][0], pools["replay"][0]) and torch.equal(pools["direct"][1], pools["replay"][1])
+    assert torch.equal(pools["remap"][0], f32(H0)), "remap wrote the caller's pool before finish()"
+    loops["remap"].finish()
+    torch.cuda.synchronize()
+    for mode in ("replay", "remap"):
+        assert torch.equal(pools["direct"][0], pools[mode][0]) and torch.equal(pools["direct"][1], pools[mode][1]), mode
     st = loops["direct"].stats
     pos = streams["direct"].pos
     assert sum(st.accept_hist) == steps * B and st.tokens == int(pos.sum()) and st.direct_commits == steps
